@@ -1,0 +1,145 @@
+/*
+ * Q-Delta fp64 CPU oracle.  TEST INFRASTRUCTURE ONLY: the tests, the smoke
+ * check and the benchmark's CPU-baseline leg load this library; the product
+ * path never does.  It shares no code, header or helper with the HIP library.
+ *
+ * What it computes: the token-by-token gated Q-Delta recurrence, exactly as the
+ * Q-Delta reading notes state it (page "Q-Delta: Beyond Key-Value Associative
+ * State Evolution" reading notes, section 2.4 "Q-Delta 的逐步计算", the boxed
+ * gated update and its teaching pseudo-code):
+ *
+ *     x_t       = k_t + lambda_t q_t            (mixed read direction, §2.1 table)
+ *     S_prior   = alpha_t S_{t-1}               (decay first)
+ *     err_t     = v_t - S_prior x_t             (error read along x_t)
+ *     S_t       = S_prior + beta_t err_t k_t^T  (rank-one write along k_t)
+ *     o_t       = S_t q_t                       (read-out uses the updated state)
+ *
+ * State convention (same page, §2.1 table): S is d_v x d_k, so the prediction
+ * along a key is S k and the read-out is S q.  In memory a state is row-major
+ * [d_v][d_k] (row = value index, column = key index).
+ *
+ * The transition acts on S from the right (S_prior (I - beta x k^T)), so each row
+ * of S evolves on its own: row i only sees v_t[i].  The loops below therefore run
+ * the row loop outside the time loop and hand independent rows to OpenMP
+ * threads.  Within a row the arithmetic is the pseudo-code above, step for step,
+ * in fp64, with no reassociation beyond plain left-to-right dot products.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see build_oracle.py).
+ */
+#include <stddef.h>
+#include <string.h>
+#include <omp.h>
+
+/* Advance one row s (length dk) by one token.
+ *   read  : direction the error is read along (x_t for Q-Delta)
+ *   write : direction the correction is written along (k_t for Q-Delta)
+ * Returns the post-update read-out s . q (the row's entry of o_t = S_t q_t). */
+static double advance_row(double *s, const double *read, const double *write,
+                          const double *q, double v_i, double alpha, double beta,
+                          int dk)
+{
+    int j;
+    double pred = 0.0, err, out = 0.0;
+    for (j = 0; j < dk; ++j) s[j] = alpha * s[j];          /* S_prior = alpha S   */
+    for (j = 0; j < dk; ++j) pred += s[j] * read[j];       /* (S_prior x)_i       */
+    err = v_i - pred;                                      /* error_i             */
+    for (j = 0; j < dk; ++j) s[j] = s[j] + beta * err * write[j]; /* + beta err k^T */
+    for (j = 0; j < dk; ++j) out += s[j] * q[j];           /* o_i = (S_t q)_i     */
+    return out;
+}
+
+/* One step with an explicit read direction and write direction, for a single
+ * state S [dv][dk] (updated in place) and one token.  o (length dv) may be NULL.
+ * Q-Delta is the case read = k + lambda q, write = k.  The general form lets a
+ * test drive the step the QED reading notes' two-dimensional example describes
+ * (page "The Query Knows What to Forget" reading notes, §2.4), where the read
+ * direction differs from the write direction. */
+void oracle_step_rw(double *S, const double *read, const double *write,
+                    const double *v, const double *q, double alpha, double beta,
+                    double *o, int dk, int dv)
+{
+    int i;
+    for (i = 0; i < dv; ++i) {
+        double out = advance_row(S + (size_t)i * dk, read, write, q, v[i], alpha, beta, dk);
+        if (o) o[i] = out;
+    }
+}
+
+/* Full layer forward by the recurrence.
+ *   q, k   : [B][T][H][dk]          v, o : [B][T][H][dv]
+ *   alpha, beta, lam : [B][T][H]    (alpha NULL means alpha == 1, lam NULL means lambda == 0)
+ *   S0     : [B][H][dv][dk] or NULL (zero initial state)
+ *   S_T    : [B][H][dv][dk] output, required; also used as the working state
+ *   o      : may be NULL (state only)
+ *   nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_qdelta_fwd(const double *q, const double *k, const double *v,
+                      const double *alpha, const double *beta, const double *lam,
+                      const double *S0, double *o, double *S_T,
+                      int B, int T, int H, int dk, int dv, int nthreads)
+{
+    long long unit, n_units;
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1 || dk > 1024) return -1;
+    if (!S_T) return -1;
+    if ((long long)B * T * H > 0 && (!q || !k || !v || !beta)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    n_units = (long long)B * H * dv;           /* one unit = one row of one (b,h) state */
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nthreads)
+    for (unit = 0; unit < n_units; ++unit) {
+        int b = (int)(unit / ((long long)H * dv));
+        int h = (int)((unit / dv) % H);
+        int i = (int)(unit % dv);
+        double *s = S_T + (((size_t)b * H + h) * dv + i) * dk;
+        double x[1024];
+        int t, j;
+        if (S0) memcpy(s, S0 + (((size_t)b * H + h) * dv + i) * dk, sizeof(double) * dk);
+        else memset(s, 0, sizeof(double) * dk);
+        for (t = 0; t < T; ++t) {
+            size_t tok = ((size_t)b * T + t) * H + h;      /* token-head index */
+            const double *qt = q + tok * dk;
+            const double *kt = k + tok * dk;
+            double a = alpha ? alpha[tok] : 1.0;
+            double be = beta[tok];
+            double la = lam ? lam[tok] : 0.0;
+            double out;
+            for (j = 0; j < dk; ++j) x[j] = kt[j] + la * qt[j];   /* x_t = k_t + lambda_t q_t */
+            out = advance_row(s, x, kt, qt, v[tok * dv + i], a, be, dk);
+            if (o) o[tok * dv + i] = out;
+        }
+    }
+    return 0;
+}
+
+/* One recurrent decode step for N independent sequences x H heads.
+ *   q, k : [N][H][dk]   v, o : [N][H][dv]   alpha, beta, lam : [N][H]
+ *   S    : [N][H][dv][dk], updated in place.   o may be NULL.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_qdelta_step(const double *q, const double *k, const double *v,
+                       const double *alpha, const double *beta, const double *lam,
+                       double *S, double *o, int N, int H, int dk, int dv, int nthreads)
+{
+    long long unit, n_units;
+    if (N < 0 || H < 0 || dk < 1 || dv < 1 || dk > 1024) return -1;
+    if ((long long)N * H > 0 && (!q || !k || !v || !beta || !S)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    n_units = (long long)N * H * dv;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (unit = 0; unit < n_units; ++unit) {
+        size_t nh = (size_t)(unit / dv);
+        int i = (int)(unit % dv);
+        const double *qt = q + nh * dk;
+        const double *kt = k + nh * dk;
+        double a = alpha ? alpha[nh] : 1.0;
+        double la = lam ? lam[nh] : 0.0;
+        double x[1024], out;
+        int j;
+        for (j = 0; j < dk; ++j) x[j] = kt[j] + la * qt[j];
+        out = advance_row(S + (nh * dv + i) * dk, x, kt, qt, v[nh * dv + i], a, beta[nh], dk);
+        if (o) o[nh * dv + i] = out;
+    }
+    return 0;
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }

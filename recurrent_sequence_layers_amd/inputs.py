@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the Q-Delta layer (shared by tests, smoke and bench).
+
+This module draws random numbers and shapes them into the workloads; it holds
+none of the layer's arithmetic.  Both the HIP path and the CPU oracle consume
+exactly the tensors returned here (the oracle takes fp64 upcasts of the very
+values handed to the GPU, after any bf16 rounding).
+
+Recipe (one torch generator per call, draws in this order):
+  q, k ~ N(0, 1), each L2-normalised over the key dimension per (token, head)
+  v    ~ N(0, 1)
+  beta   = sigmoid(N(0, 1))
+  alpha  = exp(-softplus(N(-4, 1)))          in (0, 1), typically about 0.98
+  lambda = sigmoid(N(0, 1))
+  S0     ~ N(0, s0_std) when requested (s0_std is a standard deviation)
+then q, k, v are cast to the requested dtype (round to nearest even for bf16);
+gates and states stay fp32.  These stand in for the language-model activations
+the pages train on; no dataset is involved.
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+# Workloads named by what they are, with their sizes.
+WORKLOADS = {
+    "tiny_fp32": dict(B=1, T=256, H=1, dk=64, dv=64, C=64, dtype="f32"),
+    "layer_1p3b_bf16": dict(B=8, T=4096, H=16, dk=128, dv=128, C=64, dtype="bf16"),
+    "gdn_bf16": dict(B=8, T=4096, H=16, dk=128, dv=128, C=64, dtype="bf16", lam="zero"),
+    "deltanet_bf16": dict(B=8, T=4096, H=16, dk=128, dv=128, C=64, dtype="bf16",
+                          lam="zero", alpha="one"),
+    "long_64k_bf16": dict(B=1, T=65536, H=16, dk=128, dv=128, C=64, dtype="bf16", s0_std=0.02),
+    "decode_256x16": dict(N=256, H=16, dk=128, dv=128, dtype="bf16", steps=1000, s0_std=0.02),
+}
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16,
+       torch.float32: torch.float32, torch.bfloat16: torch.bfloat16}
+
+
+def torch_dtype(name):
+    return _DT[name]
+
+
+@dataclass
+class ChunkInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    alpha: Optional[torch.Tensor]
+    beta: torch.Tensor
+    lam: Optional[torch.Tensor]
+    S0: Optional[torch.Tensor]
+    meta: dict = field(default_factory=dict)
+
+
+def _generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _unit(x: torch.Tensor) -> torch.Tensor:
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="random",
+                 s0_std=None, device="cpu", gates_as_none=False) -> ChunkInputs:
+    """Inputs for the layer forward, layout q,k [B,T,H,dk], v [B,T,H,dv],
+    gates [B,T,H], S0 [B,H,dv,dk].
+
+    lam:   "random" (sigmoid draw), "zero", "one", or a float constant.
+    alpha: "random" (exp(-softplus) draw) or "one".
+    gates_as_none: return None for alpha == 1 / lambda == 0 (the library's way of
+    selecting the specialised instances); the tensors are still drawn so that the
+    other draws do not shift."""
+    dt = _DT[dtype]
+    g = _generator(seed, device)
+    f = dict(generator=g, device=device, dtype=torch.float32)
+    q = torch.randn(B, T, H, dk, **f)
+    k = torch.randn(B, T, H, dk, **f)
+    v = torch.randn(B, T, H, dv, **f)
+    beta_logit = torch.randn(B, T, H, **f)
+    alpha_logit = torch.randn(B, T, H, **f) - 4.0
+    lam_logit = torch.randn(B, T, H, **f)
+    S0 = (torch.randn(B, H, dv, dk, **f) * float(s0_std)) if s0_std else None
+
+    q = _unit(q).to(dt).contiguous()
+    k = _unit(k).to(dt).contiguous()
+    v = v.to(dt).contiguous()
+    beta = torch.sigmoid(beta_logit).contiguous()
+    if alpha == "random":
+        alpha_t = torch.exp(-torch.nn.functional.softplus(alpha_logit)).contiguous()
+    elif alpha == "one":
+        alpha_t = None if gates_as_none else torch.ones(B, T, H, device=device)
+    else:
+        raise ValueError(alpha)
+    if lam == "random":
+        lam_t = torch.sigmoid(lam_logit).contiguous()
+    elif lam == "zero":
+        lam_t = None if gates_as_none else torch.zeros(B, T, H, device=device)
+    elif lam == "one":
+        lam_t = torch.ones(B, T, H, device=device)
+    else:
+        lam_t = torch.full((B, T, H), float(lam), device=device)
+    return ChunkInputs(q, k, v, alpha_t, beta, lam_t, S0,
+                       dict(B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, seed=seed))
+
+
+def workload_inputs(name: str, seed: int, device="cpu", gates_as_none=False) -> ChunkInputs:
+    w = dict(WORKLOADS[name])
+    return chunk_inputs(w["B"], w["T"], w["H"], w["dk"], w["dv"], w["dtype"], seed,
+                        lam=w.get("lam", "random"), alpha=w.get("alpha", "random"),
+                        s0_std=w.get("s0_std"), device=device, gates_as_none=gates_as_none)
+
+
+def decode_state(N, H, dk, dv, s0_std=0.02, seed=0, device="cpu") -> torch.Tensor:
+    """Resident fp32 decode state S ~ N(0, s0_std), layout [N,H,dv,dk]."""
+    g = _generator(seed, device)
+    return (torch.randn(N, H, dv, dk, generator=g, device=device) * float(s0_std)).contiguous()
+
+
+def decode_tokens(steps, N, H, dk, dv, dtype="bf16", seed=0, device="cpu"):
+    """Per-step decode inputs for `steps` consecutive tokens: q,k [steps,N,H,dk],
+    v [steps,N,H,dv], alpha, beta, lam [steps,N,H].  Same distributions as
+    ``chunk_inputs``."""
+    dt = _DT[dtype]
+    g = _generator(seed, device)
+    f = dict(generator=g, device=device, dtype=torch.float32)
+    q = _unit(torch.randn(steps, N, H, dk, **f)).to(dt).contiguous()
+    k = _unit(torch.randn(steps, N, H, dk, **f)).to(dt).contiguous()
+    v = torch.randn(steps, N, H, dv, **f).to(dt).contiguous()
+    beta = torch.sigmoid(torch.randn(steps, N, H, **f)).contiguous()
+    alpha = torch.exp(-torch.nn.functional.softplus(torch.randn(steps, N, H, **f) - 4.0)).contiguous()
+    lam = torch.sigmoid(torch.randn(steps, N, H, **f)).contiguous()
+    return q, k, v, alpha, beta, lam

@@ -1,0 +1,109 @@
+"""The reassociated chunk algebra the HIP kernels implement, checked in fp64
+against the recurrence oracle before (and independently of) any GPU code.
+
+Starting from the Q-Delta notes' chunk form (§2.6):
+  Z = U~ - D_g W S^T,  W = (I+L)^-1 B X,  U~ = (I+L_g)^-1 B V,
+  O = D_g Q S^T + (H o Q K^T) Z,  S_out = g_C S + Z^T K_out,
+the kernels use these exact rewrites:
+  * one solve:  I + L_g = D_g (I + L) D_g^-1, so (I + L_g)^-1 = H o (I + L)^-1;
+  * X K^T = K K^T + diag(lambda) Q K^T, and W S^T = T B (K S^T + diag(lambda) Q S^T),
+    so the state is read through K S^T and Q S^T only (Q S^T is needed for O anyway);
+  * log-space decay: g = cumsum(log alpha), every factor exp(g_r - g_c) <= 1;
+  * a short last chunk is padded with alpha = 1, beta = 0, q = k = v = 0 (an
+    exact no-op token);
+  * T = (I + L)^-1 by 16 x 16 diagonal blocks plus block doubling.
+This file restates those steps in numpy; it shares nothing with the kernels.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def blocked_unit_lower_inverse(L, nb=16):
+    """(I + L)^-1 for strictly lower L: diagonal blocks by forward substitution,
+    then doubling: [[A,0],[C,D]]^-1 = [[A^-1, 0], [-D^-1 C A^-1, D^-1]]."""
+    n = L.shape[0]
+    T = np.zeros_like(L)
+    for b0 in range(0, n, nb):
+        blk = L[b0:b0 + nb, b0:b0 + nb]
+        m = blk.shape[0]
+        Tb = np.zeros((m, m))
+        for c in range(m):               # column c, right-looking
+            acc = np.zeros(m); acc[c] = 1.0
+            for j in range(m):
+                t = acc[j]
+                Tb[j, c] = t
+                acc[j + 1:] -= blk[j + 1:, j] * t
+        T[b0:b0 + nb, b0:b0 + nb] = Tb
+    w = nb
+    while w < n:
+        for a0 in range(0, n, 2 * w):
+            c0 = a0 + w
+            if c0 >= n:
+                continue
+            c1 = min(c0 + w, n)
+            # T[c0:c1, a0:c0] = -T_dd @ L[c0:c1, a0:c0] @ T_aa
+            T[c0:c1, a0:c0] = -T[c0:c1, c0:c1] @ (L[c0:c1, a0:c0] @ T[a0:c0, a0:c0])
+        w *= 2
+    return T
+
+
+def kernel_form_fwd(q, k, v, alpha, beta, lam, S0, C):
+    B, Tn, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, Tn, H, dv)); S_T = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            ST = np.zeros((dk, dv)) if S0 is None else S0[b, h].T.copy()   # S^T held
+            for t0 in range(0, Tn, C):
+                n = min(C, Tn - t0)
+                Q = np.zeros((C, dk)); K = np.zeros((C, dk)); V = np.zeros((C, dv))
+                la = np.zeros(C); be = np.zeros(C); la_ = np.zeros(C); lg = np.zeros(C)
+                Q[:n] = q[b, t0:t0 + n, h]; K[:n] = k[b, t0:t0 + n, h]; V[:n] = v[b, t0:t0 + n, h]
+                be[:n] = beta[b, t0:t0 + n, h]
+                la[:n] = lam[b, t0:t0 + n, h]
+                lg[:n] = np.log(alpha[b, t0:t0 + n, h])
+                g = np.cumsum(lg)
+                QK = Q @ K.T; KK = K @ K.T
+                XK = KK + la[:, None] * QK
+                L = np.tril(be[:, None] * XK, -1)
+                T = blocked_unit_lower_inverse(L)
+                decay = np.tril(np.exp(g[:, None] - g[None, :]))
+                M1 = decay * T * be[None, :]
+                M2n = -(np.exp(g)[:, None] * T) * be[None, :]
+                A = decay * QK
+                U = M1 @ V
+                PK = K @ ST; PQ = Q @ ST
+                Y = PK + la[:, None] * PQ
+                Z = U + M2n @ Y
+                O = np.exp(g)[:, None] * PQ + A @ Z
+                ST = np.exp(g[-1]) * ST + K.T @ (np.exp(g[-1] - g)[:, None] * Z)
+                o[b, t0:t0 + n, h] = O[:n]
+            S_T[b, h] = ST.T
+    return o, S_T
+
+
+def test_blocked_inverse_matches_dense():
+    r = np.random.default_rng(0)
+    for n in (16, 32, 48, 64):
+        L = np.tril(0.3 * r.standard_normal((n, n)), -1)
+        np.testing.assert_allclose(blocked_unit_lower_inverse(L), np.linalg.inv(np.eye(n) + L),
+                                   atol=1e-11)
+
+
+@pytest.mark.parametrize("T,C,dk,dv", [(64, 64, 16, 16), (100, 64, 32, 16), (75, 32, 16, 32),
+                                       (3, 64, 16, 16), (130, 16, 16, 8)])
+def test_kernel_form_matches_recurrence(T, C, dk, dv):
+    r = np.random.default_rng(T + C)
+    q = r.standard_normal((2, T, 2, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((2, T, 2, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((2, T, 2, dv))
+    beta = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    alpha = np.exp(-np.log1p(np.exp(r.standard_normal((2, T, 2)) - 4.0)))
+    lam = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    S0 = 0.1 * r.standard_normal((2, 2, dv, dk))
+    o_r, S_r = oracle.qdelta_fwd(q, k, v, alpha, beta, lam, S0)
+    o_k, S_k = kernel_form_fwd(q, k, v, alpha, beta, lam, S0, C)
+    np.testing.assert_allclose(o_k, o_r, atol=1e-11)
+    np.testing.assert_allclose(S_k, S_r, atol=1e-11)
