@@ -1,0 +1,115 @@
+/*
+ * qdelta.h -- C ABI of the MI355X (gfx950) Q-Delta layer library, libqdelta.so.
+ *
+ * The library computes the forward pass of the gated Q-Delta linear-attention
+ * layer, defined per (batch b, head h) on the Q-Delta reading notes page
+ * ("Q-Delta: Beyond Key-Value Associative State Evolution"), §2.4, boxed gated
+ * update and read-out:
+ *
+ *     x_t = k_t + lambda_t q_t
+ *     S_t = alpha_t S_{t-1} (I - beta_t x_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * with the state S in R^{d_v x d_k} (§2.1 symbol table).  lambda == 0 gives
+ * Gated DeltaNet and lambda == 0, alpha == 1 gives DeltaNet (same section).
+ *
+ * Memory layouts (all row-major, contiguous, device memory):
+ *     q, k      [B][T][H][d_k]   element type per qd_dtype
+ *     v, o      [B][T][H][d_v]   element type per qd_dtype
+ *     alpha, beta, lambda  [B][T][H]  fp32
+ *     S0, S_T   [B][H][d_v][d_k] fp32  (row = value index, column = key index)
+ * For the decode step the token axis is absent: q, k [N][H][d_k], v, o
+ * [N][H][d_v], gates [N][H], S [N][H][d_v][d_k].
+ *
+ * Ownership and execution: the caller owns every buffer.  All pointers except
+ * `stream` are device pointers.  The library allocates no device memory, keeps no
+ * mutable global state, and enqueues its kernels asynchronously on `stream` (a
+ * hipStream_t; NULL means the default stream); nothing synchronises.  Buffers must
+ * stay valid until the work on `stream` completes.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a
+ * failed check returns a status and enqueues nothing.  A launch failure returns
+ * QD_ERR_HIP.  Device data are not inspected: NaN/Inf propagate, and alpha <= 0
+ * is outside the domain (the kernels take log(alpha)).
+ */
+#ifndef QDELTA_H_
+#define QDELTA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDELTA_ABI_VERSION 1
+
+typedef enum qd_status {
+    QD_OK = 0,
+    QD_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, aliasing not allowed */
+    QD_ERR_UNSUPPORTED = 2,   /* d_k, d_v, C or dtype outside the supported set            */
+    QD_ERR_WORKSPACE = 3,     /* workspace smaller than qdelta_chunk_fwd_workspace_bytes    */
+    QD_ERR_HIP = 4            /* the HIP runtime reported an error at launch                */
+} qd_status;
+
+typedef enum qd_dtype {
+    QD_F32 = 0,               /* q, k, v, o are fp32                                        */
+    QD_BF16 = 1               /* q, k, v, o are bf16 (round-to-nearest-even outputs)        */
+} qd_dtype;
+
+/* Version of this ABI (QDELTA_ABI_VERSION of the header the library was built with). */
+int qdelta_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *qdelta_status_string(int status);
+
+/* Bytes of device workspace qdelta_chunk_fwd needs for these sizes.  The current
+ * kernels keep every intermediate on chip and need none (returns 0); callers
+ * should still query it and pass a buffer of at least this size. */
+size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
+                                        int dtype);
+
+/*
+ * Layer forward in the chunkwise-parallel WY/UT-transform form (Q-Delta reading
+ * notes §2.6: the strictly-lower X K^T interaction, the triangular-solve UT
+ * transform, and the entry-state composition of Z, S_out and O).  The result is
+ * the recurrence above evaluated over T tokens from S0; C only changes rounding.
+ *
+ *   q, k, v, beta   required when B*T*H > 0.
+ *   alpha           NULL means alpha == 1 (selects the no-decay instance).
+ *   lambda          NULL means lambda == 0 (selects the Gated DeltaNet instance).
+ *   S0              NULL means a zero initial state.
+ *   o               required when B*T*H > 0.
+ *   S_T             NULL means the final state is not written.  S_T may equal S0
+ *                   (in-place state update); no other aliasing is allowed.
+ *   B, H, T >= 0 (T == 0 writes S_T = S0, or zeros); d_k, d_v in {64, 128};
+ *   C in {16, 32, 64} (chunk length; a short last chunk is handled exactly);
+ *   dtype one of qd_dtype.
+ *   workspace/ws_bytes: see qdelta_chunk_fwd_workspace_bytes (may be NULL/0
+ *                   when that returns 0).
+ */
+int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, const float *lambda,
+                     const float *S0, void *o, float *S_T,
+                     int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One recurrent decode step (Q-Delta reading notes §2.4: the boxed update for a
+ * single token, with the read-out expanded as
+ * o_t = alpha S_{t-1} q + beta (v - alpha S_{t-1} x)(k^T q)), for N independent
+ * sequences x H heads.  S is read and overwritten in place.
+ *
+ *   q, k, v, beta, S, o   required when N*H > 0.
+ *   alpha NULL means 1, lambda NULL means 0.
+ *   N, H >= 0; d_k, d_v in {64, 128}; dtype one of qd_dtype.
+ */
+int qdelta_step(const void *q, const void *k, const void *v,
+                const float *alpha, const float *beta, const float *lambda,
+                float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
+                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDELTA_H_ */

@@ -1,1 +1,153 @@
-"""Placeholder; the binding is filled in with the HIP library."""
+"""Python binding of libqdelta.so, the gfx950 Q-Delta layer library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind
+the C ABI declared in ``include/qdelta.h``.  PyTorch supplies device memory and the
+current HIP stream.  If the library is not built, the functions raise; there is no
+fallback path.
+
+    qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C=64, o=None, S_T=None)
+        -> (o, S_T)
+    qdelta_step(q, k, v, alpha, beta, lam, S, o=None) -> o        (S updated in place)
+"""
+import ctypes
+import os
+
+from . import inputs  # noqa: F401  (seeded workload generators)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqdelta.so")
+
+QD_F32, QD_BF16 = 0, 1
+_lib = None
+
+
+class QDeltaError(RuntimeError):
+    pass
+
+
+def load_library():
+    """Load libqdelta.so (built in-tree by ``python -m recurrent_sequence_layers_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise QDeltaError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m recurrent_sequence_layers_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qdelta_abi_version.restype = i
+    lib.qdelta_abi_version.argtypes = []
+    lib.qdelta_status_string.restype = ctypes.c_char_p
+    lib.qdelta_status_string.argtypes = [i]
+    lib.qdelta_chunk_fwd_workspace_bytes.restype = sz
+    lib.qdelta_chunk_fwd_workspace_bytes.argtypes = [i] * 7
+    lib.qdelta_chunk_fwd.restype = i
+    lib.qdelta_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
+    lib.qdelta_step.restype = i
+    lib.qdelta_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
+    _lib = lib
+    return lib
+
+
+def qdelta_abi_version() -> int:
+    return load_library().qdelta_abi_version()
+
+
+def qdelta_status_string(status: int) -> str:
+    return load_library().qdelta_status_string(int(status)).decode()
+
+
+def qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:
+    return int(load_library().qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, _dtype_code(dtype)))
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt in (QD_F32, QD_BF16):
+        return dt
+    if dt == torch.float32:
+        return QD_F32
+    if dt == torch.bfloat16:
+        return QD_BF16
+    raise QDeltaError(f"unsupported dtype {dt}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype=None, shape=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise QDeltaError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise QDeltaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise QDeltaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise QDeltaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _raise(rc, fn):
+    if rc != 0:
+        raise QDeltaError(f"{fn}: {qdelta_status_string(rc)} (status {rc})")
+
+
+def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_T=None,
+                     want_state: bool = True, stream=None):
+    """Layer forward, chunkwise WY/UT form.  q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or
+    bf16, same dtype); alpha, beta, lam [B,T,H] fp32 (alpha None means 1, lam None
+    means 0); S0 [B,H,d_v,d_k] fp32 or None.  Returns (o, S_T); S_T is None when
+    want_state is False.  S_T may be passed as S0 for an in-place state update."""
+    import torch
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+        _check(g, name, torch.float32, (B, T, H))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (B, T, H, dv))
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+    code = _dtype_code(dt)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = lib.qdelta_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
+    if ws:
+        raise QDeltaError("workspace-requiring path not wired in the binding")
+    rc = lib.qdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
+                              _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, None, 0,
+                              ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_chunk_fwd")
+    return o, S_T
+
+
+def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None):
+    """One decode step for N sequences x H heads.  q, k [N,H,d_k], v [N,H,d_v];
+    alpha, beta, lam [N,H] fp32 (alpha None means 1, lam None means 0);
+    S [N,H,d_v,d_k] fp32, updated in place.  Returns o [N,H,d_v]."""
+    import torch
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+        _check(g, name, torch.float32, (N, H))
+    _check(S, "S", torch.float32, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (N, H, dv))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.qdelta_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S), _ptr(o),
+                         N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_step")
+    return o

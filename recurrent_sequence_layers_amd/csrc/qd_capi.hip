@@ -1,0 +1,106 @@
+// C ABI of libqdelta.so: host-side argument checks, then kernel dispatch.
+// Every check happens before anything is enqueued; nothing here allocates.
+#include "qdelta.h"
+#include "qd_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int qdelta_abi_version(void) { return QDELTA_ABI_VERSION; }
+
+const char *qdelta_status_string(int status) {
+    switch (status) {
+        case QD_OK: return "ok";
+        case QD_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, misaligned or aliased buffer)";
+        case QD_ERR_UNSUPPORTED: return "unsupported size or dtype (d_k, d_v in {64,128}; C in {16,32,64}; fp32 or bf16)";
+        case QD_ERR_WORKSPACE: return "workspace too small";
+        case QD_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
+    (void)B; (void)T; (void)H; (void)d_k; (void)d_v; (void)C; (void)dtype;
+    return 0;  // the fused kernel keeps every chunk intermediate in LDS
+}
+
+int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, const float *lambda,
+                     const float *S0, void *o, float *S_T,
+                     int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                     void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace;
+    if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
+    if (ws_bytes < qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype)) return QD_ERR_WORKSPACE;
+    const long long bh = static_cast<long long>(B) * H;
+    if (bh == 0) return QD_OK;
+    if (bh * (d_v / 64) > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    const long long ntok = bh * T;
+    if (ntok > 0 && (!q || !k || !v || !beta || !o)) return QD_ERR_INVALID_ARG;
+    // vector loads need 16-byte aligned rows
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(S0) || !aligned16(S_T))
+        return QD_ERR_INVALID_ARG;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t state_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
+    const size_t o_bytes = static_cast<size_t>(ntok) * d_v * es;
+    // outputs must not overlap inputs (S_T == S0 exactly is the allowed in-place case)
+    if (overlaps(o, o_bytes, q, static_cast<size_t>(ntok) * d_k * es) ||
+        overlaps(o, o_bytes, k, static_cast<size_t>(ntok) * d_k * es) ||
+        overlaps(o, o_bytes, v, o_bytes) || overlaps(o, o_bytes, S_T, state_bytes) ||
+        overlaps(o, o_bytes, S0, state_bytes))
+        return QD_ERR_INVALID_ARG;
+    if (S_T && S0 && S_T != S0 && overlaps(S_T, state_bytes, S0, state_bytes)) return QD_ERR_INVALID_ARG;
+
+    qd::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta; a.lam = lambda;
+    a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.B = B; a.T = T; a.H = H; a.dv = d_v;
+    a.n_dvt = d_v / 64;
+    const hipError_t err = qd::launch_chunk_fwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
+int qdelta_step(const void *q, const void *k, const void *v,
+                const float *alpha, const float *beta, const float *lambda,
+                float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
+                void *stream) {
+    if (N < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::step_supported(dtype, d_k, d_v)) return QD_ERR_UNSUPPORTED;
+    const long long nh = static_cast<long long>(N) * H;
+    if (nh == 0) return QD_OK;
+    if (nh > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !beta || !S || !o) return QD_ERR_INVALID_ARG;
+    if (!aligned16(S)) return QD_ERR_INVALID_ARG;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t state_bytes = static_cast<size_t>(nh) * d_v * d_k * 4;
+    const size_t o_bytes = static_cast<size_t>(nh) * d_v * es;
+    if (overlaps(o, o_bytes, S, state_bytes) || overlaps(o, o_bytes, q, static_cast<size_t>(nh) * d_k * es) ||
+        overlaps(o, o_bytes, k, static_cast<size_t>(nh) * d_k * es) || overlaps(o, o_bytes, v, o_bytes) ||
+        overlaps(S, state_bytes, q, static_cast<size_t>(nh) * d_k * es) ||
+        overlaps(S, state_bytes, k, static_cast<size_t>(nh) * d_k * es) || overlaps(S, state_bytes, v, o_bytes))
+        return QD_ERR_INVALID_ARG;
+
+    qd::StepArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta; a.lam = lambda;
+    a.S = S; a.o = o; a.N = N; a.H = H;
+    const hipError_t err = qd::launch_step(dtype, d_k, d_v, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,534 @@
+// Fused chunkwise Q-Delta layer forward for gfx950.
+//
+// One workgroup owns one (batch, head, 64-wide value-column tile) and walks the
+// sequence chunk by chunk, keeping its slice of the state S^T (d_k x 64, fp32) in
+// MFMA accumulator registers for the whole sequence.  Every chunk is read from HBM
+// once (q, k, the v tile, the gates) and its output tile is written once; all
+// chunk intermediates live in LDS.  Per chunk (Q-Delta reading notes §2.6, the
+// chunkwise WY/UT form with entry state):
+//
+//   g     = cumsum(log alpha)                       (log-space decays, all factors <= 1)
+//   QK^T, KK^T on MFMA;  X K^T = K K^T + diag(lambda) Q K^T
+//   L     = strictly-lower(diag(beta) X K^T)
+//   T     = (I + L)^-1      16x16 diagonal blocks by forward substitution, then
+//                           block doubling on MFMA (UT transform, notes Eq. 27)
+//   M1    = (H o T) diag(beta),   M2 = -D_g T diag(beta),   A = H o (Q K^T)
+//   U~    = M1 V                                    ((I + L_g)^-1 B V, using
+//                                                   (I + L_g)^-1 = H o (I + L)^-1)
+//   Z     = U~ + M2 (K S^T + diag(lambda) Q S^T)    (= U~ - D_g W S^T)
+//   O     = D_g Q S^T + A Z
+//   S^T  <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z
+//
+// Waves: four per workgroup; in the state-dependent part wave w owns value columns
+// [16w, 16w + 16) of the tile, so S^T, K S^T, Q S^T, Z and O for those columns stay
+// in its registers and feed one another as MFMA operands without LDS round trips.
+// The next chunk's raw inputs are loaded into registers while the current chunk
+// computes.  A short last chunk is padded with alpha = 1, beta = 0, q = k = v = 0,
+// which leaves the state and the valid outputs unchanged.
+#include "qd_device.h"
+#include "qd_internal.h"
+
+namespace qd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kDVT = 64;  // value columns per workgroup
+
+template <class P, int DK, int CH>
+struct ChunkLayout {
+    using R = typename P::R;
+    static constexpr bool TR = P::kTransposedCopies;
+    static constexpr int PAD = 16 / P::kBytes;   // 16 bytes of row padding
+    static constexpr int PK = DK + PAD;          // pitch of Q, K rows (d_k wide)
+    static constexpr int PC = CH + PAD;          // pitch of chunk-wide rows
+    static constexpr int PV = TR ? PC : kDVT + PAD;   // V^T rows are c-wide; V rows are dv-wide
+    static constexpr int VROWS = TR ? kDVT : CH;
+    static constexpr int PO = kDVT + PAD;        // output staging pitch
+    static constexpr int NQ = CH * PK;
+    static constexpr int NKT_ = TR ? DK * PC : 0;
+    static constexpr int NV = VROWS * PV;
+    static constexpr int NCC = CH * PC;
+    static constexpr int NT = (CH * PO > NCC) ? CH * PO : NCC;  // T buffer doubles as O staging
+    static constexpr int NTT = TR ? NCC : 0;
+    // element offsets (all multiples of 16 bytes because every size is a multiple of PAD rows)
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + NQ;
+    static constexpr int oKT = oK + NQ;
+    static constexpr int oV = oKT + NKT_;
+    static constexpr int oL = oV + NV;      // L, later M1
+    static constexpr int oLT = oL + NCC;    // L^T (bf16 only), later M2
+    static constexpr int oT = oLT + NCC;    // T, later O staging
+    static constexpr int oTT = oT + NT;     // T^T (bf16 only)
+    static constexpr int oA = oTT + NTT;    // A = H o QK^T
+    static constexpr int nR = oA + NCC;
+    static constexpr int gate_bytes = 6 * CH * 4;
+    static constexpr int bytes = nR * P::kBytes + gate_bytes;
+    static_assert((oK * P::kBytes) % 16 == 0 && (oKT * P::kBytes) % 16 == 0 &&
+                  (oV * P::kBytes) % 16 == 0 && (oL * P::kBytes) % 16 == 0 &&
+                  (oLT * P::kBytes) % 16 == 0 && (oT * P::kBytes) % 16 == 0 &&
+                  (oTT * P::kBytes) % 16 == 0 && (oA * P::kBytes) % 16 == 0 &&
+                  (nR * P::kBytes) % 16 == 0, "LDS buffers must be 16-byte aligned");
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
+};
+
+// Lower-triangle block pair p -> (i, j), j <= i, row-major enumeration.
+__device__ __forceinline__ void tri_pair(int p, int &i, int &j) {
+    i = 0;
+    while ((i + 1) * (i + 2) / 2 <= p) ++i;
+    j = p - i * (i + 1) / 2;
+}
+
+template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs args) {
+    using R = typename P::R;
+    using F = typename P::F;
+    using Lay = ChunkLayout<P, DK, CH>;
+    constexpr bool TR = Lay::TR;
+    constexpr int NKT = DK / 16;       // 16-wide key tiles
+    constexpr int NCT = CH / 16;       // 16-row chunk tiles
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV, PO = Lay::PO;
+    constexpr int EPV = 16 / P::kBytes;            // elements per 16-byte vector
+    constexpr int VPRQ = DK / EPV;                 // vectors per q/k row
+    constexpr int VPRV = kDVT / EPV;               // vectors per v/o tile row
+    constexpr int NVQ = (CH * VPRQ + kThreads - 1) / kThreads;
+    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2;
+    constexpr int PPW = (NPAIR + 3) / 4;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
+    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
+    R *const KTs = reinterpret_cast<R *>(smem) + Lay::oKT;
+    R *const Vb = reinterpret_cast<R *>(smem) + Lay::oV;
+    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;
+    R *const LTs = reinterpret_cast<R *>(smem) + Lay::oLT;
+    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;
+    R *const TTs = reinterpret_cast<R *>(smem) + Lay::oTT;
+    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+    R *const M1s = Ls;
+    R *const M2s = LTs;
+    R *const Os = Ts;
+    float *const las = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
+    float *const bes = las + CH;
+    float *const lams = bes + CH;
+    float *const gs = lams + CH;
+    float *const egs = gs + CH;
+    float *const egls = egs + CH;
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int r16 = lane & 15;
+    const int g4 = lane >> 4;
+
+    // ---- workgroup -> (b, h, value tile); the value tiles of one head share an XCD
+    const int nblk = gridDim.x;
+    int logical = blockIdx.x;
+    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int dvt = logical % args.n_dvt;
+    const int bh = logical / args.n_dvt;
+    const int b = bh / args.H;
+    const int h = bh % args.H;
+    const int T = args.T, H = args.H, dv = args.dv;
+    const int dv0 = dvt * kDVT;
+
+    const R *__restrict__ gq = static_cast<const R *>(args.q);
+    const R *__restrict__ gk = static_cast<const R *>(args.k);
+    const R *__restrict__ gv = static_cast<const R *>(args.v);
+    R *__restrict__ go = static_cast<R *>(args.o);
+    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+    // ---- state slice: S^T tiles, rows d_k = 16t + 4g + i, column = this wave's value column
+    f32x4 sT[NKT];
+    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * wave + r16) * DK;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+        sT[t] = args.S0 ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
+
+    // ---- raw chunk staging registers (prefetched one chunk ahead)
+    uint4 rq[NVQ], rk[NVQ], rv[NVV];
+    float ra = 1.f, rb = 0.f, rl = 0.f;
+    auto gload = [&](int n) {
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = tid + kThreads * j;
+            const int c = vi / VPRQ, cv = vi % VPRQ;
+            if (vi < CH * VPRQ && c < clen) {
+                const size_t off = tok(t0 + c) * DK + cv * EPV;
+                rq[j] = *reinterpret_cast<const uint4 *>(gq + off);
+                rk[j] = *reinterpret_cast<const uint4 *>(gk + off);
+            } else {
+                rq[j] = make_uint4(0, 0, 0, 0);
+                rk[j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = tid + kThreads * j;
+            const int c = vi / VPRV, cv = vi % VPRV;
+            if (vi < CH * VPRV && c < clen)
+                rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(t0 + c) * dv + dv0 + cv * EPV);
+            else
+                rv[j] = make_uint4(0, 0, 0, 0);
+        }
+        if (tid < CH) {
+            const bool ok = tid < clen;
+            const size_t gi = ok ? tok(t0 + tid) : 0;
+            ra = (HAS_A && ok) ? args.alpha[gi] : 1.f;
+            rb = ok ? args.beta[gi] : 0.f;
+            rl = (HAS_L && ok) ? args.lam[gi] : 0.f;
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = tid + kThreads * j;
+            if (vi < CH * VPRQ) {
+                const int c = vi / VPRQ, cv = vi % VPRQ;
+                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = rq[j];
+                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = rk[j];
+                if constexpr (TR) {
+                    const R *e = reinterpret_cast<const R *>(&rk[j]);
+#pragma unroll
+                    for (int u = 0; u < EPV; ++u) KTs[(cv * EPV + u) * PC + c] = e[u];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = tid + kThreads * j;
+            if (vi < CH * VPRV) {
+                const int c = vi / VPRV, cv = vi % VPRV;
+                if constexpr (TR) {
+                    const R *e = reinterpret_cast<const R *>(&rv[j]);
+#pragma unroll
+                    for (int u = 0; u < EPV; ++u) Vb[(cv * EPV + u) * PV + c] = e[u];
+                } else {
+                    *reinterpret_cast<uint4 *>(Vb + c * PV + cv * EPV) = rv[j];
+                }
+            }
+        }
+        if (tid < CH) {
+            las[tid] = HAS_A ? __logf(ra) : 0.f;
+            bes[tid] = rb;
+            lams[tid] = rl;
+        }
+    };
+
+    const int NC = (T + CH - 1) / CH;
+    if (NC > 0) gload(0);
+
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+        lstore();
+        if (n + 1 < NC) gload(n + 1);
+        __syncthreads();
+
+        // ---- gate prefix sums (wave 0) while all waves form the Gram products
+        if (wave == 0) {
+            float x = (lane < CH) ? las[lane] : 0.f;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float glast = __shfl(x, CH - 1);
+            if (lane < CH) {
+                gs[lane] = x;
+                egs[lane] = __expf(x);
+                egls[lane] = __expf(glast - x);
+            }
+        }
+        f32x4 gq_[PPW], gk_[PPW];
+#pragma unroll
+        for (int u = 0; u < PPW; ++u) {
+            const int p = wave + 4 * u;
+            gq_[u] = zero4();
+            gk_[u] = zero4();
+            if (p < NPAIR) {
+                int i, j;
+                tri_pair(p, i, j);
+#pragma unroll
+                for (int s = 0; s < NKT; s += 2) {
+                    const F bk0 = frag<P>(Ks, PK, 16 * j, 16 * s);
+                    const F bk1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
+                    const F aq0 = frag<P>(Qs, PK, 16 * i, 16 * s);
+                    const F aq1 = frag<P>(Qs, PK, 16 * i, 16 * s + 16);
+                    const F ak0 = frag<P>(Ks, PK, 16 * i, 16 * s);
+                    const F ak1 = frag<P>(Ks, PK, 16 * i, 16 * s + 16);
+                    gq_[u] = P::mma2(gq_[u], aq0, aq1, bk0, bk1);
+                    gk_[u] = P::mma2(gk_[u], ak0, ak1, bk0, bk1);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- L = sl(diag(beta) X K^T) and A = H o Q K^T
+#pragma unroll
+        for (int u = 0; u < PPW; ++u) {
+            const int p = wave + 4 * u;
+            if (p < NPAIR) {
+                int i, j;
+                tri_pair(p, i, j);
+                const int c = 16 * j + r16;
+                f32x4 lv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * i + 4 * g4 + e;
+                    const float qk = gq_[u][e];
+                    const float xk = HAS_L ? gk_[u][e] + lams[r] * qk : gk_[u][e];
+                    lv[e] = (c < r) ? bes[r] * xk : 0.f;
+                    const float av = (c <= r) ? (HAS_A ? __expf(gs[r] - gs[c]) : 1.f) * qk : 0.f;
+                    Ls[r * PC + c] = P::from_f32(lv[e]);
+                    As[r * PC + c] = P::from_f32(av);
+                }
+                if constexpr (TR) P::st4(LTs + c * PC + 16 * i + 4 * g4, lv);
+            }
+        }
+        __syncthreads();
+
+        // ---- T = (I + L)^-1: diagonal 16x16 blocks, right-looking forward substitution.
+        // Wave w inverts block w; lane l computes column l % 16 (lanes >= 16 repeat it).
+        if (wave < NCT) {
+            const int o = 16 * wave;
+            const int c = r16;
+            float acc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 15; ++jj) {
+                const float t = acc[jj];
+#pragma unroll
+                for (int r = jj + 1; r < 16; ++r) {
+                    float lrj;
+                    if constexpr (TR) lrj = P::to_f32(LTs[(o + jj) * PC + o + r]);
+                    else lrj = P::to_f32(Ls[(o + r) * PC + o + jj]);
+                    acc[r] -= lrj * t;
+                }
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(acc[r]);
+                if constexpr (TR) {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        P::st4(TTs + (o + c) * PC + o + r, f32x4{acc[r], acc[r + 1], acc[r + 2], acc[r + 3]});
+                }
+            }
+        }
+        __syncthreads();
+
+        // B-fragment of block (kb, nb) of T: T[16kb + k][16nb + n]
+        auto tfragB = [&](int kb, int nb) -> F {
+            if constexpr (TR) return frag<P>(TTs, PC, 16 * nb, 16 * kb);
+            else return frag_t<P>(Ts, PC, 16 * kb, 16 * nb);
+        };
+        auto tstore = [&](int rb_, int cb_, f32x4 val) {   // block (rb_, cb_) of T from an accumulator
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
+            if constexpr (TR) P::st4(TTs + (16 * cb_ + r16) * PC + 16 * rb_ + 4 * g4, val);
+        };
+
+        // ---- block doubling, level 1: T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
+        if constexpr (NCT >= 2) {
+            if (wave < NCT / 2) {
+                const int rb_ = 2 * wave + 1, cb_ = 2 * wave;
+                const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), tfragB(cb_, cb_));
+                const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
+                tstore(rb_, cb_, -y);
+            }
+            __syncthreads();
+        }
+        // ---- level 2 (CH = 64): lower-left 32x32 quadrant, one 16x16 block per wave:
+        // T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
+        if constexpr (NCT == 4) {
+            const int ab = 2 + (wave >> 1), cb_ = wave & 1;
+            f32x4 acc = zero4();
+            for (int m = 2; m <= ab; ++m) {
+                f32x4 x = zero4();
+                for (int kb = cb_; kb <= 1; ++kb)
+                    x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), tfragB(kb, cb_));
+                acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
+            }
+            tstore(ab, cb_, -acc);
+            __syncthreads();
+        }
+
+        // ---- M1 = (H o T) diag(beta), M2 = -D_g T diag(beta) (lower block triangle only)
+        for (int idx = tid; idx < CH * CH; idx += kThreads) {
+            const int r = idx / CH, c = idx % CH;
+            if ((c >> 4) > (r >> 4)) continue;
+            const float t = (c <= r) ? P::to_f32(Ts[r * PC + c]) : 0.f;
+            const float tb = t * bes[c];
+            const float m1 = HAS_A ? __expf(gs[r] - gs[c]) * tb : tb;
+            const float m2 = HAS_A ? -egs[r] * tb : -tb;
+            M1s[r * PC + c] = P::from_f32(m1);
+            M2s[r * PC + c] = P::from_f32(m2);
+        }
+        __syncthreads();
+
+        // ---- state-dependent part: this wave's 16 value columns
+        auto vfragB = [&](int s) -> F {     // B-fragment of V[c][dv], slice s, this wave's columns
+            if constexpr (TR) return frag<P>(Vb, PV, 16 * wave, 16 * s);
+            else return frag_t<P>(Vb, PV, 16 * s, 16 * wave);
+        };
+        auto ktfragA = [&](int t, int s) -> F {  // A-fragment of K^T[dk][c], key tile t, slice s
+            if constexpr (TR) return frag<P>(KTs, PC, 16 * t, 16 * s);
+            else return frag_t<P>(Ks, PK, 16 * s, 16 * t);
+        };
+
+        // U~ = M1 V  (initial value of Z)
+        f32x4 Z[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            Z[mt] = zero4();
+#pragma unroll
+            for (int s = 0; s <= mt; s += 2) {
+                if (s + 1 <= mt)
+                    Z[mt] = P::mma2(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), frag<P>(M1s, PC, 16 * mt, 16 * s + 16),
+                                    vfragB(s), vfragB(s + 1));
+                else
+                    Z[mt] = P::mma1(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), vfragB(s));
+            }
+        }
+        // K S^T and Q S^T
+        F sTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
+        f32x4 PKs[NCT], PQs[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            PKs[mt] = zero4();
+            PQs[mt] = zero4();
+#pragma unroll
+            for (int t = 0; t < NKT; t += 2) {
+                PKs[mt] = P::mma2(PKs[mt], frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16),
+                                  sTf[t], sTf[t + 1]);
+                PQs[mt] = P::mma2(PQs[mt], frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16),
+                                  sTf[t], sTf[t + 1]);
+            }
+        }
+        // Z = U~ + M2 (K S^T + diag(lambda) Q S^T)
+        F Yf[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            f32x4 y = PKs[mt];
+            if constexpr (HAS_L) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] += lams[16 * mt + 4 * g4 + e] * PQs[mt][e];
+            }
+            Yf[mt] = P::cvt(y);
+        }
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+            for (int s = 0; s <= mt; s += 2) {
+                if (s + 1 <= mt)
+                    Z[mt] = P::mma2(Z[mt], frag<P>(M2s, PC, 16 * mt, 16 * s), frag<P>(M2s, PC, 16 * mt, 16 * s + 16),
+                                    Yf[s], Yf[s + 1]);
+                else
+                    Z[mt] = P::mma1(Z[mt], frag<P>(M2s, PC, 16 * mt, 16 * s), Yf[s]);
+            }
+        }
+        // O = D_g Q S^T + A Z
+        F Zf[NCT], Zd[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            Zf[mt] = P::cvt(Z[mt]);
+            f32x4 zd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zd[e] = (HAS_A ? egls[16 * mt + 4 * g4 + e] : 1.f) * Z[mt][e];
+            Zd[mt] = P::cvt(zd);
+        }
+        f32x4 O[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            O[mt] = PQs[mt];
+            if constexpr (HAS_A) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[mt][e] *= egs[16 * mt + 4 * g4 + e];
+            }
+#pragma unroll
+            for (int s = 0; s <= mt; s += 2) {
+                if (s + 1 <= mt)
+                    O[mt] = P::mma2(O[mt], frag<P>(As, PC, 16 * mt, 16 * s), frag<P>(As, PC, 16 * mt, 16 * s + 16),
+                                    Zf[s], Zf[s + 1]);
+                else
+                    O[mt] = P::mma1(O[mt], frag<P>(As, PC, 16 * mt, 16 * s), Zf[s]);
+            }
+        }
+        // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z
+        const float dlast = HAS_A ? egs[CH - 1] : 1.f;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            f32x4 acc = sT[t] * dlast;
+#pragma unroll
+            for (int s = 0; s < NCT; s += 2) {
+                if (s + 1 < NCT)
+                    acc = P::mma2(acc, ktfragA(t, s), ktfragA(t, s + 1), Zd[s], Zd[s + 1]);
+                else
+                    acc = P::mma1(acc, ktfragA(t, s), Zd[s]);
+            }
+            sT[t] = acc;
+        }
+        // stage O (T buffer is dead after the M build), then coalesced row stores
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PO + 16 * wave + r16] = P::from_f32(O[mt][e]);
+        }
+        __syncthreads();
+        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+            const int c = vi / VPRV, cv = vi % VPRV;
+            if (c < clen)
+                *reinterpret_cast<uint4 *>(go + tok(t0 + c) * dv + dv0 + cv * EPV) =
+                    *reinterpret_cast<const uint4 *>(Os + c * PO + cv * EPV);
+        }
+        // the next iteration's LDS writes (Q, K, K^T, V, gates) do not touch the O
+        // staging buffer, and the solve that reuses it is two barriers away.
+    }
+
+    if (args.S_T) {
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.S_T + srow + 16 * t + 4 * g4) = sT[t];
+    }
+}
+
+template <class P, int DK, int CH>
+hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
+    const int grid = a.B * a.H * a.n_dvt;
+    if (grid == 0) return hipSuccess;
+    const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
+    if (ha && hl) hipLaunchKernelGGL((chunk_fwd_kernel<P, DK, CH, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else if (ha) hipLaunchKernelGGL((chunk_fwd_kernel<P, DK, CH, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else if (hl) hipLaunchKernelGGL((chunk_fwd_kernel<P, DK, CH, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((chunk_fwd_kernel<P, DK, CH, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class P, int DK>
+hipError_t launch_dk(int C, const ChunkArgs &a, hipStream_t stream) {
+    switch (C) {
+        case 16: return launch_typed<P, DK, 16>(a, stream);
+        case 32: return launch_typed<P, DK, 32>(a, stream);
+        case 64: return launch_typed<P, DK, 64>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool chunk_fwd_supported(int dtype, int dk, int dv, int C) {
+    return (dtype == 0 || dtype == 1) && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
+           (C == 16 || C == 32 || C == 64);
+}
+
+hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {
+    if (dtype == 1) return dk == 128 ? launch_dk<Bf16, 128>(C, a, stream) : launch_dk<Bf16, 64>(C, a, stream);
+    return dk == 128 ? launch_dk<F32, 128>(C, a, stream) : launch_dk<F32, 64>(C, a, stream);
+}
+
+}  // namespace qd

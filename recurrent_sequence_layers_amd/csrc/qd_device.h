@@ -1,0 +1,123 @@
+// Device-side building blocks for the gfx950 Q-Delta kernels.
+//
+// Fragment convention (one 64-lane wavefront, MFMA 16x16 tiles):
+//   A "fragment" of a 16 x 16 block M (rows m, contraction index k) gives lane l
+//   the four values M[l % 16][4 * (l / 16) + i], i = 0..3.
+//   A "B-fragment" of a 16 x 16 block N (k x n) gives lane l the four values
+//   N[4 * (l / 16) + i][l % 16].
+//   The MFMA accumulator of a 16 x 16 output D gives lane l D[4 * (l / 16) + i][l % 16].
+// So an accumulator tile is, without moving data, the B-fragment of D (k = row)
+// and the A-fragment of D^T.  The kernels chain products through registers this
+// way.  A 16x16x32 bf16 MFMA consumes two 16-wide contraction slices at once: its
+// A and B operands are the concatenation of the two slices' fragments, in the same
+// order for both, so the pairing of contraction indices is consistent whatever
+// order the instruction assigns internally.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------- element policies
+// Raw storage type R in memory and LDS, fragment type F fed to the MFMA.
+struct Bf16 {
+    using R = uint16_t;
+    using F = bf16x4;
+    static constexpr int kBytes = 2;
+    static constexpr bool kTransposedCopies = true;  // keep K^T and V^T copies in LDS
+
+    __device__ __forceinline__ static float to_f32(R x) {
+        return __uint_as_float(static_cast<uint32_t>(x) << 16);
+    }
+    __device__ __forceinline__ static R from_f32(float x) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+    }
+    __device__ __forceinline__ static F cvt(f32x4 a) { return __builtin_convertvector(a, bf16x4); }
+    __device__ __forceinline__ static F neg(F a) { return -a; }
+    __device__ __forceinline__ static F ld4(const R *p) {      // 4 consecutive elements
+        return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(p));
+    }
+    __device__ __forceinline__ static F ld4_strided(const R *p, int stride) {
+        uint16_t a = p[0], b = p[stride], c = p[2 * stride], d = p[3 * stride];
+        uint2 u;
+        u.x = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+        u.y = static_cast<uint32_t>(c) | (static_cast<uint32_t>(d) << 16);
+        return __builtin_bit_cast(bf16x4, u);
+    }
+    __device__ __forceinline__ static void st4(R *p, f32x4 a) {
+        *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, cvt(a));
+    }
+    // acc += A(16 x 16) B(16 x 16)
+    __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                        __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
+    }
+    // acc += [A0 A1](16 x 32) [B0; B1](32 x 16)
+    __device__ __forceinline__ static f32x4 mma2(f32x4 acc, F a0, F a1, F b0, F b1) {
+        bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+
+struct F32 {
+    using R = float;
+    using F = f32x4;
+    static constexpr int kBytes = 4;
+    static constexpr bool kTransposedCopies = false;  // read transposed operands strided
+
+    __device__ __forceinline__ static float to_f32(R x) { return x; }
+    __device__ __forceinline__ static R from_f32(float x) { return x; }
+    __device__ __forceinline__ static F cvt(f32x4 a) { return a; }
+    __device__ __forceinline__ static F neg(F a) { return -a; }
+    __device__ __forceinline__ static F ld4(const R *p) { return *reinterpret_cast<const f32x4 *>(p); }
+    __device__ __forceinline__ static F ld4_strided(const R *p, int stride) {
+        f32x4 r;
+        r[0] = p[0]; r[1] = p[stride]; r[2] = p[2 * stride]; r[3] = p[3 * stride];
+        return r;
+    }
+    __device__ __forceinline__ static void st4(R *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
+    __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+        return acc;
+    }
+    __device__ __forceinline__ static f32x4 mma2(f32x4 acc, F a0, F a1, F b0, F b1) {
+        return mma1(mma1(acc, a0, b0), a1, b1);
+    }
+};
+
+// ---------------------------------------------------------------- fragment loads
+// A-fragment of the 16 x 16 block of a row-major matrix at (row0, col0):
+// lane gets M[row0 + l%16][col0 + 4(l/16) .. +3].
+template <class P>
+__device__ __forceinline__ typename P::F frag(const typename P::R *m, int pitch, int row0, int col0) {
+    const int l = lane_id();
+    return P::ld4(m + (row0 + (l & 15)) * pitch + col0 + 4 * (l >> 4));
+}
+
+// Fragment of the transpose of the block of a row-major matrix at (row0, col0),
+// i.e. lane gets M[row0 + 4(l/16) + i][col0 + l%16], i = 0..3.  Used both as the
+// A-fragment of M^T and as the B-fragment of M.
+template <class P>
+__device__ __forceinline__ typename P::F frag_t(const typename P::R *m, int pitch, int row0, int col0) {
+    const int l = lane_id();
+    return P::ld4_strided(m + (row0 + 4 * (l >> 4)) * pitch + col0 + (l & 15), pitch);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace qd

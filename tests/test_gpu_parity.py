@@ -1,0 +1,251 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Metric (per (batch, head) slice): max|y - y_ref| / max|y_ref|, reported for the
+worst slice, separately for o and the final state.  Bars: 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs.  The oracle consumes fp64 upcasts of exactly the values
+handed to the GPU.  Full-size workloads are checked on sampled (batch, head)
+slices that the oracle recomputes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recurrent_sequence_layers_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def slice_err(y, ref, axes):
+    """max over slices of max|y-ref| / max|ref|; `axes` are the reduced axes."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.abs(y - ref).max(axis=axes)
+    den = np.abs(ref).max(axis=axes)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max()) if num.size else 0.0
+
+
+def to_dev(x):
+    return None if x is None else x.cuda()
+
+
+def run_gpu(qd, x, C, S0=None, want_state=True):
+    o, S = qd.qdelta_chunk_fwd(to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.alpha), x.beta.cuda(),
+                               to_dev(x.lam), to_dev(S0 if S0 is not None else x.S0), C=C,
+                               want_state=want_state)
+    torch.cuda.synchronize()
+    return o.float().cpu(), (S.cpu() if S is not None else None)
+
+
+def check_against_oracle(o_gpu, S_gpu, x, tol, sel=None):
+    """Compare GPU results with the oracle on all, or on the sampled (b, h) pairs `sel`."""
+    if sel is None:
+        o_ref, S_ref = oracle.qdelta_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0)
+        eo = slice_err(o_gpu.numpy(), o_ref, axes=(1, 3))
+        es = slice_err(S_gpu.numpy(), S_ref, axes=(2, 3)) if S_gpu is not None else 0.0
+    else:
+        eo = es = 0.0
+        for b, h in sel:
+            g = lambda t: None if t is None else t[b:b + 1, :, h:h + 1]
+            S0 = None if x.S0 is None else x.S0[b:b + 1, h:h + 1]
+            o_ref, S_ref = oracle.qdelta_fwd(g(x.q), g(x.k), g(x.v), g(x.alpha), g(x.beta), g(x.lam), S0)
+            eo = max(eo, slice_err(o_gpu[b:b + 1, :, h:h + 1].numpy(), o_ref, axes=(1, 3)))
+            if S_gpu is not None:
+                es = max(es, slice_err(S_gpu[b:b + 1, h:h + 1].numpy(), S_ref, axes=(2, 3)))
+    print(f"  max rel err o={eo:.3e} S_T={es:.3e} (bar {tol:g})", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+    if o_gpu.numel():
+        assert float(o_gpu.abs().max()) > 1e-3, "trivially small output"
+    return eo, es
+
+
+# ------------------------------------------------------------------ small shapes, full compare
+SMALL = [
+    # B, T, H, dk, dv, C, dtype, s0
+    (1, 256, 1, 64, 64, 64, "f32", None),        # the tiny fp32 workload
+    (2, 200, 3, 128, 128, 64, "bf16", 0.05),     # several chunks, ragged tail, both value tiles
+    (1, 130, 2, 64, 128, 32, "bf16", 0.05),
+    (2, 77, 2, 128, 64, 16, "bf16", None),
+    (1, 300, 2, 128, 128, 64, "f32", 0.05),
+    (2, 45, 1, 64, 128, 16, "f32", 0.1),
+    (1, 99, 3, 128, 64, 32, "f32", None),
+    (1, 1, 2, 128, 128, 64, "bf16", 0.05),       # a single token
+    (1, 64, 1, 128, 128, 64, "bf16", None),      # exactly one full chunk
+    (1, 65, 1, 64, 64, 64, "f32", 0.05),         # one full chunk plus one token
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,C,dt,s0", SMALL)
+def test_small_shapes_full_compare(qd, B, T, H, dk, dv, C, dt, s0):
+    print(f"case B={B} T={T} H={H} dk={dk} dv={dv} C={C} {dt} s0={s0}", flush=True)
+    x = inputs.chunk_inputs(B, T, H, dk, dv, dt, seed=100 + T + dk + C, s0_std=s0)
+    o, S = run_gpu(qd, x, C)
+    check_against_oracle(o, S, x, TOL[dt])
+
+
+@pytest.mark.parametrize("lam,alpha", [("zero", "random"), ("zero", "one"), ("random", "one"),
+                                       ("one", "random")])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gate_special_cases(qd, lam, alpha, dt):
+    """lambda == 0 (Gated DeltaNet) and alpha == 1 (no decay) select the specialised
+    instances when passed as null; the oracle gets explicit zeros/ones.  lambda == 1
+    is the pages' ablation setting."""
+    print(f"case lam={lam} alpha={alpha} {dt}", flush=True)
+    x = inputs.chunk_inputs(2, 150, 2, 128, 128, dt, seed=7, lam=lam, alpha=alpha, s0_std=0.05)
+    xn = inputs.chunk_inputs(2, 150, 2, 128, 128, dt, seed=7, lam=lam, alpha=alpha, s0_std=0.05,
+                             gates_as_none=True)
+    o, S = run_gpu(qd, xn, 64)
+    check_against_oracle(o, S, x, TOL[dt])
+
+
+def test_chunk_size_invariance(qd):
+    """C changes only rounding: C = 16, 32, 64 agree with each other and with the oracle."""
+    x = inputs.chunk_inputs(1, 190, 2, 128, 128, "f32", seed=3, s0_std=0.05)
+    outs = [run_gpu(qd, x, C) for C in (16, 32, 64)]
+    for o, S in outs:
+        check_against_oracle(o, S, x, TOL["f32"])
+    np.testing.assert_allclose(outs[0][0].numpy(), outs[2][0].numpy(), atol=2e-5)
+
+
+def test_state_chaining_and_in_place(qd):
+    """fwd(T1) then fwd(T2, S0 = S_T) equals fwd(T1 + T2); S_T may alias S0."""
+    x = inputs.chunk_inputs(2, 230, 2, 128, 128, "f32", seed=11, s0_std=0.05)
+    o_full, S_full = run_gpu(qd, x, 64)
+    T1 = 100
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    a, b_, l = x.alpha.cuda(), x.beta.cuda(), x.lam.cuda()
+    S = x.S0.cuda().clone()
+    o1, _ = qd.qdelta_chunk_fwd(q[:, :T1].contiguous(), k[:, :T1].contiguous(), v[:, :T1].contiguous(),
+                                a[:, :T1].contiguous(), b_[:, :T1].contiguous(), l[:, :T1].contiguous(),
+                                S, C=64, S_T=S)                       # in place
+    o2, _ = qd.qdelta_chunk_fwd(q[:, T1:].contiguous(), k[:, T1:].contiguous(), v[:, T1:].contiguous(),
+                                a[:, T1:].contiguous(), b_[:, T1:].contiguous(), l[:, T1:].contiguous(),
+                                S, C=64, S_T=S)
+    torch.cuda.synchronize()
+    o_cat = torch.cat([o1, o2], dim=1).cpu()
+    assert slice_err(o_cat.numpy(), o_full.numpy(), (1, 3)) < 1e-5
+    assert slice_err(S.cpu().numpy(), S_full.numpy(), (2, 3)) < 1e-5
+
+
+def test_empty_and_degenerate(qd):
+    """T = 0 copies S0 to S_T (zeros when S0 is null); B = 0 is a no-op; beta = 0 is
+    pure decay."""
+    x = inputs.chunk_inputs(2, 0, 2, 64, 64, "bf16", seed=1, s0_std=0.1)
+    o, S = run_gpu(qd, x, 64)
+    assert o.shape == (2, 0, 2, 64)
+    np.testing.assert_array_equal(S.numpy(), x.S0.numpy())
+    xz = inputs.chunk_inputs(2, 0, 2, 64, 64, "bf16", seed=1)
+    _, S = run_gpu(qd, xz, 64)
+    assert float(S.abs().max()) == 0.0
+    x0 = inputs.chunk_inputs(0, 10, 2, 64, 64, "bf16", seed=1)
+    o, S = run_gpu(qd, x0, 64)
+    assert o.shape == (0, 10, 2, 64)
+    xb = inputs.chunk_inputs(1, 70, 2, 128, 64, "f32", seed=2, s0_std=0.1)
+    xb.beta.zero_()
+    o, S = run_gpu(qd, xb, 64)
+    check_against_oracle(o, S, xb, TOL["f32"])
+
+
+def test_determinism(qd):
+    """No atomics and a fixed reduction order: two runs are bitwise equal."""
+    x = inputs.chunk_inputs(2, 333, 4, 128, 128, "bf16", seed=5, s0_std=0.05)
+    o1, S1 = run_gpu(qd, x, 64)
+    o2, S2 = run_gpu(qd, x, 64)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+FULL = [
+    ("layer_1p3b_bf16", [(0, 0), (3, 7), (7, 15), (5, 2)]),
+    ("gdn_bf16", [(1, 1), (6, 9)]),
+    ("deltanet_bf16", [(2, 3), (7, 14)]),
+    ("long_64k_bf16", [(0, 0), (0, 11)]),
+]
+
+
+@pytest.mark.parametrize("name,sel", FULL)
+def test_full_size_sampled(qd, name, sel):
+    print(f"workload {name} sampled {sel}", flush=True)
+    x = inputs.workload_inputs(name, seed=2024, device="cuda", gates_as_none=True)
+    w = inputs.WORKLOADS[name]
+    o, S = qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=w["C"])
+    torch.cuda.synchronize()
+    # oracle needs explicit gates where the GPU was given null
+    B, T, H = x.beta.shape
+    xc = inputs.ChunkInputs(x.q.cpu(), x.k.cpu(), x.v.cpu(),
+                            x.alpha.cpu() if x.alpha is not None else torch.ones(B, T, H),
+                            x.beta.cpu(), x.lam.cpu() if x.lam is not None else torch.zeros(B, T, H),
+                            x.S0.cpu() if x.S0 is not None else None)
+    check_against_oracle(o.float().cpu(), S.cpu(), xc, TOL[w["dtype"]], sel=sel)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+
+
+# ------------------------------------------------------------------ decode step
+@pytest.mark.parametrize("N,H,dk,dv,dt", [(3, 2, 128, 128, "bf16"), (2, 3, 64, 128, "f32"),
+                                          (4, 1, 128, 64, "f32"), (2, 2, 64, 64, "bf16")])
+def test_step_small_full_compare(qd, N, H, dk, dv, dt):
+    steps = 20
+    q, k, v, a, b, l = inputs.decode_tokens(steps, N, H, dk, dv, dt, seed=9)
+    S0 = inputs.decode_state(N, H, dk, dv, seed=10)
+    S = S0.cuda().clone()
+    outs = []
+    for t in range(steps):
+        outs.append(qd.qdelta_step(q[t].cuda(), k[t].cuda(), v[t].cuda(), a[t].cuda(), b[t].cuda(),
+                                   l[t].cuda(), S).float().cpu())
+    torch.cuda.synchronize()
+    o_gpu = torch.stack(outs, dim=1)                       # [N, steps, H, dv]
+    # the decode sequence equals the forward over `steps` tokens (oracle pin: chaining)
+    tr = lambda t: t.transpose(0, 1).contiguous()
+    o_ref, S_ref = oracle.qdelta_fwd(tr(q), tr(k), tr(v), tr(a), tr(b), tr(l), S0)
+    eo = slice_err(o_gpu.numpy(), o_ref, (1, 3))
+    es = slice_err(S.cpu().numpy(), S_ref, (2, 3))
+    print(f"  decode max rel err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+def test_step_matches_oracle_step_exactly_one_token(qd):
+    """One step against the oracle's own step function (fp32, tight)."""
+    q, k, v, a, b, l = inputs.decode_tokens(1, 5, 3, 128, 128, "f32", seed=21)
+    S0 = inputs.decode_state(5, 3, 128, 128, seed=22)
+    S = S0.cuda().clone()
+    o = qd.qdelta_step(q[0].cuda(), k[0].cuda(), v[0].cuda(), a[0].cuda(), b[0].cuda(), l[0].cuda(), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.qdelta_step(q[0], k[0], v[0], a[0], b[0], l[0], S0)
+    assert slice_err(o.cpu().numpy(), o_ref, (2,)) < 1e-5
+    assert slice_err(S.cpu().numpy(), S_ref, (2, 3)) < 1e-5
+    # null gates select the alpha == 1 / lambda == 0 instance
+    S = S0.cuda().clone()
+    o = qd.qdelta_step(q[0].cuda(), k[0].cuda(), v[0].cuda(), None, b[0].cuda(), None, S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.qdelta_step(q[0], k[0], v[0], None, b[0], None, S0)
+    assert slice_err(o.cpu().numpy(), o_ref, (2,)) < 1e-5
+    assert slice_err(S.cpu().numpy(), S_ref, (2, 3)) < 1e-5
+
+
+def test_decode_full_size_1000_steps_sampled(qd):
+    """The decode workload: 256 sequences x 16 heads, d = 128, fp32 state resident,
+    1000 consecutive steps; sampled (sequence, head) pairs checked over all steps."""
+    w = inputs.WORKLOADS["decode_256x16"]
+    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
+    q, k, v, a, b, l = inputs.decode_tokens(steps, N, H, dk, dv, w["dtype"], seed=77, device="cuda")
+    S0 = inputs.decode_state(N, H, dk, dv, s0_std=w["s0_std"], seed=78, device="cuda")
+    S = S0.clone()
+    sel = [(0, 0), (37, 5), (255, 15), (128, 8)]
+    o_hist = torch.empty((steps, len(sel), dv), dtype=torch.float32, device="cuda")
+    idx_n = torch.tensor([s[0] for s in sel], device="cuda")
+    idx_h = torch.tensor([s[1] for s in sel], device="cuda")
+    for t in range(steps):
+        o = qd.qdelta_step(q[t], k[t], v[t], a[t], b[t], l[t], S)
+        o_hist[t] = o[idx_n, idx_h].float()
+    torch.cuda.synchronize()
+    eo = es = 0.0
+    for j, (n, h) in enumerate(sel):
+        g = lambda t: t[:, n:n + 1, h:h + 1].transpose(0, 1).contiguous().cpu()   # [1, steps, 1, *]
+        o_ref, S_ref = oracle.qdelta_fwd(g(q), g(k), g(v), g(a), g(b), g(l), S0[n:n + 1, h:h + 1].cpu())
+        eo = max(eo, slice_err(o_hist[:, j].cpu().numpy()[None, :, None], o_ref, (1, 3)))
+        es = max(es, slice_err(S[n:n + 1, h:h + 1].cpu().numpy(), S_ref, (2, 3)))
+    print(f"  decode 1000 steps max rel err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
