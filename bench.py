@@ -1,0 +1,219 @@
+"""Benchmark of the Q-Delta layer forward (chunked) and the decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+
+One timed step is one call of the chunked layer forward over the 1.3B-layer-shaped
+workload (B=8, T=4096, H=16, d_k=d_v=128, C=64, bf16 q/k/v/o, fp32 gates and
+state, S0 = 0), inputs resident in HBM.  The value is tokens/s (B*T per step).
+In the same run the decode step is timed on 256 sequences x 16 heads (fp32 state
+resident, one token per call) and reported as achieved HBM GB/s.  Kernel
+durations come from HIP events recorded on the stream the kernels run on.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd.hip",
+                        "recurrent_sequence_layers_amd/csrc/qd_device.h"]
+STEP_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_step.hip",
+                       "recurrent_sequence_layers_amd/csrc/qd_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled by the
+    plain-copy calibration factor; None if absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_sha") != source_sha(sources):
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def chunk_algorithmic(B, T, H, dk, dv, C, es):
+    """Single-pass bytes and the pages' dense-product FLOP count for one forward call."""
+    toks = B * T * H
+    bytes_ = toks * (2 * dk + 2 * dv) * es + toks * 3 * 4 + B * H * dv * dk * 4   # q,k,v,o; gates; S_T
+    flops = toks * (6 * C * dk + 4 * C * dv + 6 * dk * dv)
+    return bytes_, flops
+
+
+def step_algorithmic(N, H, dk, dv, es):
+    nh = N * H
+    return nh * dv * dk * 4 * 2 + nh * (2 * dk + 2 * dv) * es + nh * 3 * 4   # S r+w; q,k,v,o; gates
+
+
+def time_region(torch, fn, steps):
+    """Run fn() `steps` times between two HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def cpu_baseline(torch, x, budget_s=10.0):
+    """The fp64 oracle on whole batch rows of the same workload until ~budget_s spent."""
+    import numpy as np
+    import oracle
+    B, T, H = x.beta.shape
+    f = lambda t: None if t is None else np.ascontiguousarray(t.detach().cpu().double().numpy())
+    total, rows = 0.0, 0
+    for b in range(B):
+        sl = slice(b, b + 1)
+        args = [f(t[sl]) if t is not None else None for t in (x.q, x.k, x.v, x.alpha, x.beta, x.lam)]
+        t0 = time.perf_counter()
+        oracle.qdelta_fwd(*args, None)
+        total += time.perf_counter() - t0
+        rows += 1
+        if total >= budget_s:
+            break
+    return {"value": rows * T / total, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{rows} of {B} batch rows x {T} tokens x {H} heads of the same workload "
+                      f"({rows * T * H} token-heads, {total:.2f} s, fp64 recurrence, OpenMP over state rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(requested --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import recurrent_sequence_layers_amd as qd
+    from recurrent_sequence_layers_amd import inputs
+    qd.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    name = "layer_1p3b_bf16"
+    w = inputs.WORKLOADS[name]
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    log(f"[bench] generating {name} on device")
+    x = inputs.workload_inputs(name, seed=args.seed, device="cuda")
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    fwd = lambda: qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, C=C, o=o, S_T=S_T)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    log(f"[bench] chunk forward: {args.warmup} warm-up steps done, timing {args.steps}")
+    gpu_s, wall_s = time_region(torch, fwd, args.steps)
+    ms_per_step = gpu_s / args.steps * 1e3
+    alg_bytes, alg_flops = chunk_algorithmic(B, T, H, dk, dv, C, 2)
+    ach_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    log(f"[bench] chunk forward {ms_per_step:.4f} ms/step, {tokens_per_s / 1e6:.2f} M tokens/s, "
+        f"{ach_gbs:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+
+    # ---- decode step: 256 sequences x 16 heads, fp32 state resident, D consecutive steps
+    dw = inputs.WORKLOADS["decode_256x16"]
+    N, Hd, dkd, dvd = dw["N"], dw["H"], dw["dk"], dw["dv"]
+    D = args.decode_steps
+    log(f"[bench] generating decode inputs for {D} steps")
+    dq, dk_, dv_, da, db, dl = inputs.decode_tokens(D, N, Hd, dkd, dvd, dw["dtype"], seed=args.seed + 1,
+                                                    device="cuda")
+    S = inputs.decode_state(N, Hd, dkd, dvd, s0_std=dw["s0_std"], seed=args.seed + 2, device="cuda")
+    od = torch.empty((N, Hd, dvd), dtype=torch.bfloat16, device=dev)
+    lib = qd.load_library()
+    import ctypes
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t, i: ctypes.c_void_p(t[i].data_ptr())
+    calls = [(ptr(dq, i), ptr(dk_, i), ptr(dv_, i), ptr(da, i), ptr(db, i), ptr(dl, i)) for i in range(D)]
+    Sp, op = ctypes.c_void_p(S.data_ptr()), ctypes.c_void_p(od.data_ptr())
+
+    def decode_run():
+        for c in calls:
+            rc = lib.qdelta_step(c[0], c[1], c[2], c[3], c[4], c[5], Sp, op, N, Hd, dkd, dvd, 1, stream)
+            if rc:
+                raise RuntimeError(qd.qdelta_status_string(rc))
+
+    decode_run()                                   # warm-up pass over all steps
+    dec_s, dec_wall = time_region(torch, decode_run, 1)
+    us_per_step = dec_s / D * 1e6
+    dec_bytes = step_algorithmic(N, Hd, dkd, dvd, 2)
+    dec_gbs = dec_bytes / (us_per_step * 1e-6) / 1e9
+    log(f"[bench] decode {us_per_step:.2f} us/step, {dec_gbs:.0f} GB/s algorithmic, "
+        f"{N * Hd / (us_per_step * 1e-6) / 1e6:.2f} M token-heads/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores (cpu_baseline)")
+        cpu = cpu_baseline(torch, x)
+        log(f"[bench] oracle {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+
+    traffic = counter_traffic("chunk_fwd_layer_1p3b", CHUNK_KERNEL_SOURCES)
+    dec_traffic = counter_traffic("step_decode_256x16", STEP_KERNEL_SOURCES)
+    out = {
+        "metric": "Q-Delta chunk-fwd tokens/s + MFMA util (B8 T4096 H16 d128); decode HBM GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit-norm, v ~ N(0,1), sigmoid/exp-softplus gates)",
+        "config": {"workload": "Q-Delta chunked layer forward, B=8 T=4096 H=16 d_k=d_v=128 C=64, "
+                               "bf16 q/k/v/o, fp32 gates and state, S0=0",
+                   "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "C": C},
+        "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach_gbs / PEAK_HBM_GBS,
+                     "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel<Bf16,128,64,true,true>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved_tflops": tflops, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
+                 "algorithmic_flops_per_launch": alg_flops},
+        "decode": {"workload": "256 sequences x 16 heads, d_k=d_v=128, fp32 state resident, bf16 q/k/v/o, "
+                               f"{D} consecutive steps",
+                   "us_per_step": us_per_step, "token_heads_per_s": N * Hd / (us_per_step * 1e-6),
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / PEAK_HBM_GBS, "traffic": dec_traffic,
+                                "algorithmic_bytes_per_launch": dec_bytes}},
+        "cpu_baseline": cpu,
+        "timing": {"chunk_wall_s": wall_s, "decode_wall_s": dec_wall},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

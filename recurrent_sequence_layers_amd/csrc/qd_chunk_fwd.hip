@@ -22,9 +22,12 @@
 // Waves: four per workgroup; in the state-dependent part wave w owns value columns
 // [16w, 16w + 16) of the tile, so S^T, K S^T, Q S^T, Z and O for those columns stay
 // in its registers and feed one another as MFMA operands without LDS round trips.
-// The next chunk's raw inputs are loaded into registers while the current chunk
-// computes.  A short last chunk is padded with alpha = 1, beta = 0, q = k = v = 0,
-// which leaves the state and the valid outputs unchanged.
+// Every LDS matrix is row-major; operands needed transposed (K^T, V, blocks of T)
+// are read with the gfx950 LDS transpose read.  The next chunk's raw inputs are
+// loaded into registers while the current chunk computes (addresses are clamped to
+// the last valid row, so the loads carry no branches; rows past the end are zeroed
+// when they are written to LDS).  A short last chunk is padded with alpha = 1,
+// beta = 0, q = k = v = 0, which leaves the state and the valid outputs unchanged.
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -37,37 +40,27 @@ constexpr int kDVT = 64;  // value columns per workgroup
 template <class P, int DK, int CH>
 struct ChunkLayout {
     using R = typename P::R;
-    static constexpr bool TR = P::kTransposedCopies;
     static constexpr int PAD = 16 / P::kBytes;   // 16 bytes of row padding
     static constexpr int PK = DK + PAD;          // pitch of Q, K rows (d_k wide)
     static constexpr int PC = CH + PAD;          // pitch of chunk-wide rows
-    static constexpr int PV = TR ? PC : kDVT + PAD;   // V^T rows are c-wide; V rows are dv-wide
-    static constexpr int VROWS = TR ? kDVT : CH;
-    static constexpr int PO = kDVT + PAD;        // output staging pitch
+    static constexpr int PV = kDVT + PAD;        // pitch of V rows and of the output staging
     static constexpr int NQ = CH * PK;
-    static constexpr int NKT_ = TR ? DK * PC : 0;
-    static constexpr int NV = VROWS * PV;
+    static constexpr int NV = CH * PV;
     static constexpr int NCC = CH * PC;
-    static constexpr int NT = (CH * PO > NCC) ? CH * PO : NCC;  // T buffer doubles as O staging
-    static constexpr int NTT = TR ? NCC : 0;
-    // element offsets (all multiples of 16 bytes because every size is a multiple of PAD rows)
+    static constexpr int NT = (CH * PV > NCC) ? CH * PV : NCC;  // T buffer doubles as O staging
+    // element offsets (16-byte aligned: every row pitch is a multiple of 16 bytes)
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + NQ;
-    static constexpr int oKT = oK + NQ;
-    static constexpr int oV = oKT + NKT_;
+    static constexpr int oV = oK + NQ;
     static constexpr int oL = oV + NV;      // L, later M1
-    static constexpr int oLT = oL + NCC;    // L^T (bf16 only), later M2
-    static constexpr int oT = oLT + NCC;    // T, later O staging
-    static constexpr int oTT = oT + NT;     // T^T (bf16 only)
-    static constexpr int oA = oTT + NTT;    // A = H o QK^T
+    static constexpr int oM2 = oL + NCC;
+    static constexpr int oT = oM2 + NCC;    // T, later O staging
+    static constexpr int oA = oT + NT;      // A = H o QK^T
     static constexpr int nR = oA + NCC;
-    static constexpr int gate_bytes = 6 * CH * 4;
+    static constexpr int gate_bytes = 5 * CH * 4;
     static constexpr int bytes = nR * P::kBytes + gate_bytes;
-    static_assert((oK * P::kBytes) % 16 == 0 && (oKT * P::kBytes) % 16 == 0 &&
-                  (oV * P::kBytes) % 16 == 0 && (oL * P::kBytes) % 16 == 0 &&
-                  (oLT * P::kBytes) % 16 == 0 && (oT * P::kBytes) % 16 == 0 &&
-                  (oTT * P::kBytes) % 16 == 0 && (oA * P::kBytes) % 16 == 0 &&
-                  (nR * P::kBytes) % 16 == 0, "LDS buffers must be 16-byte aligned");
+    static_assert((PK * P::kBytes) % 16 == 0 && (PC * P::kBytes) % 16 == 0 && (PV * P::kBytes) % 16 == 0,
+                  "row pitches must keep 16-byte alignment");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
@@ -78,15 +71,31 @@ __device__ __forceinline__ void tri_pair(int p, int &i, int &j) {
     j = p - i * (i + 1) / 2;
 }
 
+// 16 consecutive LDS elements (16-byte aligned) as fp32
+template <class P>
+__device__ __forceinline__ void load_row16(const typename P::R *p, float (&out)[16]) {
+    constexpr int EPV = 16 / P::kBytes;
+#pragma unroll
+    for (int v = 0; v < 16 / EPV; ++v) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(p + v * EPV);
+        const typename P::R *e = reinterpret_cast<const typename P::R *>(&w);
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) out[v * EPV + u] = P::to_f32(e[u]);
+    }
+}
+
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+    return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
 template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
 __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs args) {
     using R = typename P::R;
     using F = typename P::F;
     using Lay = ChunkLayout<P, DK, CH>;
-    constexpr bool TR = Lay::TR;
     constexpr int NKT = DK / 16;       // 16-wide key tiles
     constexpr int NCT = CH / 16;       // 16-row chunk tiles
-    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV, PO = Lay::PO;
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
     constexpr int EPV = 16 / P::kBytes;            // elements per 16-byte vector
     constexpr int VPRQ = DK / EPV;                 // vectors per q/k row
     constexpr int VPRV = kDVT / EPV;               // vectors per v/o tile row
@@ -98,22 +107,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
     R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
     R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
-    R *const KTs = reinterpret_cast<R *>(smem) + Lay::oKT;
-    R *const Vb = reinterpret_cast<R *>(smem) + Lay::oV;
+    R *const Vs = reinterpret_cast<R *>(smem) + Lay::oV;
     R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;
-    R *const LTs = reinterpret_cast<R *>(smem) + Lay::oLT;
+    R *const M2s = reinterpret_cast<R *>(smem) + Lay::oM2;
     R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;
-    R *const TTs = reinterpret_cast<R *>(smem) + Lay::oTT;
     R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
     R *const M1s = Ls;
-    R *const M2s = LTs;
     R *const Os = Ts;
-    float *const las = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
-    float *const bes = las + CH;
-    float *const lams = bes + CH;
-    float *const gs = lams + CH;
-    float *const egs = gs + CH;
-    float *const egls = egs + CH;
+    float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);  // g = cumsum log alpha
+    float *const egs = gs + CH;      // exp(g)
+    float *const egls = egs + CH;    // exp(g_last - g)
+    float *const bes = egls + CH;    // beta
+    float *const lams = bes + CH;    // lambda
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -145,91 +150,59 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
     for (int t = 0; t < NKT; ++t)
         sT[t] = args.S0 ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
 
-    // ---- raw chunk staging registers (prefetched one chunk ahead)
+    // ---- raw chunk staging registers (prefetched one chunk ahead, branch-free)
     uint4 rq[NVQ], rk[NVQ], rv[NVV];
     float ra = 1.f, rb = 0.f, rl = 0.f;
     auto gload = [&](int n) {
         const int t0 = n * CH;
-        const int clen = min(CH, T - t0);
+        const int last = min(CH, T - t0) - 1;   // >= 0 for every chunk that exists
 #pragma unroll
         for (int j = 0; j < NVQ; ++j) {
             const int vi = tid + kThreads * j;
-            const int c = vi / VPRQ, cv = vi % VPRQ;
-            if (vi < CH * VPRQ && c < clen) {
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                const int c = min(vi / VPRQ, last), cv = vi % VPRQ;
                 const size_t off = tok(t0 + c) * DK + cv * EPV;
                 rq[j] = *reinterpret_cast<const uint4 *>(gq + off);
                 rk[j] = *reinterpret_cast<const uint4 *>(gk + off);
-            } else {
-                rq[j] = make_uint4(0, 0, 0, 0);
-                rk[j] = make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
             const int vi = tid + kThreads * j;
-            const int c = vi / VPRV, cv = vi % VPRV;
-            if (vi < CH * VPRV && c < clen)
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int c = min(vi / VPRV, last), cv = vi % VPRV;
                 rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(t0 + c) * dv + dv0 + cv * EPV);
-            else
-                rv[j] = make_uint4(0, 0, 0, 0);
+            }
         }
         if (tid < CH) {
-            const bool ok = tid < clen;
-            const size_t gi = ok ? tok(t0 + tid) : 0;
-            ra = (HAS_A && ok) ? args.alpha[gi] : 1.f;
-            rb = ok ? args.beta[gi] : 0.f;
-            rl = (HAS_L && ok) ? args.lam[gi] : 0.f;
+            const size_t gi = tok(t0 + min(tid, last));
+            if constexpr (HAS_A) ra = args.alpha[gi];
+            rb = args.beta[gi];
+            if constexpr (HAS_L) rl = args.lam[gi];
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int clen) {
 #pragma unroll
         for (int j = 0; j < NVQ; ++j) {
             const int vi = tid + kThreads * j;
-            if (vi < CH * VPRQ) {
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
                 const int c = vi / VPRQ, cv = vi % VPRQ;
-                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = rq[j];
-                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = rk[j];
-                if constexpr (TR) {
-                    const R *e = reinterpret_cast<const R *>(&rk[j]);
-#pragma unroll
-                    for (int u = 0; u < EPV; ++u) KTs[(cv * EPV + u) * PC + c] = e[u];
-                }
+                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = keep_if(c < clen, rq[j]);
+                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = keep_if(c < clen, rk[j]);
             }
         }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
             const int vi = tid + kThreads * j;
-            if (vi < CH * VPRV) {
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
                 const int c = vi / VPRV, cv = vi % VPRV;
-                if constexpr (TR) {
-                    const R *e = reinterpret_cast<const R *>(&rv[j]);
-#pragma unroll
-                    for (int u = 0; u < EPV; ++u) Vb[(cv * EPV + u) * PV + c] = e[u];
-                } else {
-                    *reinterpret_cast<uint4 *>(Vb + c * PV + cv * EPV) = rv[j];
-                }
+                *reinterpret_cast<uint4 *>(Vs + c * PV + cv * EPV) = keep_if(c < clen, rv[j]);
             }
         }
-        if (tid < CH) {
-            las[tid] = HAS_A ? __logf(ra) : 0.f;
-            bes[tid] = rb;
-            lams[tid] = rl;
-        }
-    };
-
-    const int NC = (T + CH - 1) / CH;
-    if (NC > 0) gload(0);
-
-    for (int n = 0; n < NC; ++n) {
-        const int t0 = n * CH;
-        const int clen = min(CH, T - t0);
-        lstore();
-        if (n + 1 < NC) gload(n + 1);
-        __syncthreads();
-
-        // ---- gate prefix sums (wave 0) while all waves form the Gram products
         if (wave == 0) {
-            float x = (lane < CH) ? las[lane] : 0.f;
+            // inclusive prefix sum of log(alpha) over the chunk (padding rows add 0)
+            const bool ok = lane < clen;
+            float x = (HAS_A && ok) ? __logf(ra) : 0.f;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -240,103 +213,90 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
                 gs[lane] = x;
                 egs[lane] = __expf(x);
                 egls[lane] = __expf(glast - x);
+                bes[lane] = ok ? rb : 0.f;
+                lams[lane] = ok ? rl : 0.f;
             }
         }
-        f32x4 gq_[PPW], gk_[PPW];
+    };
+
+    const int NC = (T + CH - 1) / CH;
+    if (NC > 0) gload(0);
+
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+        lstore(clen);
+        if (n + 1 < NC) gload(n + 1);
+        __syncthreads();
+
+        // ---- Gram blocks, computed transposed so a lane owns four consecutive columns:
+        // D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c] with r = 16i + l%16, c = 16j + 4g + e.
+        // Then L = sl(diag(beta) (K K^T + diag(lambda) Q K^T)) and A = H o Q K^T.
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
             const int p = wave + 4 * u;
-            gq_[u] = zero4();
-            gk_[u] = zero4();
             if (p < NPAIR) {
                 int i, j;
                 tri_pair(p, i, j);
+                f32x4 gq_ = zero4(), gk_ = zero4();
 #pragma unroll
                 for (int s = 0; s < NKT; s += 2) {
-                    const F bk0 = frag<P>(Ks, PK, 16 * j, 16 * s);
-                    const F bk1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
-                    const F aq0 = frag<P>(Qs, PK, 16 * i, 16 * s);
-                    const F aq1 = frag<P>(Qs, PK, 16 * i, 16 * s + 16);
-                    const F ak0 = frag<P>(Ks, PK, 16 * i, 16 * s);
-                    const F ak1 = frag<P>(Ks, PK, 16 * i, 16 * s + 16);
-                    gq_[u] = P::mma2(gq_[u], aq0, aq1, bk0, bk1);
-                    gk_[u] = P::mma2(gk_[u], ak0, ak1, bk0, bk1);
+                    const F a0 = frag<P>(Ks, PK, 16 * j, 16 * s);
+                    const F a1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
+                    gq_ = P::mma2(gq_, a0, a1, frag<P>(Qs, PK, 16 * i, 16 * s), frag<P>(Qs, PK, 16 * i, 16 * s + 16));
+                    gk_ = P::mma2(gk_, a0, a1, frag<P>(Ks, PK, 16 * i, 16 * s), frag<P>(Ks, PK, 16 * i, 16 * s + 16));
                 }
-            }
-        }
-        __syncthreads();
-
-        // ---- L = sl(diag(beta) X K^T) and A = H o Q K^T
-#pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const int p = wave + 4 * u;
-            if (p < NPAIR) {
-                int i, j;
-                tri_pair(p, i, j);
-                const int c = 16 * j + r16;
-                f32x4 lv;
+                const int r = 16 * i + r16;
+                const int c0 = 16 * j + 4 * g4;
+                const float lr = lams[r], br = bes[r], gr = gs[r];
+                const f32x4 gc = lds_f32x4(gs + c0);
+                f32x4 lv, av;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * i + 4 * g4 + e;
-                    const float qk = gq_[u][e];
-                    const float xk = HAS_L ? gk_[u][e] + lams[r] * qk : gk_[u][e];
-                    lv[e] = (c < r) ? bes[r] * xk : 0.f;
-                    const float av = (c <= r) ? (HAS_A ? __expf(gs[r] - gs[c]) : 1.f) * qk : 0.f;
-                    Ls[r * PC + c] = P::from_f32(lv[e]);
-                    As[r * PC + c] = P::from_f32(av);
+                    const int c = c0 + e;
+                    const float xk = HAS_L ? gk_[e] + lr * gq_[e] : gk_[e];
+                    lv[e] = (c < r) ? br * xk : 0.f;
+                    av[e] = (c <= r) ? (HAS_A ? __expf(gr - gc[e]) : 1.f) * gq_[e] : 0.f;
                 }
-                if constexpr (TR) P::st4(LTs + c * PC + 16 * i + 4 * g4, lv);
+                P::st4(Ls + r * PC + c0, lv);
+                P::st4(As + r * PC + c0, av);
             }
         }
         __syncthreads();
 
-        // ---- T = (I + L)^-1: diagonal 16x16 blocks, right-looking forward substitution.
-        // Wave w inverts block w; lane l computes column l % 16 (lanes >= 16 repeat it).
+        // ---- T = (I + L)^-1: diagonal 16x16 blocks by forward substitution over rows
+        // (t_r = e_r - sum_{j<r} L[r][j] t_j).  Wave w inverts block w; lane l computes
+        // column l % 16 (lanes >= 16 repeat it and do not store).
         if (wave < NCT) {
             const int o = 16 * wave;
             const int c = r16;
-            float acc[16];
+            float t[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float lr[16];
+                load_row16<P>(Ls + (o + r) * PC + o, lr);
+                float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 15; ++jj) {
-                const float t = acc[jj];
-#pragma unroll
-                for (int r = jj + 1; r < 16; ++r) {
-                    float lrj;
-                    if constexpr (TR) lrj = P::to_f32(LTs[(o + jj) * PC + o + r]);
-                    else lrj = P::to_f32(Ls[(o + r) * PC + o + jj]);
-                    acc[r] -= lrj * t;
-                }
+                for (int jj = 0; jj < r; ++jj) acc -= lr[jj] * t[jj];
+                t[r] = acc;
             }
             if (lane < 16) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(acc[r]);
-                if constexpr (TR) {
-#pragma unroll
-                    for (int r = 0; r < 16; r += 4)
-                        P::st4(TTs + (o + c) * PC + o + r, f32x4{acc[r], acc[r + 1], acc[r + 2], acc[r + 3]});
-                }
+                for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
             }
         }
         __syncthreads();
 
-        // B-fragment of block (kb, nb) of T: T[16kb + k][16nb + n]
-        auto tfragB = [&](int kb, int nb) -> F {
-            if constexpr (TR) return frag<P>(TTs, PC, 16 * nb, 16 * kb);
-            else return frag_t<P>(Ts, PC, 16 * kb, 16 * nb);
-        };
-        auto tstore = [&](int rb_, int cb_, f32x4 val) {   // block (rb_, cb_) of T from an accumulator
+        // block (rb_, cb_) of T from an accumulator tile (rows 4g + e, column l % 16)
+        auto tstore = [&](int rb_, int cb_, f32x4 val) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
-            if constexpr (TR) P::st4(TTs + (16 * cb_ + r16) * PC + 16 * rb_ + 4 * g4, val);
         };
-
         // ---- block doubling, level 1: T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
         if constexpr (NCT >= 2) {
             if (wave < NCT / 2) {
                 const int rb_ = 2 * wave + 1, cb_ = 2 * wave;
-                const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), tfragB(cb_, cb_));
+                const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), frag_b<P>(Ts, PC, 16 * cb_, 16 * cb_));
                 const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
                 tstore(rb_, cb_, -y);
             }
@@ -350,36 +310,37 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
             for (int m = 2; m <= ab; ++m) {
                 f32x4 x = zero4();
                 for (int kb = cb_; kb <= 1; ++kb)
-                    x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), tfragB(kb, cb_));
+                    x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
                 acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
             }
             tstore(ab, cb_, -acc);
             __syncthreads();
         }
 
-        // ---- M1 = (H o T) diag(beta), M2 = -D_g T diag(beta) (lower block triangle only)
-        for (int idx = tid; idx < CH * CH; idx += kThreads) {
-            const int r = idx / CH, c = idx % CH;
-            if ((c >> 4) > (r >> 4)) continue;
-            const float t = (c <= r) ? P::to_f32(Ts[r * PC + c]) : 0.f;
-            const float tb = t * bes[c];
-            const float m1 = HAS_A ? __expf(gs[r] - gs[c]) * tb : tb;
-            const float m2 = HAS_A ? -egs[r] * tb : -tb;
-            M1s[r * PC + c] = P::from_f32(m1);
-            M2s[r * PC + c] = P::from_f32(m2);
+        // ---- M1 = (H o T) diag(beta), M2 = -D_g T diag(beta), four columns per lane,
+        // lower block triangle only (the other blocks are never read)
+        for (int idx = tid; idx < NPAIR * 64; idx += kThreads) {
+            int i, j;
+            tri_pair(idx >> 6, i, j);
+            const int r = 16 * i + ((idx >> 2) & 15);
+            const int c0 = 16 * j + 4 * (idx & 3);
+            const F tf = P::ld4(Ts + r * PC + c0);
+            const f32x4 bc = lds_f32x4(bes + c0);
+            const f32x4 gc = lds_f32x4(gs + c0);
+            const float gr = gs[r], er = egs[r];
+            f32x4 m1, m2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
+                m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+                m2[e] = HAS_A ? -er * tb : -tb;
+            }
+            P::st4(M1s + r * PC + c0, m1);
+            P::st4(M2s + r * PC + c0, m2);
         }
         __syncthreads();
 
         // ---- state-dependent part: this wave's 16 value columns
-        auto vfragB = [&](int s) -> F {     // B-fragment of V[c][dv], slice s, this wave's columns
-            if constexpr (TR) return frag<P>(Vb, PV, 16 * wave, 16 * s);
-            else return frag_t<P>(Vb, PV, 16 * s, 16 * wave);
-        };
-        auto ktfragA = [&](int t, int s) -> F {  // A-fragment of K^T[dk][c], key tile t, slice s
-            if constexpr (TR) return frag<P>(KTs, PC, 16 * t, 16 * s);
-            else return frag_t<P>(Ks, PK, 16 * s, 16 * t);
-        };
-
         // U~ = M1 V  (initial value of Z)
         f32x4 Z[NCT];
 #pragma unroll
@@ -389,9 +350,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
             for (int s = 0; s <= mt; s += 2) {
                 if (s + 1 <= mt)
                     Z[mt] = P::mma2(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), frag<P>(M1s, PC, 16 * mt, 16 * s + 16),
-                                    vfragB(s), vfragB(s + 1));
+                                    frag_b<P>(Vs, PV, 16 * s, 16 * wave), frag_b<P>(Vs, PV, 16 * s + 16, 16 * wave));
                 else
-                    Z[mt] = P::mma1(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), vfragB(s));
+                    Z[mt] = P::mma1(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), frag_b<P>(Vs, PV, 16 * s, 16 * wave));
             }
         }
         // K S^T and Q S^T
@@ -416,10 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
             f32x4 y = PKs[mt];
-            if constexpr (HAS_L) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] += lams[16 * mt + 4 * g4 + e] * PQs[mt][e];
-            }
+            if constexpr (HAS_L) y += lds_f32x4(lams + 16 * mt + 4 * g4) * PQs[mt];
             Yf[mt] = P::cvt(y);
         }
 #pragma unroll
@@ -438,19 +396,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
             Zf[mt] = P::cvt(Z[mt]);
-            f32x4 zd;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zd[e] = (HAS_A ? egls[16 * mt + 4 * g4 + e] : 1.f) * Z[mt][e];
-            Zd[mt] = P::cvt(zd);
+            Zd[mt] = HAS_A ? P::cvt(lds_f32x4(egls + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
         }
         f32x4 O[NCT];
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
-            O[mt] = PQs[mt];
-            if constexpr (HAS_A) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) O[mt][e] *= egs[16 * mt + 4 * g4 + e];
-            }
+            O[mt] = HAS_A ? lds_f32x4(egs + 16 * mt + 4 * g4) * PQs[mt] : PQs[mt];
 #pragma unroll
             for (int s = 0; s <= mt; s += 2) {
                 if (s + 1 <= mt)
@@ -460,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
                     O[mt] = P::mma1(O[mt], frag<P>(As, PC, 16 * mt, 16 * s), Zf[s]);
             }
         }
-        // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z
+        // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z ; K^T blocks via transpose reads of K
         const float dlast = HAS_A ? egs[CH - 1] : 1.f;
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
@@ -468,27 +419,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
 #pragma unroll
             for (int s = 0; s < NCT; s += 2) {
                 if (s + 1 < NCT)
-                    acc = P::mma2(acc, ktfragA(t, s), ktfragA(t, s + 1), Zd[s], Zd[s + 1]);
+                    acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t),
+                                  Zd[s], Zd[s + 1]);
                 else
-                    acc = P::mma1(acc, ktfragA(t, s), Zd[s]);
+                    acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Zd[s]);
             }
             sT[t] = acc;
         }
-        // stage O (T buffer is dead after the M build), then coalesced row stores
+        // stage O (the T buffer is dead after the M build), then coalesced row stores
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PO + 16 * wave + r16] = P::from_f32(O[mt][e]);
+            for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(O[mt][e]);
         }
         __syncthreads();
         for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
             const int c = vi / VPRV, cv = vi % VPRV;
             if (c < clen)
                 *reinterpret_cast<uint4 *>(go + tok(t0 + c) * dv + dv0 + cv * EPV) =
-                    *reinterpret_cast<const uint4 *>(Os + c * PO + cv * EPV);
+                    *reinterpret_cast<const uint4 *>(Os + c * PV + cv * EPV);
         }
-        // the next iteration's LDS writes (Q, K, K^T, V, gates) do not touch the O
-        // staging buffer, and the solve that reuses it is two barriers away.
+        // the next iteration's LDS writes (Q, K, V, gates) do not touch the O staging
+        // buffer, and the T writes that reuse it are two barriers away.
     }
 
     if (args.S_T) {

@@ -35,7 +35,6 @@ struct Bf16 {
     using R = uint16_t;
     using F = bf16x4;
     static constexpr int kBytes = 2;
-    static constexpr bool kTransposedCopies = true;  // keep K^T and V^T copies in LDS
 
     __device__ __forceinline__ static float to_f32(R x) {
         return __uint_as_float(static_cast<uint32_t>(x) << 16);
@@ -75,7 +74,6 @@ struct F32 {
     using R = float;
     using F = f32x4;
     static constexpr int kBytes = 4;
-    static constexpr bool kTransposedCopies = false;  // read transposed operands strided
 
     __device__ __forceinline__ static float to_f32(R x) { return x; }
     __device__ __forceinline__ static R from_f32(float x) { return x; }
@@ -118,6 +116,29 @@ __device__ __forceinline__ typename P::F frag_t(const typename P::R *m, int pitc
     return P::ld4_strided(m + (row0 + 4 * (l >> 4)) * pitch + col0 + (l & 15), pitch);
 }
 
+// B-fragment of the 16 x 16 block of a row-major matrix at (row0, col0), i.e. lane l
+// gets M[row0 + 4(l/16) + i][col0 + l%16], i = 0..3 (equivalently the A-fragment of
+// the block's transpose).  For bf16 this is one LDS transpose read per lane: within
+// each group of 16 lanes the instruction hands lane 4p+q element q of the 8-byte
+// chunks read by lanes 4i+p, so lane 4i+p of group g reads row 4g+i, columns
+// 4p..4p+3.  For fp32 the four values are read one by one.
+__device__ __forceinline__ Bf16::F frag_b_bf16(const uint16_t *m, int pitch, int row0, int col0) {
+    const int l = lane_id();
+    const int g = l >> 4, mm = l & 15;
+    const uint16_t *p = m + (row0 + 4 * g + (mm >> 2)) * pitch + col0 + 4 * (mm & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+template <class P>
+__device__ __forceinline__ typename P::F frag_b(const typename P::R *m, int pitch, int row0, int col0) {
+    if constexpr (P::kBytes == 2) return frag_b_bf16(m, pitch, row0, col0);
+    else return frag_t<P>(m, pitch, row0, col0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4 lds_f32x4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 }  // namespace qd
