@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 512 MiB device-to-device copies, the reference the HBM "
+                         "byte counters are scaled against")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -120,6 +123,15 @@ def main():
     qd.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 copies of 512 MiB done")
+        del src, dst
 
     name = "layer_1p3b_bf16"
     w = inputs.WORKLOADS[name]
