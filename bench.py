@@ -22,7 +22,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
-CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd.hip",
+CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd_pipe.hip",
+                        "recurrent_sequence_layers_amd/csrc/qd_chunk_common.h",
                         "recurrent_sequence_layers_amd/csrc/qd_device.h"]
 STEP_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_step.hip",
                        "recurrent_sequence_layers_amd/csrc/qd_device.h"]
@@ -211,7 +212,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach_gbs / PEAK_HBM_GBS,
                      "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel<Bf16,128,64,true,true>",
+                     "kernel": "chunk_fwd_pipe_kernel<128,64,true,true>",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
                  "algorithmic_flops_per_launch": alg_flops},

@@ -28,6 +28,7 @@
 // the last valid row, so the loads carry no branches; rows past the end are zeroed
 // when they are written to LDS).  A short last chunk is padded with alpha = 1,
 // beta = 0, q = k = v = 0, which leaves the state and the valid outputs unchanged.
+#include "qd_chunk_common.h"
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -63,30 +64,6 @@ struct ChunkLayout {
                   "row pitches must keep 16-byte alignment");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
-
-// Lower-triangle block pair p -> (i, j), j <= i, row-major enumeration.
-__device__ __forceinline__ void tri_pair(int p, int &i, int &j) {
-    i = 0;
-    while ((i + 1) * (i + 2) / 2 <= p) ++i;
-    j = p - i * (i + 1) / 2;
-}
-
-// 16 consecutive LDS elements (16-byte aligned) as fp32
-template <class P>
-__device__ __forceinline__ void load_row16(const typename P::R *p, float (&out)[16]) {
-    constexpr int EPV = 16 / P::kBytes;
-#pragma unroll
-    for (int v = 0; v < 16 / EPV; ++v) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(p + v * EPV);
-        const typename P::R *e = reinterpret_cast<const typename P::R *>(&w);
-#pragma unroll
-        for (int u = 0; u < EPV; ++u) out[v * EPV + u] = P::to_f32(e[u]);
-    }
-}
-
-__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
-    return ok ? v : make_uint4(0, 0, 0, 0);
-}
 
 template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
 __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs args) {
@@ -479,7 +456,7 @@ bool chunk_fwd_supported(int dtype, int dk, int dv, int C) {
 }
 
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {
-    if (dtype == 1) return dk == 128 ? launch_dk<Bf16, 128>(C, a, stream) : launch_dk<Bf16, 64>(C, a, stream);
+    if (dtype == 1) return launch_chunk_fwd_pipe(dk, C, a, stream);
     return dk == 128 ? launch_dk<F32, 128>(C, a, stream) : launch_dk<F32, 64>(C, a, stream);
 }
 

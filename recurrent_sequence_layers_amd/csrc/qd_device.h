@@ -57,16 +57,19 @@ struct Bf16 {
     __device__ __forceinline__ static void st4(R *p, f32x4 a) {
         *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, cvt(a));
     }
-    // acc += A(16 x 16) B(16 x 16)
-    __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                        __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
-    }
     // acc += [A0 A1](16 x 32) [B0; B1](32 x 16)
     __device__ __forceinline__ static f32x4 mma2(f32x4 acc, F a0, F a1, F b0, F b1) {
         bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    // acc += A(16 x 16) B(16 x 16), issued as the same 16x16x32 instruction with a zero
+    // second slice.  Every bf16 product uses one MFMA shape: accumulation chains that
+    // mixed the 16x16x16 and 16x16x32 forms (one reading the other's result as its
+    // accumulator a few instructions later) produced wrong sums on gfx950.
+    __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
+        const F z = {};
+        return mma2(acc, a, z, b, z);
     }
 };
 

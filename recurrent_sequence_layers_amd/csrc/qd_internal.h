@@ -27,6 +27,9 @@ struct StepArgs {
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t stream);
 
+// bf16 chunk forward, eight-wave pipelined kernel (qd_chunk_fwd_pipe.hip).
+hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream);
+
 // Whether an instance exists for these sizes (checked before launching).
 bool chunk_fwd_supported(int dtype, int dk, int dv, int C);
 bool step_supported(int dtype, int dk, int dv);

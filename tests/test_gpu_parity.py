@@ -249,3 +249,24 @@ def test_decode_full_size_1000_steps_sampled(qd):
         es = max(es, slice_err(S[n:n + 1, h:h + 1].cpu().numpy(), S_ref, (2, 3)))
     print(f"  decode 1000 steps max rel err o={eo:.3e} S={es:.3e}", flush=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gate_instances_agree_bitwise(qd, C, dt):
+    """With alpha == 1 and lambda == 0 given explicitly, the four specialised instances
+    (alpha and lambda each null or not) compute exactly the same arithmetic, so their
+    outputs must be bitwise equal.  Guards against instance-specific code generation
+    (this caught accumulation chains mixing MFMA shapes)."""
+    x = inputs.chunk_inputs(2, 200, 2, 128, 128, dt, seed=31, lam="zero", alpha="one", s0_std=0.05)
+    d = lambda t: None if t is None else t.cuda()
+    outs = []
+    for a_null in (False, True):
+        for l_null in (False, True):
+            o, S = qd.qdelta_chunk_fwd(d(x.q), d(x.k), d(x.v), None if a_null else d(x.alpha), d(x.beta),
+                                       None if l_null else d(x.lam), d(x.S0), C=C)
+            torch.cuda.synchronize()
+            outs.append((o.cpu(), S.cpu()))
+    for o, S in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(S, outs[0][1])
+    check_against_oracle(outs[0][0].float(), outs[0][1], x, TOL[dt])
