@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
                 rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(t0 + c) * dv + dv0 + cv * EPV);
             }
         }
-        if (tid < CH) {
-            const size_t gi = tok(t0 + min(tid, last));
+        {   // every thread loads (clamped) so the loads carry no branch
+            const size_t gi = tok(t0 + min(tid & (kWave - 1), last));
             if constexpr (HAS_A) ra = args.alpha[gi];
             rb = args.beta[gi];
             if constexpr (HAS_L) rl = args.lam[gi];

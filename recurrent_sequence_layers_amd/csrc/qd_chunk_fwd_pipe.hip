@@ -10,8 +10,9 @@
 //                   [16w, 16w + 16) of the 64-wide tile and keeps its S^T slice in
 //                   registers for the whole sequence;
 //   prep waves 4-7  run the state-independent part of chunk n + 1 (Gram products,
-//                   L and A, the UT-transform solve for T, M1 and M2), stage chunk
-//                   n + 2's inputs into LDS and prefetch chunk n + 3 from HBM.
+//                   L and A, the UT-transform solve for T, M1 and M2).
+// The scan waves also fetch chunk n + 2 from HBM at the end of their busiest phase
+// and stage it into LDS at the end of the step.
 //
 // Every SIMD holds one wave of each role, so the latency of one role's chains is
 // hidden behind the other's work.  Each pipeline step has four intervals separated
@@ -20,10 +21,11 @@
 //
 //   interval  scan (chunk n)                  prep (chunk c = n + 1)
 //   I1        U~ = M1 V, K S^T, Q S^T,        Gram blocks, L, A; diagonal T blocks
-//             Z = U~ + M2 Y, O (staged)
+//             Z = U~ + M2 Y, O (staged);
+//             load chunk n + 2 from HBM
 //   I2        S^T update, key tiles 0..d_k/32 T level 1 (block doubling)
 //   I3        S^T update, the other half      T level 2
-//   I4        store O                         M1, M2; stage chunk c + 1; load c + 2
+//   I4        store O; stage chunk n + 2      M1, M2
 //
 // Buffers crossing roles are double-buffered by chunk parity (q, k, v, A, gates);
 // M1 and M2 are single-buffered because the scan reads them in I1 and the prep
@@ -64,27 +66,28 @@ struct PipeLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
-// Gram blocks (i, j) of the prep wave p, diagonal block first.  Balanced over the
-// four prep waves for C = 64; the wave that owns a diagonal block also inverts it.
+// Gram blocks (i, j) of the prep wave p, diagonal block first; u is a compile-time
+// slot index and p is wave-uniform, so this folds to scalar selects (a lookup table
+// would become a global load whose wait would also drain the in-flight prefetch).
+// Balanced over the four prep waves for C = 64: p0 (0,0) (3,0) (3,1); p1 (1,1) (1,0)
+// (3,2); p2 (2,2) (2,0) (2,1); p3 (3,3).  The wave owning a diagonal block inverts it.
 template <int NCT>
 __device__ __forceinline__ bool prep_block(int p, int u, int &i, int &j) {
-    if constexpr (NCT == 4) {
-        constexpr signed char tab[4][3][2] = {{{0, 0}, {3, 0}, {3, 1}},
-                                             {{1, 1}, {1, 0}, {3, 2}},
-                                             {{2, 2}, {2, 0}, {2, 1}},
-                                             {{3, 3}, {-1, -1}, {-1, -1}}};
-        i = tab[p][u][0];
-        j = tab[p][u][1];
+    i = -1;
+    j = -1;
+    if (u == 0) {
+        if (p < NCT) { i = p; j = p; }
+    } else if constexpr (NCT == 4) {
+        if (u == 1) {
+            i = (p == 0) ? 3 : p;
+            j = (p == 0) ? 0 : (p == 1) ? 0 : (p == 2) ? 0 : -1;
+            if (p == 3) i = -1;
+        } else {
+            i = (p == 3) ? -1 : (p == 2) ? 2 : 3;
+            j = (p == 0) ? 1 : (p == 1) ? 2 : 1;
+        }
     } else if constexpr (NCT == 2) {
-        constexpr signed char tab[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
-                                             {{1, 1}, {1, 0}, {-1, -1}},
-                                             {{-1, -1}, {-1, -1}, {-1, -1}},
-                                             {{-1, -1}, {-1, -1}, {-1, -1}}};
-        i = tab[p][u][0];
-        j = tab[p][u][1];
-    } else {
-        i = (p == 0 && u == 0) ? 0 : -1;
-        j = i;
+        if (u == 1 && p == 1) { i = 1; j = 0; }
     }
     return i >= 0;
 }
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
     for (int t = 0; t < NKT; ++t)
         sT[t] = (is_scan && args.S0) ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
 
-    // ---- prep role: raw chunk registers, prefetched two steps ahead of their use
+    // ---- raw chunk registers of the scan role (loaded at the end of I1, staged in I4)
     uint4 rq[NVQ], rk[NVQ], rv[NVV];
     float ra = 1.f, rb = 0.f, rl = 0.f;
     auto gload = [&](int c) {
@@ -177,8 +180,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
                 rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(t0 + cc) * dv + dv0 + cv * EPV);
             }
         }
-        if (rt < CH) {
-            const size_t gi = tok(t0 + min(rt, last));
+        {   // every role thread loads (clamped) so the loads carry no branch
+            const size_t gi = tok(t0 + min(rt & (kWave - 1), last));
             if constexpr (HAS_A) ra = args.alpha[gi];
             rb = args.beta[gi];
             if constexpr (HAS_L) rl = args.lam[gi];
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
                 *reinterpret_cast<uint4 *>(Vs + cc * PV + cv * EPV) = keep_if(cc < clen, rv[j]);
             }
         }
-        if (rw == 0) {                            // first prep wave: gate prefix sums
+        if (rw == 0) {                            // first wave of the role: gate prefix sums
             const bool ok = lane < clen;
             float x = (HAS_A && ok) ? __logf(ra) : 0.f;
 #pragma unroll
@@ -232,10 +235,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
         return;
     }
 
-    if (!is_scan) {
+    if (is_scan) {
         gload(0);
         rstore(0);
-        if (NC > 1) gload(1);
     }
     __syncthreads();
 
@@ -323,6 +325,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
                         Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = P::from_f32(o[e]);
                 }
             }
+            // fetch chunk n + 2 now, after this role's busiest phase: it is staged into the
+            // slot this role frees in I3, in I4 of this step (registers are not loop-carried)
+            if (n + 2 < NC) gload(n + 2);
         } else if (c < NC) {
             const R *Qs = Qb(ps), *Ks = Kb(ps);
             R *As = Ab(ps);
@@ -355,19 +360,28 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
                     P::st4(Ls + r * PC + c0, lv);
                     P::st4(As + r * PC + c0, av);
                     if (u == 0) {
-                        // diagonal block i == j == rw: forward substitution over rows,
-                        // lane computes column l % 16 (lanes >= 16 repeat it)
+                        // diagonal block i == j == rw, inverted from this wave's registers:
+                        // lane (row l%16, group g) holds L[row][4g..4g+3] of the block, and
+                        // every L value the forward substitution needs is read with
+                        // v_readlane (uniform), so no LDS round trips.  Lane l computes
+                        // column l % 16 of T (t_r = e_r - sum_{j<r} L[r][j] t_j); the four
+                        // lane groups repeat it.  L is rounded to bf16 as stored in LDS.
+                        f32x4 lb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lb[e] = P::to_f32(P::from_f32(lv[e]));
                         const int o = 16 * i;
                         const int cl = r16;
                         float tv[16];
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) {
-                            float lrow[16];
-                            load_row16<P>(Ls + (o + rr) * PC + o, lrow);
-                            float acc = (rr == cl) ? 1.f : 0.f;
+                            float acc = 0.f;
 #pragma unroll
-                            for (int jj = 0; jj < rr; ++jj) acc -= lrow[jj] * tv[jj];
-                            tv[rr] = acc;
+                            for (int jj = 0; jj < rr; ++jj) {
+                                const float ljj = __int_as_float(
+                                    __builtin_amdgcn_readlane(__float_as_int(lb[jj & 3]), rr + 16 * (jj >> 2)));
+                                acc -= ljj * tv[jj];
+                            }
+                            tv[rr] = (rr == cl) ? 1.f : acc;
                         }
                         if (lane < 16) {
 #pragma unroll
@@ -449,33 +463,35 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
                             *reinterpret_cast<const uint4 *>(Os + cc * PV + cv * EPV);
                 }
             }
+            if (n + 2 < NC) rstore(n + 2);            // into slot n & 1, freed in I3
         } else {
             if (c < NC) {
-                // M1 = (H o T) diag(beta), M2 = -D_g T diag(beta), four columns per lane
+                // M1 = (H o T) diag(beta), M2 = -D_g T diag(beta): one thread per 16-column
+                // row segment of the lower block triangle (NPAIR * 16 segments)
                 const float *gs = gate(ps, 0), *eg = gate(ps, 1), *bes = gate(ps, 3);
-                for (int idx = rt; idx < NPAIR * 64; idx += kRoleThreads) {
+                if (rt < NPAIR * 16) {
                     int i, j;
-                    tri_pair(idx >> 6, i, j);
-                    const int r = 16 * i + ((idx >> 2) & 15);
-                    const int c0 = 16 * j + 4 * (idx & 3);
-                    const F tf = P::ld4(Ts + r * PC + c0);
-                    const f32x4 bc = lds_f32x4(bes + c0);
-                    const f32x4 gc = lds_f32x4(gs + c0);
+                    tri_pair(rt >> 4, i, j);
+                    const int r = 16 * i + (rt & 15);
+                    const int c0 = 16 * j;
+                    float tr[16];
+                    load_row16<P>(Ts + r * PC + c0, tr);
                     const float gr = gs[r], er = eg[r];
-                    f32x4 m1, m2;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
-                        m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
-                        m2[e] = HAS_A ? -er * tb : -tb;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 bc = lds_f32x4(bes + c0 + 4 * q4);
+                        const f32x4 gc = lds_f32x4(gs + c0 + 4 * q4);
+                        f32x4 m1, m2;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float tb = (c0 + 4 * q4 + e <= r) ? tr[4 * q4 + e] * bc[e] : 0.f;
+                            m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+                            m2[e] = HAS_A ? -er * tb : -tb;
+                        }
+                        P::st4(M1s + r * PC + c0 + 4 * q4, m1);
+                        P::st4(M2s + r * PC + c0 + 4 * q4, m2);
                     }
-                    P::st4(M1s + r * PC + c0, m1);
-                    P::st4(M2s + r * PC + c0, m2);
                 }
-            }
-            if (c + 1 < NC) {
-                rstore(c + 1);                    // into slot (c + 1) & 1, freed by the scan in I3
-                if (c + 2 < NC) gload(c + 2);
             }
         }
         __syncthreads();
