@@ -456,7 +456,11 @@ bool chunk_fwd_supported(int dtype, int dk, int dv, int C) {
 }
 
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {
-    if (dtype == 1) return launch_chunk_fwd_pipe(dk, C, a, stream);
+    if (dtype == 1) {
+        // C = 32, 64: the pipelined kernel; C = 16 is too short to pair chunk positions
+        if (C != 16) return launch_chunk_fwd_pipe(dk, C, a, stream);
+        return dk == 128 ? launch_typed<Bf16, 128, 16>(a, stream) : launch_typed<Bf16, 64, 16>(a, stream);
+    }
     return dk == 128 ? launch_dk<F32, 128>(C, a, stream) : launch_dk<F32, 64>(C, a, stream);
 }
 

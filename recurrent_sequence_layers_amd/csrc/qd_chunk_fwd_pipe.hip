@@ -1,36 +1,54 @@
-// Pipelined chunkwise Q-Delta layer forward for gfx950, bf16 inputs.
+// Pipelined chunkwise Q-Delta layer forward for gfx950, bf16 inputs, C = 32 or 64.
 //
-// Same arithmetic as the sequential kernel in qd_chunk_fwd.hip (Q-Delta reading
-// notes §2.6, chunkwise WY/UT form with entry state; see that file for the
-// per-chunk formulas), scheduled as a two-stage software pipeline inside one
-// workgroup of eight waves:
+// Arithmetic: the chunkwise WY/UT form with entry state (Q-Delta reading notes
+// §2.6; the per-chunk formulas are listed in qd_chunk_fwd.hip), rearranged so that
+// the chunk's decay enters the triangular solve instead of being applied after it:
 //
-//   scan waves 0-3  run the state-dependent part of chunk n (U~ = M1 V, K S^T and
-//                   Q S^T, Z, O, the state update); wave w owns value columns
-//                   [16w, 16w + 16) of the 64-wide tile and keeps its S^T slice in
-//                   registers for the whole sequence;
-//   prep waves 4-7  run the state-independent part of chunk n + 1 (Gram products,
-//                   L and A, the UT-transform solve for T, M1 and M2).
-// The scan waves also fetch chunk n + 2 from HBM at the end of their busiest phase
-// and stage it into LDS at the end of the step.
+//   L_g = H o strictly-lower(diag(beta) X K^T),   H[r][c] = exp(g_r - g_c)
+//   T_g = (I + L_g)^-1 = H o (I + L)^-1           (diagonal scalings commute)
+//   M1  = T_g diag(beta)                          (= (H o T) diag(beta))
+//   Z   = M1 (V - D_g Y),  Y = K S^T + diag(lambda) Q S^T
+//                                                 (M2 = -D_g T diag(beta) = -M1 D_g)
+//   O   = D_g Q S^T + A Z,  A = H o (Q K^T) (lower, with diagonal)
+//   S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z
 //
-// Every SIMD holds one wave of each role, so the latency of one role's chains is
-// hidden behind the other's work.  Each pipeline step has four intervals separated
-// by workgroup barriers placed outside the role branches, so both roles always
-// execute the same barriers:
+// One workgroup of eight waves owns one (batch, head, 64-wide value tile) and runs a
+// two-stage software pipeline over the chunks:
 //
-//   interval  scan (chunk n)                  prep (chunk c = n + 1)
-//   I1        U~ = M1 V, K S^T, Q S^T,        Gram blocks, L, A; diagonal T blocks
-//             Z = U~ + M2 Y, O (staged);
-//             load chunk n + 2 from HBM
-//   I2        S^T update, key tiles 0..d_k/32 T level 1 (block doubling)
-//   I3        S^T update, the other half      T level 2
-//   I4        store O; stage chunk n + 2      M1, M2
+//   scan waves 0-3  state-dependent work of chunk n; wave w owns value columns
+//                   [16w, 16w + 16) and keeps its slice of S^T (fp32) in registers;
+//   prep waves 4-7  state-independent work of chunk c = n + 1 (Gram blocks, L_g, A,
+//                   the UT-transform solve, M1).
 //
-// Buffers crossing roles are double-buffered by chunk parity (q, k, v, A, gates);
-// M1 and M2 are single-buffered because the scan reads them in I1 and the prep
-// rewrites them in I4.  LDS: 155 KB for d_k = 128, C = 64.
-#include "qd_chunk_common.h"
+// Every SIMD hosts one wave of each role.  A pipeline step has four intervals
+// separated by workgroup barriers that both roles execute:
+//
+//   interval  scan (chunk n)                         prep (chunk c = n + 1)
+//   I1        Y, Z, O (O staged in LDS)              Gram blocks on MFMA; A and L_g written;
+//                                                    each wave inverts its diagonal 16x16
+//                                                    block of T_g in registers
+//   I2        fetch chunk n + 2 (registers);         M1 of the diagonal blocks; block
+//             S^T update, first half of the keys     doubling, level 1
+//   I3        S^T update, second half                block doubling, level 2 (C = 64)
+//   I4        stage chunk n + 2 in LDS; gate
+//             prefix sums; store O
+//
+// LDS layouts (bf16 unless noted):
+//   q, k slots [2][C][d_k + 8]  rows padded by one 16-byte quad, so 16 consecutive
+//                           rows read at one quad hit distinct banks;
+//   v slots    [2][C][72]   padded rows;
+//   A [2], M1  [C][C + 8]   columns permuted inside each 32-wide group so that one b128
+//                           read yields the eight contraction values a 16x16x32 MFMA
+//                           pairs with two register tiles (positions 4g..4g+3 and
+//                           16+4g..16+4g+3);
+//   L_g        [C][C + 8]   off-diagonal blocks (diagonal blocks stay in registers);
+//   T_g        [C][C + 8]   stored transposed (row c holds column c of T_g);
+//   O staging  [C][72];  gates [2][5][C] fp32.
+//
+// Global traffic uses buffer instructions whose resource is re-based at every chunk:
+// the range check returns zeros for rows past the end of the sequence and drops
+// their stores, so the tail chunk needs no clamping or masking (it is padded with
+// q = k = v = 0, beta = 0, alpha = 1, which leaves the state and valid outputs alone).
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -41,466 +59,627 @@ constexpr int kPipeThreads = 512;
 constexpr int kRoleThreads = 256;
 constexpr int kDVT = 64;
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// acc += A (16 x 32) B (32 x 16); every bf16 product in this kernel uses this one shape
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// acc += A (16 x 16) B (16 x 16), the same instruction with a zero second slice
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 acc) {
+    const bf16x4 z = {};
+    return mfma32(cat8(a, z), cat8(b, z), acc);
+}
+__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+__device__ __forceinline__ void sts4(uint16_t *p, f32x4 v) {
+    *reinterpret_cast<bf16x4 *>(p) = Bf16::cvt(v);
+}
+// LDS transpose read (8 bytes per lane): within each 16-lane group, lane 4p + q receives
+// element q of the four-element chunks read by lanes 4i + p, i = 0..3.
+__device__ __forceinline__ bf16x4 lds_tr(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p)));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes) {
+    // raw buffer (stride 0): accesses at offsets >= bytes read 0 and do not write
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts and row
+// broadcasts (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_src<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_src<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_src<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_src<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_src<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_src<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Value of lane k of each group of four lanes (DPP quad permutation).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
+}
+
+// acc + A B for fp32 fragments a (A operand) and b (B operand), each split into a bf16 high
+// part and a bf16 remainder: two 16x16x32 MFMAs give hi.hi + lo.hi + hi.lo + lo.lo, which
+// is exact to about 2^-16 of the operands.
+__device__ __forceinline__ f32x4 mfma_split(f32x4 a, f32x4 b, f32x4 acc) {
+    const bf16x4 ah = Bf16::cvt(a), bh = Bf16::cvt(b);
+    const bf16x4 al = Bf16::cvt(a - __builtin_convertvector(ah, f32x4));
+    const bf16x4 bl = Bf16::cvt(b - __builtin_convertvector(bh, f32x4));
+    const bf16x8 a8 = cat8(ah, al);
+    acc = mfma32(a8, cat8(bh, bh), acc);
+    return mfma32(a8, cat8(bl, bl), acc);
+}
+
+// Inverse T of a 16x16 unit lower triangular block I + L, stable block forward substitution:
+//   4x4 diagonal blocks inverted in registers (lanes 4j.. of a quad hold rows j),
+//   then T21 = -T22 L21 T11 twice (4 -> 8 -> 16) on MFMA.
+// In: lv = L[m][4g + e] (lane g = l/16, m = l%16; the MFMA A-operand layout of L, fp32).
+// Out: T[4g + e][n] (n = l%16; the accumulator layout).  Both layouts of every partial
+// inverse are produced by multiplying in both orders, so no LDS transposes are needed.
+__device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
+    // 4x4 diagonal blocks.  In the quad of lanes (g, 4g .. 4g+3), lane j holds row j of D
+    // (D = the block's strictly lower part); the others hold rows of off-diagonal blocks.
+    const int j = m & 3;
+    const bool diag = (m >> 2) == g;
+    const float d10 = quad_bcast<1>(lv[0]);
+    const float d20 = quad_bcast<2>(lv[0]), d21 = quad_bcast<2>(lv[1]);
+    const float d30 = quad_bcast<3>(lv[0]), d31 = quad_bcast<3>(lv[1]), d32 = quad_bcast<3>(lv[2]);
+    // row j of D^-1 (A layout: lane (g, m) gets T4[m][4g + e])
+    f32x4 ra;
+    ra[0] = (j == 0) ? 1.f : -lv[0] + lv[1] * d10 + lv[2] * (d20 - d21 * d10);
+    ra[1] = (j == 1) ? 1.f : -lv[1] + lv[2] * d21;
+    ra[2] = (j == 2) ? 1.f : -lv[2];
+    ra[3] = (j == 3) ? 1.f : 0.f;
+    // column j of D^-1 (B layout: lane (g, n) gets T4[4g + e][n])
+    f32x4 cb;
+    cb[0] = (j == 0) ? 1.f : 0.f;
+    cb[1] = ((j == 1) ? 1.f : 0.f) - d10 * cb[0];
+    cb[2] = ((j == 2) ? 1.f : 0.f) - d20 * cb[0] - d21 * cb[1];
+    cb[3] = ((j == 3) ? 1.f : 0.f) - d30 * cb[0] - d31 * cb[1] - d32 * cb[2];
+    const f32x4 A4 = diag ? ra : zero4(), B4 = diag ? cb : zero4();
+    // 4 -> 8: L restricted to 4x4 blocks (1,0) and (3,2)
+    const f32x4 Lm4 = ((m >> 2) == g + 1 && (g & 1) == 0) ? lv : zero4();
+    const f32x4 X = mfma_split(Lm4, B4, zero4());        // L' T4
+    const f32x4 Y = mfma_split(A4, X, zero4());          // T4 L' T4
+    const f32x4 Yt = mfma_split(X, A4, zero4());         // (T4 L' T4)^T
+    const f32x4 B8 = B4 - Y, A8 = A4 - Yt;
+    // 8 -> 16: L restricted to rows 8..15, columns 0..7
+    const f32x4 Lm8 = (m >= 8 && g < 2) ? lv : zero4();
+    const f32x4 X2 = mfma_split(Lm8, B8, zero4());
+    return B8 - mfma_split(A8, X2, zero4());
+}
+
+// Column permutation of A and M1 inside each 32-wide group: column 16h + 4g + e is
+// stored at 8g + 4h + e.
+__device__ __forceinline__ int pcol(int c) {
+    return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+
 template <int DK, int CH>
 struct PipeLayout {
-    static constexpr int PAD = 8;                 // 16 bytes of bf16 row padding
-    static constexpr int PK = DK + PAD;
-    static constexpr int PC = CH + PAD;
-    static constexpr int PV = kDVT + PAD;
+    static constexpr int NCT = CH / 16;
+    static constexpr int PC = CH + 8;             // chunk x chunk rows, 16 bytes of padding
+    static constexpr int PV = kDVT + 8;           // v rows and the output staging
+    static constexpr int PK = DK + 8;             // q, k rows
     static constexpr int NQ = CH * PK;
     static constexpr int NV = CH * PV;
     static constexpr int NCC = CH * PC;
+    // bf16 element offsets
     static constexpr int oQ = 0;                  // [2][NQ]
     static constexpr int oK = oQ + 2 * NQ;        // [2][NQ]
     static constexpr int oV = oK + 2 * NQ;        // [2][NV]
     static constexpr int oA = oV + 2 * NV;        // [2][NCC]
-    static constexpr int oM1 = oA + 2 * NCC;
-    static constexpr int oM2 = oM1 + NCC;
-    static constexpr int oL = oM2 + NCC;
-    static constexpr int oT = oL + NCC;
-    static constexpr int oO = oT + NCC;           // output staging [NV]
+    static constexpr int oM1 = oA + 2 * NCC;      // directly after A: both are zeroed together
+    static constexpr int oLg = oM1 + NCC;
+    static constexpr int oTd = oLg + NCC;
+    static constexpr int oO = oTd + NCC;
     static constexpr int nR = oO + NV;
+    // byte offset of the fp32 gates
     static constexpr int kGates = 5;              // g, exp(g), exp(g_last - g), beta, lambda
-    static constexpr int bytes = nR * 2 + 2 * kGates * CH * 4;
-    static_assert((PK * 2) % 16 == 0 && (PC * 2) % 16 == 0 && (PV * 2) % 16 == 0, "16-byte row alignment");
+    static constexpr int oGate = nR * 2;
+    static constexpr int bytes = oGate + 2 * kGates * CH * 4;
+    static_assert((PK * 2) % 16 == 0 && (PC * 2) % 16 == 0 && (PV * 2) % 16 == 0 && oGate % 16 == 0,
+                  "16-byte alignment of rows");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
-// Gram blocks (i, j) of the prep wave p, diagonal block first; u is a compile-time
-// slot index and p is wave-uniform, so this folds to scalar selects (a lookup table
-// would become a global load whose wait would also drain the in-flight prefetch).
-// Balanced over the four prep waves for C = 64: p0 (0,0) (3,0) (3,1); p1 (1,1) (1,0)
-// (3,2); p2 (2,2) (2,0) (2,1); p3 (3,3).  The wave owning a diagonal block inverts it.
-template <int NCT>
-__device__ __forceinline__ bool prep_block(int p, int u, int &i, int &j) {
-    i = -1;
-    j = -1;
-    if (u == 0) {
-        if (p < NCT) { i = p; j = p; }
-    } else if constexpr (NCT == 4) {
-        if (u == 1) {
-            i = (p == 0) ? 3 : p;
-            j = (p == 0) ? 0 : (p == 1) ? 0 : (p == 2) ? 0 : -1;
-            if (p == 3) i = -1;
-        } else {
-            i = (p == 3) ? -1 : (p == 2) ? 2 : 3;
-            j = (p == 0) ? 1 : (p == 1) ? 2 : 1;
-        }
-    } else if constexpr (NCT == 2) {
-        if (u == 1 && p == 1) { i = 1; j = 0; }
-    }
-    return i >= 0;
+// Gram blocks (i, j), j <= i, of prep wave P.  Wave P owns diagonal block P (listed first;
+// it inverts that block right after the Gram products) and a share of the off-diagonal
+// blocks, chosen so that blocks on one wave share operand tiles.
+template <int NCT, int P>
+struct GramPlan;
+template <> struct GramPlan<4, 0> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 1> { static constexpr int n = 2; static constexpr int i[4] = {1, 2, 0, 0}, j[4] = {1, 1, 0, 0}; };
+template <> struct GramPlan<4, 2> { static constexpr int n = 3; static constexpr int i[4] = {2, 2, 3, 0}, j[4] = {2, 0, 0, 0}; };
+template <> struct GramPlan<4, 3> { static constexpr int n = 3; static constexpr int i[4] = {3, 3, 3, 0}, j[4] = {3, 1, 2, 0}; };
+template <> struct GramPlan<2, 0> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<2, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<2, 2> { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<2, 3> { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+
+constexpr int tile_mask(const int (&t)[4], int n) {
+    int m = 0;
+    for (int b = 0; b < n; ++b) m |= 1 << t[b];
+    return m;
 }
 
 template <int DK, int CH, bool HAS_A, bool HAS_L>
-__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const ChunkArgs args) {
-    using P = Bf16;
-    using R = uint16_t;
-    using F = bf16x4;
+struct PipeKernel {
     using Lay = PipeLayout<DK, CH>;
-    constexpr int NKT = DK / 16;
-    constexpr int NCT = CH / 16;
-    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
-    constexpr int EPV = 8;                        // bf16 per 16-byte vector
-    constexpr int VPRQ = DK / EPV;
-    constexpr int VPRV = kDVT / EPV;
-    constexpr int NVQ = (CH * VPRQ + kRoleThreads - 1) / kRoleThreads;
-    constexpr int NVV = (CH * VPRV + kRoleThreads - 1) / kRoleThreads;
-    constexpr int NPAIR = NCT * (NCT + 1) / 2;
+    static constexpr int NKT = DK / 16, NKP = DK / 32;
+    static constexpr int NCT = CH / 16, NCP = CH / 32;
+    static constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
+    // Key layout of the register tiles: in the pair step u, lane group g supplies the
+    // eight keys of quad NKP g + u (so the four groups read quads that are d_k / 4 keys
+    // apart, and the transpose reads of the state update fall on distinct banks).
+    __device__ __forceinline__ static int kq(int g, int u) { return NKP * g + u; }
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
-    R *const base = reinterpret_cast<R *>(smem);
-    R *const M1s = base + Lay::oM1;
-    R *const M2s = base + Lay::oM2;
-    R *const Ls = base + Lay::oL;
-    R *const Ts = base + Lay::oT;
-    R *const Os = base + Lay::oO;
-    float *const gbase = reinterpret_cast<float *>(smem + Lay::nR * 2);
-    auto Qb = [&](int s) { return base + Lay::oQ + s * Lay::NQ; };
-    auto Kb = [&](int s) { return base + Lay::oK + s * Lay::NQ; };
-    auto Vb = [&](int s) { return base + Lay::oV + s * Lay::NV; };
-    auto Ab = [&](int s) { return base + Lay::oA + s * Lay::NCC; };
-    // gate arrays of slot s: 0 g, 1 exp(g), 2 exp(g_last - g), 3 beta, 4 lambda
-    auto gate = [&](int s, int which) { return gbase + (s * Lay::kGates + which) * CH; };
-
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const bool is_scan = wave < 4;
-    const int rw = wave & 3;                      // wave index within its role
-    const int rt = tid & (kRoleThreads - 1);      // thread index within its role
-    const int r16 = lane & 15;
-    const int g4 = lane >> 4;
-
-    const int nblk = gridDim.x;
-    int logical = blockIdx.x;
-    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int dvt = logical % args.n_dvt;
-    const int bh = logical / args.n_dvt;
-    const int b = bh / args.H;
-    const int h = bh % args.H;
-    const int T = args.T, H = args.H, dv = args.dv;
-    const int dv0 = dvt * kDVT;
-    const R *__restrict__ gq = static_cast<const R *>(args.q);
-    const R *__restrict__ gk = static_cast<const R *>(args.k);
-    const R *__restrict__ gv = static_cast<const R *>(args.v);
-    R *__restrict__ go = static_cast<R *>(args.o);
-    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
-    const int NC = (T + CH - 1) / CH;
-    auto chunk_len = [&](int c) { return min(CH, T - c * CH); };
-
-    // ---- scan role: state slice S^T (rows d_k = 16t + 4g + i, column = own value column)
-    f32x4 sT[NKT];
-    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * rw + r16) * DK;
+    // Gram blocks of prep wave P for the chunk in slot ps, then the A and L_g epilogue.
+    // Block (i, j): D = K_j [Q_i | K_i]^T, so lane (g, n) holds q_r.k_c and k_r.k_c for
+    // r = 16i + n, c = 16j + 4g + e.
+    template <int P>
+    __device__ __forceinline__ static void gram(const uint16_t *Qs, const uint16_t *Ks, uint16_t *As, uint16_t *Lg,
+                                                uint16_t *Td, const float *gs, const float *bes, const float *lams,
+                                                int r16, int g4, f32x4 &tdiag) {
+        using Plan = GramPlan<NCT, P>;
+        constexpr int NB = Plan::n;
+        if constexpr (NB > 0) {
+            f32x4 gq[NB], gk[NB];
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
-        sT[t] = (is_scan && args.S0) ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
-
-    // ---- raw chunk registers of the scan role (loaded at the end of I1, staged in I4)
-    uint4 rq[NVQ], rk[NVQ], rv[NVV];
-    float ra = 1.f, rb = 0.f, rl = 0.f;
-    auto gload = [&](int c) {
-        const int t0 = c * CH;
-        const int last = chunk_len(c) - 1;
+            for (int b = 0; b < NB; ++b) { gq[b] = zero4(); gk[b] = zero4(); }
+            // 16-row tiles of K and Q this wave reads (each loaded once per key pair); the
+            // tiles of the next key pair are issued before the MFMAs of the current one
+            constexpr int kmask = tile_mask(Plan::i, NB) | tile_mask(Plan::j, NB);
+            constexpr int qmask = tile_mask(Plan::i, NB);
+            bf16x8 kt[2][NCT], qt[2][NCT];
+            auto load = [&](int u, bf16x8(&k)[NCT], bf16x8(&q)[NCT]) {
 #pragma unroll
-        for (int j = 0; j < NVQ; ++j) {
-            const int vi = rt + kRoleThreads * j;
-            if (CH * VPRQ % kRoleThreads == 0 || vi < CH * VPRQ) {
-                const int cc = min(vi / VPRQ, last), cv = vi % VPRQ;
-                const size_t off = tok(t0 + cc) * DK + cv * EPV;
-                rq[j] = *reinterpret_cast<const uint4 *>(gq + off);
-                rk[j] = *reinterpret_cast<const uint4 *>(gk + off);
+                for (int m = 0; m < NCT; ++m) {
+                    const int off = (16 * m + r16) * PK + 8 * kq(g4, u);
+                    if (kmask & (1 << m)) k[m] = lds8(Ks + off);
+                    if (qmask & (1 << m)) q[m] = lds8(Qs + off);
+                }
+            };
+            load(0, kt[0], qt[0]);
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                if (u + 1 < NKP) load(u + 1, kt[(u + 1) & 1], qt[(u + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const bf16x8 a = kt[u & 1][Plan::j[b]];
+                    gq[b] = mfma32(a, qt[u & 1][Plan::i[b]], gq[b]);
+                    gk[b] = mfma32(a, kt[u & 1][Plan::i[b]], gk[b]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int i = Plan::i[b], j = Plan::j[b];
+                const int r = 16 * i + r16;
+                const int c0 = 16 * j + 4 * g4;
+                const float gr = gs[r], br = bes[r];
+                const float lr = HAS_L ? lams[r] : 0.f;
+                const f32x4 gc = lds_f32x4(gs + c0);
+                f32x4 av, lv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int cc = c0 + e;
+                    const float f = HAS_A ? __expf(gr - gc[e]) : 1.f;
+                    const float xk = HAS_L ? gk[b][e] + lr * gq[b][e] : gk[b][e];
+                    av[e] = (cc <= r) ? f * gq[b][e] : 0.f;
+                    lv[e] = (cc < r) ? (f * br) * xk : 0.f;
+                }
+                sts4(As + r * PC + 32 * (j >> 1) + 8 * g4 + 4 * (j & 1), av);
+                if (i == j) {
+                    tdiag = invert_unit_lower16(lv, g4, r16);
+                    sts4(Td + (16 * i + r16) * PC + 16 * i + 4 * g4, tdiag);   // T_g[16i + 4g + e][16i + n]
+                } else {
+                    sts4(Lg + r * PC + c0, lv);
+                }
             }
         }
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int vi = rt + kRoleThreads * j;
-            if (CH * VPRV % kRoleThreads == 0 || vi < CH * VPRV) {
-                const int cc = min(vi / VPRV, last), cv = vi % VPRV;
-                rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(t0 + cc) * dv + dv0 + cv * EPV);
-            }
-        }
-        {   // every role thread loads (clamped) so the loads carry no branch
-            const size_t gi = tok(t0 + min(rt & (kWave - 1), last));
-            if constexpr (HAS_A) ra = args.alpha[gi];
-            rb = args.beta[gi];
-            if constexpr (HAS_L) rl = args.lam[gi];
-        }
-    };
-    auto rstore = [&](int c) {                    // stage chunk c into LDS slot c & 1
-        const int s = c & 1;
-        const int clen = chunk_len(c);
-        R *Qs = Qb(s), *Ks = Kb(s), *Vs = Vb(s);
-#pragma unroll
-        for (int j = 0; j < NVQ; ++j) {
-            const int vi = rt + kRoleThreads * j;
-            if (CH * VPRQ % kRoleThreads == 0 || vi < CH * VPRQ) {
-                const int cc = vi / VPRQ, cv = vi % VPRQ;
-                *reinterpret_cast<uint4 *>(Qs + cc * PK + cv * EPV) = keep_if(cc < clen, rq[j]);
-                *reinterpret_cast<uint4 *>(Ks + cc * PK + cv * EPV) = keep_if(cc < clen, rk[j]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int vi = rt + kRoleThreads * j;
-            if (CH * VPRV % kRoleThreads == 0 || vi < CH * VPRV) {
-                const int cc = vi / VPRV, cv = vi % VPRV;
-                *reinterpret_cast<uint4 *>(Vs + cc * PV + cv * EPV) = keep_if(cc < clen, rv[j]);
-            }
-        }
-        if (rw == 0) {                            // first wave of the role: gate prefix sums
-            const bool ok = lane < clen;
-            float x = (HAS_A && ok) ? __logf(ra) : 0.f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, CH - 1);
-            if (lane < CH) {
-                gate(s, 0)[lane] = x;
-                gate(s, 1)[lane] = __expf(x);
-                gate(s, 2)[lane] = __expf(glast - x);
-                gate(s, 3)[lane] = ok ? rb : 0.f;
-                gate(s, 4)[lane] = ok ? rl : 0.f;
-            }
-        }
-    };
+    }
 
-    if (NC == 0) {
+    __device__ static void run(const ChunkArgs &args) {
+        constexpr int VPRQ = DK / 8;              // 16-byte vectors per q/k row
+        constexpr int VPRV = kDVT / 8;
+        constexpr int NVQ = CH * VPRQ / kRoleThreads;
+        constexpr int NVV = CH * VPRV / kRoleThreads;
+        constexpr int RJQ = kRoleThreads / VPRQ;  // rows between a thread's vectors
+        constexpr int RJV = kRoleThreads / VPRV;
+        static_assert(CH * VPRQ % kRoleThreads == 0 && CH * VPRV % kRoleThreads == 0, "whole vectors per thread");
+
+        __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+        uint16_t *const base = reinterpret_cast<uint16_t *>(smem);
+        uint16_t *const M1s = base + Lay::oM1;
+        uint16_t *const Lgs = base + Lay::oLg;
+        uint16_t *const Tds = base + Lay::oTd;
+        uint16_t *const Os = base + Lay::oO;
+        float *const gbase = reinterpret_cast<float *>(smem + Lay::oGate);
+        auto Qb = [&](int s) { return base + Lay::oQ + s * Lay::NQ; };
+        auto Kb = [&](int s) { return base + Lay::oK + s * Lay::NQ; };
+        auto Vb = [&](int s) { return base + Lay::oV + s * Lay::NV; };
+        auto Ab = [&](int s) { return base + Lay::oA + s * Lay::NCC; };
+        auto gate = [&](int s, int which) { return gbase + (s * Lay::kGates + which) * CH; };
+
+        const int tid = threadIdx.x;
+        const int lane = lane_id();
+        const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+        const bool is_scan = wave < 4;
+        const int rw = wave & 3;                  // wave index within its role
+        const int rt = tid & (kRoleThreads - 1);  // thread index within its role
+        const int r16 = lane & 15;
+        const int g4 = lane >> 4;
+        const int tri = r16 >> 2, trp = r16 & 3;  // transpose-read lane split: r16 = 4 tri + trp
+
+        const int nblk = gridDim.x;
+        int logical = blockIdx.x;
+        if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+        const int dvt = logical % args.n_dvt;
+        const int bh = logical / args.n_dvt;
+        const int b = bh / args.H;
+        const int h = bh % args.H;
+        const int T = args.T, H = args.H, dv = args.dv;
+        const int dv0 = dvt * kDVT;
+        const int NC = (T + CH - 1) / CH;
+        auto chunk_len = [&](int c) { return min(CH, T - c * CH); };
+
+        // token 0 of this (batch, head); consecutive tokens are H rows apart
+        const size_t tok0 = static_cast<size_t>(b) * T * H + h;
+        const uint16_t *const qbase = static_cast<const uint16_t *>(args.q) + tok0 * DK;
+        const uint16_t *const kbase = static_cast<const uint16_t *>(args.k) + tok0 * DK;
+        const uint16_t *const vbase = static_cast<const uint16_t *>(args.v) + tok0 * dv + dv0;
+        uint16_t *const obase = static_cast<uint16_t *>(args.o) + tok0 * dv + dv0;
+        const int rowQ = H * DK * 2, rowV = H * dv * 2, rowG = H * 4;   // bytes between tokens
+
+        // ---- scan role: S^T slice; sT[2u + hh][e] holds key 8 kq(g, u) + 4hh + e of column 16w + l%16
+        f32x4 sT[NKT];
+        const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * rw + r16) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+            sT[t] = (is_scan && args.S0)
+                        ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1))
+                        : zero4();
+
+        // ---- scan-role prefetch of chunk n + 2: registers, per-lane offsets fixed per chunk
+        const int vq_row = rt / VPRQ, vq_col = rt % VPRQ;
+        const int vv_row = rt / VPRV, vv_col = rt % VPRV;
+        int voffQ[NVQ], voffV[NVV];
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) voffQ[j] = (vq_row + j * RJQ) * rowQ + vq_col * 16;
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) voffV[j] = (vv_row + j * RJV) * rowV + vv_col * 16;
+        const int voffG = (rt & (kWave - 1)) * rowG;
+        const int ldsQ = vq_row * PK + vq_col * 8;        // + j * RJQ * PK
+        const int ldsV = vv_row * PV + vv_col * 8;        // + j * RJV * PV
+
+        // registers of one prefetched chunk; declared per pipeline step so that they are
+        // not carried around the loop (and so not live in the prep role's code)
+        struct Prefetch {
+            u32x4 q[NVQ], k[NVQ], v[NVV];
+            float a, b, l;
+        };
+        auto gload = [&](int c, Prefetch &pf) {
+            const int clen = chunk_len(c);
+            const size_t t0 = static_cast<size_t>(c) * CH * H;
+            const auto rsq = buffer_rsrc(qbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
+            const auto rsk = buffer_rsrc(kbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
+            const auto rsv = buffer_rsrc(vbase + t0 * dv, (clen - 1) * rowV + kDVT * 2);
+#pragma unroll
+            for (int j = 0; j < NVQ; ++j) {
+                pf.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voffQ[j], 0, 0);
+                pf.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, voffQ[j], 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) pf.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voffV[j], 0, 0);
+            const int gbytes = (clen - 1) * rowG + 4;
+            pf.a = 1.f;
+            pf.l = 0.f;
+            if constexpr (HAS_A)
+                pf.a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.alpha + tok0 + t0, gbytes), voffG, 0, 0));
+            pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.beta + tok0 + t0, gbytes), voffG, 0, 0));
+            if constexpr (HAS_L)
+                pf.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.lam + tok0 + t0, gbytes), voffG, 0, 0));
+        };
+        auto rstore = [&](int c, const Prefetch &pf) {   // stage chunk c into LDS slot c & 1
+            const int s = c & 1;
+            uint16_t *Qs = Qb(s), *Ks = Kb(s), *Vs = Vb(s);
+#pragma unroll
+            for (int j = 0; j < NVQ; ++j) {
+                *reinterpret_cast<u32x4 *>(Qs + ldsQ + j * RJQ * PK) = pf.q[j];
+                *reinterpret_cast<u32x4 *>(Ks + ldsQ + j * RJQ * PK) = pf.k[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
+            if (rw == 0) {                        // gates of the chunk, lane = position
+                const bool ok = lane < chunk_len(c);
+                const float x = wave_inclusive_sum((HAS_A && ok) ? __logf(pf.a) : 0.f);
+                const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
+                if (lane < CH) {
+                    gate(s, 0)[lane] = x;
+                    gate(s, 1)[lane] = __expf(x);
+                    gate(s, 2)[lane] = __expf(glast - x);
+                    gate(s, 3)[lane] = ok ? pf.b : 0.f;
+                    gate(s, 4)[lane] = ok ? pf.l : 0.f;
+                }
+            }
+        };
+
+        // A (both slots) and M1 start zeroed: the upper 16x16 block of each 32-wide diagonal
+        // pair is read by the scan's paired products and must hold zeros
+        for (int i = tid; i < 3 * Lay::NCC / 8; i += kPipeThreads)
+            reinterpret_cast<u32x4 *>(base + Lay::oA)[i] = u32x4{0, 0, 0, 0};
+
+        if (NC == 0) {
+            if (is_scan && args.S_T) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+                    *reinterpret_cast<f32x4 *>(args.S_T + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = sT[t];
+            }
+            return;
+        }
+
+        if (is_scan) {
+            Prefetch pf;
+            gload(0, pf);
+            rstore(0, pf);
+        }
+        __syncthreads();
+
+        for (int n = -1; n < NC; ++n) {
+            const int c = n + 1;                  // the prep role's chunk
+            const int ss = n & 1;                 // scan slot (n >= 0)
+            const int ps = c & 1;                 // prep slot
+            // lane-dependent LDS addresses are rebuilt from an opaque copy of the thread id at
+            // every step rather than hoisted out of the loop: held across the loop they would
+            // not fit the register file next to the state
+            int lid_ = threadIdx.x;
+            asm volatile("" : "+v"(lid_));
+            const int lane = lid_ & (kWave - 1), r16 = lane & 15, g4 = lane >> 4, tri = r16 >> 2, trp = r16 & 3;
+            Prefetch pf;                          // scan: chunk n + 2, loaded in I1, staged in I4
+            bf16x4 Zd[NCT];                       // scan: exp(g_last - g) Z, from I1 to I2/I3
+            f32x4 tdiag;                          // prep: the wave's diagonal block of T_g, I1 to I2
+
+            // ============================================================ I1
+            if (is_scan) {
+                if (n >= 0) {
+                    // Software-pipelined by hand: the fragments of the next tile are issued
+                    // before the MFMAs of the current one, and scheduling fences keep the
+                    // compiler from sinking each LDS read next to its use.
+                    const uint16_t *Qs = Qb(ss), *Ks = Kb(ss), *Vs = Vb(ss), *As = Ab(ss);
+                    const float *lam_s = gate(ss, 4), *eg = gate(ss, 1), *egl = gate(ss, 2);
+                    bf16x8 fk[2][NKP], fq[2][NKP];
+                    auto load_qk = [&](int mt, bf16x8(&k)[NKP], bf16x8(&q)[NKP]) {
+#pragma unroll
+                        for (int u = 0; u < NKP; ++u) {
+                            const int off = (16 * mt + r16) * PK + 8 * kq(g4, u);
+                            k[u] = lds8(Ks + off);
+                            q[u] = lds8(Qs + off);
+                        }
+                    };
+                    load_qk(0, fk[0], fq[0]);
+                    bf16x8 sTf[NKP];
+#pragma unroll
+                    for (int u = 0; u < NKP; ++u) sTf[u] = cat8(Bf16::cvt(sT[2 * u]), Bf16::cvt(sT[2 * u + 1]));
+                    bf16x8 Vf[NCP], m1f[NCT][NCP];
+                    f32x4 PK_[NCT], PQ[NCT];
+                    __builtin_amdgcn_sched_barrier(0);
+                    // K S^T and Q S^T
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) {
+                        if (mt + 1 < NCT) {
+                            load_qk(mt + 1, fk[(mt + 1) & 1], fq[(mt + 1) & 1]);
+                        } else {
+                            // operands of Z: V as the paired B operand (positions 32u + 4g + i
+                            // and 32u + 16 + 4g + i) and the M1 fragments
+#pragma unroll
+                            for (int u = 0; u < NCP; ++u) {
+                                const uint16_t *p = Vs + (32 * u + 4 * g4 + tri) * PV + 16 * rw + 4 * trp;
+                                Vf[u] = cat8(lds_tr(p), lds_tr(p + 16 * PV));
+                            }
+#pragma unroll
+                            for (int m = 0; m < NCT; ++m)
+#pragma unroll
+                                for (int u = 0; u <= (m >> 1); ++u)
+                                    m1f[m][u] = lds8(M1s + (16 * m + r16) * PC + 32 * u + 8 * g4);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        f32x4 pk = zero4(), pq = zero4();
+#pragma unroll
+                        for (int u = 0; u < NKP; ++u) {
+                            pk = mfma32(fk[mt & 1][u], sTf[u], pk);
+                            pq = mfma32(fq[mt & 1][u], sTf[u], pq);
+                        }
+                        PK_[mt] = pk;
+                        PQ[mt] = pq;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    // Yg = -D_g (K S^T + diag(lambda) Q S^T); the A fragments of O are issued here
+                    bf16x8 af[NCT][NCP];
+#pragma unroll
+                    for (int m = 0; m < NCT; ++m)
+#pragma unroll
+                        for (int u = 0; u <= (m >> 1); ++u) af[m][u] = lds8(As + (16 * m + r16) * PC + 32 * u + 8 * g4);
+                    bf16x4 Yg[NCT];
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) {
+                        f32x4 y = PK_[mt];
+                        if constexpr (HAS_L) y += lds_f32x4(lam_s + 16 * mt + 4 * g4) * PQ[mt];
+                        if constexpr (HAS_A) y *= lds_f32x4(eg + 16 * mt + 4 * g4);
+                        Yg[mt] = Bf16::cvt(-y);
+                    }
+                    // Z = M1 V + M1 Yg (both products share the M1 fragment)
+                    f32x4 Z[NCT];
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) {
+                        f32x4 z = zero4();
+#pragma unroll
+                        for (int u = 0; u <= (mt >> 1); ++u) {
+                            z = mfma32(m1f[mt][u], Vf[u], z);
+                            z = mfma32(m1f[mt][u], cat8(Yg[2 * u], Yg[2 * u + 1]), z);
+                        }
+                        Z[mt] = z;
+                    }
+                    bf16x4 Zf[NCT];
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) {
+                        Zf[mt] = Bf16::cvt(Z[mt]);
+                        Zd[mt] = HAS_A ? Bf16::cvt(lds_f32x4(egl + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
+                    }
+                    // O = D_g Q S^T + A Z, staged for the row stores of I4
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) {
+                        f32x4 o = HAS_A ? lds_f32x4(eg + 16 * mt + 4 * g4) * PQ[mt] : PQ[mt];
+#pragma unroll
+                        for (int u = 0; u <= (mt >> 1); ++u) o = mfma32(af[mt][u], cat8(Zf[2 * u], Zf[2 * u + 1]), o);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = Bf16::from_f32(o[e]);
+                    }
+                }
+            } else if (c < NC) {
+                const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
+                uint16_t *As = Ab(ps);
+                const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
+                switch (rw) {
+                    case 0: gram<0>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 1: gram<1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 2: gram<2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    default: gram<3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                }
+            }
+            __syncthreads();
+
+            // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z for key tiles [t_lo, t_hi).
+            // Output row m of tile 2u + hh is key 8 kq(m/4, u) + 4hh + m%4, read from K with
+            // the transpose read: lane (g, 4i + p) reads keys 8 kq(p, u) + 4hh.. of position
+            // 32s + 4g + i (and + 16), matching the pairing of Zd[2s], Zd[2s + 1].
+            auto state_update = [&](int t_lo, int t_hi) {
+                const uint16_t *Ks = Kb(ss);
+                const float dlast = HAS_A ? gate(ss, 1)[CH - 1] : 1.f;
+                bf16x8 zp[NCP];
+#pragma unroll
+                for (int s = 0; s < NCP; ++s) zp[s] = cat8(Zd[2 * s], Zd[2 * s + 1]);
+                bf16x8 kf[2][NCP];
+                auto load = [&](int t, bf16x8(&dst)[NCP]) {
+                    const int col = 8 * kq(trp, t >> 1) + 4 * (t & 1);
+#pragma unroll
+                    for (int s = 0; s < NCP; ++s) {
+                        const uint16_t *p = Ks + (32 * s + 4 * g4 + tri) * PK + col;
+                        dst[s] = cat8(lds_tr(p), lds_tr(p + 16 * PK));
+                    }
+                };
+                load(t_lo, kf[0]);
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    if (t < t_lo || t >= t_hi) continue;
+                    if (t + 1 < t_hi) load(t + 1, kf[(t + 1 - t_lo) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x4 acc = sT[t] * dlast;
+#pragma unroll
+                    for (int s = 0; s < NCP; ++s) acc = mfma32(kf[(t - t_lo) & 1][s], zp[s], acc);
+                    sT[t] = acc;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+
+            // ============================================================ I2
+            if (is_scan) {
+                if (n + 2 < NC) gload(n + 2, pf); // staged in I4, after this slot is released
+                if (n >= 0) state_update(0, NKT / 2);
+            } else if (c < NC) {
+                if (rw < NCT) {                   // M1 of this wave's diagonal block
+                    const int o = 16 * rw;
+                    const float bc = gate(ps, 3)[o + r16];
+                    const int pc = pcol(o + r16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) M1s[(o + 4 * g4 + e) * PC + pc] = Bf16::from_f32(tdiag[e] * bc);
+                }
+                if (rw < NCT / 2) {
+                    // T_g[2a+1][2a] = -T_g[2a+1][2a+1] L_g[2a+1][2a] T_g[2a][2a]
+                    const int aa = 2 * rw, bb = 2 * rw + 1;
+                    const f32x4 x = mfma16(lds4(Lgs + (16 * bb + r16) * PC + 16 * aa + 4 * g4),
+                                           lds4(Tds + (16 * aa + r16) * PC + 16 * aa + 4 * g4), zero4());
+                    const f32x4 y = mfma16(lds_tr(Tds + (16 * bb + 4 * g4 + tri) * PC + 16 * bb + 4 * trp), Bf16::cvt(x),
+                                           zero4());
+                    if constexpr (NCT == 4) sts4(Tds + (16 * aa + r16) * PC + 16 * bb + 4 * g4, -y);
+                    const float bc = gate(ps, 3)[16 * aa + r16];
+                    const int pc = pcol(16 * aa + r16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) M1s[(16 * bb + 4 * g4 + e) * PC + pc] = Bf16::from_f32(-y[e] * bc);
+                }
+            }
+            __syncthreads();
+
+            // ============================================================ I3
+            if (is_scan) {
+                if (n >= 0) state_update(NKT / 2, NKT);
+            } else if constexpr (NCT == 4) {
+                if (c < NC) {
+                    // lower-left 32x32 quadrant: T_g[ab][cb] = -sum_m T_g[ab][m] sum_kb L_g[m][kb] T_g[kb][cb]
+                    const int ab = 2 + (rw >> 1), cb = rw & 1;
+                    f32x4 acc = zero4();
+                    for (int m = 2; m <= ab; ++m) {
+                        f32x4 x;
+                        const bf16x4 l1 = lds4(Lgs + (16 * m + r16) * PC + 16 + 4 * g4);
+                        const bf16x4 t1 = lds4(Tds + (16 * cb + r16) * PC + 16 + 4 * g4);
+                        if (cb == 0)
+                            x = mfma32(cat8(lds4(Lgs + (16 * m + r16) * PC + 4 * g4), l1),
+                                       cat8(lds4(Tds + r16 * PC + 4 * g4), t1), zero4());
+                        else
+                            x = mfma16(l1, t1, zero4());
+                        acc = mfma16(lds_tr(Tds + (16 * m + 4 * g4 + tri) * PC + 16 * ab + 4 * trp), Bf16::cvt(x), acc);
+                    }
+                    const float bc = gate(ps, 3)[16 * cb + r16];
+                    const int pc = pcol(16 * cb + r16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) M1s[(16 * ab + 4 * g4 + e) * PC + pc] = Bf16::from_f32(-acc[e] * bc);
+                }
+            }
+            __syncthreads();
+
+            // ============================================================ I4
+            if (is_scan) {
+                // stage chunk n + 2 first: its wait for the prefetch would otherwise also wait
+                // for the output stores
+                if (n + 2 < NC) rstore(n + 2, pf); // into slot n & 1, released in I3
+                if (n >= 0) {
+                    const auto rso = buffer_rsrc(obase + static_cast<size_t>(n) * CH * H * dv,
+                                                 (chunk_len(n) - 1) * rowV + kDVT * 2);
+#pragma unroll
+                    for (int j = 0; j < NVV; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),
+                                                               rso, voffV[j], 0, 0);
+                }
+            }
+            __syncthreads();
+        }
+
         if (is_scan && args.S_T) {
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.S_T + srow + 16 * t + 4 * g4) = sT[t];
+            for (int t = 0; t < NKT; ++t)
+                *reinterpret_cast<f32x4 *>(args.S_T + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = sT[t];
         }
-        return;
     }
+};
 
-    if (is_scan) {
-        gload(0);
-        rstore(0);
-    }
-    __syncthreads();
-
-    // scan-role value carried from I1 to the state update in I2/I3
-    F Zd[NCT];
-
-    for (int n = -1; n < NC; ++n) {
-        const int c = n + 1;                      // the prep role's chunk
-        const int ss = n & 1;                     // scan slot (n >= 0)
-        const int ps = c & 1;                     // prep slot
-
-        // ================================================================ I1
-        if (is_scan) {
-            if (n >= 0) {
-                const R *Qs = Qb(ss), *Ks = Kb(ss), *Vs = Vb(ss);
-                f32x4 Z[NCT], PQs[NCT];
-                F Yf[NCT];
-                // U~ = M1 V
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-                    Z[mt] = zero4();
-#pragma unroll
-                    for (int s = 0; s <= mt; s += 2) {
-                        if (s + 1 <= mt)
-                            Z[mt] = P::mma2(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s),
-                                            frag<P>(M1s, PC, 16 * mt, 16 * s + 16),
-                                            frag_b<P>(Vs, PV, 16 * s, 16 * rw), frag_b<P>(Vs, PV, 16 * s + 16, 16 * rw));
-                        else
-                            Z[mt] = P::mma1(Z[mt], frag<P>(M1s, PC, 16 * mt, 16 * s), frag_b<P>(Vs, PV, 16 * s, 16 * rw));
-                    }
-                }
-                // K S^T, Q S^T, Y = K S^T + diag(lambda) Q S^T
-                F sTf[NKT];
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
-                const float *lam_s = gate(ss, 4);
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-                    f32x4 pk = zero4(), pq = zero4();
-#pragma unroll
-                    for (int t = 0; t < NKT; t += 2) {
-                        pk = P::mma2(pk, frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16),
-                                     sTf[t], sTf[t + 1]);
-                        pq = P::mma2(pq, frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16),
-                                     sTf[t], sTf[t + 1]);
-                    }
-                    PQs[mt] = pq;
-                    if constexpr (HAS_L) pk += lds_f32x4(lam_s + 16 * mt + 4 * g4) * pq;
-                    Yf[mt] = P::cvt(pk);
-                }
-                // Z = U~ + M2 Y
-                const R *As = Ab(ss);
-                const float *eg = gate(ss, 1), *egl = gate(ss, 2);
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-#pragma unroll
-                    for (int s = 0; s <= mt; s += 2) {
-                        if (s + 1 <= mt)
-                            Z[mt] = P::mma2(Z[mt], frag<P>(M2s, PC, 16 * mt, 16 * s),
-                                            frag<P>(M2s, PC, 16 * mt, 16 * s + 16), Yf[s], Yf[s + 1]);
-                        else
-                            Z[mt] = P::mma1(Z[mt], frag<P>(M2s, PC, 16 * mt, 16 * s), Yf[s]);
-                    }
-                }
-                F Zf[NCT];
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-                    Zf[mt] = P::cvt(Z[mt]);
-                    Zd[mt] = HAS_A ? P::cvt(lds_f32x4(egl + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
-                }
-                // O = D_g Q S^T + A Z, staged in LDS for the I4 row stores
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-                    f32x4 o = HAS_A ? lds_f32x4(eg + 16 * mt + 4 * g4) * PQs[mt] : PQs[mt];
-#pragma unroll
-                    for (int s = 0; s <= mt; s += 2) {
-                        if (s + 1 <= mt)
-                            o = P::mma2(o, frag<P>(As, PC, 16 * mt, 16 * s), frag<P>(As, PC, 16 * mt, 16 * s + 16),
-                                        Zf[s], Zf[s + 1]);
-                        else
-                            o = P::mma1(o, frag<P>(As, PC, 16 * mt, 16 * s), Zf[s]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = P::from_f32(o[e]);
-                }
-            }
-            // fetch chunk n + 2 now, after this role's busiest phase: it is staged into the
-            // slot this role frees in I3, in I4 of this step (registers are not loop-carried)
-            if (n + 2 < NC) gload(n + 2);
-        } else if (c < NC) {
-            const R *Qs = Qb(ps), *Ks = Kb(ps);
-            R *As = Ab(ps);
-            const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                int i, j;
-                if (prep_block<NCT>(rw, u, i, j)) {
-                    // D = K_j Q_i^T, K_j K_i^T: lane owns r = 16i + l%16, c = 16j + 4g + e
-                    f32x4 gq_ = zero4(), gk_ = zero4();
-#pragma unroll
-                    for (int s = 0; s < NKT; s += 2) {
-                        const F a0 = frag<P>(Ks, PK, 16 * j, 16 * s);
-                        const F a1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
-                        gq_ = P::mma2(gq_, a0, a1, frag<P>(Qs, PK, 16 * i, 16 * s), frag<P>(Qs, PK, 16 * i, 16 * s + 16));
-                        gk_ = P::mma2(gk_, a0, a1, frag<P>(Ks, PK, 16 * i, 16 * s), frag<P>(Ks, PK, 16 * i, 16 * s + 16));
-                    }
-                    const int r = 16 * i + r16;
-                    const int c0 = 16 * j + 4 * g4;
-                    const float lr = lams[r], br = bes[r], gr = gs[r];
-                    const f32x4 gc = lds_f32x4(gs + c0);
-                    f32x4 lv, av;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int cc = c0 + e;
-                        const float xk = HAS_L ? gk_[e] + lr * gq_[e] : gk_[e];
-                        lv[e] = (cc < r) ? br * xk : 0.f;
-                        av[e] = (cc <= r) ? (HAS_A ? __expf(gr - gc[e]) : 1.f) * gq_[e] : 0.f;
-                    }
-                    P::st4(Ls + r * PC + c0, lv);
-                    P::st4(As + r * PC + c0, av);
-                    if (u == 0) {
-                        // diagonal block i == j == rw, inverted from this wave's registers:
-                        // lane (row l%16, group g) holds L[row][4g..4g+3] of the block, and
-                        // every L value the forward substitution needs is read with
-                        // v_readlane (uniform), so no LDS round trips.  Lane l computes
-                        // column l % 16 of T (t_r = e_r - sum_{j<r} L[r][j] t_j); the four
-                        // lane groups repeat it.  L is rounded to bf16 as stored in LDS.
-                        f32x4 lb;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) lb[e] = P::to_f32(P::from_f32(lv[e]));
-                        const int o = 16 * i;
-                        const int cl = r16;
-                        float tv[16];
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) {
-                            float acc = 0.f;
-#pragma unroll
-                            for (int jj = 0; jj < rr; ++jj) {
-                                const float ljj = __int_as_float(
-                                    __builtin_amdgcn_readlane(__float_as_int(lb[jj & 3]), rr + 16 * (jj >> 2)));
-                                acc -= ljj * tv[jj];
-                            }
-                            tv[rr] = (rr == cl) ? 1.f : acc;
-                        }
-                        if (lane < 16) {
-#pragma unroll
-                            for (int rr = 0; rr < 16; ++rr) Ts[(o + rr) * PC + o + cl] = P::from_f32(tv[rr]);
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        auto tstore = [&](int rb_, int cb_, f32x4 val) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
-        };
-
-        // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z, key tiles [t_lo, t_hi)
-        auto state_update = [&](int t_lo, int t_hi) {
-            const R *Ks = Kb(ss);
-            const float dlast = HAS_A ? gate(ss, 1)[CH - 1] : 1.f;
-#pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                if (t < t_lo || t >= t_hi) continue;
-                f32x4 acc = sT[t] * dlast;
-#pragma unroll
-                for (int s = 0; s < NCT; s += 2) {
-                    if (s + 1 < NCT)
-                        acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t),
-                                      Zd[s], Zd[s + 1]);
-                    else
-                        acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Zd[s]);
-                }
-                sT[t] = acc;
-            }
-        };
-
-        // ================================================================ I2
-        if (is_scan) {
-            if (n >= 0) state_update(0, NKT / 2);
-        } else if (c < NC) {
-            if constexpr (NCT >= 2) {
-                if (rw < NCT / 2) {               // T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
-                    const int rb_ = 2 * rw + 1, cb_ = 2 * rw;
-                    const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_),
-                                            frag_b<P>(Ts, PC, 16 * cb_, 16 * cb_));
-                    const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
-                    tstore(rb_, cb_, -y);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ================================================================ I3
-        if (is_scan) {
-            if (n >= 0) state_update(NKT / 2, NKT);
-        } else if (c < NC) {
-            if constexpr (NCT == 4) {             // lower-left 32x32 quadrant of T, one block per wave
-                const int ab = 2 + (rw >> 1), cb_ = rw & 1;
-                f32x4 acc = zero4();
-                for (int m = 2; m <= ab; ++m) {
-                    f32x4 x = zero4();
-                    for (int kb = cb_; kb <= 1; ++kb)
-                        x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
-                    acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
-                }
-                tstore(ab, cb_, -acc);
-            }
-        }
-        __syncthreads();
-
-        // ================================================================ I4
-        if (is_scan) {
-            if (n >= 0) {
-                const int t0 = n * CH, clen = chunk_len(n);
-                for (int vi = rt; vi < CH * VPRV; vi += kRoleThreads) {
-                    const int cc = vi / VPRV, cv = vi % VPRV;
-                    if (cc < clen)
-                        *reinterpret_cast<uint4 *>(go + tok(t0 + cc) * dv + dv0 + cv * EPV) =
-                            *reinterpret_cast<const uint4 *>(Os + cc * PV + cv * EPV);
-                }
-            }
-            if (n + 2 < NC) rstore(n + 2);            // into slot n & 1, freed in I3
-        } else {
-            if (c < NC) {
-                // M1 = (H o T) diag(beta), M2 = -D_g T diag(beta): one thread per 16-column
-                // row segment of the lower block triangle (NPAIR * 16 segments)
-                const float *gs = gate(ps, 0), *eg = gate(ps, 1), *bes = gate(ps, 3);
-                if (rt < NPAIR * 16) {
-                    int i, j;
-                    tri_pair(rt >> 4, i, j);
-                    const int r = 16 * i + (rt & 15);
-                    const int c0 = 16 * j;
-                    float tr[16];
-                    load_row16<P>(Ts + r * PC + c0, tr);
-                    const float gr = gs[r], er = eg[r];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 bc = lds_f32x4(bes + c0 + 4 * q4);
-                        const f32x4 gc = lds_f32x4(gs + c0 + 4 * q4);
-                        f32x4 m1, m2;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float tb = (c0 + 4 * q4 + e <= r) ? tr[4 * q4 + e] * bc[e] : 0.f;
-                            m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
-                            m2[e] = HAS_A ? -er * tb : -tb;
-                        }
-                        P::st4(M1s + r * PC + c0 + 4 * q4, m1);
-                        P::st4(M2s + r * PC + c0 + 4 * q4, m2);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    if (is_scan && args.S_T) {
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.S_T + srow + 16 * t + 4 * g4) = sT[t];
-    }
+template <int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const ChunkArgs args) {
+    PipeKernel<DK, CH, HAS_A, HAS_L>::run(args);
 }
 
 template <int DK, int CH>
@@ -521,13 +700,11 @@ hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
     if (dk == 128) {
         switch (C) {
-            case 16: return launch_pipe_typed<128, 16>(a, stream);
             case 32: return launch_pipe_typed<128, 32>(a, stream);
             case 64: return launch_pipe_typed<128, 64>(a, stream);
         }
     } else if (dk == 64) {
         switch (C) {
-            case 16: return launch_pipe_typed<64, 16>(a, stream);
             case 32: return launch_pipe_typed<64, 32>(a, stream);
             case 64: return launch_pipe_typed<64, 64>(a, stream);
         }
