@@ -23,8 +23,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd_pipe.hip",
-                        "recurrent_sequence_layers_amd/csrc/qd_chunk_common.h",
-                        "recurrent_sequence_layers_amd/csrc/qd_device.h"]
+                        "recurrent_sequence_layers_amd/csrc/qd_device.h",
+                        "recurrent_sequence_layers_amd/csrc/qd_internal.h"]
 STEP_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_step.hip",
                        "recurrent_sequence_layers_amd/csrc/qd_device.h"]
 

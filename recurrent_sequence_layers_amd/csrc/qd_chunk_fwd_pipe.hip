@@ -197,19 +197,22 @@ struct PipeLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
-// Gram blocks (i, j), j <= i, of prep wave P.  Wave P owns diagonal block P (listed first;
-// it inverts that block right after the Gram products) and a share of the off-diagonal
-// blocks, chosen so that blocks on one wave share operand tiles.
-template <int NCT, int P>
-struct GramPlan;
-template <> struct GramPlan<4, 0> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<4, 1> { static constexpr int n = 2; static constexpr int i[4] = {1, 2, 0, 0}, j[4] = {1, 1, 0, 0}; };
-template <> struct GramPlan<4, 2> { static constexpr int n = 3; static constexpr int i[4] = {2, 2, 3, 0}, j[4] = {2, 0, 0, 0}; };
-template <> struct GramPlan<4, 3> { static constexpr int n = 3; static constexpr int i[4] = {3, 3, 3, 0}, j[4] = {3, 1, 2, 0}; };
-template <> struct GramPlan<2, 0> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<2, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
-template <> struct GramPlan<2, 2> { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<2, 3> { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+// Gram blocks (i, j), j <= i, of prep wave P in interval PH (1 or 2).  In I1 wave P owns
+// diagonal block P (listed first; it is inverted right after its Gram products) and the
+// blocks level 1 of the block doubling reads in I2; the blocks only level 2 reads (I3)
+// are formed in I2.
+template <int NCT, int P, int PH>
+struct GramPlan { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 0, 1> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 1, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<4, 2, 1> { static constexpr int n = 2; static constexpr int i[4] = {2, 3, 0, 0}, j[4] = {2, 2, 0, 0}; };
+template <> struct GramPlan<4, 3, 1> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {3, 0, 0, 0}; };
+template <> struct GramPlan<4, 0, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 1, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<4, 2, 2> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 3, 2> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<2, 0, 1> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<2, 1, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
 
 constexpr int tile_mask(const int (&t)[4], int n) {
     int m = 0;
@@ -231,11 +234,11 @@ struct PipeKernel {
     // Gram blocks of prep wave P for the chunk in slot ps, then the A and L_g epilogue.
     // Block (i, j): D = K_j [Q_i | K_i]^T, so lane (g, n) holds q_r.k_c and k_r.k_c for
     // r = 16i + n, c = 16j + 4g + e.
-    template <int P>
+    template <int P, int PH>
     __device__ __forceinline__ static void gram(const uint16_t *Qs, const uint16_t *Ks, uint16_t *As, uint16_t *Lg,
                                                 uint16_t *Td, const float *gs, const float *bes, const float *lams,
                                                 int r16, int g4, f32x4 &tdiag) {
-        using Plan = GramPlan<NCT, P>;
+        using Plan = GramPlan<NCT, P, PH>;
         constexpr int NB = Plan::n;
         if constexpr (NB > 0) {
             f32x4 gq[NB], gk[NB];
@@ -556,10 +559,10 @@ struct PipeKernel {
                 uint16_t *As = Ab(ps);
                 const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
                 switch (rw) {
-                    case 0: gram<0>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    case 1: gram<1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    case 2: gram<2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    default: gram<3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 0: gram<0, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 1: gram<1, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 2: gram<2, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    default: gram<3, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
                 }
             }
             __syncthreads();
@@ -608,6 +611,17 @@ struct PipeKernel {
                     const int pc = pcol(o + r16);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) M1s[(o + 4 * g4 + e) * PC + pc] = Bf16::from_f32(tdiag[e] * bc);
+                }
+                {
+                    const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
+                    uint16_t *As = Ab(ps);
+                    const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
+                    switch (rw) {
+                        case 0: gram<0, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                        case 1: gram<1, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                        case 2: gram<2, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                        default: gram<3, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    }
                 }
                 if (rw < NCT / 2) {
                     // T_g[2a+1][2a] = -T_g[2a+1][2a+1] L_g[2a+1][2a] T_g[2a][2a]
