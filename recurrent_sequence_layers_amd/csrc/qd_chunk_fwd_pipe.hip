@@ -112,16 +112,10 @@ __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
 }
 
-// acc + A B for fp32 fragments a (A operand) and b (B operand), each split into a bf16 high
-// part and a bf16 remainder: two 16x16x32 MFMAs give hi.hi + lo.hi + hi.lo + lo.lo, which
-// is exact to about 2^-16 of the operands.
-__device__ __forceinline__ f32x4 mfma_split(f32x4 a, f32x4 b, f32x4 acc) {
-    const bf16x4 ah = Bf16::cvt(a), bh = Bf16::cvt(b);
-    const bf16x4 al = Bf16::cvt(a - __builtin_convertvector(ah, f32x4));
-    const bf16x4 bl = Bf16::cvt(b - __builtin_convertvector(bh, f32x4));
-    const bf16x8 a8 = cat8(ah, al);
-    acc = mfma32(a8, cat8(bh, bh), acc);
-    return mfma32(a8, cat8(bl, bl), acc);
+// acc + A B for fp32 fragments a (A operand) and b (B operand), rounded to bf16 like
+// every other operand of the block doubling
+__device__ __forceinline__ f32x4 mfma_bf(f32x4 a, f32x4 b, f32x4 acc) {
+    return mfma16(Bf16::cvt(a), Bf16::cvt(b), acc);
 }
 
 // Inverse T of a 16x16 unit lower triangular block I + L, stable block forward substitution:
@@ -153,14 +147,14 @@ __device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
     const f32x4 A4 = diag ? ra : zero4(), B4 = diag ? cb : zero4();
     // 4 -> 8: L restricted to 4x4 blocks (1,0) and (3,2)
     const f32x4 Lm4 = ((m >> 2) == g + 1 && (g & 1) == 0) ? lv : zero4();
-    const f32x4 X = mfma_split(Lm4, B4, zero4());        // L' T4
-    const f32x4 Y = mfma_split(A4, X, zero4());          // T4 L' T4
-    const f32x4 Yt = mfma_split(X, A4, zero4());         // (T4 L' T4)^T
+    const f32x4 X = mfma_bf(Lm4, B4, zero4());        // L' T4
+    const f32x4 Y = mfma_bf(A4, X, zero4());          // T4 L' T4
+    const f32x4 Yt = mfma_bf(X, A4, zero4());         // (T4 L' T4)^T
     const f32x4 B8 = B4 - Y, A8 = A4 - Yt;
     // 8 -> 16: L restricted to rows 8..15, columns 0..7
     const f32x4 Lm8 = (m >= 8 && g < 2) ? lv : zero4();
-    const f32x4 X2 = mfma_split(Lm8, B8, zero4());
-    return B8 - mfma_split(A8, X2, zero4());
+    const f32x4 X2 = mfma_bf(Lm8, B8, zero4());
+    return B8 - mfma_bf(A8, X2, zero4());
 }
 
 // Column permutation of A and M1 inside each 32-wide group: column 16h + 4g + e is

@@ -63,7 +63,7 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
 
 
 def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="random",
-                 s0_std=None, device="cpu", gates_as_none=False) -> ChunkInputs:
+                 s0_std=None, device="cpu", gates_as_none=False, key_corr=0.0) -> ChunkInputs:
     """Inputs for the layer forward, layout q,k [B,T,H,dk], v [B,T,H,dv],
     gates [B,T,H], S0 [B,H,dv,dk].
 
@@ -71,7 +71,11 @@ def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="ran
     alpha: "random" (exp(-softplus) draw) or "one".
     gates_as_none: return None for alpha == 1 / lambda == 0 (the library's way of
     selecting the specialised instances); the tensors are still drawn so that the
-    other draws do not shift."""
+    other draws do not shift.
+    key_corr: weight of one shared N(0, 1) direction per (batch, head) added to every
+    q and k before normalisation (drawn last, so the other draws do not shift); at 2
+    the keys of a head have mean pairwise cosine about 0.8, at 3 about 0.9, a stress
+    case for the triangular solve."""
     dt = _DT[dtype]
     g = _generator(seed, device)
     f = dict(generator=g, device=device, dtype=torch.float32)
@@ -82,6 +86,10 @@ def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="ran
     alpha_logit = torch.randn(B, T, H, **f) - 4.0
     lam_logit = torch.randn(B, T, H, **f)
     S0 = (torch.randn(B, H, dv, dk, **f) * float(s0_std)) if s0_std else None
+    if key_corr:
+        shared = torch.randn(B, 1, H, dk, **f) * float(key_corr)
+        q = q + shared
+        k = k + shared
 
     q = _unit(q).to(dt).contiguous()
     k = _unit(k).to(dt).contiguous()

@@ -86,6 +86,17 @@ def test_small_shapes_full_compare(qd, B, T, H, dk, dv, C, dt, s0):
     check_against_oracle(o, S, x, TOL[dt])
 
 
+@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_correlated_keys(qd, C, dt):
+    """Keys of a head sharing one strong direction make the L entries large and T far
+    from the identity: the triangular solve's accuracy is what this case exercises."""
+    print(f"case correlated keys C={C} {dt}", flush=True)
+    x = inputs.chunk_inputs(1, 300, 2, 128, 128, dt, seed=31 + C, s0_std=0.05, key_corr=2.0)
+    o, S = run_gpu(qd, x, C)
+    check_against_oracle(o, S, x, TOL[dt])
+
+
 @pytest.mark.parametrize("lam,alpha", [("zero", "random"), ("zero", "one"), ("random", "one"),
                                        ("one", "random")])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

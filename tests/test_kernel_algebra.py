@@ -12,6 +12,12 @@ the kernels use these exact rewrites:
   * a short last chunk is padded with alpha = 1, beta = 0, q = k = v = 0 (an
     exact no-op token);
   * T = (I + L)^-1 by 16 x 16 diagonal blocks plus block doubling.
+The eight-wave bf16 kernel goes further:
+  * the decay enters the solve: L_g = H o L, T_g = (I + L_g)^-1 = H o T, so
+    M1 = (H o T) B = T_g B, and M2 = -D_g T B = -M1 D_g is never formed:
+    Z = M1 V + M1 (-D_g Y) with Y = K S^T + diag(lambda) Q S^T;
+  * each 16 x 16 diagonal block of T_g is inverted from its 4 x 4 diagonal blocks by
+    two levels of block substitution (4 -> 8 -> 16), T21 = -T22 L21 T11.
 This file restates those steps in numpy; it shares nothing with the kernels.
 """
 import numpy as np
@@ -107,3 +113,81 @@ def test_kernel_form_matches_recurrence(T, C, dk, dv):
     o_k, S_k = kernel_form_fwd(q, k, v, alpha, beta, lam, S0, C)
     np.testing.assert_allclose(o_k, o_r, atol=1e-11)
     np.testing.assert_allclose(S_k, S_r, atol=1e-11)
+
+
+def inverse16_by_levels(L16):
+    """(I + L)^-1 of a 16 x 16 strictly lower L: 4 x 4 diagonal blocks inverted
+    directly, then [[A,0],[C,D]]^-1 = [[A^-1,0],[-D^-1 C A^-1, D^-1]] at widths 4 and 8."""
+    T = np.zeros((16, 16))
+    for k4 in range(4):
+        s = slice(4 * k4, 4 * k4 + 4)
+        T[s, s] = np.linalg.inv(np.eye(4) + L16[s, s])
+    for w in (4, 8):
+        Lw = np.zeros((16, 16))
+        for a0 in range(0, 16, 2 * w):
+            Lw[a0 + w:a0 + 2 * w, a0:a0 + w] = L16[a0 + w:a0 + 2 * w, a0:a0 + w]
+        T = T - T @ (Lw @ T)     # T is block diagonal at width w, so this fills the new blocks
+    return T
+
+
+def pipelined_form_fwd(q, k, v, alpha, beta, lam, S0, C):
+    B, Tn, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, Tn, H, dv)); S_T = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            ST = np.zeros((dk, dv)) if S0 is None else S0[b, h].T.copy()
+            for t0 in range(0, Tn, C):
+                n = min(C, Tn - t0)
+                Q = np.zeros((C, dk)); K = np.zeros((C, dk)); V = np.zeros((C, dv))
+                la = np.zeros(C); be = np.zeros(C); lg = np.zeros(C)
+                Q[:n] = q[b, t0:t0 + n, h]; K[:n] = k[b, t0:t0 + n, h]; V[:n] = v[b, t0:t0 + n, h]
+                be[:n] = beta[b, t0:t0 + n, h]; la[:n] = lam[b, t0:t0 + n, h]
+                lg[:n] = np.log(alpha[b, t0:t0 + n, h])
+                g = np.cumsum(lg)
+                Hm = np.tril(np.exp(g[:, None] - g[None, :]))
+                QK = Q @ K.T
+                Lg = np.tril(Hm * be[:, None] * (K @ K.T + la[:, None] * QK), -1)
+                Tg = np.zeros((C, C))
+                for d0 in range(0, C, 16):
+                    Tg[d0:d0 + 16, d0:d0 + 16] = inverse16_by_levels(Lg[d0:d0 + 16, d0:d0 + 16])
+                w = 16
+                while w < C:
+                    for a0 in range(0, C, 2 * w):
+                        c0 = a0 + w
+                        Tg[c0:c0 + w, a0:c0] = -Tg[c0:c0 + w, c0:c0 + w] @ Lg[c0:c0 + w, a0:c0] @ Tg[a0:c0, a0:c0]
+                    w *= 2
+                M1 = Tg * be[None, :]
+                PQ = Q @ ST
+                Y = K @ ST + la[:, None] * PQ
+                Z = M1 @ V + M1 @ (-np.exp(g)[:, None] * Y)
+                O = np.exp(g)[:, None] * PQ + (Hm * QK) @ Z
+                ST = np.exp(g[-1]) * ST + K.T @ (np.exp(g[-1] - g)[:, None] * Z)
+                o[b, t0:t0 + n, h] = O[:n]
+            S_T[b, h] = ST.T
+    return o, S_T
+
+
+def test_inverse16_by_levels_matches_dense():
+    r = np.random.default_rng(3)
+    for scale in (0.1, 0.7, 2.0):
+        L = np.tril(scale * r.standard_normal((16, 16)), -1)
+        np.testing.assert_allclose(inverse16_by_levels(L), np.linalg.inv(np.eye(16) + L),
+                                   rtol=1e-9, atol=1e-9 * np.abs(np.linalg.inv(np.eye(16) + L)).max())
+
+
+@pytest.mark.parametrize("T,C,dk,dv", [(64, 64, 16, 16), (100, 64, 32, 16), (75, 32, 16, 32),
+                                       (3, 64, 16, 16), (161, 32, 16, 8)])
+def test_pipelined_form_matches_recurrence(T, C, dk, dv):
+    r = np.random.default_rng(7 * T + C)
+    q = r.standard_normal((2, T, 2, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((2, T, 2, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((2, T, 2, dv))
+    beta = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    alpha = np.exp(-np.log1p(np.exp(r.standard_normal((2, T, 2)) - 4.0)))
+    lam = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    S0 = 0.1 * r.standard_normal((2, 2, dv, dk))
+    o_r, S_r = oracle.qdelta_fwd(q, k, v, alpha, beta, lam, S0)
+    o_k, S_k = pipelined_form_fwd(q, k, v, alpha, beta, lam, S0, C)
+    np.testing.assert_allclose(o_k, o_r, atol=1e-10)
+    np.testing.assert_allclose(S_k, S_r, atol=1e-10)
