@@ -157,10 +157,23 @@ __device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
     return B8 - mfma_bf(A8, X2, zero4());
 }
 
-// Column permutation of A and M1 inside each 32-wide group: column 16h + 4g + e is
-// stored at 8g + 4h + e.
-__device__ __forceinline__ int pcol(int c) {
-    return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+// Fragment-order layout.  A 16 x 32 tile of an MFMA operand (16 rows, 32 contraction
+// values) is one 1 KB block of 64 16-byte slots; lane (g, r) of a b128 read takes slot
+// 16 g + (r ^ frag_swz(g)), i.e. row r and contraction values 8g .. 8g + 7 of the
+// tile's ordering.  The XOR keeps both access shapes of the kernel free of LDS bank
+// conflicts on gfx950 (measured): the b128 fragment reads, where each group of 16
+// lanes reads one 256-byte quarter, and the transpose reads of the state update, where
+// the four lanes of one row read four different quarters.
+__device__ __forceinline__ int frag_swz(int g) { return (12 * g) & 15; }
+__device__ __forceinline__ int frag_slot(int g, int r) { return 16 * g + (r ^ frag_swz(g)); }
+
+// A and M1 ([C][C], bf16) in fragment order: block (row tile, 32-column group); inside a
+// group, column 16h + 4g + e sits in slot (g, row) at element 4h + e, so one b128 read
+// yields the eight contraction values a 16x16x32 MFMA pairs with two register tiles.
+template <int CH>
+__device__ __forceinline__ int cc_off(int row, int col) {
+    const int c = col & 31;
+    return ((row >> 4) * (CH / 32) + (col >> 5)) * 512 + 8 * frag_slot((c >> 2) & 3, row & 15) + 4 * (c >> 4) + (c & 3);
 }
 
 template <int DK, int CH>
@@ -168,10 +181,10 @@ struct PipeLayout {
     static constexpr int NCT = CH / 16;
     static constexpr int PC = CH + 8;             // chunk x chunk rows, 16 bytes of padding
     static constexpr int PV = kDVT + 8;           // v rows and the output staging
-    static constexpr int PK = DK + 8;             // q, k rows
-    static constexpr int NQ = CH * PK;
+    static constexpr int NQ = CH * DK;            // q, k in fragment order (no padding)
     static constexpr int NV = CH * PV;
-    static constexpr int NCC = CH * PC;
+    static constexpr int NCC = CH * CH;           // A, M1 in fragment order
+    static constexpr int NLT = CH * PC;           // L_g, T_g: padded rows
     // bf16 element offsets
     static constexpr int oQ = 0;                  // [2][NQ]
     static constexpr int oK = oQ + 2 * NQ;        // [2][NQ]
@@ -179,14 +192,14 @@ struct PipeLayout {
     static constexpr int oA = oV + 2 * NV;        // [2][NCC]
     static constexpr int oM1 = oA + 2 * NCC;      // directly after A: both are zeroed together
     static constexpr int oLg = oM1 + NCC;
-    static constexpr int oTd = oLg + NCC;
-    static constexpr int oO = oTd + NCC;
+    static constexpr int oTd = oLg + NLT;
+    static constexpr int oO = oTd + NLT;
     static constexpr int nR = oO + NV;
     // byte offset of the fp32 gates
     static constexpr int kGates = 5;              // g, exp(g), exp(g_last - g), beta, lambda
     static constexpr int oGate = nR * 2;
     static constexpr int bytes = oGate + 2 * kGates * CH * 4;
-    static_assert((PK * 2) % 16 == 0 && (PC * 2) % 16 == 0 && (PV * 2) % 16 == 0 && oGate % 16 == 0,
+    static_assert((PC * 2) % 16 == 0 && (PV * 2) % 16 == 0 && oGate % 16 == 0,
                   "16-byte alignment of rows");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
@@ -219,11 +232,14 @@ struct PipeKernel {
     using Lay = PipeLayout<DK, CH>;
     static constexpr int NKT = DK / 16, NKP = DK / 32;
     static constexpr int NCT = CH / 16, NCP = CH / 32;
-    static constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
+    static constexpr int PC = Lay::PC, PV = Lay::PV;
     // Key layout of the register tiles: in the pair step u, lane group g supplies the
-    // eight keys of quad NKP g + u (so the four groups read quads that are d_k / 4 keys
-    // apart, and the transpose reads of the state update fall on distinct banks).
-    __device__ __forceinline__ static int kq(int g, int u) { return NKP * g + u; }
+    // eight keys of quad 4u + g (32 consecutive keys per step).
+    __device__ __forceinline__ static int kq(int g, int u) { return 4 * u + g; }
+    // q / k element offset of lane (g, r)'s slot in fragment block (row tile mt, step u)
+    __device__ __forceinline__ static int qk_off(int mt, int u, int g, int r) {
+        return (mt * NKP + u) * 512 + 8 * frag_slot(g, r);
+    }
 
     // Gram blocks of prep wave P for the chunk in slot ps, then the A and L_g epilogue.
     // Block (i, j): D = K_j [Q_i | K_i]^T, so lane (g, n) holds q_r.k_c and k_r.k_c for
@@ -246,7 +262,7 @@ struct PipeKernel {
             auto load = [&](int u, bf16x8(&k)[NCT], bf16x8(&q)[NCT]) {
 #pragma unroll
                 for (int m = 0; m < NCT; ++m) {
-                    const int off = (16 * m + r16) * PK + 8 * kq(g4, u);
+                    const int off = qk_off(m, u, g4, r16);
                     if (kmask & (1 << m)) k[m] = lds8(Ks + off);
                     if (qmask & (1 << m)) q[m] = lds8(Qs + off);
                 }
@@ -281,7 +297,7 @@ struct PipeKernel {
                     av[e] = (cc <= r) ? f * gq[b][e] : 0.f;
                     lv[e] = (cc < r) ? (f * br) * xk : 0.f;
                 }
-                sts4(As + r * PC + 32 * (j >> 1) + 8 * g4 + 4 * (j & 1), av);
+                sts4(As + cc_off<CH>(r, c0), av);
                 if (i == j) {
                     tdiag = invert_unit_lower16(lv, g4, r16);
                     sts4(Td + (16 * i + r16) * PC + 16 * i + 4 * g4, tdiag);   // T_g[16i + 4g + e][16i + n]
@@ -297,7 +313,6 @@ struct PipeKernel {
         constexpr int VPRV = kDVT / 8;
         constexpr int NVQ = CH * VPRQ / kRoleThreads;
         constexpr int NVV = CH * VPRV / kRoleThreads;
-        constexpr int RJQ = kRoleThreads / VPRQ;  // rows between a thread's vectors
         constexpr int RJV = kRoleThreads / VPRV;
         static_assert(CH * VPRQ % kRoleThreads == 0 && CH * VPRV % kRoleThreads == 0, "whole vectors per thread");
 
@@ -353,16 +368,22 @@ struct PipeKernel {
                         ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1))
                         : zero4();
 
-        // ---- scan-role prefetch of chunk n + 2: registers, per-lane offsets fixed per chunk
-        const int vq_row = rt / VPRQ, vq_col = rt % VPRQ;
+        // ---- scan-role prefetch of chunk n + 2: registers, per-lane offsets fixed per chunk.
+        // q / k: one wave instruction reads 16 / NKP whole rows; the 16 lanes of a group read
+        // four consecutive rows at the four key quads of one fragment step (lane 16G + 4i + g:
+        // row 4 (G / NKP) + i, quad kq(g, G % NKP)), so their fragment slots fall on distinct banks.
         const int vv_row = rt / VPRV, vv_col = rt % VPRV;
-        int voffQ[NVQ], voffV[NVV];
+        int voffQ[NVQ], ldsQ[NVQ], voffV[NVV];
 #pragma unroll
-        for (int j = 0; j < NVQ; ++j) voffQ[j] = (vq_row + j * RJQ) * rowQ + vq_col * 16;
+        for (int j = 0; j < NVQ; ++j) {
+            const int row = (4 * j + rw) * (16 / NKP) + 4 * (g4 / NKP) + (r16 >> 2);
+            const int u = g4 % NKP, g = r16 & 3;
+            voffQ[j] = row * rowQ + 16 * kq(g, u);
+            ldsQ[j] = qk_off(row >> 4, u, g, row & 15);
+        }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) voffV[j] = (vv_row + j * RJV) * rowV + vv_col * 16;
         const int voffG = (rt & (kWave - 1)) * rowG;
-        const int ldsQ = vq_row * PK + vq_col * 8;        // + j * RJQ * PK
         const int ldsV = vv_row * PV + vv_col * 8;        // + j * RJV * PV
 
         // registers of one prefetched chunk; declared per pipeline step so that they are
@@ -398,8 +419,8 @@ struct PipeKernel {
             uint16_t *Qs = Qb(s), *Ks = Kb(s), *Vs = Vb(s);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
-                *reinterpret_cast<u32x4 *>(Qs + ldsQ + j * RJQ * PK) = pf.q[j];
-                *reinterpret_cast<u32x4 *>(Ks + ldsQ + j * RJQ * PK) = pf.k[j];
+                *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
+                *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
@@ -464,7 +485,7 @@ struct PipeKernel {
                     auto load_qk = [&](int mt, bf16x8(&k)[NKP], bf16x8(&q)[NKP]) {
 #pragma unroll
                         for (int u = 0; u < NKP; ++u) {
-                            const int off = (16 * mt + r16) * PK + 8 * kq(g4, u);
+                            const int off = qk_off(mt, u, g4, r16);
                             k[u] = lds8(Ks + off);
                             q[u] = lds8(Qs + off);
                         }
@@ -493,7 +514,7 @@ struct PipeKernel {
                             for (int m = 0; m < NCT; ++m)
 #pragma unroll
                                 for (int u = 0; u <= (m >> 1); ++u)
-                                    m1f[m][u] = lds8(M1s + (16 * m + r16) * PC + 32 * u + 8 * g4);
+                                    m1f[m][u] = lds8(M1s + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
                         }
                         __builtin_amdgcn_sched_barrier(0);
                         f32x4 pk = zero4(), pq = zero4();
@@ -511,7 +532,7 @@ struct PipeKernel {
 #pragma unroll
                     for (int m = 0; m < NCT; ++m)
 #pragma unroll
-                        for (int u = 0; u <= (m >> 1); ++u) af[m][u] = lds8(As + (16 * m + r16) * PC + 32 * u + 8 * g4);
+                        for (int u = 0; u <= (m >> 1); ++u) af[m][u] = lds8(As + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
                     bf16x4 Yg[NCT];
 #pragma unroll
                     for (int mt = 0; mt < NCT; ++mt) {
@@ -573,11 +594,12 @@ struct PipeKernel {
                 for (int s = 0; s < NCP; ++s) zp[s] = cat8(Zd[2 * s], Zd[2 * s + 1]);
                 bf16x8 kf[2][NCP];
                 auto load = [&](int t, bf16x8(&dst)[NCP]) {
-                    const int col = 8 * kq(trp, t >> 1) + 4 * (t & 1);
+                    // keys 8 kq(trp, t / 2) + 4 (t & 1) .. + 3 of positions 32 s + 4 g4 + tri
+                    // and 16 later: slot (trp, 4 g4 + tri) of blocks (2 s, t / 2), (2 s + 1, t / 2)
 #pragma unroll
                     for (int s = 0; s < NCP; ++s) {
-                        const uint16_t *p = Ks + (32 * s + 4 * g4 + tri) * PK + col;
-                        dst[s] = cat8(lds_tr(p), lds_tr(p + 16 * PK));
+                        const uint16_t *p = Ks + qk_off(2 * s, t >> 1, trp, 4 * g4 + tri) + 4 * (t & 1);
+                        dst[s] = cat8(lds_tr(p), lds_tr(p + NKP * 512));
                     }
                 };
                 load(t_lo, kf[0]);
@@ -602,9 +624,8 @@ struct PipeKernel {
                 if (rw < NCT) {                   // M1 of this wave's diagonal block
                     const int o = 16 * rw;
                     const float bc = gate(ps, 3)[o + r16];
-                    const int pc = pcol(o + r16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) M1s[(o + 4 * g4 + e) * PC + pc] = Bf16::from_f32(tdiag[e] * bc);
+                    for (int e = 0; e < 4; ++e) M1s[cc_off<CH>(o + 4 * g4 + e, o + r16)] = Bf16::from_f32(tdiag[e] * bc);
                 }
                 {
                     const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
@@ -626,9 +647,8 @@ struct PipeKernel {
                                            zero4());
                     if constexpr (NCT == 4) sts4(Tds + (16 * aa + r16) * PC + 16 * bb + 4 * g4, -y);
                     const float bc = gate(ps, 3)[16 * aa + r16];
-                    const int pc = pcol(16 * aa + r16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) M1s[(16 * bb + 4 * g4 + e) * PC + pc] = Bf16::from_f32(-y[e] * bc);
+                    for (int e = 0; e < 4; ++e) M1s[cc_off<CH>(16 * bb + 4 * g4 + e, 16 * aa + r16)] = Bf16::from_f32(-y[e] * bc);
                 }
             }
             __syncthreads();
@@ -653,9 +673,8 @@ struct PipeKernel {
                         acc = mfma16(lds_tr(Tds + (16 * m + 4 * g4 + tri) * PC + 16 * ab + 4 * trp), Bf16::cvt(x), acc);
                     }
                     const float bc = gate(ps, 3)[16 * cb + r16];
-                    const int pc = pcol(16 * cb + r16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) M1s[(16 * ab + 4 * g4 + e) * PC + pc] = Bf16::from_f32(-acc[e] * bc);
+                    for (int e = 0; e < 4; ++e) M1s[cc_off<CH>(16 * ab + 4 * g4 + e, 16 * cb + r16)] = Bf16::from_f32(-acc[e] * bc);
                 }
             }
             __syncthreads();
