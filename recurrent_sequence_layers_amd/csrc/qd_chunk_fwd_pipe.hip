@@ -27,20 +27,18 @@
 //   I1        Y, Z, O (O staged in LDS)              Gram blocks on MFMA; A and L_g written;
 //                                                    each wave inverts its diagonal 16x16
 //                                                    block of T_g in registers
-//   I2        fetch chunk n + 2 (registers);         M1 of the diagonal blocks; block
-//             S^T update, first half of the keys     doubling, level 1
-//   I3        S^T update, second half                block doubling, level 2 (C = 64)
-//   I4        stage chunk n + 2 in LDS; gate
+//   I2        fetch chunk n + 2 (registers);         M1 of the diagonal blocks; Gram blocks
+//             S^T update, first half of the keys     of level 2; block doubling, level 1
+//   I3        S^T update, second half                -
+//   I4        stage chunk n + 2 in LDS; gate         block doubling, level 2 (C = 64)
 //             prefix sums; store O
 //
 // LDS layouts (bf16 unless noted):
-//   q, k slots [2][C][d_k + 8]  rows padded by one 16-byte quad, so 16 consecutive
-//                           rows read at one quad hit distinct banks;
+//   q, k slots [2][C x d_k] in fragment order (see frag_slot);
 //   v slots    [2][C][72]   padded rows;
-//   A [2], M1  [C][C + 8]   columns permuted inside each 32-wide group so that one b128
-//                           read yields the eight contraction values a 16x16x32 MFMA
-//                           pairs with two register tiles (positions 4g..4g+3 and
-//                           16+4g..16+4g+3);
+//   A [2], M1  [C x C] in fragment order (see cc_off): one b128 read yields the eight
+//                           contraction values a 16x16x32 MFMA pairs with two register
+//                           tiles (positions 4g..4g+3 and 16+4g..16+4g+3);
 //   L_g        [C][C + 8]   off-diagonal blocks (diagonal blocks stay in registers);
 //   T_g        [C][C + 8]   stored transposed (row c holds column c of T_g);
 //   O staging  [C][72];  gates [2][5][C] fp32.
@@ -306,6 +304,40 @@ struct PipeKernel {
                 }
             }
         }
+    }
+
+    // Block doubling, level 2 (C = 64): block (ab, cb) of the lower-left 32 x 32 quadrant,
+    //   T_g[ab][cb] = -sum_m T_g[ab][m] X[m][cb],  X[m][cb] = sum_kb L_g[m][kb] T_g[kb][cb],
+    // with M1 = T_g diag(beta) written for it.  The outer product is formed transposed,
+    // X^T T_g[ab][m]^T: the X accumulators serve as the A operand (X^T) and the transpose
+    // read of T_g[ab][m] (T_g is kept transposed) is the B operand of T_g[ab][m]^T, so each
+    // lane ends with four consecutive columns of one row of M1.
+    template <int AB, int CB>
+    __device__ __forceinline__ static void level2(const uint16_t *Lgs, const uint16_t *Tds, uint16_t *M1s,
+                                                  const float *bes, int lane) {
+        const int r16 = lane & 15, g4 = lane >> 4, tri = r16 >> 2, trp = r16 & 3;
+        // B operands T_g[kb][cb] (kept transposed: row 16 cb + n holds column 16 cb + n)
+        const bf16x4 t1 = lds4(Tds + (16 * CB + r16) * PC + 16 + 4 * g4);
+        bf16x4 t0 = {};
+        if constexpr (CB == 0) t0 = lds4(Tds + r16 * PC + 4 * g4);
+        bf16x4 l0[2], l1[2], tt[2];
+#pragma unroll
+        for (int i = 0; i < AB - 1; ++i) {
+            const int m = 2 + i;
+            l1[i] = lds4(Lgs + (16 * m + r16) * PC + 16 + 4 * g4);
+            if constexpr (CB == 0) l0[i] = lds4(Lgs + (16 * m + r16) * PC + 4 * g4);
+            tt[i] = lds_tr(Tds + (16 * m + 4 * g4 + tri) * PC + 16 * AB + 4 * trp);
+        }
+        bf16x4 xb[2];
+#pragma unroll
+        for (int i = 0; i < AB - 1; ++i) {
+            const f32x4 x = (CB == 0) ? mfma32(cat8(l0[i], l1[i]), cat8(t0, t1), zero4()) : mfma16(l1[i], t1, zero4());
+            xb[i] = Bf16::cvt(x);
+        }
+        const f32x4 acc = (AB == 3) ? mfma32(cat8(xb[0], xb[1]), cat8(tt[0], tt[1]), zero4()) : mfma16(xb[0], tt[0], zero4());
+        // lane (g, n): T_g[16 AB + n][16 CB + 4 g + e]
+        const f32x4 bc = lds_f32x4(bes + 16 * CB + 4 * g4);
+        sts4(M1s + cc_off<CH>(16 * AB + r16, 16 * CB + 4 * g4), -acc * bc);
     }
 
     __device__ static void run(const ChunkArgs &args) {
@@ -656,26 +688,6 @@ struct PipeKernel {
             // ============================================================ I3
             if (is_scan) {
                 if (n >= 0) state_update(NKT / 2, NKT);
-            } else if constexpr (NCT == 4) {
-                if (c < NC) {
-                    // lower-left 32x32 quadrant: T_g[ab][cb] = -sum_m T_g[ab][m] sum_kb L_g[m][kb] T_g[kb][cb]
-                    const int ab = 2 + (rw >> 1), cb = rw & 1;
-                    f32x4 acc = zero4();
-                    for (int m = 2; m <= ab; ++m) {
-                        f32x4 x;
-                        const bf16x4 l1 = lds4(Lgs + (16 * m + r16) * PC + 16 + 4 * g4);
-                        const bf16x4 t1 = lds4(Tds + (16 * cb + r16) * PC + 16 + 4 * g4);
-                        if (cb == 0)
-                            x = mfma32(cat8(lds4(Lgs + (16 * m + r16) * PC + 4 * g4), l1),
-                                       cat8(lds4(Tds + r16 * PC + 4 * g4), t1), zero4());
-                        else
-                            x = mfma16(l1, t1, zero4());
-                        acc = mfma16(lds_tr(Tds + (16 * m + 4 * g4 + tri) * PC + 16 * ab + 4 * trp), Bf16::cvt(x), acc);
-                    }
-                    const float bc = gate(ps, 3)[16 * cb + r16];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) M1s[cc_off<CH>(16 * ab + 4 * g4 + e, 16 * cb + r16)] = Bf16::from_f32(-acc[e] * bc);
-                }
             }
             __syncthreads();
 
@@ -691,6 +703,15 @@ struct PipeKernel {
                     for (int j = 0; j < NVV; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),
                                                                rso, voffV[j], 0, 0);
+                }
+            } else if constexpr (NCT == 4) {
+                if (c < NC) {
+                    switch (rw) {
+                        case 0: level2<2, 0>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
+                        case 1: level2<2, 1>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
+                        case 2: level2<3, 0>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
+                        default: level2<3, 1>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
+                    }
                 }
             }
             __syncthreads();
