@@ -6,7 +6,10 @@ One timed step is one call of the chunked layer forward over the 1.3B-layer-shap
 workload (B=8, T=4096, H=16, d_k=d_v=128, C=64, bf16 q/k/v/o, fp32 gates and
 state, S0 = 0), inputs resident in HBM.  The value is tokens/s (B*T per step).
 In the same run the decode step is timed on 256 sequences x 16 heads (fp32 state
-resident, one token per call) and reported as achieved HBM GB/s.  Kernel
+resident, one token per call) and reported as achieved HBM GB/s, and the layer is
+timed with lambda = 0 (Gated DeltaNet), with lambda = 0 and alpha = 1 (DeltaNet), and
+on the long-context workload (B=1, T=65536, S0 given), each reported beside the
+headline figure.  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -108,6 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the Gated DeltaNet, DeltaNet and long-context timings (used for the "
+                         "profiled runs, so that per-kernel statistics cover the headline workload only)")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device-to-device copies, the reference the HBM "
@@ -154,6 +160,40 @@ def main():
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     log(f"[bench] chunk forward {ms_per_step:.4f} ms/step, {tokens_per_s / 1e6:.2f} M tokens/s, "
         f"{ach_gbs:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+
+    # ---- the same layer with lambda = 0 (Gated DeltaNet) and lambda = 0, alpha = 1 (DeltaNet),
+    # gates passed as NULL so the specialised kernel instances run; and the long-context
+    # workload (B=1, T=65536, S0 given, S_T returned): reported beside the headline figure
+    variants = {}
+    for vname, vsteps in (() if args.headline_only else
+                          (("gdn_bf16", args.steps), ("deltanet_bf16", args.steps), ("long_64k_bf16", 5))):
+        vw = inputs.WORKLOADS[vname]
+        vB, vT, vH = vw["B"], vw["T"], vw["H"]
+        log(f"[bench] generating {vname} on device")
+        vx = inputs.workload_inputs(vname, seed=args.seed, device="cuda", gates_as_none=True)
+        vo = torch.empty((vB, vT, vH, vw["dv"]), dtype=torch.bfloat16, device=dev)
+        vS = torch.empty((vB, vH, vw["dv"], vw["dk"]), dtype=torch.float32, device=dev)
+        vf = lambda: qd.qdelta_chunk_fwd(vx.q, vx.k, vx.v, vx.alpha, vx.beta, vx.lam, vx.S0, C=vw["C"],
+                                         o=vo, S_T=vS)
+        for _ in range(max(1, min(args.warmup, vsteps))):
+            vf()
+        torch.cuda.synchronize()
+        v_s, _ = time_region(torch, vf, vsteps)
+        v_ms = v_s / vsteps * 1e3
+        vbytes, vflops = chunk_algorithmic(vB, vT, vH, vw["dk"], vw["dv"], vw["C"], 2)
+        vbytes -= vB * vT * vH * 4 * ((vx.lam is None) + (vx.alpha is None))   # gates not read
+        vbytes += 0 if vx.S0 is None else vB * vH * vw["dv"] * vw["dk"] * 4
+        variants[vname] = {"B": vB, "T": vT, "H": vH, "lambda": "0" if vx.lam is None else "sigmoid draw",
+                           "alpha": "1" if vx.alpha is None else "exp(-softplus) draw",
+                           "S0": None if vx.S0 is None else "N(0, 0.02)", "steps": vsteps,
+                           "ms_per_call": v_ms, "tokens_per_s": vB * vT / (v_ms * 1e-3),
+                           "hbm_frac": vbytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "time_ratio_to_headline": v_ms / ms_per_step,
+                           "us_per_chunk_step": v_ms * 1e3 / ((vT + vw["C"] - 1) // vw["C"])}
+        log(f"[bench] {vname}: {v_ms:.4f} ms/call, {vB * vT / (v_ms * 1e-3) / 1e6:.2f} M tokens/s, "
+            f"{v_ms / ms_per_step:.3f} x the headline time")
+        del vx, vo, vS
+    torch.cuda.synchronize()
 
     # ---- decode step: 256 sequences x 16 heads, fp32 state resident, D consecutive steps
     dw = inputs.WORKLOADS["decode_256x16"]
@@ -222,6 +262,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": dec_gbs / PEAK_HBM_GBS, "traffic": dec_traffic,
                                 "algorithmic_bytes_per_launch": dec_bytes}},
+        "other_workloads": variants,
         "cpu_baseline": cpu,
         "timing": {"chunk_wall_s": wall_s, "decode_wall_s": dec_wall},
     }
