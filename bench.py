@@ -173,8 +173,10 @@ def main():
         vx = inputs.workload_inputs(vname, seed=args.seed, device="cuda", gates_as_none=True)
         vo = torch.empty((vB, vT, vH, vw["dv"]), dtype=torch.bfloat16, device=dev)
         vS = torch.empty((vB, vH, vw["dv"], vw["dk"]), dtype=torch.float32, device=dev)
+        nws = qd.qdelta_chunk_fwd_workspace_bytes(vB, vT, vH, vw["dk"], vw["dv"], vw["C"], torch.bfloat16)
+        vws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None   # allocated outside the timing
         vf = lambda: qd.qdelta_chunk_fwd(vx.q, vx.k, vx.v, vx.alpha, vx.beta, vx.lam, vx.S0, C=vw["C"],
-                                         o=vo, S_T=vS)
+                                         o=vo, S_T=vS, workspace=vws)
         for _ in range(max(1, min(args.warmup, vsteps))):
             vf()
         torch.cuda.synchronize()
@@ -189,10 +191,11 @@ def main():
                            "ms_per_call": v_ms, "tokens_per_s": vB * vT / (v_ms * 1e-3),
                            "hbm_frac": vbytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "time_ratio_to_headline": v_ms / ms_per_step,
-                           "us_per_chunk_step": v_ms * 1e3 / ((vT + vw["C"] - 1) // vw["C"])}
+                           "us_per_chunk_step": v_ms * 1e3 / ((vT + vw["C"] - 1) // vw["C"]),
+                           "schedule": (f"segmented ({nws} B workspace)" if nws else "single pass")}
         log(f"[bench] {vname}: {v_ms:.4f} ms/call, {vB * vT / (v_ms * 1e-3) / 1e6:.2f} M tokens/s, "
             f"{v_ms / ms_per_step:.3f} x the headline time")
-        del vx, vo, vS
+        del vx, vo, vS, vws
     torch.cuda.synchronize()
 
     # ---- decode step: 256 sequences x 16 heads, fp32 state resident, D consecutive steps

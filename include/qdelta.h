@@ -62,9 +62,14 @@ int qdelta_abi_version(void);
 /* Static description of a status code; never NULL. */
 const char *qdelta_status_string(int status);
 
-/* Bytes of device workspace qdelta_chunk_fwd needs for these sizes.  The current
- * kernels keep every intermediate on chip and need none (returns 0); callers
- * should still query it and pass a buffer of at least this size. */
+/* Bytes of device workspace qdelta_chunk_fwd needs for these sizes, on the current
+ * device.  0 for the single-pass schedule, which keeps every chunk intermediate on
+ * chip.  Non-zero when the sequence is long and B*H*d_v/64 workgroups would leave
+ * most compute units idle (bf16, C = 32 or 64): the forward then cuts the sequence
+ * into P segments and composes their affine state maps (S_out = S_in M + G, from the
+ * recurrence of the Q-Delta reading notes §2.4 acting on the state from the right).
+ * The size is B*P*H*(d_k*d_k + 2*d_v*d_k)*4 bytes, P in {2, 4, 8, 16}.  Callers pass a
+ * caller-owned, 16-byte aligned device buffer of at least this size. */
 size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
                                         int dtype);
 
@@ -72,7 +77,8 @@ size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, i
  * Layer forward in the chunkwise-parallel WY/UT-transform form (Q-Delta reading
  * notes §2.6: the strictly-lower X K^T interaction, the triangular-solve UT
  * transform, and the entry-state composition of Z, S_out and O).  The result is
- * the recurrence above evaluated over T tokens from S0; C only changes rounding.
+ * the recurrence above evaluated over T tokens from S0; C and the schedule (single
+ * pass or segmented, see qdelta_chunk_fwd_workspace_bytes) only change rounding.
  *
  *   q, k, v, beta   required when B*T*H > 0.
  *   alpha           NULL means alpha == 1 (selects the no-decay instance).
@@ -85,7 +91,9 @@ size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, i
  *   C in {16, 32, 64} (chunk length; a short last chunk is handled exactly);
  *   dtype one of qd_dtype.
  *   workspace/ws_bytes: see qdelta_chunk_fwd_workspace_bytes (may be NULL/0
- *                   when that returns 0).
+ *                   when that returns 0; otherwise QD_ERR_WORKSPACE if it is NULL
+ *                   or smaller).  It must not overlap any other argument, and the
+ *                   library overwrites it; its contents are not needed afterwards.
  */
 int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
                      const float *alpha, const float *beta, const float *lambda,

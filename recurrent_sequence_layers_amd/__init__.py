@@ -96,11 +96,14 @@ def _raise(rc, fn):
 
 
 def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_T=None,
-                     want_state: bool = True, stream=None):
+                     want_state: bool = True, stream=None, workspace=None):
     """Layer forward, chunkwise WY/UT form.  q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or
     bf16, same dtype); alpha, beta, lam [B,T,H] fp32 (alpha None means 1, lam None
     means 0); S0 [B,H,d_v,d_k] fp32 or None.  Returns (o, S_T); S_T is None when
-    want_state is False.  S_T may be passed as S0 for an in-place state update."""
+    want_state is False.  S_T may be passed as S0 for an in-place state update.
+    workspace: a device tensor of at least qdelta_chunk_fwd_workspace_bytes(...) bytes
+    (long sequences over few heads run a segmented schedule that needs one); when None
+    and one is needed, it is allocated here."""
     import torch
     lib = load_library()
     B, T, H, dk = q.shape
@@ -120,10 +123,11 @@ def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     ws = lib.qdelta_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
-    if ws:
-        raise QDeltaError("workspace-requiring path not wired in the binding")
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     rc = lib.qdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
-                              _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, None, 0,
+                              _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes,
                               ctypes.c_void_p(stream))
     _raise(rc, "qdelta_chunk_fwd")
     return o, S_T

@@ -33,8 +33,11 @@ const char *qdelta_status_string(int status) {
 }
 
 size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
-    (void)B; (void)T; (void)H; (void)d_k; (void)d_v; (void)C; (void)dtype;
-    return 0;  // the fused kernel keeps every chunk intermediate in LDS
+    if (B < 0 || T < 0 || H < 0 || !qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return 0;
+    // single pass: every chunk intermediate stays in LDS; segmented schedule: the
+    // per-segment transition maps and states
+    const int P = qd::chunk_fwd_segments(dtype, B, T, H, d_k, d_v, C);
+    return qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
 }
 
 int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
@@ -42,7 +45,6 @@ int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
                      const float *S0, void *o, float *S_T,
                      int B, int T, int H, int d_k, int d_v, int C, int dtype,
                      void *workspace, size_t ws_bytes, void *stream) {
-    (void)workspace;
     if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
     if (!qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
     if (ws_bytes < qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype)) return QD_ERR_WORKSPACE;
@@ -71,7 +73,20 @@ int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.dv = d_v;
     a.n_dvt = d_v / 64;
-    const hipError_t err = qd::launch_chunk_fwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
+    const int P = qd::chunk_fwd_segments(dtype, B, T, H, d_k, d_v, C);
+    hipError_t err;
+    if (P > 1) {
+        const size_t need = qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
+        if (!workspace || !aligned16(workspace)) return QD_ERR_WORKSPACE;
+        if (overlaps(workspace, need, q, static_cast<size_t>(ntok) * d_k * es) ||
+            overlaps(workspace, need, k, static_cast<size_t>(ntok) * d_k * es) ||
+            overlaps(workspace, need, v, o_bytes) || overlaps(workspace, need, o, o_bytes) ||
+            overlaps(workspace, need, S0, state_bytes) || overlaps(workspace, need, S_T, state_bytes))
+            return QD_ERR_INVALID_ARG;
+        err = qd::launch_chunk_fwd_segmented(dtype, d_k, C, a, P, workspace, static_cast<hipStream_t>(stream));
+    } else {
+        err = qd::launch_chunk_fwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
+    }
     return err == hipSuccess ? QD_OK : QD_ERR_HIP;
 }
 

@@ -387,8 +387,14 @@ struct PipeKernel {
         const size_t tok0 = static_cast<size_t>(b) * T * H + h;
         const uint16_t *const qbase = static_cast<const uint16_t *>(args.q) + tok0 * DK;
         const uint16_t *const kbase = static_cast<const uint16_t *>(args.k) + tok0 * DK;
-        const uint16_t *const vbase = static_cast<const uint16_t *>(args.v) + tok0 * dv + dv0;
-        uint16_t *const obase = static_cast<uint16_t *>(args.o) + tok0 * dv + dv0;
+        // v == null reads as zeros and o == null drops the output (state-only passes of the
+        // segmented schedule): their buffer resources get an empty range, so no branch is
+        // needed in the loop and no address is formed from a null pointer
+        const bool has_v = args.v != nullptr, has_o = args.o != nullptr;
+        const uint16_t *const vbase =
+            static_cast<const uint16_t *>(has_v ? args.v : args.q) + (has_v ? tok0 * dv + dv0 : 0);
+        uint16_t *const obase = has_o ? static_cast<uint16_t *>(args.o) + tok0 * dv + dv0
+                                      : static_cast<uint16_t *>(const_cast<void *>(args.q));
         const int rowQ = H * DK * 2, rowV = H * dv * 2, rowG = H * 4;   // bytes between tokens
 
         // ---- scan role: S^T slice; sT[2u + hh][e] holds key 8 kq(g, u) + 4hh + e of column 16w + l%16
@@ -429,7 +435,7 @@ struct PipeKernel {
             const size_t t0 = static_cast<size_t>(c) * CH * H;
             const auto rsq = buffer_rsrc(qbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
             const auto rsk = buffer_rsrc(kbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
-            const auto rsv = buffer_rsrc(vbase + t0 * dv, (clen - 1) * rowV + kDVT * 2);
+            const auto rsv = buffer_rsrc(vbase + (has_v ? t0 * dv : 0), has_v ? (clen - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
                 pf.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voffQ[j], 0, 0);
@@ -697,8 +703,8 @@ struct PipeKernel {
                 // for the output stores
                 if (n + 2 < NC) rstore(n + 2, pf); // into slot n & 1, released in I3
                 if (n >= 0) {
-                    const auto rso = buffer_rsrc(obase + static_cast<size_t>(n) * CH * H * dv,
-                                                 (chunk_len(n) - 1) * rowV + kDVT * 2);
+                    const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * CH * H * dv : 0),
+                                                 has_o ? (chunk_len(n) - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
                     for (int j = 0; j < NVV; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),

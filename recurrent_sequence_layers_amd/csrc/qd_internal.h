@@ -6,10 +6,11 @@
 namespace qd {
 
 struct ChunkArgs {
-    const void *q, *k, *v;          // [B][T][H][d_k] / [B][T][H][d_v], element type per dtype
+    const void *q, *k, *v;          // [B][T][H][d_k] / [B][T][H][d_v], element type per dtype;
+                                    // v may be null (read as zeros) for the bf16 C = 32, 64 kernel
     const float *alpha, *beta, *lam; // [B][T][H]; alpha/lam may be null (selects the instance)
     const float *S0;                // [B][H][d_v][d_k] or null
-    void *o;                        // [B][T][H][d_v]
+    void *o;                        // [B][T][H][d_v]; may be null (not written) for that kernel
     float *S_T;                     // [B][H][d_v][d_k] or null
     int B, T, H, dv;
     int n_dvt;                      // number of 64-wide value-column tiles, d_v / 64
@@ -29,6 +30,14 @@ hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t
 
 // bf16 chunk forward, eight-wave pipelined kernel (qd_chunk_fwd_pipe.hip).
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream);
+
+// Segmented schedule (qd_segment.hip) for long sequences over few heads: the number of
+// segments P the sequence is cut into (1 = the single-pass schedule), the workspace it
+// needs, and the launch sequence.
+int chunk_fwd_segments(int dtype, int B, int T, int H, int dk, int dv, int C);
+size_t chunk_fwd_segment_workspace(int B, int T, int H, int dk, int dv, int P);
+hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
+                                      hipStream_t stream);
 
 // Whether an instance exists for these sizes (checked before launching).
 bool chunk_fwd_supported(int dtype, int dk, int dv, int C);

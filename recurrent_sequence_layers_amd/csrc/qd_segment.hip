@@ -1,0 +1,150 @@
+// Segmented schedule of the chunk forward for long sequences over few heads.
+//
+// The recurrence acts on the state from the right (Q-Delta reading notes §2.4):
+//   S_t = S_{t-1} A_t + beta_t v_t k_t^T,   A_t = alpha_t (I - beta_t x_t k_t^T),
+// so over a run of tokens the exit state is affine in the entry state:
+//   S_out = S_in M + G,   M = A_1 ... A_n,   G = S_out when S_in = 0.
+// M itself is the exit state of the same recurrence started from S_in = I with v = 0,
+// and G is the exit state started from 0 with the real v.  Both therefore come from
+// the ordinary chunk kernel, run over the sequence cut into P segments that are laid
+// side by side as P batch entries ([B][T][H][d] is [B*P][T/P][H][d] in memory):
+//
+//   1. M_p: chunk kernel on every segment, v = 0, S0 = I (d_k x d_k), no output;
+//   2. G_p: chunk kernel on every segment, real v, S0 = 0, no output;
+//   3. S_in[0] = S0, S_in[p+1] = S_in[p] M_p + G_p (fp32, below); S_T = S_in[P-1] M + G;
+//   4. the chunk kernel on every segment from its S_in, writing o.
+//
+// Each pass has P times the parallelism of the single-pass schedule, for three passes
+// of work.  It pays when the single pass leaves most compute units idle.
+#include "qd_device.h"
+#include "qd_internal.h"
+
+namespace qd {
+namespace {
+
+// M[s][i][j] = (i == j) for every segment-head s
+__global__ __launch_bounds__(256) void identity_fill_kernel(float *M, int dk, size_t n) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int e = static_cast<int>(i % (static_cast<size_t>(dk) * dk));
+    M[i] = (e / dk == e % dk) ? 1.f : 0.f;
+}
+
+// Entry states of the segments and the exit state of the sequence, for rows
+// [R * blockIdx.y, R * blockIdx.y + R) of S for (batch, head) blockIdx.x:
+//   S <- S0 (or 0); for p: S_in[b P + p] = S; S <- S M[b P + p] + G[b P + p];  S_T = S.
+// M is streamed through LDS 32 rows at a time; each thread owns DK / 32 columns of one row.
+template <int DK>
+__global__ __launch_bounds__(256) void segment_propagate_kernel(const float *S0, const float *M, const float *G,
+                                                                float *Sin, float *S_T, int P, int H, int dv) {
+    constexpr int R = 8, CPT = DK / 32;
+    __shared__ __attribute__((aligned(16))) float Ss[R][DK];
+    __shared__ __attribute__((aligned(16))) float Ms[32][DK];
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int r0 = R * blockIdx.y;
+    const int t = threadIdx.x, row = t / 32, c0 = (t % 32) * CPT;
+    {
+        const size_t off = ((static_cast<size_t>(bh)) * dv + r0 + row) * DK + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Ss[row][c0 + c] = S0 ? S0[off + c] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p < P; ++p) {
+        const size_t seg = static_cast<size_t>(b * P + p) * H + h;
+        const size_t off = (seg * dv + r0 + row) * DK + c0;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            Sin[off + c] = Ss[row][c0 + c];
+            acc[c] = G[off + c];
+        }
+        const float *Mp = M + seg * DK * DK;
+        for (int js = 0; js < DK / 32; ++js) {
+            __syncthreads();                           // previous slice consumed
+            for (int i = t; i < 32 * DK / 4; i += 256)
+                reinterpret_cast<f32x4 *>(&Ms[0][0])[i] = reinterpret_cast<const f32x4 *>(Mp + 32 * js * DK)[i];
+            __syncthreads();
+#pragma unroll 8
+            for (int i = 0; i < 32; ++i) {
+                const float s = Ss[row][32 * js + i];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) acc[c] += s * Ms[i][c0 + c];
+            }
+        }
+        __syncthreads();                               // every thread has read Ss
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Ss[row][c0 + c] = acc[c];
+        __syncthreads();
+    }
+    if (S_T) {
+        const size_t off = ((static_cast<size_t>(bh)) * dv + r0 + row) * DK + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) S_T[off + c] = Ss[row][c0 + c];
+    }
+}
+
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+}  // namespace
+
+int chunk_fwd_segments(int dtype, int B, int T, int H, int dk, int dv, int C) {
+    // the state-only passes use the bf16 eight-wave kernel (null v and o)
+    if (dtype != 1 || (C != 32 && C != 64) || B <= 0 || H <= 0 || T <= 0) return 1;
+    const long long units = static_cast<long long>(B) * H * (dv > dk ? dv : dk) / 64;
+    const int cus = compute_units();
+    int P = 1;
+    while (P < 16 && units * 2 * P <= cus && T % (2 * P * C) == 0 && T / (2 * P * C) >= 8) P *= 2;
+    return P;
+}
+
+size_t chunk_fwd_segment_workspace(int B, int T, int H, int dk, int dv, int P) {
+    (void)T;
+    if (P <= 1) return 0;
+    const size_t nseg = static_cast<size_t>(B) * P * H;
+    return nseg * (static_cast<size_t>(dk) * dk + 2 * static_cast<size_t>(dv) * dk) * sizeof(float);
+}
+
+hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
+                                      hipStream_t stream) {
+    const size_t nseg = static_cast<size_t>(a.B) * P * a.H;
+    float *const Mseg = static_cast<float *>(ws);                       // [B P][H][d_k][d_k]
+    float *const Gseg = Mseg + nseg * dk * dk;                          // [B P][H][d_v][d_k]
+    float *const Sin = Gseg + nseg * a.dv * dk;                         // [B P][H][d_v][d_k]
+    const size_t nM = nseg * dk * dk;
+    hipLaunchKernelGGL(identity_fill_kernel, dim3(static_cast<unsigned>((nM + 255) / 256)), dim3(256), 0, stream,
+                       Mseg, dk, nM);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    ChunkArgs seg = a;
+    seg.B = a.B * P;
+    seg.T = a.T / P;
+    // 1. transition maps: v = 0, S0 = I, state updated in place, no output
+    ChunkArgs m = seg;
+    m.v = nullptr; m.o = nullptr; m.S0 = Mseg; m.S_T = Mseg; m.dv = dk; m.n_dvt = dk / 64;
+    if ((err = launch_chunk_fwd(dtype, dk, C, m, stream)) != hipSuccess) return err;
+    // 2. exit states from zero entry states, no output
+    ChunkArgs g = seg;
+    g.o = nullptr; g.S0 = nullptr; g.S_T = Gseg;
+    if ((err = launch_chunk_fwd(dtype, dk, C, g, stream)) != hipSuccess) return err;
+    // 3. entry states of the segments and the exit state of the sequence
+    const dim3 pg(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(a.dv / 8));
+    if (dk == 128)
+        hipLaunchKernelGGL((segment_propagate_kernel<128>), pg, dim3(256), 0, stream, a.S0, Mseg, Gseg, Sin, a.S_T, P,
+                           a.H, a.dv);
+    else
+        hipLaunchKernelGGL((segment_propagate_kernel<64>), pg, dim3(256), 0, stream, a.S0, Mseg, Gseg, Sin, a.S_T, P,
+                           a.H, a.dv);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // 4. the outputs, every segment from its entry state
+    ChunkArgs f = seg;
+    f.S0 = Sin; f.S_T = nullptr;
+    return launch_chunk_fwd(dtype, dk, C, f, stream);
+}
+
+}  // namespace qd

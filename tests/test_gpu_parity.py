@@ -281,3 +281,57 @@ def test_gate_instances_agree_bitwise(qd, C, dt):
     for o, S in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(S, outs[0][1])
     check_against_oracle(outs[0][0].float(), outs[0][1], x, TOL[dt])
+
+
+# ------------------------------------------------------------------ segmented schedule
+# Few heads over a long sequence: the library cuts the sequence into P segments (here 8
+# on a 256-CU MI355X), finds every segment's transition map and offset with the chunk
+# kernel, propagates the entry states and reruns the segments.  Full compare with the
+# oracle, which runs the plain recurrence.
+SEG = [
+    # B, T, H, dk, dv, C, lam, alpha, s0
+    (1, 8192, 2, 128, 128, 64, "random", "random", 0.05),
+    (1, 8192, 1, 64, 64, 32, "zero", "random", None),
+    (1, 8192, 2, 128, 64, 64, "zero", "one", 0.05),
+    (2, 4096, 1, 64, 128, 64, "random", "one", None),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,C,lam,alpha,s0", SEG)
+def test_segmented_schedule(qd, B, T, H, dk, dv, C, lam, alpha, s0):
+    ws = qd.qdelta_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
+    print(f"B={B} T={T} H={H} dk={dk} dv={dv} C={C} lam={lam} alpha={alpha} workspace {ws} bytes", flush=True)
+    assert ws > 0, "expected the segmented schedule for this shape"
+    x = inputs.chunk_inputs(B, T, H, dk, dv, "bf16", seed=T + dk + C, lam=lam, alpha=alpha, s0_std=s0,
+                            gates_as_none=True)
+    o, S = run_gpu(qd, x, C)
+    xc = inputs.ChunkInputs(x.q, x.k, x.v, x.alpha if x.alpha is not None else torch.ones(B, T, H), x.beta,
+                            x.lam if x.lam is not None else torch.zeros(B, T, H), x.S0)
+    check_against_oracle(o, S, xc, TOL["bf16"])
+
+
+def test_segmented_in_place_and_no_state(qd):
+    B, T, H, d, C = 1, 8192, 2, 128, 64
+    x = inputs.chunk_inputs(B, T, H, d, d, "bf16", seed=77, s0_std=0.05, device="cuda")
+    o_ref, S_ref = qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=C)
+    S = x.S0.clone()
+    o_in, S_in = qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, S, C=C, S_T=S)
+    o_ns, S_ns = qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=C, want_state=False)
+    torch.cuda.synchronize()
+    assert S_ns is None
+    assert torch.equal(o_in, o_ref) and torch.equal(S, S_ref) and torch.equal(o_ns, o_ref)
+
+
+def test_segmented_requires_workspace(qd):
+    import ctypes
+    B, T, H, d, C = 1, 8192, 1, 64, 64
+    assert qd.qdelta_chunk_fwd_workspace_bytes(B, T, H, d, d, C, torch.bfloat16) > 0
+    x = inputs.chunk_inputs(B, T, H, d, d, "bf16", seed=5, device="cuda")
+    o = torch.empty_like(x.v)
+    lib = qd.load_library()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = lib.qdelta_chunk_fwd(p(x.q), p(x.k), p(x.v), p(x.alpha), p(x.beta), p(x.lam), None, p(o), None,
+                              B, T, H, d, d, C, 1, None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 3, qd.qdelta_status_string(rc)   # QD_ERR_WORKSPACE, nothing launched
+    # the headline shape keeps the single-pass schedule and needs none
+    assert qd.qdelta_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, torch.bfloat16) == 0

@@ -191,3 +191,43 @@ def test_pipelined_form_matches_recurrence(T, C, dk, dv):
     o_k, S_k = pipelined_form_fwd(q, k, v, alpha, beta, lam, S0, C)
     np.testing.assert_allclose(o_k, o_r, atol=1e-10)
     np.testing.assert_allclose(S_k, S_r, atol=1e-10)
+
+
+def segmented_fwd(q, k, v, alpha, beta, lam, S0, P):
+    """The segmented schedule in fp64 on the oracle: each segment's transition map
+    M = (state after the segment from S = I with v = 0) and offset G = (state after it
+    from S = 0), entry states S_in[p+1] = S_in[p] M_p + G_p, then every segment rerun
+    from its entry state."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    L = T // P
+    o = np.zeros((B, T, H, dv))
+    S_T = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        S = np.zeros((1, H, dv, dk)) if S0 is None else S0[b:b + 1].copy()
+        for p in range(P):
+            sl = (slice(b, b + 1), slice(p * L, (p + 1) * L))
+            seg = [t[sl] for t in (q, k, v, alpha, beta, lam)]
+            eye = np.broadcast_to(np.eye(dk), (1, H, dk, dk)).copy()
+            _, M = oracle.qdelta_fwd(seg[0], seg[1], np.zeros((1, L, H, dk)), seg[3], seg[4], seg[5], eye)
+            _, G = oracle.qdelta_fwd(*seg, None)
+            o[b, p * L:(p + 1) * L] = oracle.qdelta_fwd(*seg, S)[0][0]
+            S = np.einsum('xhij,xhjk->xhik', S, M) + G
+        S_T[b] = S[0]
+    return o, S_T
+
+
+@pytest.mark.parametrize("T,P,dk,dv", [(64, 4, 16, 16), (96, 3, 16, 8), (60, 5, 8, 16)])
+def test_segmented_schedule_matches_recurrence(T, P, dk, dv):
+    r = np.random.default_rng(11 * T + P)
+    q = r.standard_normal((2, T, 2, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((2, T, 2, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((2, T, 2, dv))
+    beta = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    alpha = np.exp(-np.log1p(np.exp(r.standard_normal((2, T, 2)) - 4.0)))
+    lam = 1 / (1 + np.exp(-r.standard_normal((2, T, 2))))
+    S0 = 0.1 * r.standard_normal((2, 2, dv, dk))
+    o_r, S_r = oracle.qdelta_fwd(q, k, v, alpha, beta, lam, S0)
+    o_s, S_s = segmented_fwd(q, k, v, alpha, beta, lam, S0, P)
+    np.testing.assert_allclose(o_s, o_r, atol=1e-11)
+    np.testing.assert_allclose(S_s, S_r, atol=1e-11)
