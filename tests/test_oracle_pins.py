@@ -323,3 +323,51 @@ def test_beta_zero_is_pure_decay_and_empty_sequence():
     o0, S00 = oracle.qdelta_fwd(q[:, :0], k[:, :0], v[:, :0], a[:, :0], beta[:, :0], la[:, :0], S0)
     assert o0.shape == (B, 0, H, dv)
     np.testing.assert_array_equal(S00, S0)
+
+
+# ------------------------------------------------------------------ layer prologue (fused entry points)
+from oracle import prologue as pro
+
+
+def test_prologue_closed_forms():
+    # sigma(0) = 1/2; alpha at logit 0 is exp(-log 2) = 1/2; softplus(0) = log 2
+    assert pro.sigmoid(0.0) == 0.5
+    assert abs(pro.softplus(0.0) - np.log(2.0)) < 1e-15
+    assert abs(pro.decay(0.0) - 0.5) < 1e-15
+    # alpha = exp(-softplus(a)) is the logistic function of -a: a second, independent form
+    a = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(pro.decay(a), 1.0 / (1.0 + np.exp(a)), rtol=1e-13, atol=0)
+    # the overflow-free softplus agrees with log1p(exp(z)), which is accurate where exp(z) fits
+    z = np.linspace(-20, 20, 81)
+    np.testing.assert_allclose(pro.softplus(z), np.log1p(np.exp(z)), rtol=1e-14)
+    # limits: no overflow at large logits; the decay stays in (0, 1)
+    assert pro.softplus(800.0) == 800.0 and pro.decay(-800.0) == 1.0
+    assert 0.0 < pro.decay(40.0) < 1e-17
+
+
+def test_prologue_normalisation():
+    r = np.random.default_rng(4)
+    x = r.standard_normal((5, 7, 3, 64)) * r.uniform(0.1, 10.0, (5, 7, 3, 1))
+    y = pro.l2_normalise(x)
+    n = np.sqrt((x * x).sum(-1))
+    # unit norm up to the epsilon: |y| = |x| / sqrt(|x|^2 + eps)
+    np.testing.assert_allclose(np.sqrt((y * y).sum(-1)), n / np.sqrt(n * n + pro.EPS), rtol=1e-13)
+    # direction kept, positive rescaling of the input changes nothing beyond the epsilon
+    np.testing.assert_allclose(pro.l2_normalise(3.0 * x), y, rtol=1e-6)
+    assert np.all(pro.l2_normalise(np.zeros((2, 8))) == 0.0)
+
+
+def test_prologue_feeds_the_recurrence():
+    """Raw inputs through the prologue give the recurrence of the mapped inputs."""
+    r = np.random.default_rng(9)
+    B, T, H, dk, dv = 1, 20, 2, 16, 8
+    q, k = r.standard_normal((B, T, H, dk)) * 3, r.standard_normal((B, T, H, dk)) * 0.5
+    v = r.standard_normal((B, T, H, dv))
+    a, b, l = (r.standard_normal((B, T, H)) for _ in range(3))
+    qh, kh, al, be, la = pro.prologue(q, k, a, b, l)
+    o1, S1 = oracle.qdelta_fwd(qh, kh, v, al, be, la, None)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o2, S2 = oracle.qdelta_fwd(qn, kn, v, 1 / (1 + np.exp(a)), 1 / (1 + np.exp(-b)), 1 / (1 + np.exp(-l)), None)
+    np.testing.assert_allclose(o1, o2, atol=1e-6)
+    np.testing.assert_allclose(S1, S2, atol=1e-6)
