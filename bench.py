@@ -197,6 +197,30 @@ def main():
             f"{v_ms / ms_per_step:.3f} x the headline time")
         del vx, vo, vS, vws
     torch.cuda.synchronize()
+    if not args.headline_only:
+        # the headline layer through the fused prologue: unnormalised q, k and gate logits
+        # (qdelta_chunk_fwd_raw), against the headline call on prepared inputs
+        g = torch.Generator(device=dev).manual_seed(args.seed + 3)
+        rq = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
+        rk = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
+        ra = torch.randn(B, T, H, generator=g, device=dev) - 4.0
+        rb = torch.randn(B, T, H, generator=g, device=dev)
+        rl = torch.randn(B, T, H, generator=g, device=dev)
+        rf = lambda: qd.qdelta_chunk_fwd(rq, rk, x.v, ra, rb, rl, None, C=C, o=o, S_T=S_T, raw=True)
+        for _ in range(args.warmup):
+            rf()
+        torch.cuda.synchronize()
+        r_s, _ = time_region(torch, rf, args.steps)
+        r_ms = r_s / args.steps * 1e3
+        variants["layer_1p3b_raw_prologue"] = {
+            "B": B, "T": T, "H": H, "inputs": "q, k unnormalised; alpha, beta, lambda as logits",
+            "steps": args.steps, "ms_per_call": r_ms, "tokens_per_s": B * T / (r_ms * 1e-3),
+            "time_ratio_to_headline": r_ms / ms_per_step,
+            "separate_prologue_pass_bytes": 2 * B * T * H * dk * 2 * 2 + 3 * B * T * H * 4 * 2,
+            "separate_prologue_pass_us_at_peak": (2 * B * T * H * dk * 2 * 2 + 3 * B * T * H * 4 * 2)
+                                                 / (PEAK_HBM_GBS * 1e3)}
+        log(f"[bench] layer_1p3b raw prologue: {r_ms:.4f} ms/call, {r_ms / ms_per_step:.3f} x the headline time")
+        del rq, rk, ra, rb, rl
 
     # ---- decode step: 256 sequences x 16 heads, fp32 state resident, D consecutive steps
     dw = inputs.WORKLOADS["decode_256x16"]

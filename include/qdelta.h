@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define QDELTA_ABI_VERSION 1
+#define QDELTA_ABI_VERSION 2
 
 typedef enum qd_status {
     QD_OK = 0,
@@ -115,6 +115,32 @@ int qdelta_step(const void *q, const void *k, const void *v,
                 const float *alpha, const float *beta, const float *lambda,
                 float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
                 void *stream);
+
+/*
+ * The same two calls with the layer's prologue fused in (the layer of the Q-Delta
+ * reading notes §1, trained as in §3.1, feeds the recurrence unit-norm q and k and
+ * gates mapped into their ranges).  Arguments, layouts, workspace, aliasing and
+ * status codes are those of qdelta_chunk_fwd and qdelta_step, except:
+ *
+ *   q, k            unnormalised; each (token, head) vector is divided by
+ *                   sqrt(|x|^2 + 1e-6) before use (a zero vector stays zero);
+ *   alpha_logit     a, alpha = exp(-softplus(a)) = 1 / (1 + exp(a)); NULL means alpha = 1;
+ *   beta_logit      b, beta = 1 / (1 + exp(-b)); required;
+ *   lambda_logit    l, lambda = 1 / (1 + exp(-l)); NULL means lambda = 0.
+ *
+ * This replaces a separate pass that would read and rewrite q and k in HBM.
+ * qdelta_chunk_fwd_raw supports bf16 with C in {32, 64} (QD_ERR_UNSUPPORTED
+ * otherwise); qdelta_step_raw supports every qdelta_step configuration.
+ */
+int qdelta_chunk_fwd_raw(const void *q, const void *k, const void *v,
+                         const float *alpha_logit, const float *beta_logit,
+                         const float *lambda_logit, const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                         void *workspace, size_t ws_bytes, void *stream);
+int qdelta_step_raw(const void *q, const void *k, const void *v,
+                    const float *alpha_logit, const float *beta_logit,
+                    const float *lambda_logit, float *S, void *o, int N, int H,
+                    int d_k, int d_v, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -43,8 +43,12 @@ def load_library():
     lib.qdelta_chunk_fwd_workspace_bytes.argtypes = [i] * 7
     lib.qdelta_chunk_fwd.restype = i
     lib.qdelta_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
+    lib.qdelta_chunk_fwd_raw.restype = i
+    lib.qdelta_chunk_fwd_raw.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
     lib.qdelta_step.restype = i
     lib.qdelta_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
+    lib.qdelta_step_raw.restype = i
+    lib.qdelta_step_raw.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
     _lib = lib
     return lib
 
@@ -96,14 +100,16 @@ def _raise(rc, fn):
 
 
 def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_T=None,
-                     want_state: bool = True, stream=None, workspace=None):
+                     want_state: bool = True, stream=None, workspace=None, raw: bool = False):
     """Layer forward, chunkwise WY/UT form.  q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or
     bf16, same dtype); alpha, beta, lam [B,T,H] fp32 (alpha None means 1, lam None
     means 0); S0 [B,H,d_v,d_k] fp32 or None.  Returns (o, S_T); S_T is None when
     want_state is False.  S_T may be passed as S0 for an in-place state update.
     workspace: a device tensor of at least qdelta_chunk_fwd_workspace_bytes(...) bytes
     (long sequences over few heads run a segmented schedule that needs one); when None
-    and one is needed, it is allocated here."""
+    and one is needed, it is allocated here.
+    raw: q and k unnormalised and alpha, beta, lam given as logits (qdelta_chunk_fwd_raw:
+    the layer's normalisation and gate maps run inside the kernel)."""
     import torch
     lib = load_library()
     B, T, H, dk = q.shape
@@ -126,17 +132,18 @@ def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_
     if ws and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    rc = lib.qdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
-                              _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes,
-                              ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_chunk_fwd")
+    fn = lib.qdelta_chunk_fwd_raw if raw else lib.qdelta_chunk_fwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
+            _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_chunk_fwd_raw" if raw else "qdelta_chunk_fwd")
     return o, S_T
 
 
-def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None):
+def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None, raw: bool = False):
     """One decode step for N sequences x H heads.  q, k [N,H,d_k], v [N,H,d_v];
     alpha, beta, lam [N,H] fp32 (alpha None means 1, lam None means 0);
-    S [N,H,d_v,d_k] fp32, updated in place.  Returns o [N,H,d_v]."""
+    S [N,H,d_v,d_k] fp32, updated in place.  Returns o [N,H,d_v].
+    raw: q and k unnormalised and the gates as logits (qdelta_step_raw)."""
     import torch
     lib = load_library()
     N, H, dk = q.shape
@@ -151,7 +158,8 @@ def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None):
     _check(o, "o", dt, (N, H, dv))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.qdelta_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S), _ptr(o),
-                         N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_step")
+    fn = lib.qdelta_step_raw if raw else lib.qdelta_step
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S), _ptr(o),
+            N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_step_raw" if raw else "qdelta_step")
     return o

@@ -40,13 +40,16 @@ size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, i
     return qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
 }
 
-int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
-                     const float *alpha, const float *beta, const float *lambda,
-                     const float *S0, void *o, float *S_T,
-                     int B, int T, int H, int d_k, int d_v, int C, int dtype,
-                     void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+              const float *lambda, const float *S0, void *o, float *S_T, int B, int T, int H, int d_k, int d_v,
+              int C, int dtype, void *workspace, size_t ws_bytes, void *stream, bool raw) {
     if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
     if (!qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
+    if (raw && (dtype != QD_BF16 || (C != 32 && C != 64))) return QD_ERR_UNSUPPORTED;
     if (ws_bytes < qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype)) return QD_ERR_WORKSPACE;
     const long long bh = static_cast<long long>(B) * H;
     if (bh == 0) return QD_OK;
@@ -73,6 +76,7 @@ int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.dv = d_v;
     a.n_dvt = d_v / 64;
+    a.raw = raw;
     const int P = qd::chunk_fwd_segments(dtype, B, T, H, d_k, d_v, C);
     hipError_t err;
     if (P > 1) {
@@ -90,10 +94,8 @@ int qdelta_chunk_fwd(const void *q, const void *k, const void *v,
     return err == hipSuccess ? QD_OK : QD_ERR_HIP;
 }
 
-int qdelta_step(const void *q, const void *k, const void *v,
-                const float *alpha, const float *beta, const float *lambda,
-                float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
-                void *stream) {
+int step(const void *q, const void *k, const void *v, const float *alpha, const float *beta, const float *lambda,
+         float *S, void *o, int N, int H, int d_k, int d_v, int dtype, void *stream, bool raw) {
     if (N < 0 || H < 0) return QD_ERR_INVALID_ARG;
     if (!qd::step_supported(dtype, d_k, d_v)) return QD_ERR_UNSUPPORTED;
     const long long nh = static_cast<long long>(N) * H;
@@ -114,8 +116,39 @@ int qdelta_step(const void *q, const void *k, const void *v,
     a.q = q; a.k = k; a.v = v;
     a.alpha = alpha; a.beta = beta; a.lam = lambda;
     a.S = S; a.o = o; a.N = N; a.H = H;
+    a.raw = raw;
     const hipError_t err = qd::launch_step(dtype, d_k, d_v, a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qdelta_chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                     const float *lambda, const float *S0, void *o, float *S_T, int B, int T, int H, int d_k,
+                     int d_v, int C, int dtype, void *workspace, size_t ws_bytes, void *stream) {
+    return chunk_fwd(q, k, v, alpha, beta, lambda, S0, o, S_T, B, T, H, d_k, d_v, C, dtype, workspace, ws_bytes,
+                     stream, false);
+}
+
+int qdelta_chunk_fwd_raw(const void *q, const void *k, const void *v, const float *alpha_logit,
+                         const float *beta_logit, const float *lambda_logit, const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int d_k, int d_v, int C, int dtype, void *workspace, size_t ws_bytes,
+                         void *stream) {
+    return chunk_fwd(q, k, v, alpha_logit, beta_logit, lambda_logit, S0, o, S_T, B, T, H, d_k, d_v, C, dtype,
+                     workspace, ws_bytes, stream, true);
+}
+
+int qdelta_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                const float *lambda, float *S, void *o, int N, int H, int d_k, int d_v, int dtype, void *stream) {
+    return step(q, k, v, alpha, beta, lambda, S, o, N, H, d_k, d_v, dtype, stream, false);
+}
+
+int qdelta_step_raw(const void *q, const void *k, const void *v, const float *alpha_logit, const float *beta_logit,
+                    const float *lambda_logit, float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
+                    void *stream) {
+    return step(q, k, v, alpha_logit, beta_logit, lambda_logit, S, o, N, H, d_k, d_v, dtype, stream, true);
 }
 
 }  // extern "C"

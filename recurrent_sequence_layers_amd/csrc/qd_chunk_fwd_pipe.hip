@@ -110,6 +110,42 @@ __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
 }
 
+// Layer prologue of the raw entry point (the layer of the Q-Delta reading notes §1 and
+// §3.1 normalises q and k and maps the gate logits): row segment of a staging lane,
+// 8 bf16 of one q or k row, L2-normalised over the row, q / sqrt(|q|^2 + 1e-6).  The
+// row's 16 segments sit in the lanes that differ in lane-id bits 0-1 and in the bits of
+// the fragment step: bit 4 for d_k = 64, bits 4-5 for d_k = 128.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+template <int NKP>
+__device__ __forceinline__ u32x4 normalise_row_segment(u32x4 v) {
+    f32x4 lo, hi;                                          // elements 2i and 2i + 1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = __builtin_bit_cast(float, v[i] << 16);
+        hi[i] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
+    ss += dpp_f32<0xb1>(ss);                               // lane ^ 1
+    ss += dpp_f32<0x4e>(ss);                               // lane ^ 2
+    if constexpr (NKP >= 2) ss += __shfl_xor(ss, 16);
+    if constexpr (NKP >= 4) ss += __shfl_xor(ss, 32);
+    const float r = __frsqrt_rn(ss + 1e-6f);
+    const bf16x4 a = Bf16::cvt(f32x4{lo[0], hi[0], lo[1], hi[1]} * r);
+    const bf16x4 b = Bf16::cvt(f32x4{lo[2], hi[2], lo[3], hi[3]} * r);
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return u32x4{ua.x, ua.y, ub.x, ub.y};
+}
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+// log(alpha) = -softplus(a) = -(max(a, 0) + log(1 + exp(-|a|)))
+__device__ __forceinline__ float log_decay_from_logit(float a) {
+    return -(fmaxf(a, 0.f) + __logf(1.f + __expf(-fabsf(a))));
+}
+
 // acc + A B for fp32 fragments a (A operand) and b (B operand), rounded to bf16 like
 // every other operand of the block doubling
 __device__ __forceinline__ f32x4 mfma_bf(f32x4 a, f32x4 b, f32x4 acc) {
@@ -225,7 +261,9 @@ constexpr int tile_mask(const int (&t)[4], int n) {
     return m;
 }
 
-template <int DK, int CH, bool HAS_A, bool HAS_L>
+// RAW: q and k arrive unnormalised and alpha, beta, lambda as logits; both are mapped
+// while the chunk is staged into LDS, so everything downstream is the same as without.
+template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW>
 struct PipeKernel {
     using Lay = PipeLayout<DK, CH>;
     static constexpr int NKT = DK / 16, NKP = DK / 32;
@@ -457,21 +495,27 @@ struct PipeKernel {
             uint16_t *Qs = Qb(s), *Ks = Kb(s), *Vs = Vb(s);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
-                *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
-                *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
+                if constexpr (RAW) {
+                    *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = normalise_row_segment<NKP>(pf.q[j]);
+                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = normalise_row_segment<NKP>(pf.k[j]);
+                } else {
+                    *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
+                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
+                }
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
             if (rw == 0) {                        // gates of the chunk, lane = position
                 const bool ok = lane < chunk_len(c);
-                const float x = wave_inclusive_sum((HAS_A && ok) ? __logf(pf.a) : 0.f);
+                const float la = RAW ? log_decay_from_logit(pf.a) : __logf(pf.a);
+                const float x = wave_inclusive_sum((HAS_A && ok) ? la : 0.f);
                 const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
                 if (lane < CH) {
                     gate(s, 0)[lane] = x;
                     gate(s, 1)[lane] = __expf(x);
                     gate(s, 2)[lane] = __expf(glast - x);
-                    gate(s, 3)[lane] = ok ? pf.b : 0.f;
-                    gate(s, 4)[lane] = ok ? pf.l : 0.f;
+                    gate(s, 3)[lane] = ok ? (RAW ? sigmoid_f(pf.b) : pf.b) : 0.f;
+                    gate(s, 4)[lane] = ok ? ((RAW && HAS_L) ? sigmoid_f(pf.l) : pf.l) : 0.f;
                 }
             }
         };
@@ -731,9 +775,9 @@ struct PipeKernel {
     }
 };
 
-template <int DK, int CH, bool HAS_A, bool HAS_L>
+template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const ChunkArgs args) {
-    PipeKernel<DK, CH, HAS_A, HAS_L>::run(args);
+    PipeKernel<DK, CH, HAS_A, HAS_L, RAW>::run(args);
 }
 
 template <int DK, int CH>
@@ -742,10 +786,17 @@ hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
     if (grid == 0) return hipSuccess;
     const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
     const dim3 blk(kPipeThreads);
-    if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, true>), dim3(grid), blk, 0, stream, a);
-    else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, false>), dim3(grid), blk, 0, stream, a);
-    else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, true>), dim3(grid), blk, 0, stream, a);
-    else hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, false>), dim3(grid), blk, 0, stream, a);
+    if (a.raw) {
+        if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, true, true>), dim3(grid), blk, 0, stream, a);
+        else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, false, true>), dim3(grid), blk, 0, stream, a);
+        else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, true, true>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, false, true>), dim3(grid), blk, 0, stream, a);
+    } else {
+        if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, true, false>), dim3(grid), blk, 0, stream, a);
+        else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, true, false, false>), dim3(grid), blk, 0, stream, a);
+        else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, true, false>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_fwd_pipe_kernel<DK, CH, false, false, false>), dim3(grid), blk, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ struct ChunkArgs {
     float *S_T;                     // [B][H][d_v][d_k] or null
     int B, T, H, dv;
     int n_dvt;                      // number of 64-wide value-column tiles, d_v / 64
+    bool raw = false;               // q, k unnormalised and gates as logits (bf16 C = 32, 64 only)
 };
 
 struct StepArgs {
@@ -22,6 +23,7 @@ struct StepArgs {
     float *S;                       // [N][H][d_v][d_k], in place
     void *o;                        // [N][H][d_v]
     int N, H;
+    bool raw = false;               // q, k unnormalised and gates as logits
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Return hipSuccess or the launch error.

@@ -28,7 +28,10 @@ __device__ __forceinline__ float group8_sum(float x) {
     return x;
 }
 
-template <class P, int DK, int DV, bool HAS_A, bool HAS_L>
+// RAW: q and k arrive unnormalised and alpha, beta, lambda as logits (the layer's
+// prologue, Q-Delta reading notes §1 and §3.1): q / sqrt(|q|^2 + 1e-6), likewise k;
+// beta = sigmoid(b), lambda = sigmoid(l), alpha = exp(-softplus(a)) = 1 / (1 + exp(a)).
+template <class P, int DK, int DV, bool HAS_A, bool HAS_L, bool RAW>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs args) {
     using R = typename P::R;
     constexpr int NG = DK / (4 * kLanesPerRow);           // float4 column groups per lane
@@ -59,11 +62,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs args)
             s[p][m] = *reinterpret_cast<const f32x4 *>(S + static_cast<size_t>(row) * DK + 4 * (m * kLanesPerRow + sub));
     }
 
-    const float alpha = HAS_A ? args.alpha[nh] : 1.f;
-    const float beta = args.beta[nh];
-    const float lam = HAS_L ? args.lam[nh] : 0.f;
+    const float alpha = HAS_A ? (RAW ? 1.f / (1.f + __expf(args.alpha[nh])) : args.alpha[nh]) : 1.f;
+    const float beta = RAW ? 1.f / (1.f + __expf(-args.beta[nh])) : args.beta[nh];
+    const float lam = HAS_L ? (RAW ? 1.f / (1.f + __expf(-args.lam[nh])) : args.lam[nh]) : 0.f;
     f32x4 kk[NG], qq[NG], xx[NG];
-    float kq = 0.f;
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
         const int c = 4 * (m * kLanesPerRow + sub);
@@ -71,10 +73,32 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs args)
         for (int i = 0; i < 4; ++i) {
             kk[m][i] = P::to_f32(gk[c + i]);
             qq[m][i] = P::to_f32(gq[c + i]);
+        }
+    }
+    if constexpr (RAW) {                      // the eight lanes of a row hold all of q and k
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int m = 0; m < NG; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sk += kk[m][i] * kk[m][i];
+                sq += qq[m][i] * qq[m][i];
+            }
+        const float rk = __frsqrt_rn(group8_sum(sk) + 1e-6f), rq = __frsqrt_rn(group8_sum(sq) + 1e-6f);
+#pragma unroll
+        for (int m = 0; m < NG; ++m) {
+            kk[m] *= rk;
+            qq[m] *= rq;
+        }
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < NG; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             xx[m][i] = HAS_L ? kk[m][i] + lam * qq[m][i] : kk[m][i];
             kq += kk[m][i] * qq[m][i];
         }
-    }
     kq = group8_sum(kq);
 
 #pragma unroll
@@ -105,15 +129,21 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs args)
     }
 }
 
+template <class P, int DK, int DV, bool RAW>
+void launch_step_gates(const StepArgs &a, hipStream_t stream) {
+    const dim3 grid(a.N * a.H), blk(kStepThreads);
+    const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
+    if (ha && hl) hipLaunchKernelGGL((step_kernel<P, DK, DV, true, true, RAW>), grid, blk, 0, stream, a);
+    else if (ha) hipLaunchKernelGGL((step_kernel<P, DK, DV, true, false, RAW>), grid, blk, 0, stream, a);
+    else if (hl) hipLaunchKernelGGL((step_kernel<P, DK, DV, false, true, RAW>), grid, blk, 0, stream, a);
+    else hipLaunchKernelGGL((step_kernel<P, DK, DV, false, false, RAW>), grid, blk, 0, stream, a);
+}
+
 template <class P, int DK, int DV>
 hipError_t launch_step_typed(const StepArgs &a, hipStream_t stream) {
-    const int grid = a.N * a.H;
-    if (grid == 0) return hipSuccess;
-    const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
-    if (ha && hl) hipLaunchKernelGGL((step_kernel<P, DK, DV, true, true>), dim3(grid), dim3(kStepThreads), 0, stream, a);
-    else if (ha) hipLaunchKernelGGL((step_kernel<P, DK, DV, true, false>), dim3(grid), dim3(kStepThreads), 0, stream, a);
-    else if (hl) hipLaunchKernelGGL((step_kernel<P, DK, DV, false, true>), dim3(grid), dim3(kStepThreads), 0, stream, a);
-    else hipLaunchKernelGGL((step_kernel<P, DK, DV, false, false>), dim3(grid), dim3(kStepThreads), 0, stream, a);
+    if (a.N * a.H == 0) return hipSuccess;
+    if (a.raw) launch_step_gates<P, DK, DV, true>(a, stream);
+    else launch_step_gates<P, DK, DV, false>(a, stream);
     return hipGetLastError();
 }
 

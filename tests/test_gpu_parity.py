@@ -335,3 +335,76 @@ def test_segmented_requires_workspace(qd):
     assert rc == 3, qd.qdelta_status_string(rc)   # QD_ERR_WORKSPACE, nothing launched
     # the headline shape keeps the single-pass schedule and needs none
     assert qd.qdelta_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, torch.bfloat16) == 0
+
+
+# ------------------------------------------------------------------ fused prologue (raw entry points)
+from oracle import prologue as pro
+
+
+def raw_inputs(B, T, H, dk, dv, dt, seed, lam=True, alpha=True):
+    """Unnormalised q, k of mixed magnitudes (one all-zero token) and gate logits."""
+    g = torch.Generator().manual_seed(seed)
+    f = dict(generator=g, dtype=torch.float32)
+    q = torch.randn(B, T, H, dk, **f) * torch.exp(torch.randn(B, T, H, 1, **f))
+    k = torch.randn(B, T, H, dk, **f) * torch.exp(torch.randn(B, T, H, 1, **f))
+    q[0, T // 2, 0] = 0.0
+    k[0, T // 2, 0] = 0.0
+    v = torch.randn(B, T, H, dv, **f)
+    a = torch.randn(B, T, H, **f) - 4.0 if alpha else None
+    b = torch.randn(B, T, H, **f)
+    l = torch.randn(B, T, H, **f) if lam else None
+    dtt = inputs.torch_dtype(dt)
+    return q.to(dtt), k.to(dtt), v.to(dtt), a, b, l
+
+
+RAW = [
+    # B, T, H, dk, dv, C, lam, alpha
+    (2, 200, 3, 128, 128, 64, True, True),
+    (1, 130, 2, 64, 128, 32, True, True),
+    (1, 300, 2, 128, 64, 64, False, True),
+    (2, 77, 1, 64, 64, 32, True, False),
+    (1, 8192, 2, 128, 128, 64, True, True),      # the segmented schedule
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,C,lam,alpha", RAW)
+def test_raw_chunk_fwd(qd, B, T, H, dk, dv, C, lam, alpha):
+    print(f"raw B={B} T={T} H={H} dk={dk} dv={dv} C={C} lam={lam} alpha={alpha}", flush=True)
+    q, k, v, a, b, l = raw_inputs(B, T, H, dk, dv, "bf16", seed=B * T + dk + C, lam=lam, alpha=alpha)
+    g = torch.Generator().manual_seed(3)
+    S0 = 0.05 * torch.randn(B, H, dv, dk, generator=g)
+    o, S = qd.qdelta_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), to_dev(a), b.cuda(), to_dev(l), S0.cuda(), C=C,
+                               raw=True)
+    torch.cuda.synchronize()
+    qh, kh, al, be, la = pro.prologue(q, k, a, b, l)
+    al = np.ones((B, T, H)) if al is None else al
+    la = np.zeros((B, T, H)) if la is None else la
+    x = inputs.ChunkInputs(qh, kh, v, al, be, la, S0)
+    check_against_oracle(o.float().cpu(), S.cpu(), x, TOL["bf16"])
+
+
+@pytest.mark.parametrize("N,H,dk,dv,dt", [(3, 2, 128, 128, "bf16"), (2, 3, 64, 128, "f32"), (2, 2, 64, 64, "bf16")])
+def test_raw_step(qd, N, H, dk, dv, dt):
+    q, k, v, a, b, l = raw_inputs(1, N, H, dk, dv, dt, seed=N * H + dk)
+    q, k, v, a, b, l = q[0], k[0], v[0], a[0], b[0], l[0]
+    g = torch.Generator().manual_seed(5)
+    S = 0.05 * torch.randn(N, H, dv, dk, generator=g)
+    S_dev = S.clone().cuda()
+    o = qd.qdelta_step(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), l.cuda(), S_dev, raw=True)
+    torch.cuda.synchronize()
+    qh, kh, al, be, la = pro.prologue(q, k, a, b, l)
+    o_ref, S_ref = oracle.qdelta_step(qh, kh, v, al, be, la, S)
+    tol = TOL[dt]
+    eo = slice_err(o.float().cpu().numpy(), o_ref, axes=(2,))
+    es = slice_err(S_dev.cpu().numpy(), S_ref, axes=(2, 3))
+    print(f"  max rel err o={eo:.3e} S={es:.3e} (bar {tol:g})", flush=True)
+    assert eo <= tol and es <= tol
+
+
+def test_raw_chunk_unsupported_configurations(qd):
+    q, k, v, a, b, l = raw_inputs(1, 64, 1, 64, 64, "f32", seed=1)
+    with pytest.raises(qd.QDeltaError, match="unsupported"):
+        qd.qdelta_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), l.cuda(), C=64, raw=True)
+    q, k, v, a, b, l = raw_inputs(1, 64, 1, 64, 64, "bf16", seed=1)
+    with pytest.raises(qd.QDeltaError, match="unsupported"):
+        qd.qdelta_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), l.cuda(), C=16, raw=True)
