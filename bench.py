@@ -279,7 +279,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach_gbs / PEAK_HBM_GBS,
                      "traffic": traffic,
-                     "kernel": "chunk_fwd_pipe_kernel<128,64,true,true>",
+                     "kernel": "chunk_fwd_pipe_kernel<128,64,true,true,false>",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
                  "algorithmic_flops_per_launch": alg_flops},
