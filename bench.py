@@ -99,9 +99,35 @@ def cpu_baseline(torch, x, budget_s=10.0):
         rows += 1
         if total >= budget_s:
             break
+    host = {"cpu_model": _cpu_model(), "nproc": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+    # the tiny fp32 workload (B1 T256 H1 d64) on one thread, as a per-core reference
+    tw = inputs_mod().WORKLOADS["tiny_fp32"]
+    tx = inputs_mod().workload_inputs("tiny_fp32", seed=7)
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 0.5:
+        oracle.qdelta_fwd(tx.q, tx.k, tx.v, tx.alpha, tx.beta, tx.lam, None, nthreads=1)
+        reps += 1
+    one = reps * tw["B"] * tw["T"] / (time.perf_counter() - t0)
     return {"value": rows * T / total, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{rows} of {B} batch rows x {T} tokens x {H} heads of the same workload "
-                      f"({rows * T * H} token-heads, {total:.2f} s, fp64 recurrence, OpenMP over state rows)"}
+                      f"({rows * T * H} token-heads, {total:.2f} s, fp64 recurrence, OpenMP over state rows)",
+            "host": host, "one_thread_tiny_fp32_tokens_per_s": one}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def inputs_mod():
+    from recurrent_sequence_layers_amd import inputs
+    return inputs
 
 
 def main():
