@@ -9,6 +9,8 @@ Contents
   * ``qdelta_fwd``  -- the token-by-token gated recurrence (C, fp64, OpenMP).
   * ``qdelta_step`` -- one decode step of the same recurrence.
   * ``step_rw``     -- one step with explicit read and write directions.
+  * ``qdelta_bwd``  -- gradients of ``qdelta_fwd`` by the hand-derived adjoint of
+                       the recurrence, token by token in reverse (C, fp64).
   * ``chunk_form``  -- the chunkwise WY/UT-transform algebra in fp64 numpy
                        (module ``oracle.chunk_form``), used to pin that the
                        chunked algebra reproduces the recurrence.
@@ -42,6 +44,8 @@ def _load():
     lib.oracle_step_rw.restype = None
     lib.oracle_step_rw.argtypes = [_dp] * 5 + [ctypes.c_double, ctypes.c_double, _dp,
                                                 ctypes.c_int, ctypes.c_int]
+    lib.oracle_qdelta_bwd.restype = ctypes.c_int
+    lib.oracle_qdelta_bwd.argtypes = [_dp] * 16 + [ctypes.c_int] * 6
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -108,3 +112,25 @@ def step_rw(S, read, write, v, q, alpha: float, beta: float):
     _load().oracle_step_rw(_ptr(S), _ptr(read), _ptr(write), _ptr(v), _ptr(q),
                            float(alpha), float(beta), _ptr(o), dk, dv)
     return o, S
+
+
+def qdelta_bwd(q, k, v, alpha, beta, lam, S0, dO, dST=None, nthreads: int = 0):
+    """Gradients of the loss sum(o * dO) + sum(S_T * dST) with respect to every input
+    of ``qdelta_fwd``.  Shapes as ``qdelta_fwd``; dO [B,T,H,dv]; dST [B,H,dv,dk] or
+    None (zero).  Returns a dict of fp64 arrays dq, dk, dv, dalpha, dbeta, dlam, dS0
+    (dalpha and dlam are taken at alpha = 1 and lambda = 0 when those are None)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, beta, lam, S0 = _f64(alpha), _f64(beta), _f64(lam), _f64(S0)
+    dO, dST = _f64(dO), _f64(dST)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.empty((B, T, H, dk)), dk=np.empty((B, T, H, dk)), dv=np.empty((B, T, H, dv)),
+               dalpha=np.empty((B, T, H)), dbeta=np.empty((B, T, H)), dlam=np.empty((B, T, H)),
+               dS0=np.empty((B, H, dv, dk)))
+    rc = _load().oracle_qdelta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam),
+                                   _ptr(S0), _ptr(dO), _ptr(dST),
+                                   *[_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dlam", "dS0")],
+                                   B, T, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_qdelta_bwd failed (%d)" % rc)
+    return out

@@ -27,6 +27,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see build_oracle.py).
  */
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 #include <omp.h>
 
@@ -143,3 +144,172 @@ int oracle_qdelta_step(const double *q, const double *k, const double *v,
 }
 
 int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* ------------------------------------------------------------------ backward
+ * Gradients of the layer forward above, by reverse-mode differentiation of the
+ * recurrence one token at a time.  The pages state the forward only; this is the
+ * adjoint of each of its lines, derived by hand (there is nothing more to it than
+ * the chain rule).  For token t, with P = S_{t-1} the entry state:
+ *
+ *     forward                          adjoint (G = dLoss/dS_t, accumulated)
+ *     x   = k + lam q                  G    += do_t q^T            (o_t = S_t q)
+ *     pre = alpha P x                  dq   += S_t^T do_t
+ *     u   = v - pre                    gk    = G k
+ *     S_t = alpha P + beta u k^T       dbeta = u . gk ;  du = beta gk ;  dv = du
+ *     o_t = S_t q                      dk   += beta G^T u
+ *                                      dalpha = <G, P> - du . (P x)
+ *                                      dx    = -alpha P^T du
+ *                                      dk   += dx ; dq += lam dx ; dlam = q . dx
+ *                                      G     <- alpha G - alpha du x^T   (= dLoss/dS_{t-1})
+ *
+ * and dS0 is G after the first token.  The entry states are recomputed, not
+ * inverted: the forward keeps a copy of the state every SEG tokens, and the
+ * reverse sweep regenerates the SEG states of one stretch from its copy before
+ * walking back through it.  That changes memory use, not the arithmetic.
+ */
+#define ORACLE_BWD_SEG 64
+
+/* S <- alpha S + beta (v - alpha S x) k^T for one (dv x dk) state (the same step as
+ * advance_row, written for a whole state). */
+static void step_state(double *S, const double *x, const double *kt, const double *vt,
+                       double a, double be, int dk, int dv)
+{
+    int i;
+    for (i = 0; i < dv; ++i)
+        advance_row(S + (size_t)i * dk, x, kt, kt, vt[i], a, be, dk);
+}
+
+/* Backward of oracle_qdelta_fwd for the loss sum(o * dO) + sum(S_T * dST).
+ *   q, k, v, alpha, beta, lam, S0 : as oracle_qdelta_fwd (alpha/lam/S0 may be NULL)
+ *   dO  : [B][T][H][dv]   dST : [B][H][dv][dk] or NULL (zero)
+ *   outputs dq, dk [B][T][H][dk]; dv [B][T][H][dv]; dalpha, dbeta, dlam [B][T][H];
+ *   dS0 [B][H][dv][dk].  All required (dalpha and dlam are the gradients at the
+ *   values used, alpha = 1 and lambda = 0 when those inputs are NULL).
+ * One OpenMP unit per (b, h).  Returns 0, -1 on a bad argument, -2 if memory runs out. */
+int oracle_qdelta_bwd(const double *q, const double *k, const double *v,
+                      const double *alpha, const double *beta, const double *lam,
+                      const double *S0, const double *dO, const double *dST,
+                      double *dq, double *dk, double *dv, double *dalpha, double *dbeta,
+                      double *dlam, double *dS0,
+                      int B, int T, int H, int dkn, int dvn, int nthreads)
+{
+    long long unit, n_units;
+    int failed = 0;
+    if (B < 0 || T < 0 || H < 0 || dkn < 1 || dvn < 1 || dkn > 1024 || dvn > 1024) return -1;
+    if (!dq || !dk || !dv || !dalpha || !dbeta || !dlam || !dS0) return -1;
+    if ((long long)B * T * H > 0 && (!q || !k || !v || !beta || !dO)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    n_units = (long long)B * H;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (unit = 0; unit < n_units; ++unit) {
+        const int b = (int)(unit / H), h = (int)(unit % H);
+        const size_t ns = (size_t)dvn * dkn;
+        const int nseg = (T + ORACLE_BWD_SEG - 1) / ORACLE_BWD_SEG;
+        double *ckpt = malloc(sizeof(double) * ns * (size_t)(nseg > 0 ? nseg : 1));
+        double *states = malloc(sizeof(double) * ns * (ORACLE_BWD_SEG + 1));
+        double *G = malloc(sizeof(double) * ns);
+        double x[1024], gk[1024], u[1024], du[1024], px[1024], dx[1024];
+        double *S;
+        int t, i, j, sg;
+        if (!ckpt || !states || !G) {
+            free(ckpt); free(states); free(G);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        /* forward, keeping the state at the start of every stretch */
+        S = states;
+        if (S0) memcpy(S, S0 + unit * ns, sizeof(double) * ns);
+        else memset(S, 0, sizeof(double) * ns);
+        for (t = 0; t < T; ++t) {
+            size_t tok = ((size_t)b * T + t) * H + h;
+            double la = lam ? lam[tok] : 0.0;
+            if (t % ORACLE_BWD_SEG == 0) memcpy(ckpt + (size_t)(t / ORACLE_BWD_SEG) * ns, S, sizeof(double) * ns);
+            for (j = 0; j < dkn; ++j) x[j] = k[tok * dkn + j] + la * q[tok * dkn + j];
+            step_state(S, x, k + tok * dkn, v + tok * dvn, alpha ? alpha[tok] : 1.0, beta[tok], dkn, dvn);
+        }
+        /* reverse sweep */
+        if (dST) memcpy(G, dST + unit * ns, sizeof(double) * ns);
+        else memset(G, 0, sizeof(double) * ns);
+        for (sg = nseg - 1; sg >= 0; --sg) {
+            const int t0 = sg * ORACLE_BWD_SEG;
+            const int t1 = (t0 + ORACLE_BWD_SEG < T) ? t0 + ORACLE_BWD_SEG : T;
+            memcpy(states, ckpt + (size_t)sg * ns, sizeof(double) * ns);
+            for (t = t0; t < t1; ++t) {   /* states[t - t0] = S_{t-1} (entry state of token t) */
+                size_t tok = ((size_t)b * T + t) * H + h;
+                double la = lam ? lam[tok] : 0.0;
+                double *nxt = states + (size_t)(t - t0 + 1) * ns;
+                memcpy(nxt, states + (size_t)(t - t0) * ns, sizeof(double) * ns);
+                for (j = 0; j < dkn; ++j) x[j] = k[tok * dkn + j] + la * q[tok * dkn + j];
+                step_state(nxt, x, k + tok * dkn, v + tok * dvn, alpha ? alpha[tok] : 1.0, beta[tok], dkn, dvn);
+            }
+            for (t = t1 - 1; t >= t0; --t) {
+                size_t tok = ((size_t)b * T + t) * H + h;
+                const double *qt = q + tok * dkn, *kt = k + tok * dkn, *vt = v + tok * dvn;
+                const double *dot = dO + tok * dvn;
+                const double *P = states + (size_t)(t - t0) * ns;       /* S_{t-1} */
+                const double *St = states + (size_t)(t - t0 + 1) * ns;  /* S_t     */
+                double a = alpha ? alpha[tok] : 1.0, be = beta[tok], la = lam ? lam[tok] : 0.0;
+                double acc, da, db, dl;
+                double *dqt = dq + tok * dkn, *dkt = dk + tok * dkn, *dvt = dv + tok * dvn;
+                for (j = 0; j < dkn; ++j) x[j] = kt[j] + la * qt[j];
+                /* o_t = S_t q */
+                for (i = 0; i < dvn; ++i)
+                    for (j = 0; j < dkn; ++j) G[(size_t)i * dkn + j] += dot[i] * qt[j];
+                for (j = 0; j < dkn; ++j) {
+                    acc = 0.0;
+                    for (i = 0; i < dvn; ++i) acc += St[(size_t)i * dkn + j] * dot[i];
+                    dqt[j] = acc;
+                }
+                /* S_t = alpha P + beta u k^T,  u = v - alpha P x */
+                for (i = 0; i < dvn; ++i) {
+                    double s1 = 0.0, s2 = 0.0;
+                    for (j = 0; j < dkn; ++j) {
+                        s1 += G[(size_t)i * dkn + j] * kt[j];
+                        s2 += P[(size_t)i * dkn + j] * x[j];
+                    }
+                    gk[i] = s1;
+                    px[i] = s2;
+                    u[i] = vt[i] - a * s2;
+                }
+                db = 0.0;
+                for (i = 0; i < dvn; ++i) db += u[i] * gk[i];
+                for (i = 0; i < dvn; ++i) {
+                    du[i] = be * gk[i];
+                    dvt[i] = du[i];
+                }
+                for (j = 0; j < dkn; ++j) {
+                    acc = 0.0;
+                    for (i = 0; i < dvn; ++i) acc += G[(size_t)i * dkn + j] * u[i];
+                    dkt[j] = be * acc;
+                }
+                da = 0.0;
+                for (i = 0; i < dvn; ++i)
+                    for (j = 0; j < dkn; ++j) da += G[(size_t)i * dkn + j] * P[(size_t)i * dkn + j];
+                for (i = 0; i < dvn; ++i) da -= du[i] * px[i];
+                for (j = 0; j < dkn; ++j) {
+                    acc = 0.0;
+                    for (i = 0; i < dvn; ++i) acc += P[(size_t)i * dkn + j] * du[i];
+                    dx[j] = -a * acc;
+                }
+                dl = 0.0;
+                for (j = 0; j < dkn; ++j) {
+                    dkt[j] += dx[j];
+                    dqt[j] += la * dx[j];
+                    dl += qt[j] * dx[j];
+                }
+                dalpha[tok] = da;
+                dbeta[tok] = db;
+                dlam[tok] = dl;
+                /* dLoss/dS_{t-1} */
+                for (i = 0; i < dvn; ++i)
+                    for (j = 0; j < dkn; ++j)
+                        G[(size_t)i * dkn + j] = a * G[(size_t)i * dkn + j] - a * du[i] * x[j];
+            }
+        }
+        memcpy(dS0 + unit * ns, G, sizeof(double) * ns);
+        free(ckpt); free(states); free(G);
+    }
+    return failed ? -2 : 0;
+}
