@@ -231,3 +231,122 @@ def test_segmented_schedule_matches_recurrence(T, P, dk, dv):
     o_s, S_s = segmented_fwd(q, k, v, alpha, beta, lam, S0, P)
     np.testing.assert_allclose(o_s, o_r, atol=1e-11)
     np.testing.assert_allclose(S_s, S_r, atol=1e-11)
+
+
+# ---------------------------------------------------------------- backward
+def kernel_form_bwd(q, k, v, alpha, beta, lam, S0, dO, dST, C):
+    """The three passes of the chunked backward, per (batch, head), in the kernels'
+    transposed state convention (S^T is d_k x d_v).  Within a chunk, with
+    g = cumsum log alpha, G[t,j] = exp(g_t - g_j), D_g = diag(exp g),
+    D_r = diag(exp(g_last - g)), A = G o lower(Q K^T), N = G o strict(X K^T),
+    T_g = (I + diag(beta) N)^-1, M1 = T_g diag(beta), the forward is
+        Y = X S^T, R = V - D_g Y, Z = M1 R, O = D_g Q S^T + A Z,
+        S'^T = g_C S^T + K^T D_r Z.
+    1. forward over chunks, keeping every chunk's entry state S^T;
+    2. reverse over chunks with the exit-state gradient dS'^T:
+        dZ = A^T dO + D_r K dS'^T,  dR = M1^T dZ  (= dV),
+        dS^T = g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR;
+    3. every chunk on its own, from its S^T and dS'^T:
+        P = T_g^T dZ, U = R - N Z (the per-token errors), dbeta = rowdot(P, U),
+        dA = lower(dO Z^T), dN-part dLg = -strict(P Z^T) (gradient of diag(beta) N),
+        W_o = dO S, W_r = dR S, W_z = Z dS',
+        dX = -D_g W_r + diag(beta) (dLg o G) K,
+        dQ = (dA o G) K + D_g W_o + diag(lambda) dX,
+        dK = (dA o G)^T Q + (dLg o G)^T diag(beta) X + D_r W_z + dX,
+        dlambda = rowdot(Q, dX),
+        dg = rowsum(dA o A) - colsum(dA o A) + rowsum(dLg o Lg) - colsum(dLg o Lg)
+             + rowdot(D_g W_o, Q) - rowdot(D_g W_r, X) - rowdot(D_r W_z, K)
+             + e_last (g_C <dS', S> + sum_j rowdot(D_r W_z, K)_j),
+        dalpha = reverse-cumsum(dg) / alpha."""
+    B, Tn, H, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.zeros((B, Tn, H, dk)), dk=np.zeros((B, Tn, H, dk)), dv=np.zeros((B, Tn, H, dv)),
+               dalpha=np.zeros((B, Tn, H)), dbeta=np.zeros((B, Tn, H)), dlam=np.zeros((B, Tn, H)),
+               dS0=np.zeros((B, H, dv, dk)))
+    starts = list(range(0, Tn, C))
+
+    def chunk(b, h, t0):
+        n = min(C, Tn - t0)
+        sl = slice(t0, t0 + n)
+        Q, K, V, dOc = q[b, sl, h], k[b, sl, h], v[b, sl, h], dO[b, sl, h]
+        be, la, al = beta[b, sl, h], lam[b, sl, h], alpha[b, sl, h]
+        g = np.cumsum(np.log(al))
+        X = K + la[:, None] * Q
+        G = np.exp(g[:, None] - g[None, :])
+        A = G * np.tril(Q @ K.T)
+        N = G * np.tril(X @ K.T, -1)
+        Tg = np.linalg.inv(np.eye(n) + be[:, None] * N)
+        return dict(Q=Q, K=K, V=V, dO=dOc, be=be, la=la, al=al, g=g, X=X, G=G, A=A, N=N, Tg=Tg,
+                    M1=Tg * be[None, :], Dg=np.exp(g), Dr=np.exp(g[-1] - g), gC=np.exp(g[-1]), sl=sl)
+
+    for b in range(B):
+        for h in range(H):
+            # pass 1: entry states
+            ST = np.zeros((dk, dv)) if S0 is None else S0[b, h].T.copy()
+            Hs = []
+            for t0 in starts:
+                c = chunk(b, h, t0)
+                Hs.append(ST.copy())
+                Z = c["M1"] @ (c["V"] - c["Dg"][:, None] * (c["X"] @ ST))
+                ST = c["gC"] * ST + c["K"].T @ (c["Dr"][:, None] * Z)
+            # pass 2: exit-state gradients, dV, dS0
+            dST_ = np.zeros((dk, dv)) if dST is None else dST[b, h].T.copy()
+            dHs = [None] * len(starts)
+            for i in reversed(range(len(starts))):
+                c = chunk(b, h, starts[i])
+                dHs[i] = dST_.copy()
+                dZ = c["A"].T @ c["dO"] + c["Dr"][:, None] * (c["K"] @ dST_)
+                dR = c["M1"].T @ dZ
+                out["dv"][b, c["sl"], h] = dR
+                dST_ = (c["gC"] * dST_ + c["Q"].T @ (c["Dg"][:, None] * (c["dO"] - c["la"][:, None] * dR))
+                        - c["K"].T @ (c["Dg"][:, None] * dR))
+            out["dS0"][b, h] = dST_.T
+            # pass 3: every chunk on its own
+            for i, t0 in enumerate(starts):
+                c = chunk(b, h, t0)
+                ST, dSpT = Hs[i], dHs[i]
+                S, dSp = ST.T, dSpT.T
+                Q, K, X, G, Dg, Dr, be, la = c["Q"], c["K"], c["X"], c["G"], c["Dg"], c["Dr"], c["be"], c["la"]
+                R = c["V"] - Dg[:, None] * (X @ ST)
+                Z = c["M1"] @ R
+                dZ = c["A"].T @ c["dO"] + Dr[:, None] * (K @ dSpT)
+                P = c["Tg"].T @ dZ
+                dR = be[:, None] * P
+                U = R - c["N"] @ Z
+                dA = np.tril(c["dO"] @ Z.T)
+                dLg = -np.tril(P @ Z.T, -1)
+                Lg = be[:, None] * c["N"]
+                Wo, Wr, Wz = c["dO"] @ S, dR @ S, Z @ dSp
+                dX = -Dg[:, None] * Wr + be[:, None] * ((dLg * G) @ K)
+                dQ = (dA * G) @ K + Dg[:, None] * Wo + la[:, None] * dX
+                dK = (dA * G).T @ Q + (dLg * G).T @ (be[:, None] * X) + Dr[:, None] * Wz + dX
+                wz = np.einsum("tj,tj->t", Dr[:, None] * Wz, K)
+                dg = ((dA * c["A"]).sum(1) - (dA * c["A"]).sum(0) + (dLg * Lg).sum(1) - (dLg * Lg).sum(0)
+                      + np.einsum("tj,tj->t", Dg[:, None] * Wo, Q) - np.einsum("tj,tj->t", Dg[:, None] * Wr, X) - wz)
+                dg[-1] += c["gC"] * (dSp * S).sum() + wz.sum()
+                out["dq"][b, c["sl"], h] = dQ
+                out["dk"][b, c["sl"], h] = dK
+                out["dbeta"][b, c["sl"], h] = np.einsum("tj,tj->t", P, U)
+                out["dlam"][b, c["sl"], h] = np.einsum("tj,tj->t", Q, dX)
+                out["dalpha"][b, c["sl"], h] = dg[::-1].cumsum()[::-1] / c["al"]
+    return out
+
+
+@pytest.mark.parametrize("T,C,dk,dv", [(64, 16, 8, 6), (150, 32, 8, 5), (97, 64, 6, 8), (33, 16, 4, 4)])
+def test_chunked_backward_matches_oracle(T, C, dk, dv):
+    r = np.random.default_rng(T + C)
+    B, H = 2, 2
+    q = r.standard_normal((B, T, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((B, T, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, dv))
+    alpha = np.exp(-np.log1p(np.exp(r.standard_normal((B, T, H)) - 2.0)))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H))))
+    lam = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H))))
+    S0 = 0.3 * r.standard_normal((B, H, dv, dk))
+    dO = r.standard_normal((B, T, H, dv))
+    dST = r.standard_normal((B, H, dv, dk))
+    got = kernel_form_bwd(q, k, v, alpha, beta, lam, S0, dO, dST, C)
+    ref = oracle.qdelta_bwd(q, k, v, alpha, beta, lam, S0, dO, dST)
+    for n in ref:
+        err = np.abs(got[n] - ref[n]).max() / np.abs(ref[n]).max()
+        assert err < 1e-10, (n, err)
