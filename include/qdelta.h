@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define QDELTA_ABI_VERSION 2
+#define QDELTA_ABI_VERSION 3
 
 typedef enum qd_status {
     QD_OK = 0,
@@ -141,6 +141,44 @@ int qdelta_step_raw(const void *q, const void *k, const void *v,
                     const float *alpha_logit, const float *beta_logit,
                     const float *lambda_logit, float *S, void *o, int N, int H,
                     int d_k, int d_v, int dtype, void *stream);
+
+/* Bytes of device workspace qdelta_chunk_bwd needs: the entry state of every chunk and
+ * the gradient with respect to every chunk's exit state, 2*B*H*ceil(T/C)*d_v*d_k*4
+ * bytes (0 when B*H*T == 0 or the sizes are unsupported). */
+size_t qdelta_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
+                                        int dtype);
+
+/*
+ * Layer backward: the gradients of the scalar sum(o * d_o) + sum(S_T * dS_T) with
+ * respect to every input of qdelta_chunk_fwd, o and S_T being that call's results for
+ * the same inputs.  The pages give the forward only (Q-Delta reading notes §2.4, the
+ * gated update, and §2.6, the chunkwise form); this is its reverse-mode derivative,
+ * evaluated in the chunk form in three passes: the forward again, keeping each chunk's
+ * entry state; a reverse scan over the chunks for the state gradients and dv; and a
+ * parallel pass over the chunks for dq, dk, dalpha, dbeta, dlambda.  C only changes
+ * rounding.
+ *
+ *   q, k, v, alpha, beta, lambda, S0, C, dtype   as for qdelta_chunk_fwd.
+ *   d_o       [B][T][H][d_v], dtype elements; required when B*T*H > 0.
+ *   dS_T      [B][H][d_v][d_k] fp32, or NULL (zero).
+ *   dq, dk    [B][T][H][d_k], dv [B][T][H][d_v], dtype elements; required.
+ *   dbeta     [B][T][H] fp32; required.
+ *   dalpha    [B][T][H] fp32 or NULL (not written); must be NULL when alpha is NULL.
+ *   dlambda   [B][T][H] fp32 or NULL (not written); must be NULL when lambda is NULL.
+ *   dS0       [B][H][d_v][d_k] fp32 or NULL (not written).
+ *   workspace at least qdelta_chunk_bwd_workspace_bytes, 16-byte aligned; its contents
+ *             are overwritten and not needed afterwards.
+ *   Supported: d_k, d_v in {64, 128}; C in {16, 32, 64} for bf16 and {16, 32} for fp32.
+ *   Every output and the workspace must be disjoint from every input and from one
+ *   another (QD_ERR_INVALID_ARG otherwise).
+ */
+int qdelta_chunk_bwd(const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, const float *lambda,
+                     const float *S0, const void *d_o, const float *dS_T,
+                     void *dq, void *dk, void *dv, float *dalpha, float *dbeta,
+                     float *dlambda, float *dS0,
+                     int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                     void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,8 @@ fallback path.
     qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C=64, o=None, S_T=None)
         -> (o, S_T)
     qdelta_step(q, k, v, alpha, beta, lam, S, o=None) -> o        (S updated in place)
+    qdelta_chunk_bwd(q, k, v, alpha, beta, lam, S0, d_o, dS_T=None, C=64)
+        -> dict(dq, dk, dv, dalpha, dbeta, dlam, dS0)
 """
 import ctypes
 import os
@@ -49,6 +51,10 @@ def load_library():
     lib.qdelta_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
     lib.qdelta_step_raw.restype = i
     lib.qdelta_step_raw.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
+    lib.qdelta_chunk_bwd_workspace_bytes.restype = sz
+    lib.qdelta_chunk_bwd_workspace_bytes.argtypes = [i] * 7
+    lib.qdelta_chunk_bwd.restype = i
+    lib.qdelta_chunk_bwd.argtypes = [vp] * 16 + [i] * 7 + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -137,6 +143,58 @@ def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_
             _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
     _raise(rc, "qdelta_chunk_fwd_raw" if raw else "qdelta_chunk_fwd")
     return o, S_T
+
+
+def qdelta_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:
+    return int(load_library().qdelta_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, C, _dtype_code(dtype)))
+
+
+def qdelta_chunk_bwd(q, k, v, alpha, beta, lam, S0, d_o, dS_T=None, C: int = 64, want_dS0: bool = True,
+                     out=None, workspace=None, stream=None):
+    """Layer backward: gradients of sum(o * d_o) + sum(S_T * dS_T) for the forward of
+    ``qdelta_chunk_fwd`` on the same inputs.  d_o [B,T,H,d_v] in the input dtype; dS_T
+    [B,H,d_v,d_k] fp32 or None.  Returns a dict with dq, dk (like q), dv (like v), dbeta,
+    and dalpha / dlam (fp32 [B,T,H], None when alpha / lam are None) and dS0 (fp32, None
+    unless want_dS0).  ``out`` may supply any of those tensors; ``workspace`` a device
+    buffer of at least qdelta_chunk_bwd_workspace_bytes(...) bytes (allocated when None)."""
+    import torch
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+    _check(d_o, "d_o", dt, (B, T, H, dv))
+    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+        _check(g, name, torch.float32, (B, T, H))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    _check(dS_T, "dS_T", torch.float32, (B, H, dv, dk))
+    out = dict(out or {})
+    shapes = dict(dq=((B, T, H, dk), dt), dk=((B, T, H, dk), dt), dv=((B, T, H, dv), dt),
+                  dbeta=((B, T, H), torch.float32), dalpha=((B, T, H), torch.float32),
+                  dlam=((B, T, H), torch.float32), dS0=((B, H, dv, dk), torch.float32))
+    wanted = dict(dq=True, dk=True, dv=True, dbeta=True, dalpha=alpha is not None, dlam=lam is not None,
+                  dS0=want_dS0)
+    for name, (shape, dtype) in shapes.items():
+        if not wanted[name]:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+        _check(out[name], name, dtype, shape)
+    code = _dtype_code(dt)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = lib.qdelta_chunk_bwd_workspace_bytes(B, T, H, dk, dv, C, code)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    rc = lib.qdelta_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0), _ptr(d_o),
+                              _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                              _ptr(out["dbeta"]), _ptr(out["dlam"]), _ptr(out["dS0"]), B, T, H, dk, dv, int(C), code,
+                              ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_chunk_bwd")
+    return out
 
 
 def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None, raw: bool = False):

@@ -40,6 +40,61 @@ size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, i
     return qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
 }
 
+size_t qdelta_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
+    if (B < 0 || T < 0 || H < 0 || !qd::chunk_bwd_supported(dtype, d_k, d_v, C)) return 0;
+    return qd::chunk_bwd_workspace(B, T, H, d_k, d_v, C);
+}
+
+int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                     const float *lambda, const float *S0, const void *d_o, const float *dS_T, void *dq, void *dk,
+                     void *dv, float *dalpha, float *dbeta, float *dlambda, float *dS0, int B, int T, int H,
+                     int d_k, int d_v, int C, int dtype, void *workspace, size_t ws_bytes, void *stream) {
+    if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::chunk_bwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
+    const long long bh = static_cast<long long>(B) * H;
+    if (bh == 0) return QD_OK;
+    const long long nc = (static_cast<long long>(T) + C - 1) / C;
+    if (bh * (d_v / 64) > 0x7fffffffLL || bh * nc > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    if ((alpha == nullptr && dalpha != nullptr) || (lambda == nullptr && dlambda != nullptr)) return QD_ERR_INVALID_ARG;
+    const long long ntok = bh * T;
+    if (ntok > 0 && (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta)) return QD_ERR_INVALID_ARG;
+    const size_t need = qd::chunk_bwd_workspace(B, T, H, d_k, d_v, C);
+    if (ws_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return QD_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv) || !aligned16(S0) || !aligned16(dS_T) || !aligned16(dS0))
+        return QD_ERR_INVALID_ARG;
+    // every output and the workspace must be disjoint from every input and from one another
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, v_bytes = static_cast<size_t>(ntok) * d_v * es;
+    const size_t g_bytes = static_cast<size_t>(ntok) * 4, st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
+    const struct { const void *p; size_t n; } ins[] = {
+        {q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {alpha, g_bytes}, {beta, g_bytes}, {lambda, g_bytes},
+        {S0, st_bytes}, {d_o, v_bytes}, {dS_T, st_bytes}};
+    const struct { const void *p; size_t n; } outs[] = {
+        {dq, qk_bytes}, {dk, qk_bytes}, {dv, v_bytes}, {dalpha, g_bytes}, {dbeta, g_bytes}, {dlambda, g_bytes},
+        {dS0, st_bytes}, {workspace, need}};
+    for (const auto &o : outs) {
+        for (const auto &i : ins)
+            if (overlaps(o.p, o.n, i.p, i.n)) return QD_ERR_INVALID_ARG;
+        for (const auto &o2 : outs)
+            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return QD_ERR_INVALID_ARG;
+    }
+
+    qd::BwdArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta; a.lam = lambda;
+    a.S0 = S0; a.dO = d_o; a.dST = dS_T;
+    a.g_q = dq; a.g_k = dk; a.g_v = dv;
+    a.g_alpha = dalpha; a.g_beta = dbeta; a.g_lam = dlambda; a.g_S0 = dS0;
+    float *ws = static_cast<float *>(workspace);
+    a.Hs = ws;
+    a.dHs = ws ? ws + need / (2 * sizeof(float)) : nullptr;
+    a.B = B; a.T = T; a.H = H; a.dv = d_v;
+    a.n_dvt = d_v / 64;
+    const hipError_t err = qd::launch_chunk_bwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

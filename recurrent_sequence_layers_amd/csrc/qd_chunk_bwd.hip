@@ -1,0 +1,785 @@
+// Layer backward for gfx950: gradients of sum(o dO) + sum(S_T dST) with respect to
+// q, k, v, alpha, beta, lambda and S0.
+//
+// The pages define the forward only (Q-Delta reading notes §2.4, the gated update, and
+// §2.6, its chunkwise WY/UT form); the backward below is the reverse-mode derivative of
+// that chunk form.  Per chunk, with g = cumsum log alpha, G[t][j] = exp(g_t - g_j),
+// D_g = diag(exp g), D_r = diag(exp(g_last - g)), X = K + diag(lambda) Q,
+// A = G o lower(Q K^T), N = G o strict(X K^T), T_g = (I + diag(beta) N)^-1, the forward is
+//     Y = X S^T,  R = V - D_g Y,  Z = T_g diag(beta) R,  O = D_g Q S^T + A Z,
+//     S'^T = g_C S^T + K^T D_r Z.
+// Three passes:
+//   1. the forward over the chunks, keeping every chunk's entry state S^T (generic
+//      forward kernel, no output);
+//   2. chunk_bwd_scan_kernel, the reverse scan: one workgroup per (batch, head, 64 value
+//      columns) walks the chunks last to first holding the exit-state gradient dS'^T,
+//      stores it per chunk, and writes dV:
+//        dZ = A^T dO + D_r K dS'^T,  dV = dR = diag(beta) T_g^T dZ,
+//        dS^T = g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR;
+//      the last dS^T is dS0;
+//   3. chunk_bwd_grad_kernel: one workgroup per chunk, independent of the others, from
+//      the chunk's S and dS' recomputes R, Z, dZ, P = T_g^T dZ and the token errors
+//      U = R - N Z, and forms dQ, dK, dbeta, dlambda and dalpha:
+//        dA = lower(dO Z^T), dL = -strict(P Z^T) (the gradient of diag(beta) N),
+//        W_o = dO S, W_p = P S, W_z = Z dS',
+//        Mq = G o dA + diag(lambda) dLb,  dLb = diag(beta) (G o dL),
+//        dX = dLb K - D_g diag(beta) W_p,
+//        dQ = Mq K + D_g (W_o - diag(lambda beta) W_p),
+//        dK = Mq^T Q + dLb^T K + D_r W_z + dX,
+//        dbeta = rowdot(P, U), dlambda = rowdot(Q, dX),
+//        dg = rowsum(dA o A) - colsum(dA o A) + rowsum(dL o beta N) - colsum(dL o beta N)
+//             + rowdot(D_g W_o, Q) - rowdot(D_g diag(beta) W_p, X) - rowdot(D_r W_z, K)
+//             + [last row] (g_C <dS', S> + sum of rowdot(D_r W_z, K)),
+//           where the four pair sums are taken as rowdot(Q, Mq K) + rowdot(K, dLb K)
+//           - rowdot(K, Mq^T Q + dLb^T K) (the same sums regrouped; fp32 accumulators and
+//           exact q, k instead of rounded A and N),
+//        dalpha = (reverse cumulative sum of dg over the chunk) / alpha.
+// Both kernels use the element policy of the inputs (bf16 or fp32 MFMA operands, fp32
+// accumulation) and the same Gram and triangular-inverse steps as the forward.  A short
+// last chunk is padded with alpha = 1, beta = 0 and zero q, k, v, dO rows, which adds
+// nothing to any gradient.
+#include "qd_chunk_common.h"
+#include "qd_device.h"
+#include "qd_internal.h"
+
+namespace qd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kDVT = 64;  // value columns per tile
+
+// ------------------------------------------------------------------ pass 2: reverse scan
+template <class P, int DK, int CH>
+struct ScanLayout {
+    static constexpr int PAD = 16 / P::kBytes;
+    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
+    static constexpr int NQ = CH * PK, NV = CH * PV, NCC = CH * PC;
+    static constexpr int NT = (NV > NCC) ? NV : NCC;  // T buffer doubles as dV staging
+    static constexpr int oQ = 0, oK = oQ + NQ, oD = oK + NQ, oL = oD + NV, oT = oL + NCC, oA = oT + NT;
+    static constexpr int nR = oA + NCC;
+    static constexpr int bytes = nR * P::kBytes + 5 * CH * 4;
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
+};
+
+template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdArgs args) {
+    using R = typename P::R;
+    using F = typename P::F;
+    using Lay = ScanLayout<P, DK, CH>;
+    constexpr int NKT = DK / 16, NCT = CH / 16;
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
+    constexpr int EPV = 16 / P::kBytes;
+    constexpr int VPRQ = DK / EPV, VPRV = kDVT / EPV;
+    constexpr int NVQ = (CH * VPRQ + kThreads - 1) / kThreads;
+    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
+    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
+    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;   // dO tile
+    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;   // L, later M1 = T_g diag(beta)
+    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;   // T, later dV staging
+    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+    float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
+    float *const egs = gs + CH;
+    float *const egls = egs + CH;
+    float *const bes = egls + CH;
+    float *const lams = bes + CH;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    const int nblk = gridDim.x;
+    int logical = blockIdx.x;
+    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int dvt = logical % args.n_dvt;
+    const int bh = logical / args.n_dvt;
+    const int b = bh / args.H, h = bh % args.H;
+    const int T = args.T, H = args.H, dv = args.dv;
+    const int dv0 = dvt * kDVT;
+
+    const R *__restrict__ gq = static_cast<const R *>(args.q);
+    const R *__restrict__ gk = static_cast<const R *>(args.k);
+    const R *__restrict__ gdo = static_cast<const R *>(args.dO);
+    R *__restrict__ gdv = static_cast<R *>(args.g_v);
+    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+    // dS'^T tiles: rows d_k = 16t + 4g + i, column = this wave's value column
+    f32x4 sT[NKT];
+    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * wave + r16) * DK;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+        sT[t] = args.dST ? *reinterpret_cast<const f32x4 *>(args.dST + srow + 16 * t + 4 * g4) : zero4();
+
+    uint4 rq[NVQ], rk[NVQ], rd[NVV];
+    float ra = 1.f, rb = 0.f, rl = 0.f;
+    auto gload = [&](int n) {
+        const int t0 = n * CH;
+        const int last = min(CH, T - t0) - 1;
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                const int c = min(vi / VPRQ, last), cv = vi % VPRQ;
+                const size_t off = tok(t0 + c) * DK + cv * EPV;
+                rq[j] = *reinterpret_cast<const uint4 *>(gq + off);
+                rk[j] = *reinterpret_cast<const uint4 *>(gk + off);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int c = min(vi / VPRV, last), cv = vi % VPRV;
+                rd[j] = *reinterpret_cast<const uint4 *>(gdo + tok(t0 + c) * dv + dv0 + cv * EPV);
+            }
+        }
+        const size_t gi = tok(t0 + min(tid & (kWave - 1), last));
+        if constexpr (HAS_A) ra = args.alpha[gi];
+        rb = args.beta[gi];
+        if constexpr (HAS_L) rl = args.lam[gi];
+    };
+    auto lstore = [&](int clen) {
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                const int c = vi / VPRQ, cv = vi % VPRQ;
+                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = keep_if(c < clen, rq[j]);
+                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = keep_if(c < clen, rk[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int c = vi / VPRV, cv = vi % VPRV;
+                *reinterpret_cast<uint4 *>(Ds + c * PV + cv * EPV) = keep_if(c < clen, rd[j]);
+            }
+        }
+        if (wave == 0) {
+            const bool ok = lane < clen;
+            float x = (HAS_A && ok) ? __logf(ra) : 0.f;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float glast = __shfl(x, CH - 1);
+            if (lane < CH) {
+                gs[lane] = x;
+                egs[lane] = __expf(x);
+                egls[lane] = __expf(glast - x);
+                bes[lane] = ok ? rb : 0.f;
+                lams[lane] = ok ? rl : 0.f;
+            }
+        }
+    };
+
+    const int NC = (T + CH - 1) / CH;
+    if (NC > 0) gload(NC - 1);
+    for (int n = NC - 1; n >= 0; --n) {
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+        {   // gradient with respect to chunk n's exit state
+            float *dh = args.dHs + (static_cast<size_t>(bh) * NC + n) * dv * DK +
+                        static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(dh + 16 * t) = sT[t];
+        }
+        lstore(clen);
+        if (n > 0) gload(n - 1);
+        __syncthreads();
+
+        gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, nullptr);
+        __syncthreads();
+        unit_lower_inverse<P, CH, PC>(Ls, Ts);
+
+        // M1 = (H o T) diag(beta) = T_g diag(beta), in place of L (lower block triangle)
+        for (int idx = tid; idx < NPAIR * 64; idx += kThreads) {
+            int i, j;
+            tri_pair(idx >> 6, i, j);
+            const int r = 16 * i + ((idx >> 2) & 15);
+            const int c0 = 16 * j + 4 * (idx & 3);
+            const F tf = P::ld4(Ts + r * PC + c0);
+            const f32x4 bc = lds_f32x4(bes + c0);
+            const f32x4 gc = lds_f32x4(gs + c0);
+            const float gr = gs[r];
+            f32x4 m1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
+                m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+            }
+            P::st4(Ls + r * PC + c0, m1);
+        }
+        __syncthreads();
+
+        // ---- this wave's 16 value columns
+        F sTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
+        // dZ = D_r K dS'^T + A^T dO   (A^T upper: blocks s >= mt)
+        f32x4 dZ[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            f32x4 kd = zero4();
+#pragma unroll
+            for (int t = 0; t < NKT; t += 2)
+                kd = P::mma2(kd, frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16), sTf[t],
+                             sTf[t + 1]);
+            dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+#pragma unroll
+            for (int s = mt; s < NCT; s += 2) {
+                if (s + 1 < NCT)
+                    dZ[mt] = P::mma2(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(As, PC, 16 * s + 16, 16 * mt),
+                                     frag_b<P>(Ds, PV, 16 * s, 16 * wave), frag_b<P>(Ds, PV, 16 * s + 16, 16 * wave));
+                else
+                    dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
+            }
+        }
+        // dR = M1^T dZ
+        F dZf[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) dZf[mt] = P::cvt(dZ[mt]);
+        f32x4 dR[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            dR[mt] = zero4();
+#pragma unroll
+            for (int s = mt; s < NCT; s += 2) {
+                if (s + 1 < NCT)
+                    dR[mt] = P::mma2(dR[mt], frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ls, PC, 16 * s + 16, 16 * mt),
+                                     dZf[s], dZf[s + 1]);
+                else
+                    dR[mt] = P::mma1(dR[mt], frag_b<P>(Ls, PC, 16 * s, 16 * mt), dZf[s]);
+            }
+        }
+        // dS^T <- g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR
+        F Ef[NCT], Ff[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            const f32x4 dof = P::f32(frag_b<P>(Ds, PV, 16 * mt, 16 * wave));
+            const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4);
+            f32x4 e = HAS_L ? dof - lds_f32x4(lams + 16 * mt + 4 * g4) * dR[mt] : dof;
+            f32x4 f = -dR[mt];
+            if constexpr (HAS_A) {
+                e = eg * e;
+                f = eg * f;
+            }
+            Ef[mt] = P::cvt(e);
+            Ff[mt] = P::cvt(f);
+        }
+        const float dlast = HAS_A ? egs[CH - 1] : 1.f;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            f32x4 acc = sT[t] * dlast;
+#pragma unroll
+            for (int s = 0; s < NCT; s += 2) {
+                if (s + 1 < NCT) {
+                    acc = P::mma2(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), frag_b<P>(Qs, PK, 16 * s + 16, 16 * t), Ef[s],
+                                  Ef[s + 1]);
+                    acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t), Ff[s],
+                                  Ff[s + 1]);
+                } else {
+                    acc = P::mma1(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), Ef[s]);
+                    acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Ff[s]);
+                }
+            }
+            sT[t] = acc;
+        }
+        // dV: stage (the T buffer is dead after the M1 build), then coalesced row stores
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ts[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(dR[mt][e]);
+        }
+        __syncthreads();
+        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+            const int c = vi / VPRV, cv = vi % VPRV;
+            if (c < clen)
+                *reinterpret_cast<uint4 *>(gdv + tok(t0 + c) * dv + dv0 + cv * EPV) =
+                    *reinterpret_cast<const uint4 *>(Ts + c * PV + cv * EPV);
+        }
+        // the next chunk's LDS writes (q, k, dO, gates) do not touch the staging buffer,
+        // and the T writes that reuse it are two barriers away
+    }
+    if (args.g_S0) {
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.g_S0 + srow + 16 * t + 4 * g4) = sT[t];
+    }
+}
+
+// ------------------------------------------------------------------ pass 3: per-chunk gradients
+template <class P, int DK, int CH>
+struct GradLayout {
+    static constexpr int PAD = 16 / P::kBytes;
+    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
+    static constexpr int NQ = CH * PK, NV = CH * PV, NS = kDVT * PK, NCC = CH * PC;
+    static_assert(NS >= NQ, "the S tiles double as the dQ and dK staging");
+    static constexpr int oQ = 0, oK = oQ + NQ, oV = oK + NQ, oD = oV + NV, oS = oD + NV, oDS = oS + NS;
+    static constexpr int oZ = oDS + NS, oP = oZ + NV, oL = oP + NV, oN = oL + NCC, oT = oN + NCC, oA = oT + NCC;
+    static constexpr int nR = oA + NCC;
+    static constexpr int nF = 6 * CH + 3 * 4 * CH + 8;   // gates; per-wave row partials; scalars
+    static constexpr int bytes = nR * P::kBytes + nF * 4;
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
+};
+
+template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdArgs args) {
+    using R = typename P::R;
+    using F = typename P::F;
+    using Lay = GradLayout<P, DK, CH>;
+    constexpr int NKT = DK / 16, NCT = CH / 16, NKW = NKT / 4;   // d_k blocks per wave in the d_k-wide products
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
+    constexpr int EPV = 16 / P::kBytes;
+    constexpr int VPRQ = DK / EPV, VPRV = kDVT / EPV;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + 3) / 4;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
+    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
+    R *const Vs = reinterpret_cast<R *>(smem) + Lay::oV;
+    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;    // dO tile
+    R *const Ss = reinterpret_cast<R *>(smem) + Lay::oS;    // S tile [value row][d_k], later dQ staging
+    R *const dSs = reinterpret_cast<R *>(smem) + Lay::oDS;  // dS' tile, later dK staging
+    R *const Zs = reinterpret_cast<R *>(smem) + Lay::oZ;
+    R *const Ps = reinterpret_cast<R *>(smem) + Lay::oP;
+    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;    // diag(beta) strict(X K^T), later dLb
+    R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;
+    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;    // T, then T_g, later Mq
+    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+    float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
+    float *const egs = gs + CH;
+    float *const egls = egs + CH;
+    float *const bes = egls + CH;
+    float *const lams = bes + CH;
+    float *const als = lams + CH;
+    float *const pdb = als + CH;         // [4][CH] per-wave row partials: dbeta
+    float *const pdl = pdb + 4 * CH;     //   dlambda
+    float *const pdg = pdl + 4 * CH;     //   dg
+    float *const psc = pdg + 4 * CH;     // [0..3] <dS', S> per wave, [4..7] sum rowdot(D_r W_z, K) per wave
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int T = args.T, H = args.H, dv = args.dv;
+    const int NC = (T + CH - 1) / CH;
+    const int n = blockIdx.x % NC;
+    const int bh = blockIdx.x / NC;
+    const int b = bh / H, h = bh % H;
+    const int t0 = n * CH;
+    const int clen = min(CH, T - t0);
+
+    const R *__restrict__ gq = static_cast<const R *>(args.q);
+    const R *__restrict__ gk = static_cast<const R *>(args.k);
+    const R *__restrict__ gv = static_cast<const R *>(args.v);
+    const R *__restrict__ gdo = static_cast<const R *>(args.dO);
+    R *__restrict__ gdq = static_cast<R *>(args.g_q);
+    R *__restrict__ gdk = static_cast<R *>(args.g_k);
+    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+    // ---- q, k rows, gates, zeroed partials
+    for (int vi = tid; vi < CH * VPRQ; vi += kThreads) {
+        const int c = vi / VPRQ, cv = vi % VPRQ;
+        uint4 xq = make_uint4(0, 0, 0, 0), xk = xq;
+        if (c < clen) {
+            const size_t off = tok(t0 + c) * DK + cv * EPV;
+            xq = *reinterpret_cast<const uint4 *>(gq + off);
+            xk = *reinterpret_cast<const uint4 *>(gk + off);
+        }
+        *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = xq;
+        *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = xk;
+    }
+    if (wave == 0) {
+        const bool ok = lane < clen;
+        const size_t gi = tok(t0 + min(lane, clen - 1));
+        const float a = (HAS_A && ok) ? args.alpha[gi] : 1.f;
+        float x = (HAS_A && ok) ? __logf(a) : 0.f;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        const float glast = __shfl(x, CH - 1);
+        if (lane < CH) {
+            gs[lane] = x;
+            egs[lane] = __expf(x);
+            egls[lane] = __expf(glast - x);
+            bes[lane] = ok ? args.beta[gi] : 0.f;
+            lams[lane] = (HAS_L && ok) ? args.lam[gi] : 0.f;
+            als[lane] = a;
+        }
+    }
+    for (int i = tid; i < 3 * 4 * CH + 8; i += kThreads) pdb[i] = 0.f;
+    __syncthreads();
+
+    // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
+    gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
+    __syncthreads();
+    unit_lower_inverse<P, CH, PC>(Ls, Ts);
+    if constexpr (HAS_A) {
+        for (int idx = tid; idx < NPAIR * 64; idx += kThreads) {
+            int i, j;
+            tri_pair(idx >> 6, i, j);
+            const int r = 16 * i + ((idx >> 2) & 15);
+            const int c0 = 16 * j + 4 * (idx & 3);
+            const F tf = P::ld4(Ts + r * PC + c0);
+            const f32x4 gc = lds_f32x4(gs + c0);
+            const float gr = gs[r];
+            f32x4 tg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tg[e] = (c0 + e <= r) ? __expf(gr - gc[e]) * static_cast<float>(tf[e]) : 0.f;
+            P::st4(Ts + r * PC + c0, tg);
+        }
+        __syncthreads();
+    }
+
+    // ---- value tiles: column-local quantities per wave, then the value contractions
+    f32x4 Wo[NCT][NKW], Wp[NCT][NKW], Wz[NCT][NKW];
+    f32x4 dAacc[PPW], dLacc[PPW], dbacc[NCT];
+#pragma unroll
+    for (int mt = 0; mt < NCT; ++mt) {
+        dbacc[mt] = zero4();
+#pragma unroll
+        for (int c = 0; c < NKW; ++c) Wo[mt][c] = Wp[mt][c] = Wz[mt][c] = zero4();
+    }
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) dAacc[u] = dLacc[u] = zero4();
+    float sdot = 0.f;
+
+    for (int jt = 0; jt < args.n_dvt; ++jt) {
+        const int dv0 = jt * kDVT;
+        if (jt > 0) __syncthreads();   // every wave is done with the previous tile
+        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+            const int c = vi / VPRV, cv = vi % VPRV;
+            uint4 xv = make_uint4(0, 0, 0, 0), xd = xv;
+            if (c < clen) {
+                const size_t off = tok(t0 + c) * dv + dv0 + cv * EPV;
+                xv = *reinterpret_cast<const uint4 *>(gv + off);
+                xd = *reinterpret_cast<const uint4 *>(gdo + off);
+            }
+            *reinterpret_cast<uint4 *>(Vs + c * PV + cv * EPV) = xv;
+            *reinterpret_cast<uint4 *>(Ds + c * PV + cv * EPV) = xd;
+        }
+        {
+            const size_t base = ((static_cast<size_t>(bh) * NC + n) * dv + dv0) * DK;
+            const float *hs = args.Hs + base;
+            const float *dhs = args.dHs + base;
+            for (int vi = tid; vi < kDVT * DK / 4; vi += kThreads) {
+                const int row = vi / (DK / 4), c4 = 4 * (vi % (DK / 4));
+                const f32x4 sv = *reinterpret_cast<const f32x4 *>(hs + row * DK + c4);
+                const f32x4 dsv = *reinterpret_cast<const f32x4 *>(dhs + row * DK + c4);
+                sdot += sv[0] * dsv[0] + sv[1] * dsv[1] + sv[2] * dsv[2] + sv[3] * dsv[3];
+                P::st4(Ss + row * PK + c4, sv);
+                P::st4(dSs + row * PK + c4, dsv);
+            }
+        }
+        __syncthreads();
+
+        // column-local part, value columns [16 wave, 16 wave + 16) of the tile
+        F sTf[NKT], dsTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            sTf[t] = frag<P>(Ss, PK, 16 * wave, 16 * t);     // B-fragments of S^T and dS'^T
+            dsTf[t] = frag<P>(dSs, PK, 16 * wave, 16 * t);
+        }
+        f32x4 Rr[NCT], dZ[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            f32x4 pk = zero4(), pq = zero4(), kd = zero4();
+#pragma unroll
+            for (int t = 0; t < NKT; t += 2) {
+                const F k0 = frag<P>(Ks, PK, 16 * mt, 16 * t), k1 = frag<P>(Ks, PK, 16 * mt, 16 * t + 16);
+                pk = P::mma2(pk, k0, k1, sTf[t], sTf[t + 1]);
+                kd = P::mma2(kd, k0, k1, dsTf[t], dsTf[t + 1]);
+                if constexpr (HAS_L)
+                    pq = P::mma2(pq, frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16), sTf[t],
+                                 sTf[t + 1]);
+            }
+            const f32x4 y = HAS_L ? pk + lds_f32x4(lams + 16 * mt + 4 * g4) * pq : pk;
+            const f32x4 vf = P::f32(frag_b<P>(Vs, PV, 16 * mt, 16 * wave));
+            Rr[mt] = HAS_A ? vf - lds_f32x4(egs + 16 * mt + 4 * g4) * y : vf - y;
+            dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+        }
+        // Z = T_g diag(beta) R;  dZ += A^T dO
+        F bRf[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) bRf[mt] = P::cvt(lds_f32x4(bes + 16 * mt + 4 * g4) * Rr[mt]);
+        f32x4 Z[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            Z[mt] = zero4();
+#pragma unroll
+            for (int s = 0; s <= mt; ++s) Z[mt] = P::mma1(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), bRf[s]);
+#pragma unroll
+            for (int s = mt; s < NCT; ++s)
+                dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
+        }
+        // P = T_g^T dZ;  U = R - N Z;  dbeta += rowdot(P, U)
+        F dZf[NCT], Zf[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            dZf[mt] = P::cvt(dZ[mt]);
+            Zf[mt] = P::cvt(Z[mt]);
+        }
+        f32x4 Pm[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            Pm[mt] = zero4();
+#pragma unroll
+            for (int s = mt; s < NCT; ++s) Pm[mt] = P::mma1(Pm[mt], frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
+            f32x4 U = Rr[mt];
+#pragma unroll
+            for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dbacc[mt][e] += sum16(Pm[mt][e] * U[e]);
+        }
+        // Z and P of the tile to LDS for the value contractions
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
+                Zs[o] = P::from_f32(Z[mt][e]);
+                Ps[o] = P::from_f32(Pm[mt][e]);
+            }
+        }
+        __syncthreads();
+
+        // dA += dO Z^T, dL += P Z^T on this wave's lower blocks
+#pragma unroll
+        for (int u = 0; u < PPW; ++u) {
+            const int p = wave + 4 * u;
+            if (p < NPAIR) {
+                int i, j;
+                tri_pair(p, i, j);
+#pragma unroll
+                for (int vv = 0; vv < kDVT / 16; vv += 2) {
+                    const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
+                    dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
+                                       z0, z1);
+                    dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
+                                       z0, z1);
+                }
+            }
+        }
+        // W_o += dO S, W_p += P S, W_z += Z dS' on this wave's d_k blocks
+#pragma unroll
+        for (int c = 0; c < NKW; ++c) {
+            const int kk = NKW * wave + c;
+#pragma unroll
+            for (int vv = 0; vv < kDVT / 16; vv += 2) {
+                const F s0 = frag_b<P>(Ss, PK, 16 * vv, 16 * kk), s1 = frag_b<P>(Ss, PK, 16 * vv + 16, 16 * kk);
+                const F d0 = frag_b<P>(dSs, PK, 16 * vv, 16 * kk), d1 = frag_b<P>(dSs, PK, 16 * vv + 16, 16 * kk);
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt) {
+                    Wo[mt][c] = P::mma2(Wo[mt][c], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16),
+                                        s0, s1);
+                    Wp[mt][c] = P::mma2(Wp[mt][c], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16),
+                                        s0, s1);
+                    Wz[mt][c] = P::mma2(Wz[mt][c], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16),
+                                        d0, d1);
+                }
+            }
+        }
+    }
+    __syncthreads();   // the tile buffers, T_g and L are free from here on
+
+    // ---- dA and dL on this wave's blocks -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int p = wave + 4 * u;
+        if (p < NPAIR) {
+            int i, j;
+            tri_pair(p, i, j);
+            const int c = 16 * j + r16;
+            const float gc = gs[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * g4 + e;
+                const float G = HAS_A ? __expf(gs[r] - gc) : 1.f;
+                const float da = (c <= r) ? dAacc[u][e] : 0.f;
+                const float dlb = (c < r) ? -bes[r] * G * dLacc[u][e] : 0.f;
+                Ts[r * PC + c] = P::from_f32(da * G + (HAS_L ? lams[r] * dlb : 0.f));
+                Ls[r * PC + c] = P::from_f32(dlb);
+            }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = dbacc[mt][e];
+    }
+    __syncthreads();   // Mq and dLb published
+
+    // ---- on this wave's d_k blocks:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K, and
+    //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
+    //   dK = KT + D_r W_z + dX.
+    // The decay gradient's pair terms are row dot products of these products:
+    //   rowsum(dA o A) + rowsum(dL o beta N) = rowdot(Q, MqK) + rowdot(K, LbK),
+    //   colsum(dA o A) + colsum(dL o beta N) = rowdot(K, KT),
+    // taken from the fp32 accumulators with the exact q and k.
+    float wz = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NCT; ++mt) {
+        const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
+        const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
+        f32x4 dlp = zero4(), dgp = zero4();
+#pragma unroll
+        for (int c = 0; c < NKW; ++c) {
+            const int kk = NKW * wave + c;
+            f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
+#pragma unroll
+            for (int s = 0; s <= mt; ++s) {
+                const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
+                lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
+                mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
+            }
+#pragma unroll
+            for (int s = mt; s < NCT; ++s) {
+                kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
+                kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
+            }
+            const f32x4 dX = lbk - eg * bt * Wp[mt][c];
+            const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[mt][c] - lm * bt * Wp[mt][c]) : eg * Wo[mt][c]);
+            const f32x4 dK = kt + el * Wz[mt][c] + dX;
+            const f32x4 qf = P::f32(frag_b<P>(Qs, PK, 16 * mt, 16 * kk));
+            const f32x4 kf = P::f32(frag_b<P>(Ks, PK, 16 * mt, 16 * kk));
+            if constexpr (HAS_L) dlp += qf * dX;
+            if constexpr (HAS_A) {
+                const f32x4 xf = HAS_L ? kf + lm * qf : kf;
+                const f32x4 wzk = el * Wz[mt][c] * kf;
+                dgp += qf * mqk + kf * lbk - kf * kt + eg * (Wo[mt][c] * qf - bt * Wp[mt][c] * xf) - wzk;
+                wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * mt + 4 * g4 + e) * PK + 16 * kk + r16;
+                Ss[o] = P::from_f32(dQ[e]);
+                dSs[o] = P::from_f32(dK[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * mt + 4 * g4 + e;
+            if constexpr (HAS_L) {
+                const float rs = sum16(dlp[e]);
+                if (r16 == 0) pdl[wave * CH + r] = rs;
+            }
+            if constexpr (HAS_A) {
+                const float rs = sum16(dgp[e]);
+                if (r16 == 0) pdg[wave * CH + r] = rs;
+            }
+        }
+    }
+    if constexpr (HAS_A) {
+        wz = sum64(wz);
+        const float sd = sum64(sdot);
+        if (lane == 0) {
+            psc[wave] = sd;
+            psc[4 + wave] = wz;
+        }
+    }
+    __syncthreads();
+
+    // ---- stores: dQ, dK rows; per-token dbeta, dlambda, dalpha
+    for (int vi = tid; vi < CH * VPRQ; vi += kThreads) {
+        const int c = vi / VPRQ, cv = vi % VPRQ;
+        if (c < clen) {
+            const size_t off = tok(t0 + c) * DK + cv * EPV;
+            *reinterpret_cast<uint4 *>(gdq + off) = *reinterpret_cast<const uint4 *>(Ss + c * PK + cv * EPV);
+            *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(dSs + c * PK + cv * EPV);
+        }
+    }
+    if (wave == 0) {
+        float db = 0.f, dl = 0.f, dg = 0.f;
+        if (lane < CH) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                db += pdb[w * CH + lane];
+                dl += pdl[w * CH + lane];
+                dg += pdg[w * CH + lane];
+            }
+            if (HAS_A && lane == CH - 1)
+                dg += egs[CH - 1] * (psc[0] + psc[1] + psc[2] + psc[3]) + (psc[4] + psc[5] + psc[6] + psc[7]);
+        }
+        // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_down(dg, off);
+            if (lane + off < kWave) dg += y;
+        }
+        if (lane < clen) {
+            const size_t gi = tok(t0 + lane);
+            args.g_beta[gi] = db;
+            if (HAS_L && args.g_lam) args.g_lam[gi] = dl;
+            if (HAS_A && args.g_alpha) args.g_alpha[gi] = dg / als[lane];
+        }
+    }
+}
+
+template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
+hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
+    const int NC = (a.T + CH - 1) / CH;
+    const int g2 = a.B * a.H * a.n_dvt;
+    hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || NC == 0) return err;
+    hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <class P, int DK, int CH>
+hipError_t launch_gates(const BwdArgs &a, hipStream_t stream) {
+    const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
+    if (ha && hl) return launch_passes<P, DK, CH, true, true>(a, stream);
+    if (ha) return launch_passes<P, DK, CH, true, false>(a, stream);
+    if (hl) return launch_passes<P, DK, CH, false, true>(a, stream);
+    return launch_passes<P, DK, CH, false, false>(a, stream);
+}
+
+template <class P, int DK>
+hipError_t launch_chunk(int C, const BwdArgs &a, hipStream_t stream) {
+    switch (C) {
+        case 16: return launch_gates<P, DK, 16>(a, stream);
+        case 32: return launch_gates<P, DK, 32>(a, stream);
+        case 64:
+            if constexpr (P::kBytes == 2) return launch_gates<P, DK, 64>(a, stream);
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int dtype, int dk, int dv, int C) {
+    // fp32 C = 64 would exceed the per-chunk kernel's LDS budget
+    return (dtype == 0 || dtype == 1) && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
+           (C == 16 || C == 32 || (C == 64 && dtype == 1));
+}
+
+size_t chunk_bwd_workspace(int B, int T, int H, int dk, int dv, int C) {
+    if (B <= 0 || T <= 0 || H <= 0 || C <= 0) return 0;
+    const size_t NC = (static_cast<size_t>(T) + C - 1) / C;
+    return 2 * static_cast<size_t>(B) * H * NC * dv * dk * sizeof(float);
+}
+
+hipError_t launch_chunk_bwd(int dtype, int dk, int C, const BwdArgs &a, hipStream_t stream) {
+    if (a.B == 0 || a.H == 0) return hipSuccess;
+    // pass 1: the forward, keeping the chunk entry states
+    ChunkArgs f;
+    f.q = a.q; f.k = a.k; f.v = a.v;
+    f.alpha = a.alpha; f.beta = a.beta; f.lam = a.lam;
+    f.S0 = a.S0; f.o = nullptr; f.S_T = nullptr;
+    f.B = a.B; f.T = a.T; f.H = a.H; f.dv = a.dv; f.n_dvt = a.n_dvt;
+    f.Hs = a.Hs;
+    hipError_t err = hipSuccess;
+    if (a.T > 0 && (err = launch_chunk_fwd_states(dtype, dk, C, f, stream)) != hipSuccess) return err;
+    if (dtype == 1) return dk == 128 ? launch_chunk<Bf16, 128>(C, a, stream) : launch_chunk<Bf16, 64>(C, a, stream);
+    return dk == 128 ? launch_chunk<F32, 128>(C, a, stream) : launch_chunk<F32, 64>(C, a, stream);
+}
+
+}  // namespace qd

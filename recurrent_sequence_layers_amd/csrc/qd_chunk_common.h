@@ -30,3 +30,133 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
 }
 
 }  // namespace qd
+
+namespace qd {
+
+// Gram blocks of one chunk, four waves over the lower block triangle.  Each block is
+// computed transposed (D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c], r = 16i + l%16,
+// c = 16j + 4g + e) so a lane owns four consecutive columns of a row.  Writes
+//   L = strictly-lower(diag(beta) X K^T),  X K^T = K K^T + diag(lambda) Q K^T,
+//   A = G o lower(Q K^T),   and, when N is non-null,  N = G o strictly-lower(X K^T),
+// with G[r][c] = exp(g_r - g_c).  Blocks above the block diagonal are not written.
+template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L>
+__device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
+                                            const float *bes, const float *lams, typename P::R *Ls,
+                                            typename P::R *As, typename P::R *Ns) {
+    using F = typename P::F;
+    constexpr int NKT = DK / 16, NCT = CH / 16;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + 3) / 4;
+    const int wave = wave_id(), lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int p = wave + 4 * u;
+        if (p < NPAIR) {
+            int i, j;
+            tri_pair(p, i, j);
+            f32x4 gq_ = zero4(), gk_ = zero4();
+#pragma unroll
+            for (int s = 0; s < NKT; s += 2) {
+                const F a0 = frag<P>(Ks, PK, 16 * j, 16 * s);
+                const F a1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
+                gq_ = P::mma2(gq_, a0, a1, frag<P>(Qs, PK, 16 * i, 16 * s), frag<P>(Qs, PK, 16 * i, 16 * s + 16));
+                gk_ = P::mma2(gk_, a0, a1, frag<P>(Ks, PK, 16 * i, 16 * s), frag<P>(Ks, PK, 16 * i, 16 * s + 16));
+            }
+            const int r = 16 * i + r16;
+            const int c0 = 16 * j + 4 * g4;
+            const float lr = lams[r], br = bes[r], gr = gs[r];
+            const f32x4 gc = lds_f32x4(gs + c0);
+            f32x4 lv, av, nv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c0 + e;
+                const float xk = HAS_L ? gk_[e] + lr * gq_[e] : gk_[e];
+                const float dec = HAS_A ? __expf(gr - gc[e]) : 1.f;
+                lv[e] = (c < r) ? br * xk : 0.f;
+                av[e] = (c <= r) ? dec * gq_[e] : 0.f;
+                nv[e] = (c < r) ? dec * xk : 0.f;
+            }
+            P::st4(Ls + r * PC + c0, lv);
+            P::st4(As + r * PC + c0, av);
+            if (Ns) P::st4(Ns + r * PC + c0, nv);
+        }
+    }
+}
+
+// T = (I + L)^-1 for the strictly lower CH x CH matrix L in LDS (pitch PC), four waves.
+// The 16 x 16 diagonal blocks by forward substitution over rows (t_r = e_r -
+// sum_{j<r} L[r][j] t_j; wave w inverts block w, lane l computes column l % 16), then
+// block doubling on MFMA (T21 = -T22 L21 T11 for 16- and then 32-row halves).  Only
+// the lower block triangle of T is written; the upper triangle of each diagonal block
+// comes out exactly zero.  Called after a barrier that publishes L; ends with one.
+template <class P, int CH, int PC>
+__device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, typename P::R *Ts) {
+    constexpr int NCT = CH / 16;
+    const int wave = wave_id(), lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+    if (wave < NCT) {
+        const int o = 16 * wave;
+        const int c = r16;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float lr[16];
+            load_row16<P>(Ls + (o + r) * PC + o, lr);
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < r; ++jj) acc -= lr[jj] * t[jj];
+            t[r] = acc;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
+        }
+    }
+    __syncthreads();
+    // block (rb_, cb_) of T from an accumulator tile (rows 4g + e, column l % 16)
+    auto tstore = [&](int rb_, int cb_, f32x4 val) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
+    };
+    // level 1: T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
+    if constexpr (NCT >= 2) {
+        if (wave < NCT / 2) {
+            const int rb_ = 2 * wave + 1, cb_ = 2 * wave;
+            const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), frag_b<P>(Ts, PC, 16 * cb_, 16 * cb_));
+            const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
+            tstore(rb_, cb_, -y);
+        }
+        __syncthreads();
+    }
+    // level 2 (CH = 64): lower-left 32x32 quadrant, one 16x16 block per wave:
+    // T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
+    if constexpr (NCT == 4) {
+        const int ab = 2 + (wave >> 1), cb_ = wave & 1;
+        f32x4 acc = zero4();
+        for (int m = 2; m <= ab; ++m) {
+            f32x4 x = zero4();
+            for (int kb = cb_; kb <= 1; ++kb)
+                x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
+            acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
+        }
+        tstore(ab, cb_, -acc);
+        __syncthreads();
+    }
+}
+
+// Sum over the 16 lanes that share l / 16 (one row of an accumulator tile).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+// Sum over the wave.
+__device__ __forceinline__ float sum64(float x) {
+    x = sum16(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+}  // namespace qd

@@ -79,7 +79,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
     constexpr int NVQ = (CH * VPRQ + kThreads - 1) / kThreads;
     constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;
     constexpr int NPAIR = NCT * (NCT + 1) / 2;
-    constexpr int PPW = (NPAIR + 3) / 4;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
     R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
@@ -202,97 +201,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * CH;
         const int clen = min(CH, T - t0);
+        if (args.Hs) {   // entry state of chunk n, [B][H][NC][d_v][d_k] (kept for the backward)
+            float *hs = args.Hs + (static_cast<size_t>(bh) * NC + n) * dv * DK +
+                        static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(hs + 16 * t) = sT[t];
+        }
         lstore(clen);
         if (n + 1 < NC) gload(n + 1);
         __syncthreads();
 
-        // ---- Gram blocks, computed transposed so a lane owns four consecutive columns:
-        // D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c] with r = 16i + l%16, c = 16j + 4g + e.
-        // Then L = sl(diag(beta) (K K^T + diag(lambda) Q K^T)) and A = H o Q K^T.
-#pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const int p = wave + 4 * u;
-            if (p < NPAIR) {
-                int i, j;
-                tri_pair(p, i, j);
-                f32x4 gq_ = zero4(), gk_ = zero4();
-#pragma unroll
-                for (int s = 0; s < NKT; s += 2) {
-                    const F a0 = frag<P>(Ks, PK, 16 * j, 16 * s);
-                    const F a1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
-                    gq_ = P::mma2(gq_, a0, a1, frag<P>(Qs, PK, 16 * i, 16 * s), frag<P>(Qs, PK, 16 * i, 16 * s + 16));
-                    gk_ = P::mma2(gk_, a0, a1, frag<P>(Ks, PK, 16 * i, 16 * s), frag<P>(Ks, PK, 16 * i, 16 * s + 16));
-                }
-                const int r = 16 * i + r16;
-                const int c0 = 16 * j + 4 * g4;
-                const float lr = lams[r], br = bes[r], gr = gs[r];
-                const f32x4 gc = lds_f32x4(gs + c0);
-                f32x4 lv, av;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = c0 + e;
-                    const float xk = HAS_L ? gk_[e] + lr * gq_[e] : gk_[e];
-                    lv[e] = (c < r) ? br * xk : 0.f;
-                    av[e] = (c <= r) ? (HAS_A ? __expf(gr - gc[e]) : 1.f) * gq_[e] : 0.f;
-                }
-                P::st4(Ls + r * PC + c0, lv);
-                P::st4(As + r * PC + c0, av);
-            }
-        }
+        // ---- Gram blocks: L = sl(diag(beta) X K^T), A = H o Q K^T; then T = (I + L)^-1
+        gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, nullptr);
         __syncthreads();
-
-        // ---- T = (I + L)^-1: diagonal 16x16 blocks by forward substitution over rows
-        // (t_r = e_r - sum_{j<r} L[r][j] t_j).  Wave w inverts block w; lane l computes
-        // column l % 16 (lanes >= 16 repeat it and do not store).
-        if (wave < NCT) {
-            const int o = 16 * wave;
-            const int c = r16;
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float lr[16];
-                load_row16<P>(Ls + (o + r) * PC + o, lr);
-                float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int jj = 0; jj < r; ++jj) acc -= lr[jj] * t[jj];
-                t[r] = acc;
-            }
-            if (lane < 16) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
-            }
-        }
-        __syncthreads();
-
-        // block (rb_, cb_) of T from an accumulator tile (rows 4g + e, column l % 16)
-        auto tstore = [&](int rb_, int cb_, f32x4 val) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
-        };
-        // ---- block doubling, level 1: T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
-        if constexpr (NCT >= 2) {
-            if (wave < NCT / 2) {
-                const int rb_ = 2 * wave + 1, cb_ = 2 * wave;
-                const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), frag_b<P>(Ts, PC, 16 * cb_, 16 * cb_));
-                const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
-                tstore(rb_, cb_, -y);
-            }
-            __syncthreads();
-        }
-        // ---- level 2 (CH = 64): lower-left 32x32 quadrant, one 16x16 block per wave:
-        // T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
-        if constexpr (NCT == 4) {
-            const int ab = 2 + (wave >> 1), cb_ = wave & 1;
-            f32x4 acc = zero4();
-            for (int m = 2; m <= ab; ++m) {
-                f32x4 x = zero4();
-                for (int kb = cb_; kb <= 1; ++kb)
-                    x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
-                acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
-            }
-            tstore(ab, cb_, -acc);
-            __syncthreads();
-        }
+        unit_lower_inverse<P, CH, PC>(Ls, Ts);
 
         // ---- M1 = (H o T) diag(beta), M2 = -D_g T diag(beta), four columns per lane,
         // lower block triangle only (the other blocks are never read)
@@ -403,6 +325,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
             }
             sT[t] = acc;
         }
+        if (!go) {   // state-only pass: no output; the barrier keeps the next chunk's LDS writes
+            __syncthreads();   // behind every wave's reads of this chunk's K
+            continue;
+        }
         // stage O (the T buffer is dead after the M build), then coalesced row stores
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
@@ -453,6 +379,11 @@ hipError_t launch_dk(int C, const ChunkArgs &a, hipStream_t stream) {
 bool chunk_fwd_supported(int dtype, int dk, int dv, int C) {
     return (dtype == 0 || dtype == 1) && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
            (C == 16 || C == 32 || C == 64);
+}
+
+hipError_t launch_chunk_fwd_states(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {
+    if (dtype == 1) return dk == 128 ? launch_dk<Bf16, 128>(C, a, stream) : launch_dk<Bf16, 64>(C, a, stream);
+    return dk == 128 ? launch_dk<F32, 128>(C, a, stream) : launch_dk<F32, 64>(C, a, stream);
 }
 
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {

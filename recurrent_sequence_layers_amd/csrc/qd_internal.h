@@ -15,6 +15,22 @@ struct ChunkArgs {
     int B, T, H, dv;
     int n_dvt;                      // number of 64-wide value-column tiles, d_v / 64
     bool raw = false;               // q, k unnormalised and gates as logits (bf16 C = 32, 64 only)
+    float *Hs = nullptr;            // [B][H][NC][d_v][d_k]: every chunk's entry state (generic kernel only)
+};
+
+// Layer backward (qd_chunk_bwd.hip).  Gradients of sum(o dO) + sum(S_T dST).
+struct BwdArgs {
+    const void *q, *k, *v;          // [B][T][H][d_k] / [B][T][H][d_v]
+    const float *alpha, *beta, *lam; // [B][T][H]; alpha/lam may be null
+    const float *S0;                // [B][H][d_v][d_k] or null
+    const void *dO;                 // [B][T][H][d_v]
+    const float *dST;               // [B][H][d_v][d_k] or null
+    void *g_q, *g_k, *g_v;          // gradients: [B][T][H][d_k] / [B][T][H][d_v]
+    float *g_alpha, *g_beta, *g_lam; // [B][T][H]; g_alpha/g_lam may be null
+    float *g_S0;                    // [B][H][d_v][d_k] or null
+    float *Hs, *dHs;                // workspace: [B][H][NC][d_v][d_k] entry states and exit-state gradients
+    int B, T, H, dv;
+    int n_dvt;
 };
 
 struct StepArgs {
@@ -40,6 +56,15 @@ int chunk_fwd_segments(int dtype, int B, int T, int H, int dk, int dv, int C);
 size_t chunk_fwd_segment_workspace(int B, int T, int H, int dk, int dv, int P);
 hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
                                       hipStream_t stream);
+
+// The generic (four-wave) forward kernel for every dtype and C, which can keep the
+// chunk entry states (ChunkArgs::Hs) and skip the output (o == null).
+hipError_t launch_chunk_fwd_states(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
+
+// Backward: workspace size and the three passes (states, reverse scan, per-chunk gradients).
+bool chunk_bwd_supported(int dtype, int dk, int dv, int C);
+size_t chunk_bwd_workspace(int B, int T, int H, int dk, int dv, int C);
+hipError_t launch_chunk_bwd(int dtype, int dk, int C, const BwdArgs &a, hipStream_t stream);
 
 // Whether an instance exists for these sizes (checked before launching).
 bool chunk_fwd_supported(int dtype, int dk, int dv, int C);

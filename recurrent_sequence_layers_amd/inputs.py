@@ -120,6 +120,18 @@ def workload_inputs(name: str, seed: int, device="cpu", gates_as_none=False) -> 
                         s0_std=w.get("s0_std"), device=device, gates_as_none=gates_as_none)
 
 
+def upstream_grads(B, T, H, dk, dv, dtype="bf16", seed=0, dst_std=None, device="cpu"):
+    """Gradients arriving from above for the layer backward: dO ~ N(0, 1) in the
+    input dtype [B,T,H,dv] and, when dst_std is given, dS_T ~ N(0, dst_std) fp32
+    [B,H,dv,dk].  Drawn from their own generator (seed), so the forward inputs of the
+    same seed do not shift."""
+    g = _generator(seed, device)
+    f = dict(generator=g, device=device, dtype=torch.float32)
+    dO = torch.randn(B, T, H, dv, **f).to(_DT[dtype]).contiguous()
+    dST = (torch.randn(B, H, dv, dk, **f) * float(dst_std)).contiguous() if dst_std else None
+    return dO, dST
+
+
 def decode_state(N, H, dk, dv, s0_std=0.02, seed=0, device="cpu") -> torch.Tensor:
     """Resident fp32 decode state S ~ N(0, s0_std), layout [N,H,dv,dk]."""
     g = _generator(seed, device)

@@ -321,7 +321,14 @@ def kernel_form_bwd(q, k, v, alpha, beta, lam, S0, dO, dST, C):
                 dQ = (dA * G) @ K + Dg[:, None] * Wo + la[:, None] * dX
                 dK = (dA * G).T @ Q + (dLg * G).T @ (be[:, None] * X) + Dr[:, None] * Wz + dX
                 wz = np.einsum("tj,tj->t", Dr[:, None] * Wz, K)
-                dg = ((dA * c["A"]).sum(1) - (dA * c["A"]).sum(0) + (dLg * Lg).sum(1) - (dLg * Lg).sum(0)
+                pair = (dA * c["A"]).sum(1) - (dA * c["A"]).sum(0) + (dLg * Lg).sum(1) - (dLg * Lg).sum(0)
+                # the kernel's regrouping of the same sums into row dot products of its products
+                dLb = be[:, None] * (dLg * G)
+                Mq = dA * G + la[:, None] * dLb
+                rd = lambda a_, b_: np.einsum("tj,tj->t", a_, b_)
+                regrouped = rd(Q, Mq @ K) + rd(K, dLb @ K) - rd(K, Mq.T @ Q + dLb.T @ K)
+                assert np.allclose(regrouped, pair, rtol=1e-9, atol=1e-12 * max(1.0, np.abs(pair).max()))
+                dg = (pair
                       + np.einsum("tj,tj->t", Dg[:, None] * Wo, Q) - np.einsum("tj,tj->t", Dg[:, None] * Wr, X) - wz)
                 dg[-1] += c["gC"] * (dSp * S).sum() + wz.sum()
                 out["dq"][b, c["sl"], h] = dQ
