@@ -143,8 +143,10 @@ int qdelta_step_raw(const void *q, const void *k, const void *v,
                     int d_k, int d_v, int dtype, void *stream);
 
 /* Bytes of device workspace qdelta_chunk_bwd needs: the entry state of every chunk and
- * the gradient with respect to every chunk's exit state, 2*B*H*ceil(T/C)*d_v*d_k*4
- * bytes (0 when B*H*T == 0 or the sizes are unsupported). */
+ * the gradient with respect to every chunk's exit state, kept in the input element
+ * type (the kernels feed them to the matrix cores in that type):
+ * 2*B*H*ceil(T/C)*d_v*d_k*(2 for bf16, 4 for fp32) bytes; 0 when B*H*T == 0 or the
+ * sizes are unsupported. */
 size_t qdelta_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
                                         int dtype);
 

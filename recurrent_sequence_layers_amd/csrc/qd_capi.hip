@@ -42,7 +42,7 @@ size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, i
 
 size_t qdelta_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
     if (B < 0 || T < 0 || H < 0 || !qd::chunk_bwd_supported(dtype, d_k, d_v, C)) return 0;
-    return qd::chunk_bwd_workspace(B, T, H, d_k, d_v, C);
+    return qd::chunk_bwd_workspace(dtype, B, T, H, d_k, d_v, C);
 }
 
 int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
@@ -58,7 +58,7 @@ int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *a
     if ((alpha == nullptr && dalpha != nullptr) || (lambda == nullptr && dlambda != nullptr)) return QD_ERR_INVALID_ARG;
     const long long ntok = bh * T;
     if (ntok > 0 && (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta)) return QD_ERR_INVALID_ARG;
-    const size_t need = qd::chunk_bwd_workspace(B, T, H, d_k, d_v, C);
+    const size_t need = qd::chunk_bwd_workspace(dtype, B, T, H, d_k, d_v, C);
     if (ws_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return QD_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
         !aligned16(dv) || !aligned16(S0) || !aligned16(dS_T) || !aligned16(dS0))
@@ -86,9 +86,9 @@ int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *a
     a.S0 = S0; a.dO = d_o; a.dST = dS_T;
     a.g_q = dq; a.g_k = dk; a.g_v = dv;
     a.g_alpha = dalpha; a.g_beta = dbeta; a.g_lam = dlambda; a.g_S0 = dS0;
-    float *ws = static_cast<float *>(workspace);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
     a.Hs = ws;
-    a.dHs = ws ? ws + need / (2 * sizeof(float)) : nullptr;
+    a.dHs = ws ? ws + need / 2 : nullptr;
     a.B = B; a.T = T; a.H = H; a.dv = d_v;
     a.n_dvt = d_v / 64;
     const hipError_t err = qd::launch_chunk_bwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));

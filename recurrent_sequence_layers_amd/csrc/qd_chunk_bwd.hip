@@ -183,10 +183,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdAr
         const int t0 = n * CH;
         const int clen = min(CH, T - t0);
         {   // gradient with respect to chunk n's exit state
-            float *dh = args.dHs + (static_cast<size_t>(bh) * NC + n) * dv * DK +
-                        static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
+            R *dh = static_cast<R *>(args.dHs) + (static_cast<size_t>(bh) * NC + n) * dv * DK +
+                    static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(dh + 16 * t) = sT[t];
+            for (int t = 0; t < NKT; ++t) P::st4(dh + 16 * t, sT[t]);
         }
         lstore(clen);
         if (n > 0) gload(n - 1);
@@ -379,17 +379,79 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
     R *__restrict__ gdk = static_cast<R *>(args.g_k);
     auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
 
-    // ---- q, k rows, gates, zeroed partials
-    for (int vi = tid; vi < CH * VPRQ; vi += kThreads) {
-        const int c = vi / VPRQ, cv = vi % VPRQ;
-        uint4 xq = make_uint4(0, 0, 0, 0), xk = xq;
-        if (c < clen) {
-            const size_t off = tok(t0 + c) * DK + cv * EPV;
-            xq = *reinterpret_cast<const uint4 *>(gq + off);
-            xk = *reinterpret_cast<const uint4 *>(gk + off);
+    // ---- global loads, issued ahead of their LDS stores: the q, k rows now, and the first
+    // value tile (V, dO, S, dS' rows), which stays in registers through the Gram and
+    // inverse phase; each later tile is fetched while the previous one is computed.
+    constexpr int NLQ = (CH * VPRQ + kThreads - 1) / kThreads;       // q, k vectors per thread
+    constexpr int NLV = (CH * VPRV + kThreads - 1) / kThreads;       // v, dO vectors per thread
+    constexpr int NLS = kDVT * VPRQ / kThreads;                      // S, dS' vectors per thread
+    static_assert(kDVT * VPRQ % kThreads == 0, "S tile vectors split evenly over the threads");
+    const R *__restrict__ ghs = static_cast<const R *>(args.Hs);
+    const R *__restrict__ gdhs = static_cast<const R *>(args.dHs);
+    uint4 lv[NLV], ld[NLV], ls[NLS], lds_[NLS];
+    auto tile_load = [&](int jt) {
+        const int dv0 = jt * kDVT;
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int vi = tid + kThreads * j;
+            lv[j] = ld[j] = make_uint4(0, 0, 0, 0);
+            if ((CH * VPRV % kThreads == 0 || vi < CH * VPRV) && vi / VPRV < clen) {
+                const size_t off = tok(t0 + vi / VPRV) * dv + dv0 + (vi % VPRV) * EPV;
+                lv[j] = *reinterpret_cast<const uint4 *>(gv + off);
+                ld[j] = *reinterpret_cast<const uint4 *>(gdo + off);
+            }
         }
-        *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = xq;
-        *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = xk;
+        const size_t base = ((static_cast<size_t>(bh) * NC + n) * dv + dv0) * DK;
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int vi = tid + kThreads * j;
+            ls[j] = *reinterpret_cast<const uint4 *>(ghs + base + vi * EPV);
+            lds_[j] = *reinterpret_cast<const uint4 *>(gdhs + base + vi * EPV);
+        }
+    };
+    float sdot = 0.f;
+    auto tile_store = [&]() {
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                *reinterpret_cast<uint4 *>(Vs + (vi / VPRV) * PV + (vi % VPRV) * EPV) = lv[j];
+                *reinterpret_cast<uint4 *>(Ds + (vi / VPRV) * PV + (vi % VPRV) * EPV) = ld[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int vi = tid + kThreads * j;
+            const int o = (vi / VPRQ) * PK + (vi % VPRQ) * EPV;
+            *reinterpret_cast<uint4 *>(Ss + o) = ls[j];
+            *reinterpret_cast<uint4 *>(dSs + o) = lds_[j];
+            const R *a = reinterpret_cast<const R *>(&ls[j]);
+            const R *d = reinterpret_cast<const R *>(&lds_[j]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) sdot += P::to_f32(a[e]) * P::to_f32(d[e]);
+        }
+    };
+    {
+        uint4 xq[NLQ], xk[NLQ];
+#pragma unroll
+        for (int j = 0; j < NLQ; ++j) {
+            const int vi = tid + kThreads * j;
+            xq[j] = xk[j] = make_uint4(0, 0, 0, 0);
+            if ((CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) && vi / VPRQ < clen) {
+                const size_t off = tok(t0 + vi / VPRQ) * DK + (vi % VPRQ) * EPV;
+                xq[j] = *reinterpret_cast<const uint4 *>(gq + off);
+                xk[j] = *reinterpret_cast<const uint4 *>(gk + off);
+            }
+        }
+        tile_load(0);
+#pragma unroll
+        for (int j = 0; j < NLQ; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                *reinterpret_cast<uint4 *>(Qs + (vi / VPRQ) * PK + (vi % VPRQ) * EPV) = xq[j];
+                *reinterpret_cast<uint4 *>(Ks + (vi / VPRQ) * PK + (vi % VPRQ) * EPV) = xk[j];
+            }
+        }
     }
     if (wave == 0) {
         const bool ok = lane < clen;
@@ -437,44 +499,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
 
     // ---- value tiles: column-local quantities per wave, then the value contractions
     f32x4 Wo[NCT][NKW], Wp[NCT][NKW], Wz[NCT][NKW];
-    f32x4 dAacc[PPW], dLacc[PPW], dbacc[NCT];
+    f32x4 dAacc[PPW], dLacc[PPW];
 #pragma unroll
     for (int mt = 0; mt < NCT; ++mt) {
-        dbacc[mt] = zero4();
 #pragma unroll
         for (int c = 0; c < NKW; ++c) Wo[mt][c] = Wp[mt][c] = Wz[mt][c] = zero4();
     }
 #pragma unroll
     for (int u = 0; u < PPW; ++u) dAacc[u] = dLacc[u] = zero4();
-    float sdot = 0.f;
 
     for (int jt = 0; jt < args.n_dvt; ++jt) {
-        const int dv0 = jt * kDVT;
         if (jt > 0) __syncthreads();   // every wave is done with the previous tile
-        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
-            const int c = vi / VPRV, cv = vi % VPRV;
-            uint4 xv = make_uint4(0, 0, 0, 0), xd = xv;
-            if (c < clen) {
-                const size_t off = tok(t0 + c) * dv + dv0 + cv * EPV;
-                xv = *reinterpret_cast<const uint4 *>(gv + off);
-                xd = *reinterpret_cast<const uint4 *>(gdo + off);
-            }
-            *reinterpret_cast<uint4 *>(Vs + c * PV + cv * EPV) = xv;
-            *reinterpret_cast<uint4 *>(Ds + c * PV + cv * EPV) = xd;
-        }
-        {
-            const size_t base = ((static_cast<size_t>(bh) * NC + n) * dv + dv0) * DK;
-            const float *hs = args.Hs + base;
-            const float *dhs = args.dHs + base;
-            for (int vi = tid; vi < kDVT * DK / 4; vi += kThreads) {
-                const int row = vi / (DK / 4), c4 = 4 * (vi % (DK / 4));
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(hs + row * DK + c4);
-                const f32x4 dsv = *reinterpret_cast<const f32x4 *>(dhs + row * DK + c4);
-                sdot += sv[0] * dsv[0] + sv[1] * dsv[1] + sv[2] * dsv[2] + sv[3] * dsv[3];
-                P::st4(Ss + row * PK + c4, sv);
-                P::st4(dSs + row * PK + c4, dsv);
-            }
-        }
+        tile_store();
+        if (jt + 1 < args.n_dvt) tile_load(jt + 1);
         __syncthreads();
 
         // column-local part, value columns [16 wave, 16 wave + 16) of the tile
@@ -533,7 +570,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
 #pragma unroll
             for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dbacc[mt][e] += sum16(Pm[mt][e] * U[e]);
+            for (int e = 0; e < 4; ++e) {
+                const float db = sum16(Pm[mt][e] * U[e]);
+                if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] += db;   // this wave's row partial
+            }
         }
         // Z and P of the tile to LDS for the value contractions
 #pragma unroll
@@ -605,12 +645,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
                 Ls[r * PC + c] = P::from_f32(dlb);
             }
         }
-    }
-#pragma unroll
-    for (int mt = 0; mt < NCT; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = dbacc[mt][e];
     }
     __syncthreads();   // Mq and dLb published
 
@@ -761,10 +795,11 @@ bool chunk_bwd_supported(int dtype, int dk, int dv, int C) {
            (C == 16 || C == 32 || (C == 64 && dtype == 1));
 }
 
-size_t chunk_bwd_workspace(int B, int T, int H, int dk, int dv, int C) {
+size_t chunk_bwd_workspace(int dtype, int B, int T, int H, int dk, int dv, int C) {
     if (B <= 0 || T <= 0 || H <= 0 || C <= 0) return 0;
     const size_t NC = (static_cast<size_t>(T) + C - 1) / C;
-    return 2 * static_cast<size_t>(B) * H * NC * dv * dk * sizeof(float);
+    const size_t es = dtype == 1 ? 2 : 4;   // states kept in the input element type
+    return 2 * static_cast<size_t>(B) * H * NC * dv * dk * es;
 }
 
 hipError_t launch_chunk_bwd(int dtype, int dk, int C, const BwdArgs &a, hipStream_t stream) {

@@ -142,12 +142,19 @@ __device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, type
     }
 }
 
-// Sum over the 16 lanes that share l / 16 (one row of an accumulator tile).
+// x of another lane through a DPP lane pattern (no LDS traffic)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes that share l / 16 (one row of an accumulator tile): lane ^ 1 and
+// lane ^ 2 within each quad, then rotations of the 16-lane row by 4 and by 8.
 __device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += dpp_mov<0xb1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4e>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x128>(x);   // row_ror:8
     return x;
 }
 

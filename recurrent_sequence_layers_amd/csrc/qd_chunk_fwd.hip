@@ -202,10 +202,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
         const int t0 = n * CH;
         const int clen = min(CH, T - t0);
         if (args.Hs) {   // entry state of chunk n, [B][H][NC][d_v][d_k] (kept for the backward)
-            float *hs = args.Hs + (static_cast<size_t>(bh) * NC + n) * dv * DK +
-                        static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
+            R *hs = static_cast<R *>(args.Hs) + (static_cast<size_t>(bh) * NC + n) * dv * DK +
+                    static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(hs + 16 * t) = sT[t];
+            for (int t = 0; t < NKT; ++t) P::st4(hs + 16 * t, sT[t]);
         }
         lstore(clen);
         if (n + 1 < NC) gload(n + 1);
@@ -382,7 +382,10 @@ bool chunk_fwd_supported(int dtype, int dk, int dv, int C) {
 }
 
 hipError_t launch_chunk_fwd_states(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream) {
-    if (dtype == 1) return dk == 128 ? launch_dk<Bf16, 128>(C, a, stream) : launch_dk<Bf16, 64>(C, a, stream);
+    if (dtype == 1) {
+        if (C != 16) return launch_chunk_fwd_pipe_states(dk, C, a, stream);
+        return dk == 128 ? launch_typed<Bf16, 128, 16>(a, stream) : launch_typed<Bf16, 64, 16>(a, stream);
+    }
     return dk == 128 ? launch_dk<F32, 128>(C, a, stream) : launch_dk<F32, 64>(C, a, stream);
 }
 

@@ -263,7 +263,9 @@ constexpr int tile_mask(const int (&t)[4], int n) {
 
 // RAW: q and k arrive unnormalised and alpha, beta, lambda as logits; both are mapped
 // while the chunk is staged into LDS, so everything downstream is the same as without.
-template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW>
+// STATES: also keep every chunk's entry state S (bf16, [B][H][NC][d_v][d_k], ChunkArgs::Hs)
+// for the backward.
+template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW, bool STATES = false>
 struct PipeKernel {
     using Lay = PipeLayout<DK, CH>;
     static constexpr int NKT = DK / 16, NKP = DK / 32;
@@ -407,7 +409,6 @@ struct PipeKernel {
         const int rt = tid & (kRoleThreads - 1);  // thread index within its role
         const int r16 = lane & 15;
         const int g4 = lane >> 4;
-        const int tri = r16 >> 2, trp = r16 & 3;  // transpose-read lane split: r16 = 4 tri + trp
 
         const int nblk = gridDim.x;
         int logical = blockIdx.x;
@@ -558,6 +559,13 @@ struct PipeKernel {
             // ============================================================ I1
             if (is_scan) {
                 if (n >= 0) {
+                    if constexpr (STATES) {   // chunk n's entry state, rounded to bf16
+                        uint16_t *hs = static_cast<uint16_t *>(args.Hs) +
+                                       ((static_cast<size_t>(bh) * NC + n) * dv + dv0 + 16 * rw + r16) * DK;
+#pragma unroll
+                        for (int t = 0; t < NKT; ++t)
+                            *reinterpret_cast<bf16x4 *>(hs + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = Bf16::cvt(sT[t]);
+                    }
                     // Software-pipelined by hand: the fragments of the next tile are issued
                     // before the MFMAs of the current one, and scheduling fences keep the
                     // compiler from sinking each LDS read next to its use.
@@ -780,6 +788,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const C
     PipeKernel<DK, CH, HAS_A, HAS_L, RAW>::run(args);
 }
 
+template <int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_states_kernel(const ChunkArgs args) {
+    PipeKernel<DK, CH, HAS_A, HAS_L, false, true>::run(args);
+}
+
+template <int DK, int CH>
+hipError_t launch_pipe_states(const ChunkArgs &a, hipStream_t stream) {
+    const int grid = a.B * a.H * a.n_dvt;
+    if (grid == 0) return hipSuccess;
+    const bool ha = a.alpha != nullptr, hl = a.lam != nullptr;
+    const dim3 blk(kPipeThreads);
+    if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_states_kernel<DK, CH, true, true>), dim3(grid), blk, 0, stream, a);
+    else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_states_kernel<DK, CH, true, false>), dim3(grid), blk, 0, stream, a);
+    else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_states_kernel<DK, CH, false, true>), dim3(grid), blk, 0, stream, a);
+    else hipLaunchKernelGGL((chunk_fwd_pipe_states_kernel<DK, CH, false, false>), dim3(grid), blk, 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DK, int CH>
 hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
     const int grid = a.B * a.H * a.n_dvt;
@@ -801,6 +827,11 @@ hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
+    if (dk == 128) return C == 64 ? launch_pipe_states<128, 64>(a, stream) : launch_pipe_states<128, 32>(a, stream);
+    return C == 64 ? launch_pipe_states<64, 64>(a, stream) : launch_pipe_states<64, 32>(a, stream);
+}
 
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
     if (dk == 128) {

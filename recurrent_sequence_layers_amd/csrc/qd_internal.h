@@ -15,7 +15,8 @@ struct ChunkArgs {
     int B, T, H, dv;
     int n_dvt;                      // number of 64-wide value-column tiles, d_v / 64
     bool raw = false;               // q, k unnormalised and gates as logits (bf16 C = 32, 64 only)
-    float *Hs = nullptr;            // [B][H][NC][d_v][d_k]: every chunk's entry state (generic kernel only)
+    void *Hs = nullptr;             // [B][H][NC][d_v][d_k] in the element type: every chunk's entry state
+                                    // (generic kernel only)
 };
 
 // Layer backward (qd_chunk_bwd.hip).  Gradients of sum(o dO) + sum(S_T dST).
@@ -28,7 +29,8 @@ struct BwdArgs {
     void *g_q, *g_k, *g_v;          // gradients: [B][T][H][d_k] / [B][T][H][d_v]
     float *g_alpha, *g_beta, *g_lam; // [B][T][H]; g_alpha/g_lam may be null
     float *g_S0;                    // [B][H][d_v][d_k] or null
-    float *Hs, *dHs;                // workspace: [B][H][NC][d_v][d_k] entry states and exit-state gradients
+    void *Hs, *dHs;                 // workspace: [B][H][NC][d_v][d_k] entry states and exit-state gradients,
+                                    // in the element type
     int B, T, H, dv;
     int n_dvt;
 };
@@ -46,8 +48,10 @@ struct StepArgs {
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t stream);
 
-// bf16 chunk forward, eight-wave pipelined kernel (qd_chunk_fwd_pipe.hip).
+// bf16 chunk forward, eight-wave pipelined kernel (qd_chunk_fwd_pipe.hip), C = 32 or 64;
+// the _states variant also writes ChunkArgs::Hs.
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream);
 
 // Segmented schedule (qd_segment.hip) for long sequences over few heads: the number of
 // segments P the sequence is cut into (1 = the single-pass schedule), the workspace it
@@ -57,13 +61,13 @@ size_t chunk_fwd_segment_workspace(int B, int T, int H, int dk, int dv, int P);
 hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
                                       hipStream_t stream);
 
-// The generic (four-wave) forward kernel for every dtype and C, which can keep the
-// chunk entry states (ChunkArgs::Hs) and skip the output (o == null).
+// The forward keeping every chunk's entry state (ChunkArgs::Hs, element type) with no
+// output (o == null): the eight-wave kernel for bf16 C = 32, 64, else the generic one.
 hipError_t launch_chunk_fwd_states(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
 
 // Backward: workspace size and the three passes (states, reverse scan, per-chunk gradients).
 bool chunk_bwd_supported(int dtype, int dk, int dv, int C);
-size_t chunk_bwd_workspace(int B, int T, int H, int dk, int dv, int C);
+size_t chunk_bwd_workspace(int dtype, int B, int T, int H, int dk, int dv, int C);
 hipError_t launch_chunk_bwd(int dtype, int dk, int C, const BwdArgs &a, hipStream_t stream);
 
 // Whether an instance exists for these sizes (checked before launching).
