@@ -9,7 +9,8 @@ In the same run the decode step is timed on 256 sequences x 16 heads (fp32 state
 resident, one token per call) and reported as achieved HBM GB/s, and the layer is
 timed with lambda = 0 (Gated DeltaNet), with lambda = 0 and alpha = 1 (DeltaNet), and
 on the long-context workload (B=1, T=65536, S0 given), each reported beside the
-headline figure.  Kernel
+headline figure, and the layer backward (qdelta_chunk_bwd, all three passes) is timed on
+the headline workload with dO ~ N(0, 1).  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -61,6 +62,14 @@ def chunk_algorithmic(B, T, H, dk, dv, C, es):
     bytes_ = toks * (2 * dk + 2 * dv) * es + toks * 3 * 4 + B * H * dv * dk * 4   # q,k,v,o; gates; S_T
     flops = toks * (6 * C * dk + 4 * C * dv + 6 * dk * dv)
     return bytes_, flops
+
+
+def bwd_algorithmic(B, T, H, dk, dv, es):
+    """Bytes one backward call must move at least: q, k, v, dO and the gates read once; dq,
+    dk, dv and the gate gradients written once (the chunk states the passes exchange are a
+    choice of the schedule, not counted)."""
+    toks = B * T * H
+    return toks * (2 * dk + 2 * dv) * es + toks * (2 * dk + dv) * es + toks * 3 * 4 * 2
 
 
 def step_algorithmic(N, H, dk, dv, es):
@@ -140,6 +149,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the Gated DeltaNet, DeltaNet and long-context timings (used for the "
                          "profiled runs, so that per-kernel statistics cover the headline workload only)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the layer backward on the headline workload (profiled runs of its kernels)")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device-to-device copies, the reference the HBM "
@@ -171,6 +182,33 @@ def main():
     B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
     log(f"[bench] generating {name} on device")
     x = inputs.workload_inputs(name, seed=args.seed, device="cuda")
+
+    def backward_run(steps):
+        """The layer backward on the headline workload: dO ~ N(0, 1), dS_T = 0, S0 = 0."""
+        dO, _ = inputs.upstream_grads(B, T, H, dk, dv, "bf16", seed=args.seed + 5, device="cuda")
+        nws = qd.qdelta_chunk_bwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        grads = qd.qdelta_chunk_bwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, dO, None, C=C, workspace=ws)
+        bf = lambda: qd.qdelta_chunk_bwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, dO, None, C=C,
+                                         workspace=ws, out=grads)
+        for _ in range(args.warmup):
+            bf()
+        torch.cuda.synchronize()
+        b_s, _ = time_region(torch, bf, steps)
+        b_ms = b_s / steps * 1e3
+        bbytes = bwd_algorithmic(B, T, H, dk, dv, 2)
+        log(f"[bench] layer backward {b_ms:.4f} ms/call, {B * T / (b_ms * 1e-3) / 1e6:.2f} M tokens/s")
+        del dO, ws, grads
+        return {"workload": "gradients of the headline layer forward (dq, dk, dv, dalpha, dbeta, dlambda; "
+                            "dO ~ N(0,1), dS_T = 0), three passes: forward keeping the chunk states, reverse "
+                            "state-gradient scan, per-chunk gradients",
+                "C": C, "steps": steps, "ms_per_call": b_ms, "tokens_per_s": B * T / (b_ms * 1e-3),
+                "workspace_bytes": nws, "algorithmic_bytes_per_call": bbytes,
+                "hbm_frac": bbytes / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+    if args.backward_only:
+        print(json.dumps({"backward": backward_run(args.steps)}), flush=True)
+        return
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     fwd = lambda: qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, C=C, o=o, S_T=S_T)
@@ -224,6 +262,9 @@ def main():
         del vx, vo, vS, vws
     torch.cuda.synchronize()
     if not args.headline_only:
+        bwd = backward_run(max(5, args.steps // 5))
+        bwd["time_ratio_to_headline"] = bwd["ms_per_call"] / ms_per_step
+        variants["layer_1p3b_backward"] = bwd
         # the headline layer through the fused prologue: unnormalised q, k and gate logits
         # (qdelta_chunk_fwd_raw), against the headline call on prepared inputs
         g = torch.Generator(device=dev).manual_seed(args.seed + 3)
