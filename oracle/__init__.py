@@ -11,6 +11,8 @@ Contents
   * ``step_rw``     -- one step with explicit read and write directions.
   * ``qdelta_bwd``  -- gradients of ``qdelta_fwd`` by the hand-derived adjoint of
                        the recurrence, token by token in reverse (C, fp64).
+  * ``qed_fwd``     -- the QED / GDN-2 recurrence with per-channel decay and vector
+                       erase and write gates (the QED reading notes §2.1-2.2; C, fp64).
   * ``chunk_form``  -- the chunkwise WY/UT-transform algebra in fp64 numpy
                        (module ``oracle.chunk_form``), used to pin that the
                        chunked algebra reproduces the recurrence.
@@ -46,6 +48,8 @@ def _load():
                                                 ctypes.c_int, ctypes.c_int]
     lib.oracle_qdelta_bwd.restype = ctypes.c_int
     lib.oracle_qdelta_bwd.argtypes = [_dp] * 16 + [ctypes.c_int] * 6
+    lib.oracle_qed_fwd.restype = ctypes.c_int
+    lib.oracle_qed_fwd.argtypes = [_dp] * 10 + [ctypes.c_int] * 6
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -134,3 +138,20 @@ def qdelta_bwd(q, k, v, alpha, beta, lam, S0, dO, dST=None, nthreads: int = 0):
     if rc != 0:
         raise ValueError("oracle_qdelta_bwd failed (%d)" % rc)
     return out
+
+
+def qed_fwd(q, k, v, g, b, w, lam_h, S0=None, nthreads: int = 0, want_o: bool = True):
+    """QED / GDN-2 recurrence.  q, k, g, b [B,T,H,dk]; v, w [B,T,H,dv]; lam_h [H] (the
+    head's strength; 0 gives GDN-2); S0 [B,H,dv,dk] or None.  State convention as
+    ``qdelta_fwd`` (d_v x d_k).  Returns (o [B,T,H,dv] or None, S_T [B,H,dv,dk])."""
+    q, k, v, g, b, w = (_f64(t) for t in (q, k, v, g, b, w))
+    lam_h, S0 = _f64(lam_h), _f64(S0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.empty((B, T, H, dv)) if want_o else None
+    S_T = np.empty((B, H, dv, dk))
+    rc = _load().oracle_qed_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S0),
+                                _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_qed_fwd rejected its arguments")
+    return o, S_T

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "liboracle_qdelta.so")
 def build(verbose: bool = False) -> str:
     cc = os.environ.get("ORACLE_CC", "gcc")
     cmd = [cc, "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC]
+           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -26,6 +26,7 @@
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see build_oracle.py).
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
@@ -312,4 +313,62 @@ int oracle_qdelta_bwd(const double *q, const double *k, const double *v,
         free(ckpt); free(states); free(G);
     }
     return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------ QED / GDN-2
+ * The QED reading notes' update (page "The Query Knows What to Forget" reading notes,
+ * §2.1 and §2.2, the boxed update), written in this file's state convention: their
+ * state is K x V, the transpose of ours, so S here is d_v x d_k and their S^T x is
+ * our S x.  Per token, with per-key-channel log decay g (d_k), erase gate b (d_k),
+ * write gate w (d_v) and the head's strength lambda_h:
+ *
+ *     S_bar = S_{t-1} Diag(exp g)              (decay each key column)
+ *     u     = b . q                             (gate the query first ...)
+ *     d     = u - k (k^T u)                     (... then project off k; |k| = 1)
+ *     a     = b . k + lambda_h d                (erase / read direction)
+ *     r     = w . v - S_bar a                   (residual, d_v)
+ *     S_t   = S_bar + r k^T                     (rank-one write along k)
+ *     o_t   = S_t q
+ *
+ * lambda_h = 0 is GDN-2 (same page, §2.1).  Rows of S evolve independently.
+ */
+int oracle_qed_fwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *b, const double *w, const double *lam_h,
+                   const double *S0, double *o, double *S_T,
+                   int B, int T, int H, int dk, int dv, int nthreads)
+{
+    long long unit, n_units;
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1 || dk > 1024) return -1;
+    if (!S_T) return -1;
+    if ((long long)B * T * H > 0 && (!q || !k || !v || !g || !b || !w || !lam_h)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    n_units = (long long)B * H * dv;
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nthreads)
+    for (unit = 0; unit < n_units; ++unit) {
+        int bb = (int)(unit / ((long long)H * dv));
+        int h = (int)((unit / dv) % H);
+        int i = (int)(unit % dv);
+        double *s = S_T + (((size_t)bb * H + h) * dv + i) * dk;
+        double u[1024], a[1024];
+        int t, j;
+        if (S0) memcpy(s, S0 + (((size_t)bb * H + h) * dv + i) * dk, sizeof(double) * dk);
+        else memset(s, 0, sizeof(double) * dk);
+        for (t = 0; t < T; ++t) {
+            size_t tok = ((size_t)bb * T + t) * H + h;
+            const double *qt = q + tok * dk, *kt = k + tok * dk;
+            const double *gt = g + tok * dk, *bt = b + tok * dk;
+            double ku = 0.0, pred = 0.0, r, out = 0.0;
+            for (j = 0; j < dk; ++j) u[j] = bt[j] * qt[j];
+            for (j = 0; j < dk; ++j) ku += kt[j] * u[j];
+            for (j = 0; j < dk; ++j) a[j] = bt[j] * kt[j] + lam_h[h] * (u[j] - kt[j] * ku);
+            for (j = 0; j < dk; ++j) s[j] = s[j] * exp(gt[j]);              /* S_bar */
+            for (j = 0; j < dk; ++j) pred += s[j] * a[j];                     /* (S_bar a)_i */
+            r = w[tok * dv + i] * v[tok * dv + i] - pred;
+            for (j = 0; j < dk; ++j) s[j] = s[j] + r * kt[j];                 /* + r k^T */
+            for (j = 0; j < dk; ++j) out += s[j] * qt[j];
+            if (o) o[tok * dv + i] = out;
+        }
+    }
+    return 0;
 }
