@@ -357,3 +357,64 @@ def test_chunked_backward_matches_oracle(T, C, dk, dv):
     for n in ref:
         err = np.abs(got[n] - ref[n]).max() / np.abs(ref[n]).max()
         assert err < 1e-10, (n, err)
+
+
+# ---------------------------------------------------------------- QED / GDN-2 chunk form
+def qed_kernel_form(q, k, v, g, b, w, lam_h, S0, C, nb=16):
+    """QED chunk form with per-channel decay, in the kernels' arrangement (S^T held,
+    d_k x d_v).  Within a chunk, with the per-channel cumulative log decay
+    Gm_t = sum_{s<=t} g_s and the erase direction a_t = b.k + lam_h P_k(b.q):
+        (I + L) R = W.V - At S^T,   At_t = a_t . exp(Gm_t)
+        O = Qt S^T + M R,           Qt_t = q_t . exp(Gm_t)
+        S'^T = diag(exp Gm_C) S^T + Kh^T R,   Kh_j = k_j . exp(Gm_C - Gm_j)
+    with L[t,j] = sum_c a_t[c] k_j[c] exp(Gm_t[c] - Gm_j[c]) (j < t) and M likewise with q
+    (j <= t).  L and M are formed from nb x nb blocks: block (I, J < I) as the product of
+    row operands x_t . exp(Gm_t - Gm_r) and column operands k_j . exp(Gm_r - Gm_j) with r the
+    first token of block I (every factor <= 1); diagonal blocks with r the block's middle
+    token (factors within 8 tokens of decay of 1)."""
+    B, Tn, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, Tn, H, dv)); S_T = np.zeros((B, H, dv, dk))
+    for bb in range(B):
+        for h in range(H):
+            ST = np.zeros((dk, dv)) if S0 is None else S0[bb, h].T.copy()
+            for t0 in range(0, Tn, C):
+                n = min(C, Tn - t0)
+                sl = slice(t0, t0 + n)
+                Q, K, V = q[bb, sl, h], k[bb, sl, h], v[bb, sl, h]
+                Bg, Wg = b[bb, sl, h], w[bb, sl, h]
+                Gm = np.cumsum(g[bb, sl, h], axis=0)                      # n x dk
+                U = Bg * Q
+                A = Bg * K + lam_h[h] * (U - K * np.sum(K * U, axis=1, keepdims=True))
+                L = np.zeros((n, n)); M = np.zeros((n, n))
+                for I in range(0, n, nb):
+                    for J in range(0, I + 1, nb):
+                        rI, cJ = slice(I, min(I + nb, n)), slice(J, min(J + nb, n))
+                        r = I if J < I else min(I + nb // 2, n - 1)
+                        ker = K[cJ] * np.exp(Gm[r] - Gm[cJ])
+                        L[rI, cJ] = (A[rI] * np.exp(Gm[rI] - Gm[r])) @ ker.T
+                        M[rI, cJ] = (Q[rI] * np.exp(Gm[rI] - Gm[r])) @ ker.T
+                L = np.tril(L, -1); M = np.tril(M)
+                R = np.linalg.solve(np.eye(n) + L, Wg * V - (A * np.exp(Gm)) @ ST)
+                o[bb, sl, h] = (Q * np.exp(Gm)) @ ST + M @ R
+                ST = np.exp(Gm[-1])[:, None] * ST + (K * np.exp(Gm[-1] - Gm)).T @ R
+            S_T[bb, h] = ST.T
+    return o, S_T
+
+
+@pytest.mark.parametrize("T,C,nb", [(64, 16, 16), (150, 32, 16), (97, 64, 16), (33, 16, 4), (70, 64, 8)])
+def test_qed_chunk_form_matches_recurrence(T, C, nb):
+    r = np.random.default_rng(T * C)
+    B, H, dk, dv = 2, 2, 8, 6
+    q = r.standard_normal((B, T, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((B, T, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, dv))
+    g = -np.log1p(np.exp(r.standard_normal((B, T, H, dk)) - 1.0))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H, dk))))
+    w = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H, dv))))
+    lam = 0.25 / (1.0 + np.exp(-r.standard_normal(H)))
+    S0 = 0.3 * r.standard_normal((B, H, dv, dk))
+    o, S = qed_kernel_form(q, k, v, g, b, w, lam, S0, C, nb)
+    ro, rS = oracle.qed_fwd(q, k, v, g, b, w, lam, S0)
+    assert np.abs(o - ro).max() / np.abs(ro).max() < 1e-11
+    assert np.abs(S - rS).max() / np.abs(rS).max() < 1e-11
