@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define QDELTA_ABI_VERSION 3
+#define QDELTA_ABI_VERSION 4
 
 typedef enum qd_status {
     QD_OK = 0,
@@ -181,6 +181,39 @@ int qdelta_chunk_bwd(const void *q, const void *k, const void *v,
                      float *dlambda, float *dS0,
                      int B, int T, int H, int d_k, int d_v, int C, int dtype,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * QED / GDN-2 layer (page "The Query Knows What to Forget", reading notes, §2.1 GDN-2
+ * update and §2.2 the boxed QED update), in this header's d_v x d_k state convention
+ * (the notes' K x V state transposed; their S^T x is S x here).  Per (b, h), per token:
+ *
+ *     S_bar = S_{t-1} Diag(exp g_t)                   (per key channel decay)
+ *     a_t   = b_t . k_t + lambda_h (u_t - k_t (k_t . u_t)),   u_t = b_t . q_t
+ *     S_t   = S_bar + (w_t . v_t - S_bar a_t) k_t^T,   o_t = S_t q_t
+ *
+ * lambda_h = 0 is GDN-2.  q, k, v, o, S0, S_T, dtype, B, T, H, d_k, d_v, stream as for
+ * qdelta_chunk_fwd; additionally (all fp32, device, 16-byte aligned where a row is):
+ *   g         [B][T][H][d_k] log decay (<= 0 in the layer; the chunk kernel needs
+ *             exp(-(sum of any 8 consecutive g)) within the fp32 range, i.e. per-token
+ *             log decays above about -11)
+ *   b         [B][T][H][d_k] erase gate
+ *   w         [B][T][H][d_v] write gate
+ *   lambda_h  [H] strength of the query-derived direction per head.
+ * q and k are expected L2-normalised (the projection uses |k| = 1).  C is the chunk
+ * length: 16 or 32 for bf16, 16 for fp32 (QD_ERR_UNSUPPORTED otherwise); it changes
+ * rounding only.  S_T may equal S0; o must not overlap any input.  No workspace.
+ */
+int qdelta_qed_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *b, const float *w, const float *lambda_h,
+                         const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int d_k, int d_v, int C, int dtype, void *stream);
+
+/* One QED / GDN-2 decode step for N sequences x H heads (the same update for a single
+ * token): q, k [N][H][d_k], v, o [N][H][d_v], g, b [N][H][d_k], w [N][H][d_v],
+ * lambda_h [H]; S [N][H][d_v][d_k] fp32 updated in place.  d_k, d_v in {64, 128}. */
+int qdelta_qed_step(const void *q, const void *k, const void *v,
+                    const float *g, const float *b, const float *w, const float *lambda_h,
+                    float *S, void *o, int N, int H, int d_k, int d_v, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,10 @@ def load_library():
     lib.qdelta_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
     lib.qdelta_step_raw.restype = i
     lib.qdelta_step_raw.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 5 + [vp]
+    lib.qdelta_qed_chunk_fwd.restype = i
+    lib.qdelta_qed_chunk_fwd.argtypes = [vp] * 10 + [i] * 7 + [vp]
+    lib.qdelta_qed_step.restype = i
+    lib.qdelta_qed_step.argtypes = [vp] * 9 + [i] * 5 + [vp]
     lib.qdelta_chunk_bwd_workspace_bytes.restype = sz
     lib.qdelta_chunk_bwd_workspace_bytes.argtypes = [i] * 7
     lib.qdelta_chunk_bwd.restype = i
@@ -195,6 +199,56 @@ def qdelta_chunk_bwd(q, k, v, alpha, beta, lam, S0, d_o, dS_T=None, C: int = 64,
                               ws_ptr, ws_bytes, ctypes.c_void_p(stream))
     _raise(rc, "qdelta_chunk_bwd")
     return out
+
+
+def qdelta_qed_chunk_fwd(q, k, v, g, b, w, lam_h, S0=None, C: int = 32, o=None, S_T=None, want_state=True,
+                         stream=None):
+    """QED / GDN-2 layer forward.  q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or bf16); g, b
+    [B,T,H,d_k], w [B,T,H,d_v], lam_h [H], S0 [B,H,d_v,d_k] fp32.  Returns (o, S_T)."""
+    import torch
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+    _check(g, "g", torch.float32, (B, T, H, dk)); _check(b, "b", torch.float32, (B, T, H, dk))
+    _check(w, "w", torch.float32, (B, T, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (B, T, H, dv))
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.qdelta_qed_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S0),
+                                  _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), _dtype_code(dt), ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_qed_chunk_fwd")
+    return o, S_T
+
+
+def qdelta_qed_step(q, k, v, g, b, w, lam_h, S, o=None, stream=None):
+    """One QED / GDN-2 decode step.  q, k [N,H,d_k], v [N,H,d_v]; g, b [N,H,d_k], w [N,H,d_v],
+    lam_h [H] fp32; S [N,H,d_v,d_k] fp32 updated in place.  Returns o [N,H,d_v]."""
+    import torch
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+    _check(g, "g", torch.float32, (N, H, dk)); _check(b, "b", torch.float32, (N, H, dk))
+    _check(w, "w", torch.float32, (N, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
+    _check(S, "S", torch.float32, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (N, H, dv))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.qdelta_qed_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S), _ptr(o),
+                             N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_qed_step")
+    return o
 
 
 def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None, raw: bool = False):

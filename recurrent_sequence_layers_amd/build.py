@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqdelta.so")
 SOURCES = ["qd_capi.hip", "qd_chunk_bwd.hip", "qd_chunk_fwd.hip", "qd_chunk_fwd_pipe.hip", "qd_segment.hip",
-           "qd_step.hip"]
+           "qd_qed.hip", "qd_step.hip"]
 ARCH = os.environ.get("QDELTA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

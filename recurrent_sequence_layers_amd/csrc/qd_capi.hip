@@ -95,6 +95,63 @@ int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *a
     return err == hipSuccess ? QD_OK : QD_ERR_HIP;
 }
 
+int qdelta_qed_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *b, const float *w,
+                         const float *lambda_h, const float *S0, void *o, float *S_T, int B, int T, int H, int d_k,
+                         int d_v, int C, int dtype, void *stream) {
+    if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::qed_chunk_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
+    const long long bh = static_cast<long long>(B) * H;
+    if (bh == 0) return QD_OK;
+    if (bh * (d_v / 64) > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    const long long ntok = bh * T;
+    if (!lambda_h || (ntok > 0 && (!q || !k || !v || !g || !b || !w || !o))) return QD_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(g) || !aligned16(b) ||
+        !aligned16(S0) || !aligned16(S_T))
+        return QD_ERR_INVALID_ARG;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t o_bytes = static_cast<size_t>(ntok) * d_v * es, st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
+    const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, gb_bytes = static_cast<size_t>(ntok) * d_k * 4;
+    const size_t w_bytes = static_cast<size_t>(ntok) * d_v * 4;
+    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {v, o_bytes}, {g, gb_bytes},
+                                                      {b, gb_bytes}, {w, w_bytes}, {lambda_h, H * sizeof(float)}};
+    for (const auto &i : ins)
+        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S_T, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
+    if (overlaps(o, o_bytes, S0, st_bytes) || overlaps(o, o_bytes, S_T, st_bytes)) return QD_ERR_INVALID_ARG;
+    if (S_T && S0 && S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)) return QD_ERR_INVALID_ARG;
+    qd::QedChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w; a.lam_h = lambda_h;
+    a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.B = B; a.T = T; a.H = H; a.dv = d_v; a.n_dvt = d_v / 64;
+    const hipError_t err = qd::launch_qed_chunk(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
+int qdelta_qed_step(const void *q, const void *k, const void *v, const float *g, const float *b, const float *w,
+                    const float *lambda_h, float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
+                    void *stream) {
+    if (N < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::step_supported(dtype, d_k, d_v)) return QD_ERR_UNSUPPORTED;
+    const long long nh = static_cast<long long>(N) * H;
+    if (nh == 0) return QD_OK;
+    if (nh > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !g || !b || !w || !lambda_h || !S || !o) return QD_ERR_INVALID_ARG;
+    if (!aligned16(S) || !aligned16(g) || !aligned16(b)) return QD_ERR_INVALID_ARG;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t st_bytes = static_cast<size_t>(nh) * d_v * d_k * 4, o_bytes = static_cast<size_t>(nh) * d_v * es;
+    const struct { const void *p; size_t n; } ins[] = {
+        {q, static_cast<size_t>(nh) * d_k * es}, {k, static_cast<size_t>(nh) * d_k * es}, {v, o_bytes},
+        {g, static_cast<size_t>(nh) * d_k * 4}, {b, static_cast<size_t>(nh) * d_k * 4},
+        {w, static_cast<size_t>(nh) * d_v * 4}, {lambda_h, H * sizeof(float)}};
+    for (const auto &i : ins)
+        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
+    if (overlaps(o, o_bytes, S, st_bytes)) return QD_ERR_INVALID_ARG;
+    qd::QedStepArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w; a.lam_h = lambda_h;
+    a.S = S; a.o = o; a.N = N; a.H = H;
+    const hipError_t err = qd::launch_qed_step(dtype, d_k, d_v, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

@@ -44,6 +44,30 @@ struct StepArgs {
     bool raw = false;               // q, k unnormalised and gates as logits
 };
 
+// QED / GDN-2 (qd_qed.hip): per-key-channel log decay g and erase gate b [..][d_k] fp32,
+// write gate w [..][d_v] fp32, strength lam_h [H] fp32.
+struct QedChunkArgs {
+    const void *q, *k, *v;          // [B][T][H][d_k] / [B][T][H][d_v]
+    const float *g, *b, *w;         // [B][T][H][d_k], [B][T][H][d_k], [B][T][H][d_v]
+    const float *lam_h;             // [H]
+    const float *S0;                // [B][H][d_v][d_k] or null
+    void *o;                        // [B][T][H][d_v]
+    float *S_T;                     // [B][H][d_v][d_k] or null
+    int B, T, H, dv;
+    int n_dvt;
+};
+struct QedStepArgs {
+    const void *q, *k, *v;          // [N][H][d_k] / [N][H][d_v]
+    const float *g, *b, *w;         // [N][H][d_k], [N][H][d_k], [N][H][d_v]
+    const float *lam_h;             // [H]
+    float *S;                       // [N][H][d_v][d_k], in place
+    void *o;                        // [N][H][d_v]
+    int N, H;
+};
+bool qed_chunk_supported(int dtype, int dk, int dv, int C);
+hipError_t launch_qed_chunk(int dtype, int dk, int C, const QedChunkArgs &a, hipStream_t stream);
+hipError_t launch_qed_step(int dtype, int dk, int dv, const QedStepArgs &a, hipStream_t stream);
+
 // dtype: 0 = fp32, 1 = bf16.  Return hipSuccess or the launch error.
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t stream);

@@ -1,0 +1,444 @@
+// QED / GDN-2 layer for gfx950: per-key-channel decay, vector erase and write gates and
+// the query-derived erase direction (page "The Query Knows What to Forget" reading notes,
+// §2.1 and §2.2, the boxed update), in the d_v x d_k state convention of this library
+// (the notes' K x V state transposed, so their S^T x is S x here):
+//
+//   S_bar = S_{t-1} Diag(exp g_t)
+//   a_t   = b_t . k_t + lambda_h (u_t - k_t (k_t . u_t)),   u_t = b_t . q_t
+//   r_t   = w_t . v_t - S_bar a_t
+//   S_t   = S_bar + r_t k_t^T,       o_t = S_t q_t
+//
+// lambda_h = 0 is GDN-2.  Two kernels:
+//
+// qed_step_kernel: one token for N sequences x H heads, the decode form.  Eight lanes
+//   share a state row as in the Q-Delta step kernel; the row's exp(g), a, q and k are
+//   formed once per lane for its columns (k . u reduced over the eight lanes).
+//
+// qed_chunk_kernel: the chunked forward.  Within a chunk, with the per-channel cumulative
+//   log decay Gm_t = sum_{s<=t} g_s (the recurrence unrolled; derived here, the notes give
+//   only the step):
+//     (I + L) R = W.V - At S^T,          At_t = a_t . exp(Gm_t)
+//     O = Qt S^T + M R,                  Qt_t = q_t . exp(Gm_t)
+//     S'^T = diag(exp Gm_C) S^T + Kh^T R,  Kh_j = k_j . exp(Gm_C - Gm_j)
+//   with L[t,j] = sum_c a_t[c] k_j[c] exp(Gm_t[c] - Gm_j[c]) (j < t) and M the same with
+//   q (j <= t).  L and M are built from 16 x 16 blocks as products of row operands
+//   x_t . exp(Gm_t - Gm_r) and column operands k_j . exp(Gm_r - Gm_j): for a block below
+//   the diagonal r is the first token of the row block (every factor <= 1); for a
+//   diagonal block r is its ninth token, so a factor exceeds 1 by at most eight tokens of
+//   decay.  That is the kernel's domain: exp(-(g_s + ... + g_{s+7})) must stay within the
+//   fp32 range (per-token log decays above about -11).  T = (I + L)^-1 uses the shared
+//   blocked inverse; the state-dependent part is the generic forward's, one wave per 16
+//   value columns holding S^T in MFMA accumulators.
+#include "qd_chunk_common.h"
+#include "qd_device.h"
+#include "qd_internal.h"
+
+namespace qd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 8;
+constexpr int kDVT = 64;
+
+__device__ __forceinline__ float group8_sum(float x) {
+    x += __shfl_xor(x, 1, kLanesPerRow);
+    x += __shfl_xor(x, 2, kLanesPerRow);
+    x += __shfl_xor(x, 4, kLanesPerRow);
+    return x;
+}
+
+// ------------------------------------------------------------------ decode step
+template <class P, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void qed_step_kernel(const QedStepArgs args) {
+    using R = typename P::R;
+    constexpr int NG = DK / (4 * kLanesPerRow);
+    constexpr int ROWS_PER_PASS = kWave / kLanesPerRow;
+    constexpr int ROWS_PER_WAVE = DV / 4;
+    constexpr int NPASS = ROWS_PER_WAVE / ROWS_PER_PASS;
+    static_assert(NPASS >= 1 && NG >= 1, "unsupported step shape");
+
+    const int nh = blockIdx.x;
+    const int h = nh % args.H;
+    const int lane = lane_id(), wave = wave_id();
+    const int sub = lane % kLanesPerRow, grp = lane / kLanesPerRow;
+
+    const R *gq = static_cast<const R *>(args.q) + static_cast<size_t>(nh) * DK;
+    const R *gk = static_cast<const R *>(args.k) + static_cast<size_t>(nh) * DK;
+    const R *gv = static_cast<const R *>(args.v) + static_cast<size_t>(nh) * DV;
+    const float *gg = args.g + static_cast<size_t>(nh) * DK;
+    const float *gb = args.b + static_cast<size_t>(nh) * DK;
+    const float *gw = args.w + static_cast<size_t>(nh) * DV;
+    R *go = static_cast<R *>(args.o) + static_cast<size_t>(nh) * DV;
+    float *S = args.S + static_cast<size_t>(nh) * DV * DK;
+
+    f32x4 s[NPASS][NG];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = wave * ROWS_PER_WAVE + p * ROWS_PER_PASS + grp;
+#pragma unroll
+        for (int m = 0; m < NG; ++m)
+            s[p][m] = *reinterpret_cast<const f32x4 *>(S + static_cast<size_t>(row) * DK + 4 * (m * kLanesPerRow + sub));
+    }
+
+    const float lam = args.lam_h[h];
+    f32x4 kk[NG], qq[NG], aa[NG], dec[NG];
+    float ku = 0.f, kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < NG; ++m) {
+        const int c = 4 * (m * kLanesPerRow + sub);
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(gg + c);
+        const f32x4 bm = *reinterpret_cast<const f32x4 *>(gb + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kk[m][i] = P::to_f32(gk[c + i]);
+            qq[m][i] = P::to_f32(gq[c + i]);
+            dec[m][i] = __expf(gm[i]);
+            aa[m][i] = bm[i] * qq[m][i];            // u = b . q for now
+            ku += kk[m][i] * aa[m][i];
+            kq += kk[m][i] * qq[m][i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aa[m][i] = bm[i] * kk[m][i] + lam * aa[m][i];   // b.k + lambda u
+    }
+    ku = group8_sum(ku);
+    kq = group8_sum(kq);
+#pragma unroll
+    for (int m = 0; m < NG; ++m) aa[m] -= (lam * ku) * kk[m];                   // - lambda k (k . u)
+
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = wave * ROWS_PER_WAVE + p * ROWS_PER_PASS + grp;
+        float pred = 0.f, c = 0.f;
+#pragma unroll
+        for (int m = 0; m < NG; ++m) {
+            s[p][m] *= dec[m];                       // S_bar
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pred += s[p][m][i] * aa[m][i];
+                c += s[p][m][i] * qq[m][i];
+            }
+        }
+        pred = group8_sum(pred);
+        c = group8_sum(c);
+        const float r = gw[row] * P::to_f32(gv[row]) - pred;
+#pragma unroll
+        for (int m = 0; m < NG; ++m)
+            *reinterpret_cast<f32x4 *>(S + static_cast<size_t>(row) * DK + 4 * (m * kLanesPerRow + sub)) =
+                s[p][m] + r * kk[m];
+        if (sub == 0) go[row] = P::from_f32(c + r * kq);   // o = S_bar q + r (k . q)
+    }
+}
+
+// ------------------------------------------------------------------ chunked forward
+template <class P, int DK, int CH>
+struct QedLayout {
+    static constexpr int PAD = 16 / P::kBytes;
+    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
+    static constexpr int PF = DK + 4, PW = kDVT + 4;     // fp32 pitches
+    static constexpr int NQ = CH * PK, NCC = CH * PC;
+    // element-type arrays: q, k, a; the decayed At, Qt, Kh; L, M, T; O staging
+    static constexpr int oQ = 0, oK = oQ + NQ, oA = oK + NQ, oAt = oA + NQ, oQt = oAt + NQ, oKh = oQt + NQ;
+    static constexpr int oL = oKh + NQ, oM = oL + NCC, oT = oM + NCC, oO = oT + NCC;
+    static constexpr int nR = oO + CH * PV;
+    // fp32 arrays: Gm (cumulative log decay), w . v tile, exp(Gm_C)
+    static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + CH * PW;
+    static constexpr int nF = fE + DK;
+    static constexpr int bytes = ((nR * P::kBytes + 15) / 16) * 16 + nF * 4;
+    static_assert((PK * P::kBytes) % 16 == 0 && (PC * P::kBytes) % 16 == 0 && (PV * P::kBytes) % 16 == 0,
+                  "row pitches keep 16-byte alignment");
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
+};
+
+template <class P, int DK, int CH>
+__global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkArgs args) {
+    using R = typename P::R;
+    using F = typename P::F;
+    using Lay = QedLayout<P, DK, CH>;
+    constexpr int NKT = DK / 16, NCT = CH / 16;
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV, PF = Lay::PF, PW = Lay::PW;
+    constexpr int EPV = 16 / P::kBytes;
+    constexpr int VPRV = kDVT / EPV;
+    constexpr int TPR = kThreads / CH;             // staging threads per chunk row
+    constexpr int CPT = DK / TPR;                  // key columns per staging thread
+    static_assert(CPT % 4 == 0 && CPT <= 32, "staging split");
+    constexpr int NPAIR = NCT * (NCT + 1) / 2;
+    static_assert(NPAIR <= 4, "one 16 x 16 block pair per wave");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
+    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
+    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+    R *const Ats = reinterpret_cast<R *>(smem) + Lay::oAt;
+    R *const Qts = reinterpret_cast<R *>(smem) + Lay::oQt;
+    R *const Khs = reinterpret_cast<R *>(smem) + Lay::oKh;
+    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;
+    R *const Ms = reinterpret_cast<R *>(smem) + Lay::oM;
+    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;
+    R *const Os = reinterpret_cast<R *>(smem) + Lay::oO;
+    float *const fbase = reinterpret_cast<float *>(smem + ((Lay::nR * P::kBytes + 15) / 16) * 16);
+    float *const Gs = fbase + Lay::fG;
+    float *const WVs = fbase + Lay::fW;
+    float *const eGC = fbase + Lay::fE;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    const int nblk = gridDim.x;
+    int logical = blockIdx.x;
+    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int dvt = logical % args.n_dvt;
+    const int bh = logical / args.n_dvt;
+    const int b = bh / args.H, h = bh % args.H;
+    const int T = args.T, H = args.H, dv = args.dv;
+    const int dv0 = dvt * kDVT;
+    const float lam = args.lam_h[h];
+
+    const R *__restrict__ gq = static_cast<const R *>(args.q);
+    const R *__restrict__ gk = static_cast<const R *>(args.k);
+    const R *__restrict__ gv = static_cast<const R *>(args.v);
+    R *__restrict__ go = static_cast<R *>(args.o);
+    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+    f32x4 sT[NKT];
+    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * wave + r16) * DK;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+        sT[t] = args.S0 ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
+
+    // staging thread -> (row sr, key columns [sc0, sc0 + CPT))
+    const int sr = tid / TPR, sc0 = (tid % TPR) * CPT;
+
+    const int NC = (T + CH - 1) / CH;
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+        const bool ok = sr < clen;
+
+        // ---- stage: q, k, a = b.k + lambda (b.q - k (k . b.q)), g; w . v tile
+        float qf[CPT], kf[CPT], af[CPT];
+        {
+            float ku = 0.f;
+            const size_t base = tok(t0 + min(sr, clen - 1)) * DK + sc0;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                f32x4 gg = zero4(), bb = zero4();
+                if (ok) {
+                    gg = *reinterpret_cast<const f32x4 *>(args.g + base + c);
+                    bb = *reinterpret_cast<const f32x4 *>(args.b + base + c);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qf[c + i] = ok ? P::to_f32(gq[base + c + i]) : 0.f;
+                    kf[c + i] = ok ? P::to_f32(gk[base + c + i]) : 0.f;
+                    af[c + i] = bb[i] * qf[c + i];                       // u = b . q
+                    ku += kf[c + i] * af[c + i];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) af[c + i] = bb[i] * kf[c + i] + lam * af[c + i];
+                *reinterpret_cast<f32x4 *>(Gs + sr * PF + sc0 + c) = gg;
+            }
+            // the TPR threads of a row are consecutive lanes of one wave
+#pragma unroll
+            for (int off = 1; off < TPR; off <<= 1) ku += __shfl_xor(ku, off, TPR);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) af[c] -= lam * ku * kf[c];
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                P::st4(Qs + sr * PK + sc0 + c, f32x4{qf[c], qf[c + 1], qf[c + 2], qf[c + 3]});
+                P::st4(Ks + sr * PK + sc0 + c, f32x4{kf[c], kf[c + 1], kf[c + 2], kf[c + 3]});
+                P::st4(As + sr * PK + sc0 + c, f32x4{af[c], af[c + 1], af[c + 2], af[c + 3]});
+            }
+        }
+        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+            const int c = vi / VPRV, cv = vi % VPRV;
+            float wv[EPV];
+            if (c < clen) {
+                const size_t off = tok(t0 + c) * dv + dv0 + cv * EPV;
+                const uint4 raw = *reinterpret_cast<const uint4 *>(gv + off);
+                const R *e = reinterpret_cast<const R *>(&raw);
+#pragma unroll
+                for (int u = 0; u < EPV; ++u) wv[u] = args.w[off + u] * P::to_f32(e[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < EPV; ++u) wv[u] = 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < EPV; u += 4)
+                *reinterpret_cast<f32x4 *>(WVs + c * PW + cv * EPV + u) = f32x4{wv[u], wv[u + 1], wv[u + 2], wv[u + 3]};
+        }
+        __syncthreads();
+        // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0)
+        for (int c = tid; c < DK; c += kThreads) {
+            float acc = 0.f;
+            for (int t = 0; t < CH; ++t) {
+                acc += Gs[t * PF + c];
+                Gs[t * PF + c] = acc;
+            }
+            eGC[c] = __expf(acc);
+        }
+        __syncthreads();
+        // ---- decayed operands: At = a . exp(Gm_t), Qt = q . exp(Gm_t), Kh = k . exp(Gm_C - Gm_t)
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4) {
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gs + sr * PF + sc0 + c);
+            const f32x4 gC = *reinterpret_cast<const f32x4 *>(Gs + (CH - 1) * PF + sc0 + c);
+            f32x4 at, qt, kh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = __expf(gm[i]);
+                at[i] = af[c + i] * e;
+                qt[i] = qf[c + i] * e;
+                kh[i] = kf[c + i] * __expf(gC[i] - gm[i]);
+            }
+            P::st4(Ats + sr * PK + sc0 + c, at);
+            P::st4(Qts + sr * PK + sc0 + c, qt);
+            P::st4(Khs + sr * PK + sc0 + c, kh);
+        }
+        // ---- L and M blocks, one 16 x 16 block pair per wave, from scaled fragments
+        if (wave < NPAIR) {
+            int I, J;
+            tri_pair(wave, I, J);
+            const int rref = (J < I) ? 16 * I : 16 * I + 8;
+            const int tr = 16 * I + r16, tc = 16 * J + r16;       // this lane's row and column token
+            f32x4 lacc = zero4(), macc = zero4();
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const int c0 = 16 * s + 4 * g4;
+                const f32x4 gr = *reinterpret_cast<const f32x4 *>(Gs + rref * PF + c0);
+                const f32x4 gt = *reinterpret_cast<const f32x4 *>(Gs + tr * PF + c0);
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(Gs + tc * PF + c0);
+                const f32x4 xa = P::f32(P::ld4(As + tr * PK + c0));
+                const f32x4 xq = P::f32(P::ld4(Qs + tr * PK + c0));
+                const f32x4 xk = P::f32(P::ld4(Ks + tc * PK + c0));
+                f32x4 ea, ek;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ea[i] = __expf(gt[i] - gr[i]);
+                    ek[i] = __expf(gr[i] - gj[i]);
+                }
+                const F kb = P::cvt(xk * ek);
+                lacc = P::mma1(lacc, P::cvt(xa * ea), kb);
+                macc = P::mma1(macc, P::cvt(xq * ea), kb);
+            }
+            // accumulator: rows 16 I + 4 g + e, column 16 J + l % 16
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * I + 4 * g4 + e, c = 16 * J + r16;
+                Ls[r * PC + c] = P::from_f32(c < r ? lacc[e] : 0.f);
+                Ms[r * PC + c] = P::from_f32(c <= r ? macc[e] : 0.f);
+            }
+        }
+        __syncthreads();
+        unit_lower_inverse<P, CH, PC>(Ls, Ts);
+
+        // ---- this wave's 16 value columns
+        F sTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
+        F Ef[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            f32x4 y = zero4();
+#pragma unroll
+            for (int t = 0; t < NKT; t += 2)
+                y = P::mma2(y, frag<P>(Ats, PK, 16 * mt, 16 * t), frag<P>(Ats, PK, 16 * mt, 16 * t + 16), sTf[t],
+                            sTf[t + 1]);
+            f32x4 wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = WVs[(16 * mt + 4 * g4 + e) * PW + 16 * wave + r16];
+            Ef[mt] = P::cvt(wv - y);
+        }
+        f32x4 Rr[NCT];
+        F Rf[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            Rr[mt] = zero4();
+#pragma unroll
+            for (int s = 0; s <= mt; ++s) Rr[mt] = P::mma1(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), Ef[s]);
+            Rf[mt] = P::cvt(Rr[mt]);
+        }
+        f32x4 O[NCT];
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            O[mt] = zero4();
+#pragma unroll
+            for (int t = 0; t < NKT; t += 2)
+                O[mt] = P::mma2(O[mt], frag<P>(Qts, PK, 16 * mt, 16 * t), frag<P>(Qts, PK, 16 * mt, 16 * t + 16),
+                                sTf[t], sTf[t + 1]);
+#pragma unroll
+            for (int s = 0; s <= mt; ++s) O[mt] = P::mma1(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), Rf[s]);
+        }
+        // S^T <- diag(exp Gm_C) S^T + Kh^T R
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            f32x4 acc = lds_f32x4(eGC + 16 * t + 4 * g4) * sT[t];
+#pragma unroll
+            for (int s = 0; s < NCT; ++s) acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
+            sT[t] = acc;
+        }
+        // output rows through LDS
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(O[mt][e]);
+        }
+        __syncthreads();
+        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+            const int c = vi / VPRV, cv = vi % VPRV;
+            if (c < clen)
+                *reinterpret_cast<uint4 *>(go + tok(t0 + c) * dv + dv0 + cv * EPV) =
+                    *reinterpret_cast<const uint4 *>(Os + c * PV + cv * EPV);
+        }
+        __syncthreads();   // the next chunk's staging rewrites every buffer read above
+    }
+    if (args.S_T) {
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.S_T + srow + 16 * t + 4 * g4) = sT[t];
+    }
+}
+
+template <class P, int DK, int DV>
+hipError_t launch_qed_step_typed(const QedStepArgs &a, hipStream_t stream) {
+    if (a.N * a.H == 0) return hipSuccess;
+    hipLaunchKernelGGL((qed_step_kernel<P, DK, DV>), dim3(a.N * a.H), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class P>
+hipError_t launch_qed_step_p(int dk, int dv, const QedStepArgs &a, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_qed_step_typed<P, 128, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_qed_step_typed<P, 128, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_qed_step_typed<P, 64, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_qed_step_typed<P, 64, 64>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+template <class P, int DK, int CH>
+hipError_t launch_qed_chunk_typed(const QedChunkArgs &a, hipStream_t stream) {
+    const int grid = a.B * a.H * a.n_dvt;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((qed_chunk_kernel<P, DK, CH>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool qed_chunk_supported(int dtype, int dk, int dv, int C) {
+    return (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
+           ((dtype == 1 && (C == 16 || C == 32)) || (dtype == 0 && C == 16));
+}
+
+hipError_t launch_qed_step(int dtype, int dk, int dv, const QedStepArgs &a, hipStream_t stream) {
+    return dtype == 1 ? launch_qed_step_p<Bf16>(dk, dv, a, stream) : launch_qed_step_p<F32>(dk, dv, a, stream);
+}
+
+hipError_t launch_qed_chunk(int dtype, int dk, int C, const QedChunkArgs &a, hipStream_t stream) {
+    if (dtype == 1) {
+        if (C == 32) return dk == 128 ? launch_qed_chunk_typed<Bf16, 128, 32>(a, stream)
+                                      : launch_qed_chunk_typed<Bf16, 64, 32>(a, stream);
+        return dk == 128 ? launch_qed_chunk_typed<Bf16, 128, 16>(a, stream) : launch_qed_chunk_typed<Bf16, 64, 16>(a, stream);
+    }
+    return dk == 128 ? launch_qed_chunk_typed<F32, 128, 16>(a, stream) : launch_qed_chunk_typed<F32, 64, 16>(a, stream);
+}
+
+}  // namespace qd

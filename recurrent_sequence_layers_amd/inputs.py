@@ -120,6 +120,43 @@ def workload_inputs(name: str, seed: int, device="cpu", gates_as_none=False) -> 
                         s0_std=w.get("s0_std"), device=device, gates_as_none=gates_as_none)
 
 
+@dataclass
+class QedInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    b: torch.Tensor
+    w: torch.Tensor
+    lam_h: torch.Tensor
+    S0: Optional[torch.Tensor]
+
+
+def qed_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, s0_std=None, decay_mean=-3.0, decay_std=1.5,
+               lam_zero=False, device="cpu") -> QedInputs:
+    """Inputs for the QED / GDN-2 layer (q, k [B,T,H,dk] unit-norm; v [B,T,H,dv]), drawn in
+    this order: q, k, v ~ N(0, 1); g = -softplus(N(decay_mean, decay_std)) per key channel
+    (log decay, exp(g) in (0, 1)); b = sigmoid(N(0, 1)) per key channel; w = sigmoid(N(0, 1))
+    per value channel; lam_h = 0.25 sigmoid(N(-2, 1)) per head (the QED notes' strength
+    parametrisation with its initial logit -2 as the mean); S0 ~ N(0, s0_std) if asked.
+    lam_zero gives lam_h = 0 (GDN-2) without shifting the other draws."""
+    dt = _DT[dtype]
+    gen = _generator(seed, device)
+    f = dict(generator=gen, device=device, dtype=torch.float32)
+    q = torch.randn(B, T, H, dk, **f)
+    k = torch.randn(B, T, H, dk, **f)
+    v = torch.randn(B, T, H, dv, **f)
+    g = -torch.nn.functional.softplus(torch.randn(B, T, H, dk, **f) * decay_std + decay_mean)
+    b = torch.sigmoid(torch.randn(B, T, H, dk, **f))
+    w = torch.sigmoid(torch.randn(B, T, H, dv, **f))
+    lam = 0.25 * torch.sigmoid(torch.randn(H, **f) - 2.0)
+    S0 = (torch.randn(B, H, dv, dk, **f) * float(s0_std)) if s0_std else None
+    if lam_zero:
+        lam = torch.zeros_like(lam)
+    return QedInputs(_unit(q).to(dt).contiguous(), _unit(k).to(dt).contiguous(), v.to(dt).contiguous(),
+                     g.contiguous(), b.contiguous(), w.contiguous(), lam.contiguous(), S0)
+
+
 def upstream_grads(B, T, H, dk, dv, dtype="bf16", seed=0, dst_std=None, device="cpu"):
     """Gradients arriving from above for the layer backward: dO ~ N(0, 1) in the
     input dtype [B,T,H,dv] and, when dst_std is given, dS_T ~ N(0, dst_std) fp32
