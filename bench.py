@@ -10,7 +10,8 @@ resident, one token per call) and reported as achieved HBM GB/s, and the layer i
 timed with lambda = 0 (Gated DeltaNet), with lambda = 0 and alpha = 1 (DeltaNet), and
 on the long-context workload (B=1, T=65536, S0 given), each reported beside the
 headline figure, and the layer backward (qdelta_chunk_bwd, all three passes) is timed on
-the headline workload with dO ~ N(0, 1).  Kernel
+the headline workload with dO ~ N(0, 1); the QED / GDN-2 variant (per-channel decay,
+vector gates) is timed at the headline shapes (C = 32) and as a decode step.  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -151,6 +152,8 @@ def main():
                          "profiled runs, so that per-kernel statistics cover the headline workload only)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the layer backward on the headline workload (profiled runs of its kernels)")
+    ap.add_argument("--qed-only", action="store_true",
+                    help="time only the QED / GDN-2 chunk forward and decode step (profiled runs of its kernels)")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device-to-device copies, the reference the HBM "
@@ -205,6 +208,48 @@ def main():
                 "C": C, "steps": steps, "ms_per_call": b_ms, "tokens_per_s": B * T / (b_ms * 1e-3),
                 "workspace_bytes": nws, "algorithmic_bytes_per_call": bbytes,
                 "hbm_frac": bbytes / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+    def qed_run(steps, dsteps):
+        """QED / GDN-2: the chunk forward at the headline shapes (C = 32) and a decode step on
+        256 sequences x 16 heads."""
+        qx = inputs.qed_inputs(B, T, H, dk, dv, "bf16", seed=args.seed + 7, device="cuda")
+        qo = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        qS = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        qf = lambda: qd.qdelta_qed_chunk_fwd(qx.q, qx.k, qx.v, qx.g, qx.b, qx.w, qx.lam_h, None, C=32, o=qo, S_T=qS)
+        for _ in range(args.warmup):
+            qf()
+        torch.cuda.synchronize()
+        q_s, _ = time_region(torch, qf, steps)
+        q_ms = q_s / steps * 1e3
+        toks = B * T * H
+        qbytes = toks * (2 * dk + 2 * dv) * 2 + toks * (2 * dk + dv) * 4 + B * H * dv * dk * 4
+        del qx, qo, qS
+        N, Hd = 256, 16
+        sx = inputs.qed_inputs(N, dsteps, Hd, dk, dv, "bf16", seed=args.seed + 8, s0_std=0.02, device="cuda")
+        Sd = sx.S0.clone()
+        od = torch.empty((N, Hd, dv), dtype=torch.bfloat16, device=dev)
+        toks_d = [tuple(t[:, i].contiguous() for t in (sx.q, sx.k, sx.v, sx.g, sx.b, sx.w)) for i in range(dsteps)]
+        def decode():
+            for tq, tk, tv, tg, tb, tw in toks_d:
+                qd.qdelta_qed_step(tq, tk, tv, tg, tb, tw, sx.lam_h, Sd, o=od)
+        decode()
+        d_s, _ = time_region(torch, decode, 1)
+        d_us = d_s / dsteps * 1e6
+        dbytes = N * Hd * (2 * dv * dk * 4 + (2 * dk + 2 * dv) * 2 + (2 * dk + dv) * 4)
+        log(f"[bench] QED chunk forward {q_ms:.4f} ms/call, {B * T / (q_ms * 1e-3) / 1e6:.2f} M tokens/s; "
+            f"QED decode {d_us:.2f} us/step, {dbytes / (d_us * 1e-6) / 1e9:.0f} GB/s")
+        return {"chunk_fwd": {"workload": "QED / GDN-2 layer forward, B=8 T=4096 H=16 d_k=d_v=128 C=32, bf16 q/k/v/o, "
+                                          "fp32 per-channel g, b and w, lambda_h per head",
+                              "steps": steps, "ms_per_call": q_ms, "tokens_per_s": B * T / (q_ms * 1e-3),
+                              "algorithmic_bytes_per_call": qbytes,
+                              "hbm_frac": qbytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                "decode_step": {"workload": "256 sequences x 16 heads, d_k=d_v=128, fp32 state resident",
+                                "steps": dsteps, "us_per_step": d_us, "algorithmic_bytes_per_step": dbytes,
+                                "hbm_frac": dbytes / (d_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+
+    if args.qed_only:
+        print(json.dumps({"qed": qed_run(args.steps, 200)}), flush=True)
+        return
 
     if args.backward_only:
         print(json.dumps({"backward": backward_run(args.steps)}), flush=True)
@@ -265,6 +310,9 @@ def main():
         bwd = backward_run(max(5, args.steps // 5))
         bwd["time_ratio_to_headline"] = bwd["ms_per_call"] / ms_per_step
         variants["layer_1p3b_backward"] = bwd
+        qed = qed_run(args.steps, 200)
+        qed["chunk_fwd"]["time_ratio_to_headline"] = qed["chunk_fwd"]["ms_per_call"] / ms_per_step
+        variants["qed_gdn2"] = qed
         # the headline layer through the fused prologue: unnormalised q, k and gate logits
         # (qdelta_chunk_fwd_raw), against the headline call on prepared inputs
         g = torch.Generator(device=dev).manual_seed(args.seed + 3)

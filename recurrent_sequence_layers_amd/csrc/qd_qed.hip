@@ -158,8 +158,11 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
     constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV, PF = Lay::PF, PW = Lay::PW;
     constexpr int EPV = 16 / P::kBytes;
     constexpr int VPRV = kDVT / EPV;
-    constexpr int TPR = kThreads / CH;             // staging threads per chunk row
-    constexpr int CPT = DK / TPR;                  // key columns per staging thread
+    // staging threads per chunk row (each takes at least one 16-byte vector of q and k) and
+    // key columns per staging thread; threads beyond CH * TPR stage nothing
+    constexpr int VMIN = EPV > 4 ? EPV : 4;
+    constexpr int TPR = (kThreads / CH < DK / VMIN) ? kThreads / CH : DK / VMIN;
+    constexpr int CPT = DK / TPR;
     static_assert(CPT % 4 == 0 && CPT <= 32, "staging split");
     constexpr int NPAIR = NCT * (NCT + 1) / 2;
     static_assert(NPAIR <= 4, "one 16 x 16 block pair per wave");
@@ -205,81 +208,121 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
     for (int t = 0; t < NKT; ++t)
         sT[t] = args.S0 ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
 
-    // staging thread -> (row sr, key columns [sc0, sc0 + CPT))
+    // staging thread -> (row sr, key columns [sc0, sc0 + CPT)); the next chunk's raw rows are
+    // loaded into registers while the current chunk computes (rows past the end are clamped
+    // to the last valid row when loaded and zeroed when staged)
     const int sr = tid / TPR, sc0 = (tid % TPR) * CPT;
+    const bool stager = sr < CH;
+    constexpr int QV = CPT / EPV;                  // 16-byte vectors of q or k per staging thread
+    constexpr int GV = CPT / 4;                    // float4 of g or b per staging thread
+    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;   // v vectors per thread
+    constexpr int WPV = EPV / 4;                   // float4 of w per v vector
+    uint4 rq[QV], rk[QV], rv[NVV];
+    f32x4 rg[GV], rb[GV], rw[NVV][WPV];
+    auto gload = [&](int n) {
+        const int t0 = n * CH;
+        const int last = min(CH, T - t0) - 1;
+        if (stager) {
+            const size_t base = tok(t0 + min(sr, last)) * DK + sc0;
+#pragma unroll
+            for (int j = 0; j < QV; ++j) {
+                rq[j] = *reinterpret_cast<const uint4 *>(gq + base + j * EPV);
+                rk[j] = *reinterpret_cast<const uint4 *>(gk + base + j * EPV);
+            }
+#pragma unroll
+            for (int j = 0; j < GV; ++j) {
+                rg[j] = *reinterpret_cast<const f32x4 *>(args.g + base + 4 * j);
+                rb[j] = *reinterpret_cast<const f32x4 *>(args.b + base + 4 * j);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = tid + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const size_t off = tok(t0 + min(vi / VPRV, last)) * dv + dv0 + (vi % VPRV) * EPV;
+                rv[j] = *reinterpret_cast<const uint4 *>(gv + off);
+#pragma unroll
+                for (int u = 0; u < WPV; ++u) rw[j][u] = *reinterpret_cast<const f32x4 *>(args.w + off + 4 * u);
+            }
+        }
+    };
 
     const int NC = (T + CH - 1) / CH;
+    if (NC > 0) gload(0);
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * CH;
         const int clen = min(CH, T - t0);
-        const bool ok = sr < clen;
+        const bool ok = sr < clen;   // (false for the threads that stage nothing)
 
-        // ---- stage: q, k, a = b.k + lambda (b.q - k (k . b.q)), g; w . v tile
+        // ---- stage: q, k, a = b.k + lambda (b.q - k (k . b.q)), raw g; w . v tile
         float qf[CPT], kf[CPT], af[CPT];
         {
-            float ku = 0.f;
-            const size_t base = tok(t0 + min(sr, clen - 1)) * DK + sc0;
 #pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                f32x4 gg = zero4(), bb = zero4();
-                if (ok) {
-                    gg = *reinterpret_cast<const f32x4 *>(args.g + base + c);
-                    bb = *reinterpret_cast<const f32x4 *>(args.b + base + c);
+            for (int j = 0; j < QV; ++j) {
+                const R *eq = reinterpret_cast<const R *>(&rq[j]);
+                const R *ek = reinterpret_cast<const R *>(&rk[j]);
+#pragma unroll
+                for (int u = 0; u < EPV; ++u) {
+                    qf[j * EPV + u] = ok ? P::to_f32(eq[u]) : 0.f;
+                    kf[j * EPV + u] = ok ? P::to_f32(ek[u]) : 0.f;
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qf[c + i] = ok ? P::to_f32(gq[base + c + i]) : 0.f;
-                    kf[c + i] = ok ? P::to_f32(gk[base + c + i]) : 0.f;
-                    af[c + i] = bb[i] * qf[c + i];                       // u = b . q
-                    ku += kf[c + i] * af[c + i];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) af[c + i] = bb[i] * kf[c + i] + lam * af[c + i];
-                *reinterpret_cast<f32x4 *>(Gs + sr * PF + sc0 + c) = gg;
             }
+            float ku = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                af[c] = rb[c / 4][c % 4] * qf[c];                        // u = b . q
+                ku += kf[c] * af[c];
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) af[c] = rb[c / 4][c % 4] * kf[c] + lam * af[c];
             // the TPR threads of a row are consecutive lanes of one wave
 #pragma unroll
             for (int off = 1; off < TPR; off <<= 1) ku += __shfl_xor(ku, off, TPR);
 #pragma unroll
             for (int c = 0; c < CPT; ++c) af[c] -= lam * ku * kf[c];
+            if (stager) {
 #pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                P::st4(Qs + sr * PK + sc0 + c, f32x4{qf[c], qf[c + 1], qf[c + 2], qf[c + 3]});
-                P::st4(Ks + sr * PK + sc0 + c, f32x4{kf[c], kf[c + 1], kf[c + 2], kf[c + 3]});
-                P::st4(As + sr * PK + sc0 + c, f32x4{af[c], af[c + 1], af[c + 2], af[c + 3]});
-            }
-        }
-        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
-            const int c = vi / VPRV, cv = vi % VPRV;
-            float wv[EPV];
-            if (c < clen) {
-                const size_t off = tok(t0 + c) * dv + dv0 + cv * EPV;
-                const uint4 raw = *reinterpret_cast<const uint4 *>(gv + off);
-                const R *e = reinterpret_cast<const R *>(&raw);
-#pragma unroll
-                for (int u = 0; u < EPV; ++u) wv[u] = args.w[off + u] * P::to_f32(e[u]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < EPV; ++u) wv[u] = 0.f;
+                for (int c = 0; c < CPT; c += 4) {
+                    P::st4(Qs + sr * PK + sc0 + c, f32x4{qf[c], qf[c + 1], qf[c + 2], qf[c + 3]});
+                    P::st4(Ks + sr * PK + sc0 + c, f32x4{kf[c], kf[c + 1], kf[c + 2], kf[c + 3]});
+                    P::st4(As + sr * PK + sc0 + c, f32x4{af[c], af[c + 1], af[c + 2], af[c + 3]});
+                    *reinterpret_cast<f32x4 *>(Gs + sr * PF + sc0 + c) = ok ? rg[c / 4] : zero4();
+                }
             }
 #pragma unroll
-            for (int u = 0; u < EPV; u += 4)
-                *reinterpret_cast<f32x4 *>(WVs + c * PW + cv * EPV + u) = f32x4{wv[u], wv[u + 1], wv[u + 2], wv[u + 3]};
+            for (int j = 0; j < NVV; ++j) {
+                const int vi = tid + kThreads * j;
+                if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                    const int c = vi / VPRV, cv = vi % VPRV;
+                    const R *e = reinterpret_cast<const R *>(&rv[j]);
+#pragma unroll
+                    for (int u = 0; u < WPV; ++u) {
+                        f32x4 wv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) wv[i] = c < clen ? rw[j][u][i] * P::to_f32(e[4 * u + i]) : 0.f;
+                        *reinterpret_cast<f32x4 *>(WVs + c * PW + cv * EPV + 4 * u) = wv;
+                    }
+                }
+            }
         }
+        if (n + 1 < NC) gload(n + 1);
         __syncthreads();
-        // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0)
+        // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0): the
+        // column is read into registers, summed, and written back
         for (int c = tid; c < DK; c += kThreads) {
-            float acc = 0.f;
-            for (int t = 0; t < CH; ++t) {
-                acc += Gs[t * PF + c];
-                Gs[t * PF + c] = acc;
-            }
-            eGC[c] = __expf(acc);
+            float col[CH];
+#pragma unroll
+            for (int t = 0; t < CH; ++t) col[t] = Gs[t * PF + c];
+#pragma unroll
+            for (int t = 1; t < CH; ++t) col[t] += col[t - 1];
+#pragma unroll
+            for (int t = 0; t < CH; ++t) Gs[t * PF + c] = col[t];
+            eGC[c] = __expf(col[CH - 1]);
         }
         __syncthreads();
         // ---- decayed operands: At = a . exp(Gm_t), Qt = q . exp(Gm_t), Kh = k . exp(Gm_C - Gm_t)
 #pragma unroll
-        for (int c = 0; c < CPT; c += 4) {
+        for (int c = 0; c < (stager ? CPT : 0); c += 4) {
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gs + sr * PF + sc0 + c);
             const f32x4 gC = *reinterpret_cast<const f32x4 *>(Gs + (CH - 1) * PF + sc0 + c);
             f32x4 at, qt, kh;
