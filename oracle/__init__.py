@@ -13,6 +13,8 @@ Contents
                        the recurrence, token by token in reverse (C, fp64).
   * ``qed_fwd``     -- the QED / GDN-2 recurrence with per-channel decay and vector
                        erase and write gates (the QED reading notes §2.1-2.2; C, fp64).
+  * ``eda_fwd``     -- Erase-then-Delta: erase along e, then a delta write along k (the
+                       EDA explainer's two-step pseudo-code; C, fp64).
   * ``chunk_form``  -- the chunkwise WY/UT-transform algebra in fp64 numpy
                        (module ``oracle.chunk_form``), used to pin that the
                        chunked algebra reproduces the recurrence.
@@ -50,6 +52,8 @@ def _load():
     lib.oracle_qdelta_bwd.argtypes = [_dp] * 16 + [ctypes.c_int] * 6
     lib.oracle_qed_fwd.restype = ctypes.c_int
     lib.oracle_qed_fwd.argtypes = [_dp] * 10 + [ctypes.c_int] * 6
+    lib.oracle_eda_fwd.restype = ctypes.c_int
+    lib.oracle_eda_fwd.argtypes = [_dp] * 7 + [ctypes.c_int] * 6
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -154,4 +158,19 @@ def qed_fwd(q, k, v, g, b, w, lam_h, S0=None, nthreads: int = 0, want_o: bool = 
                                 _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_qed_fwd rejected its arguments")
+    return o, S_T
+
+
+def eda_fwd(q, k, v, e, S0=None, nthreads: int = 0, want_o: bool = True):
+    """Erase-then-Delta recurrence.  q, k, e [B,T,H,dk] (e unit-norm); v [B,T,H,dv]; S0
+    [B,H,dv,dk] or None.  Returns (o [B,T,H,dv] or None, S_T [B,H,dv,dk])."""
+    q, k, v, e, S0 = (_f64(t) for t in (q, k, v, e, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.empty((B, T, H, dv)) if want_o else None
+    S_T = np.empty((B, H, dv, dk))
+    rc = _load().oracle_eda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S0), _ptr(o), _ptr(S_T),
+                                B, T, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_eda_fwd rejected its arguments")
     return o, S_T

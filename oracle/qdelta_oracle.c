@@ -372,3 +372,49 @@ int oracle_qed_fwd(const double *q, const double *k, const double *v,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ EDA
+ * Erase-then-Delta (page "Erase-then-Delta Attention" explainer, core method, the
+ * two-step pseudo-code), in this file's d_v x d_k convention (the page's K x V memory
+ * transposed).  Per token, with a unit erase direction e:
+ *
+ *     S <- S - (S e) e^T                   (step 1: zero the component along e)
+ *     S <- S + (v - S k) k^T               (step 2: delta write along k; no beta)
+ *     o  = S q                             (read-out from the updated state)
+ *
+ * Rows of S evolve independently. */
+int oracle_eda_fwd(const double *q, const double *k, const double *v, const double *e,
+                   const double *S0, double *o, double *S_T,
+                   int B, int T, int H, int dk, int dv, int nthreads)
+{
+    long long unit, n_units;
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1) return -1;
+    if (!S_T) return -1;
+    if ((long long)B * T * H > 0 && (!q || !k || !v || !e)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    n_units = (long long)B * H * dv;
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nthreads)
+    for (unit = 0; unit < n_units; ++unit) {
+        int bb = (int)(unit / ((long long)H * dv));
+        int h = (int)((unit / dv) % H);
+        int i = (int)(unit % dv);
+        double *s = S_T + (((size_t)bb * H + h) * dv + i) * dk;
+        int t, j;
+        if (S0) memcpy(s, S0 + (((size_t)bb * H + h) * dv + i) * dk, sizeof(double) * dk);
+        else memset(s, 0, sizeof(double) * dk);
+        for (t = 0; t < T; ++t) {
+            size_t tok = ((size_t)bb * T + t) * H + h;
+            const double *qt = q + tok * dk, *kt = k + tok * dk, *et = e + tok * dk;
+            double se = 0.0, sk = 0.0, err, out = 0.0;
+            for (j = 0; j < dk; ++j) se += s[j] * et[j];               /* (S e)_i */
+            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];        /* step 1   */
+            for (j = 0; j < dk; ++j) sk += s[j] * kt[j];               /* (S k)_i */
+            err = v[tok * dv + i] - sk;
+            for (j = 0; j < dk; ++j) s[j] = s[j] + err * kt[j];       /* step 2   */
+            for (j = 0; j < dk; ++j) out += s[j] * qt[j];
+            if (o) o[tok * dv + i] = out;
+        }
+    }
+    return 0;
+}
