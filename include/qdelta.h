@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define QDELTA_ABI_VERSION 4
+#define QDELTA_ABI_VERSION 5
 
 typedef enum qd_status {
     QD_OK = 0,
@@ -214,6 +214,34 @@ int qdelta_qed_chunk_fwd(const void *q, const void *k, const void *v,
 int qdelta_qed_step(const void *q, const void *k, const void *v,
                     const float *g, const float *b, const float *w, const float *lambda_h,
                     float *S, void *o, int N, int H, int d_k, int d_v, int dtype, void *stream);
+
+/*
+ * Erase-then-Delta (page "Erase-then-Delta Attention" explainer, core method, its
+ * two-step pseudo-code), in this header's d_v x d_k convention (the page's K x V memory
+ * transposed).  Per (b, h), per token, with a unit erase direction e:
+ *
+ *     S <- S - (S e) e^T ;   S <- S + (v - S k) k^T ;   o_t = S q
+ *
+ * (no beta and no decay, as the page writes it).  q, k, e [B][T][H][d_k] and v, o
+ * [B][T][H][d_v] in the dtype's elements; S0, S_T, C, dtype and the other sizes as for
+ * qdelta_chunk_fwd.  The erase is a delta step with key e, value 0 and beta 1, so the
+ * chunked form is DeltaNet over the interleaved sequence e_1, k_1, e_2, k_2, ... read at
+ * the k tokens: the call writes that sequence into the workspace, runs the chunk forward
+ * over it and gathers o.  workspace: at least qdelta_eda_chunk_fwd_workspace_bytes
+ * (2*B*T*H*((2 d_k + 2 d_v) e + 4) bytes, e = element size), 16-byte aligned, disjoint
+ * from every other argument; QD_ERR_WORKSPACE otherwise.
+ */
+size_t qdelta_eda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
+                                            int dtype);
+int qdelta_eda_chunk_fwd(const void *q, const void *k, const void *v, const void *e,
+                         const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* One Erase-then-Delta decode step for N sequences x H heads: q, k, e [N][H][d_k], v, o
+ * [N][H][d_v]; S [N][H][d_v][d_k] fp32 updated in place.  d_k, d_v in {64, 128}. */
+int qdelta_eda_step(const void *q, const void *k, const void *v, const void *e, float *S,
+                    void *o, int N, int H, int d_k, int d_v, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

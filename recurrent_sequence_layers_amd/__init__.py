@@ -55,6 +55,12 @@ def load_library():
     lib.qdelta_qed_chunk_fwd.argtypes = [vp] * 10 + [i] * 7 + [vp]
     lib.qdelta_qed_step.restype = i
     lib.qdelta_qed_step.argtypes = [vp] * 9 + [i] * 5 + [vp]
+    lib.qdelta_eda_chunk_fwd_workspace_bytes.restype = sz
+    lib.qdelta_eda_chunk_fwd_workspace_bytes.argtypes = [i] * 7
+    lib.qdelta_eda_chunk_fwd.restype = i
+    lib.qdelta_eda_chunk_fwd.argtypes = [vp] * 7 + [i] * 7 + [vp, sz, vp]
+    lib.qdelta_eda_step.restype = i
+    lib.qdelta_eda_step.argtypes = [vp] * 6 + [i] * 5 + [vp]
     lib.qdelta_chunk_bwd_workspace_bytes.restype = sz
     lib.qdelta_chunk_bwd_workspace_bytes.argtypes = [i] * 7
     lib.qdelta_chunk_bwd.restype = i
@@ -248,6 +254,62 @@ def qdelta_qed_step(q, k, v, g, b, w, lam_h, S, o=None, stream=None):
     rc = lib.qdelta_qed_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S), _ptr(o),
                              N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
     _raise(rc, "qdelta_qed_step")
+    return o
+
+
+def qdelta_eda_chunk_fwd(q, k, v, e, S0=None, C: int = 64, o=None, S_T=None, want_state=True, workspace=None,
+                         stream=None):
+    """Erase-then-Delta layer forward.  q, k, e [B,T,H,d_k] (unit-norm), v [B,T,H,d_v], same
+    dtype; S0 [B,H,d_v,d_k] fp32.  Returns (o, S_T).  workspace: a device buffer of at least
+    qdelta_eda_chunk_fwd_workspace_bytes(...) bytes (allocated here when None)."""
+    import torch
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (B, T, H, dv))
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+    code = _dtype_code(dt)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = lib.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    rc = lib.qdelta_eda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                  int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_eda_chunk_fwd")
+    return o, S_T
+
+
+def qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:
+    return int(load_library().qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, _dtype_code(dtype)))
+
+
+def qdelta_eda_step(q, k, v, e, S, o=None, stream=None):
+    """One Erase-then-Delta decode step.  q, k, e [N,H,d_k], v [N,H,d_v]; S [N,H,d_v,d_k] fp32,
+    updated in place.  Returns o [N,H,d_v]."""
+    import torch
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+    _check(S, "S", torch.float32, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check(o, "o", dt, (N, H, dv))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.qdelta_eda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S), _ptr(o), N, H, dk, dv, _dtype_code(dt),
+                             ctypes.c_void_p(stream))
+    _raise(rc, "qdelta_eda_step")
     return o
 
 

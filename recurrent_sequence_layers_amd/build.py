@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqdelta.so")
-SOURCES = ["qd_capi.hip", "qd_chunk_bwd.hip", "qd_chunk_fwd.hip", "qd_chunk_fwd_pipe.hip", "qd_segment.hip",
+SOURCES = ["qd_capi.hip", "qd_chunk_bwd.hip", "qd_chunk_fwd.hip", "qd_chunk_fwd_pipe.hip", "qd_eda.hip", "qd_segment.hip",
            "qd_qed.hip", "qd_step.hip"]
 ARCH = os.environ.get("QDELTA_OFFLOAD_ARCH", "gfx950")
 

@@ -152,6 +152,66 @@ int qdelta_qed_step(const void *q, const void *k, const void *v, const float *g,
     return err == hipSuccess ? QD_OK : QD_ERR_HIP;
 }
 
+size_t qdelta_eda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
+    if (B < 0 || T < 0 || H < 0 || !qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return 0;
+    if (static_cast<long long>(B) * T * H == 0) return 0;
+    return qd::eda_chunk_workspace(dtype, B, T, H, d_k, d_v);
+}
+
+int qdelta_eda_chunk_fwd(const void *q, const void *k, const void *v, const void *e, const float *S0, void *o,
+                         float *S_T, int B, int T, int H, int d_k, int d_v, int C, int dtype, void *workspace,
+                         size_t ws_bytes, void *stream) {
+    if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
+    const long long bh = static_cast<long long>(B) * H;
+    if (bh == 0) return QD_OK;
+    if (bh * (d_v / 64) > 0x7fffffffLL || static_cast<long long>(T) * 2 > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    const long long ntok = bh * T;
+    if (ntok > 0 && (!q || !k || !v || !e || !o)) return QD_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(e) || !aligned16(o) || !aligned16(S0) ||
+        !aligned16(S_T))
+        return QD_ERR_INVALID_ARG;
+    const size_t need = qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype);
+    if (ws_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return QD_ERR_WORKSPACE;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, o_bytes = static_cast<size_t>(ntok) * d_v * es;
+    const size_t st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
+    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes},
+                                                      {S0, st_bytes}};
+    for (const auto &i : ins)
+        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(workspace, need, i.p, i.n)) return QD_ERR_INVALID_ARG;
+    if (overlaps(workspace, need, o, o_bytes) || overlaps(workspace, need, S_T, st_bytes) ||
+        overlaps(o, o_bytes, S_T, st_bytes) || (S_T && S0 && S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)))
+        return QD_ERR_INVALID_ARG;
+    qd::EdaChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.e = e; a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.B = B; a.T = T; a.H = H; a.dv = d_v;
+    const hipError_t err = qd::launch_eda_chunk(dtype, d_k, C, a, workspace, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
+int qdelta_eda_step(const void *q, const void *k, const void *v, const void *e, float *S, void *o, int N, int H,
+                    int d_k, int d_v, int dtype, void *stream) {
+    if (N < 0 || H < 0) return QD_ERR_INVALID_ARG;
+    if (!qd::step_supported(dtype, d_k, d_v)) return QD_ERR_UNSUPPORTED;
+    const long long nh = static_cast<long long>(N) * H;
+    if (nh == 0) return QD_OK;
+    if (nh > 0x7fffffffLL) return QD_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !e || !S || !o) return QD_ERR_INVALID_ARG;
+    if (!aligned16(S)) return QD_ERR_INVALID_ARG;
+    const size_t es = dtype == QD_BF16 ? 2 : 4;
+    const size_t st_bytes = static_cast<size_t>(nh) * d_v * d_k * 4, o_bytes = static_cast<size_t>(nh) * d_v * es;
+    const size_t qk_bytes = static_cast<size_t>(nh) * d_k * es;
+    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes}};
+    for (const auto &i : ins)
+        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
+    if (overlaps(o, o_bytes, S, st_bytes)) return QD_ERR_INVALID_ARG;
+    qd::EdaStepArgs a;
+    a.q = q; a.k = k; a.v = v; a.e = e; a.S = S; a.o = o; a.N = N; a.H = H;
+    const hipError_t err = qd::launch_eda_step(dtype, d_k, d_v, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? QD_OK : QD_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

@@ -68,6 +68,24 @@ bool qed_chunk_supported(int dtype, int dk, int dv, int C);
 hipError_t launch_qed_chunk(int dtype, int dk, int C, const QedChunkArgs &a, hipStream_t stream);
 hipError_t launch_qed_step(int dtype, int dk, int dv, const QedStepArgs &a, hipStream_t stream);
 
+// Erase-then-Delta (qd_eda.hip): erase direction e [..][d_k] in the element type.
+struct EdaChunkArgs {
+    const void *q, *k, *v, *e;      // [B][T][H][d_k] (q, k, e) / [B][T][H][d_v]
+    const float *S0;                // [B][H][d_v][d_k] or null
+    void *o;                        // [B][T][H][d_v]
+    float *S_T;                     // [B][H][d_v][d_k] or null
+    int B, T, H, dv;
+};
+struct EdaStepArgs {
+    const void *q, *k, *v, *e;      // [N][H][d_k] / [N][H][d_v]
+    float *S;                       // [N][H][d_v][d_k], in place
+    void *o;                        // [N][H][d_v]
+    int N, H;
+};
+size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv);
+hipError_t launch_eda_chunk(int dtype, int dk, int C, const EdaChunkArgs &a, void *ws, hipStream_t stream);
+hipError_t launch_eda_step(int dtype, int dk, int dv, const EdaStepArgs &a, hipStream_t stream);
+
 // dtype: 0 = fp32, 1 = bf16.  Return hipSuccess or the launch error.
 hipError_t launch_chunk_fwd(int dtype, int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t stream);

@@ -157,6 +157,21 @@ def qed_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, s0_std=None, decay_mean=-3
                      g.contiguous(), b.contiguous(), w.contiguous(), lam.contiguous(), S0)
 
 
+def eda_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, s0_std=None, device="cpu"):
+    """Inputs for Erase-then-Delta, drawn in this order: q, k, e ~ N(0, 1) each L2-normalised
+    per (token, head); v ~ N(0, 1); S0 ~ N(0, s0_std) if asked.  Returns (q, k, v, e, S0)."""
+    dt = _DT[dtype]
+    gen = _generator(seed, device)
+    f = dict(generator=gen, device=device, dtype=torch.float32)
+    q = torch.randn(B, T, H, dk, **f)
+    k = torch.randn(B, T, H, dk, **f)
+    e = torch.randn(B, T, H, dk, **f)
+    v = torch.randn(B, T, H, dv, **f)
+    S0 = (torch.randn(B, H, dv, dk, **f) * float(s0_std)) if s0_std else None
+    return (_unit(q).to(dt).contiguous(), _unit(k).to(dt).contiguous(), v.to(dt).contiguous(),
+            _unit(e).to(dt).contiguous(), S0)
+
+
 def upstream_grads(B, T, H, dk, dv, dtype="bf16", seed=0, dst_std=None, device="cpu"):
     """Gradients arriving from above for the layer backward: dO ~ N(0, 1) in the
     input dtype [B,T,H,dv] and, when dst_std is given, dS_T ~ N(0, dst_std) fp32

@@ -144,8 +144,10 @@ QED_MUTANTS = {
                          "            for (j = 0; j < dk; ++j) s[j] = s[j] * exp(gt[j]);"),
     "write_gate_dropped": ("r = w[tok * dv + i] * v[tok * dv + i] - pred;", "r = v[tok * dv + i] - pred;"),
     "write_along_a": ("s[j] = s[j] + r * kt[j];                 /* + r k^T */", "s[j] = s[j] + r * a[j];"),
-    "readout_before_write": ("for (j = 0; j < dk; ++j) out += s[j] * qt[j];\n            if (o) o[tok * dv + i] = out;",
-                             "if (o) o[tok * dv + i] = out;"),
+    "readout_before_write": ("for (j = 0; j < dk; ++j) s[j] = s[j] + r * kt[j];                 /* + r k^T */\n"
+                             "            for (j = 0; j < dk; ++j) out += s[j] * qt[j];",
+                             "for (j = 0; j < dk; ++j) out += s[j] * qt[j];\n"
+                             "            for (j = 0; j < dk; ++j) s[j] = s[j] + r * kt[j];"),
 }
 
 
