@@ -11,7 +11,8 @@ timed with lambda = 0 (Gated DeltaNet), with lambda = 0 and alpha = 1 (DeltaNet)
 on the long-context workload (B=1, T=65536, S0 given), each reported beside the
 headline figure, and the layer backward (qdelta_chunk_bwd, all three passes) is timed on
 the headline workload with dO ~ N(0, 1); the QED / GDN-2 variant (per-channel decay,
-vector gates) is timed at the headline shapes (C = 32) and as a decode step.  Kernel
+vector gates) is timed at the headline shapes (C = 32) and as a decode step, and so is
+Erase-then-Delta (C = 64).  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -154,6 +155,8 @@ def main():
                     help="time only the layer backward on the headline workload (profiled runs of its kernels)")
     ap.add_argument("--qed-only", action="store_true",
                     help="time only the QED / GDN-2 chunk forward and decode step (profiled runs of its kernels)")
+    ap.add_argument("--eda-only", action="store_true",
+                    help="time only the Erase-then-Delta chunk forward and decode step (profiled runs)")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device-to-device copies, the reference the HBM "
@@ -247,6 +250,51 @@ def main():
                                 "steps": dsteps, "us_per_step": d_us, "algorithmic_bytes_per_step": dbytes,
                                 "hbm_frac": dbytes / (d_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
+    def eda_run(steps, dsteps):
+        """Erase-then-Delta: the chunk forward at the headline shapes (C = 64) and a decode step
+        on 256 sequences x 16 heads."""
+        eq, ek, ev, ee, _ = inputs.eda_inputs(B, T, H, dk, dv, "bf16", seed=args.seed + 9, device="cuda")
+        eo = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        eS = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        nws = qd.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
+        ews = torch.empty(nws, dtype=torch.uint8, device=dev)
+        ef = lambda: qd.qdelta_eda_chunk_fwd(eq, ek, ev, ee, None, C=C, o=eo, S_T=eS, workspace=ews)
+        for _ in range(args.warmup):
+            ef()
+        torch.cuda.synchronize()
+        e_s, _ = time_region(torch, ef, steps)
+        e_ms = e_s / steps * 1e3
+        toks = B * T * H
+        ebytes = toks * (3 * dk + 2 * dv) * 2 + B * H * dv * dk * 4
+        del eq, ek, ev, ee, eo, eS, ews
+        N, Hd = 256, 16
+        sq, sk, sv, se, S0 = inputs.eda_inputs(N, dsteps, Hd, dk, dv, "bf16", seed=args.seed + 10, s0_std=0.02,
+                                               device="cuda")
+        Sd = S0.clone()
+        od = torch.empty((N, Hd, dv), dtype=torch.bfloat16, device=dev)
+        toks_d = [tuple(t[:, i].contiguous() for t in (sq, sk, sv, se)) for i in range(dsteps)]
+        def decode():
+            for tq, tk, tv, te in toks_d:
+                qd.qdelta_eda_step(tq, tk, tv, te, Sd, o=od)
+        decode()
+        d_s, _ = time_region(torch, decode, 1)
+        d_us = d_s / dsteps * 1e6
+        dbytes = N * Hd * (2 * dv * dk * 4 + (3 * dk + 2 * dv) * 2)
+        log(f"[bench] EDA chunk forward {e_ms:.4f} ms/call, {B * T / (e_ms * 1e-3) / 1e6:.2f} M tokens/s; "
+            f"EDA decode {d_us:.2f} us/step, {dbytes / (d_us * 1e-6) / 1e9:.0f} GB/s")
+        return {"chunk_fwd": {"workload": "Erase-then-Delta layer forward, B=8 T=4096 H=16 d_k=d_v=128 C=64, bf16 "
+                                          "q/k/e/v/o; run as DeltaNet over the interleaved 2T-token sequence",
+                              "steps": steps, "ms_per_call": e_ms, "tokens_per_s": B * T / (e_ms * 1e-3),
+                              "workspace_bytes": nws, "algorithmic_bytes_per_call": ebytes,
+                              "hbm_frac": ebytes / (e_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                "decode_step": {"workload": "256 sequences x 16 heads, d_k=d_v=128, fp32 state resident",
+                                "steps": dsteps, "us_per_step": d_us, "algorithmic_bytes_per_step": dbytes,
+                                "hbm_frac": dbytes / (d_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+
+    if args.eda_only:
+        print(json.dumps({"eda": eda_run(args.steps, 200)}), flush=True)
+        return
+
     if args.qed_only:
         print(json.dumps({"qed": qed_run(args.steps, 200)}), flush=True)
         return
@@ -313,6 +361,9 @@ def main():
         qed = qed_run(args.steps, 200)
         qed["chunk_fwd"]["time_ratio_to_headline"] = qed["chunk_fwd"]["ms_per_call"] / ms_per_step
         variants["qed_gdn2"] = qed
+        eda = eda_run(args.steps, 200)
+        eda["chunk_fwd"]["time_ratio_to_headline"] = eda["chunk_fwd"]["ms_per_call"] / ms_per_step
+        variants["erase_then_delta"] = eda
         # the headline layer through the fused prologue: unnormalised q, k and gate logits
         # (qdelta_chunk_fwd_raw), against the headline call on prepared inputs
         g = torch.Generator(device=dev).manual_seed(args.seed + 3)
