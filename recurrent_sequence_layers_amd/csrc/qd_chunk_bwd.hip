@@ -17,8 +17,9 @@
 //        dZ = A^T dO + D_r K dS'^T,  dV = dR = diag(beta) T_g^T dZ,
 //        dS^T = g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR;
 //      the last dS^T is dS0;
-//   3. chunk_bwd_grad_kernel: one workgroup per chunk, independent of the others, from
-//      the chunk's S and dS' recomputes R, Z, dZ, P = T_g^T dZ and the token errors
+//   3. chunk_bwd_grad_kernel: one workgroup per chunk, independent of the others, one wave
+//      per 16 value columns; from the chunk's S and dS' (read from global memory as MFMA
+//      fragments) it recomputes R, Z, dZ, P = T_g^T dZ and the token errors
 //      U = R - N Z, and forms dQ, dK, dbeta, dlambda and dalpha:
 //        dA = lower(dO Z^T), dL = -strict(P Z^T) (the gradient of diag(beta) N),
 //        W_o = dO S, W_p = P S, W_z = Z dS',
@@ -312,58 +313,67 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdAr
 }
 
 // ------------------------------------------------------------------ pass 3: per-chunk gradients
-template <class P, int DK, int CH>
+// One workgroup per chunk with one wave per 16 value columns (DV / 16 waves: all value
+// columns at once).  LDS holds the chunk's q, k, v, dO rows, Z and P, and the C x C
+// matrices; the states S and dS' are read from global memory as MFMA fragments (the
+// column-local Y = X S^T and K dS'^T take each wave's 16 rows of S and dS'; the value
+// contractions W_o = dO S, W_p = P S, W_z = Z dS' take 4 x 16 blocks of them).
+template <class P, int DK, int CH, int DV>
 struct GradLayout {
+    static constexpr int NW = DV / 16;
     static constexpr int PAD = 16 / P::kBytes;
-    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
-    static constexpr int NQ = CH * PK, NV = CH * PV, NS = kDVT * PK, NCC = CH * PC;
-    static_assert(NS >= NQ, "the S tiles double as the dQ and dK staging");
-    static constexpr int oQ = 0, oK = oQ + NQ, oV = oK + NQ, oD = oV + NV, oS = oD + NV, oDS = oS + NS;
-    static constexpr int oZ = oDS + NS, oP = oZ + NV, oL = oP + NV, oN = oL + NCC, oT = oN + NCC, oA = oT + NCC;
+    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = DV + PAD;
+    static constexpr int NQ = CH * PK, NV = CH * PV, NCC = CH * PC;
+    static_assert(4 * NV >= 2 * NQ, "dO, Z, P and v double as the dQ and dK staging");
+    static constexpr int oQ = 0, oK = oQ + NQ, oD = oK + NQ, oZ = oD + NV, oP = oZ + NV, oV = oP + NV;
+    static constexpr int oL = oV + NV, oN = oL + NCC, oT = oN + NCC, oA = oT + NCC;
     static constexpr int nR = oA + NCC;
-    static constexpr int nF = 6 * CH + 3 * 4 * CH + 8;   // gates; per-wave row partials; scalars
+    static constexpr int nF = 6 * CH + 3 * NW * CH + 2 * NW;   // gates; per-wave row partials; scalars
     static constexpr int bytes = nR * P::kBytes + nF * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
-template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
-__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdArgs args) {
+template <class P, int DK, int CH, int DV, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs args) {
     using R = typename P::R;
     using F = typename P::F;
-    using Lay = GradLayout<P, DK, CH>;
-    constexpr int NKT = DK / 16, NCT = CH / 16, NKW = NKT / 4;   // d_k blocks per wave in the d_k-wide products
+    using Lay = GradLayout<P, DK, CH, DV>;
+    constexpr int NW = Lay::NW, NT = NW * kWave;                 // waves, threads
+    constexpr int NKT = DK / 16, NCT = CH / 16, NVT = DV / 16;
+    constexpr int NB = NCT * NKT, NBW = (NB + NW - 1) / NW;      // d_k output blocks, per wave
     constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
     constexpr int EPV = 16 / P::kBytes;
-    constexpr int VPRQ = DK / EPV, VPRV = kDVT / EPV;
-    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + 3) / 4;
+    constexpr int VPRQ = DK / EPV, VPRV = DV / EPV;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
+    constexpr int NLQ = (CH * VPRQ + NT - 1) / NT, NLV = (CH * VPRV + NT - 1) / NT;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
     R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
     R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
     R *const Vs = reinterpret_cast<R *>(smem) + Lay::oV;
-    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;    // dO tile
-    R *const Ss = reinterpret_cast<R *>(smem) + Lay::oS;    // S tile [value row][d_k], later dQ staging
-    R *const dSs = reinterpret_cast<R *>(smem) + Lay::oDS;  // dS' tile, later dK staging
+    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;    // dO
     R *const Zs = reinterpret_cast<R *>(smem) + Lay::oZ;
     R *const Ps = reinterpret_cast<R *>(smem) + Lay::oP;
     R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;    // diag(beta) strict(X K^T), later dLb
     R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;
     R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;    // T, then T_g, later Mq
     R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+    R *const Qst = Ds;                                       // dQ staging (after the value phase)
+    R *const Kst = Ds + Lay::NQ;                             // dK staging
     float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
     float *const egs = gs + CH;
     float *const egls = egs + CH;
     float *const bes = egls + CH;
     float *const lams = bes + CH;
     float *const als = lams + CH;
-    float *const pdb = als + CH;         // [4][CH] per-wave row partials: dbeta
-    float *const pdl = pdb + 4 * CH;     //   dlambda
-    float *const pdg = pdl + 4 * CH;     //   dg
-    float *const psc = pdg + 4 * CH;     // [0..3] <dS', S> per wave, [4..7] sum rowdot(D_r W_z, K) per wave
+    float *const pdb = als + CH;         // [NW][CH] per-wave row partials: dbeta
+    float *const pdl = pdb + NW * CH;    //   dlambda
+    float *const pdg = pdl + NW * CH;    //   dg
+    float *const psc = pdg + NW * CH;    // [0, NW) <dS', S> per wave, [NW, 2 NW) sum rowdot(D_r W_z, K) per wave
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int T = args.T, H = args.H, dv = args.dv;
+    const int T = args.T, H = args.H;
     const int NC = (T + CH - 1) / CH;
     const int n = blockIdx.x % NC;
     const int bh = blockIdx.x / NC;
@@ -377,79 +387,56 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
     const R *__restrict__ gdo = static_cast<const R *>(args.dO);
     R *__restrict__ gdq = static_cast<R *>(args.g_q);
     R *__restrict__ gdk = static_cast<R *>(args.g_k);
+    const R *__restrict__ hs = static_cast<const R *>(args.Hs) + (static_cast<size_t>(bh) * NC + n) * DV * DK;
+    const R *__restrict__ dhs = static_cast<const R *>(args.dHs) + (static_cast<size_t>(bh) * NC + n) * DV * DK;
     auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
 
-    // ---- global loads, issued ahead of their LDS stores: the q, k rows now, and the first
-    // value tile (V, dO, S, dS' rows), which stays in registers through the Gram and
-    // inverse phase; each later tile is fetched while the previous one is computed.
-    constexpr int NLQ = (CH * VPRQ + kThreads - 1) / kThreads;       // q, k vectors per thread
-    constexpr int NLV = (CH * VPRV + kThreads - 1) / kThreads;       // v, dO vectors per thread
-    constexpr int NLS = kDVT * VPRQ / kThreads;                      // S, dS' vectors per thread
-    static_assert(kDVT * VPRQ % kThreads == 0, "S tile vectors split evenly over the threads");
-    const R *__restrict__ ghs = static_cast<const R *>(args.Hs);
-    const R *__restrict__ gdhs = static_cast<const R *>(args.dHs);
-    uint4 lv[NLV], ld[NLV], ls[NLS], lds_[NLS];
-    auto tile_load = [&](int jt) {
-        const int dv0 = jt * kDVT;
-#pragma unroll
-        for (int j = 0; j < NLV; ++j) {
-            const int vi = tid + kThreads * j;
-            lv[j] = ld[j] = make_uint4(0, 0, 0, 0);
-            if ((CH * VPRV % kThreads == 0 || vi < CH * VPRV) && vi / VPRV < clen) {
-                const size_t off = tok(t0 + vi / VPRV) * dv + dv0 + (vi % VPRV) * EPV;
-                lv[j] = *reinterpret_cast<const uint4 *>(gv + off);
-                ld[j] = *reinterpret_cast<const uint4 *>(gdo + off);
-            }
-        }
-        const size_t base = ((static_cast<size_t>(bh) * NC + n) * dv + dv0) * DK;
-#pragma unroll
-        for (int j = 0; j < NLS; ++j) {
-            const int vi = tid + kThreads * j;
-            ls[j] = *reinterpret_cast<const uint4 *>(ghs + base + vi * EPV);
-            lds_[j] = *reinterpret_cast<const uint4 *>(gdhs + base + vi * EPV);
-        }
-    };
+    // ---- global loads first: this wave's S^T and dS'^T fragments (S rows 16 wave + l % 16),
+    // then the chunk's q, k, v, dO rows
+    F sTf[NKT], dsTf[NKT];
     float sdot = 0.f;
-    auto tile_store = [&]() {
 #pragma unroll
-        for (int j = 0; j < NLV; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
-                *reinterpret_cast<uint4 *>(Vs + (vi / VPRV) * PV + (vi % VPRV) * EPV) = lv[j];
-                *reinterpret_cast<uint4 *>(Ds + (vi / VPRV) * PV + (vi % VPRV) * EPV) = ld[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NLS; ++j) {
-            const int vi = tid + kThreads * j;
-            const int o = (vi / VPRQ) * PK + (vi % VPRQ) * EPV;
-            *reinterpret_cast<uint4 *>(Ss + o) = ls[j];
-            *reinterpret_cast<uint4 *>(dSs + o) = lds_[j];
-            const R *a = reinterpret_cast<const R *>(&ls[j]);
-            const R *d = reinterpret_cast<const R *>(&lds_[j]);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) sdot += P::to_f32(a[e]) * P::to_f32(d[e]);
-        }
-    };
+    for (int t = 0; t < NKT; ++t) {
+        const size_t off = static_cast<size_t>(16 * wave + r16) * DK + 16 * t + 4 * g4;
+        sTf[t] = P::ld4(hs + off);
+        dsTf[t] = P::ld4(dhs + off);
+    }
     {
-        uint4 xq[NLQ], xk[NLQ];
+        uint4 xq[NLQ], xk[NLQ], xv[NLV], xd[NLV];
 #pragma unroll
         for (int j = 0; j < NLQ; ++j) {
-            const int vi = tid + kThreads * j;
+            const int vi = tid + NT * j;
             xq[j] = xk[j] = make_uint4(0, 0, 0, 0);
-            if ((CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) && vi / VPRQ < clen) {
+            if ((CH * VPRQ % NT == 0 || vi < CH * VPRQ) && vi / VPRQ < clen) {
                 const size_t off = tok(t0 + vi / VPRQ) * DK + (vi % VPRQ) * EPV;
                 xq[j] = *reinterpret_cast<const uint4 *>(gq + off);
                 xk[j] = *reinterpret_cast<const uint4 *>(gk + off);
             }
         }
-        tile_load(0);
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int vi = tid + NT * j;
+            xv[j] = xd[j] = make_uint4(0, 0, 0, 0);
+            if ((CH * VPRV % NT == 0 || vi < CH * VPRV) && vi / VPRV < clen) {
+                const size_t off = tok(t0 + vi / VPRV) * DV + (vi % VPRV) * EPV;
+                xv[j] = *reinterpret_cast<const uint4 *>(gv + off);
+                xd[j] = *reinterpret_cast<const uint4 *>(gdo + off);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NLQ; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+            const int vi = tid + NT * j;
+            if (CH * VPRQ % NT == 0 || vi < CH * VPRQ) {
                 *reinterpret_cast<uint4 *>(Qs + (vi / VPRQ) * PK + (vi % VPRQ) * EPV) = xq[j];
                 *reinterpret_cast<uint4 *>(Ks + (vi / VPRQ) * PK + (vi % VPRQ) * EPV) = xk[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int vi = tid + NT * j;
+            if (CH * VPRV % NT == 0 || vi < CH * VPRV) {
+                *reinterpret_cast<uint4 *>(Vs + (vi / VPRV) * PV + (vi % VPRV) * EPV) = xv[j];
+                *reinterpret_cast<uint4 *>(Ds + (vi / VPRV) * PV + (vi % VPRV) * EPV) = xd[j];
             }
         }
     }
@@ -473,15 +460,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
             als[lane] = a;
         }
     }
-    for (int i = tid; i < 3 * 4 * CH + 8; i += kThreads) pdb[i] = 0.f;
+    for (int i = tid; i < 3 * NW * CH + 2 * NW; i += NT) pdb[i] = 0.f;
     __syncthreads();
 
     // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
-    gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
+    gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, NW>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
     __syncthreads();
     unit_lower_inverse<P, CH, PC>(Ls, Ts);
     if constexpr (HAS_A) {
-        for (int idx = tid; idx < NPAIR * 64; idx += kThreads) {
+        for (int idx = tid; idx < NPAIR * 64; idx += NT) {
             int i, j;
             tri_pair(idx >> 6, i, j);
             const int r = 16 * i + ((idx >> 2) & 15);
@@ -497,30 +484,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
         __syncthreads();
     }
 
-    // ---- value tiles: column-local quantities per wave, then the value contractions
-    f32x4 Wo[NCT][NKW], Wp[NCT][NKW], Wz[NCT][NKW];
-    f32x4 dAacc[PPW], dLacc[PPW];
-#pragma unroll
-    for (int mt = 0; mt < NCT; ++mt) {
-#pragma unroll
-        for (int c = 0; c < NKW; ++c) Wo[mt][c] = Wp[mt][c] = Wz[mt][c] = zero4();
-    }
-#pragma unroll
-    for (int u = 0; u < PPW; ++u) dAacc[u] = dLacc[u] = zero4();
-
-    for (int jt = 0; jt < args.n_dvt; ++jt) {
-        if (jt > 0) __syncthreads();   // every wave is done with the previous tile
-        tile_store();
-        if (jt + 1 < args.n_dvt) tile_load(jt + 1);
-        __syncthreads();
-
-        // column-local part, value columns [16 wave, 16 wave + 16) of the tile
-        F sTf[NKT], dsTf[NKT];
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            sTf[t] = frag<P>(Ss, PK, 16 * wave, 16 * t);     // B-fragments of S^T and dS'^T
-            dsTf[t] = frag<P>(dSs, PK, 16 * wave, 16 * t);
-        }
+    // ---- column-local part: value columns [16 wave, 16 wave + 16)
+    {
         f32x4 Rr[NCT], dZ[NCT];
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
@@ -538,6 +503,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
             const f32x4 vf = P::f32(frag_b<P>(Vs, PV, 16 * mt, 16 * wave));
             Rr[mt] = HAS_A ? vf - lds_f32x4(egs + 16 * mt + 4 * g4) * y : vf - y;
             dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+        }
+        if constexpr (HAS_A) {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                const f32x4 a = P::f32(sTf[t]), d = P::f32(dsTf[t]);
+                sdot += a[0] * d[0] + a[1] * d[1] + a[2] * d[2] + a[3] * d[3];
+            }
         }
         // Z = T_g diag(beta) R;  dZ += A^T dO
         F bRf[NCT];
@@ -560,76 +532,73 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
             dZf[mt] = P::cvt(dZ[mt]);
             Zf[mt] = P::cvt(Z[mt]);
         }
-        f32x4 Pm[NCT];
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt) {
-            Pm[mt] = zero4();
+            f32x4 Pm = zero4();
 #pragma unroll
-            for (int s = mt; s < NCT; ++s) Pm[mt] = P::mma1(Pm[mt], frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
+            for (int s = mt; s < NCT; ++s) Pm = P::mma1(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
             f32x4 U = Rr[mt];
 #pragma unroll
             for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float db = sum16(Pm[mt][e] * U[e]);
-                if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] += db;   // this wave's row partial
-            }
-        }
-        // Z and P of the tile to LDS for the value contractions
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
+                const float db = sum16(Pm[e] * U[e]);
                 const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
+                if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = db;
                 Zs[o] = P::from_f32(Z[mt][e]);
-                Ps[o] = P::from_f32(Pm[mt][e]);
-            }
-        }
-        __syncthreads();
-
-        // dA += dO Z^T, dL += P Z^T on this wave's lower blocks
-#pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const int p = wave + 4 * u;
-            if (p < NPAIR) {
-                int i, j;
-                tri_pair(p, i, j);
-#pragma unroll
-                for (int vv = 0; vv < kDVT / 16; vv += 2) {
-                    const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
-                    dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
-                                       z0, z1);
-                    dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
-                                       z0, z1);
-                }
-            }
-        }
-        // W_o += dO S, W_p += P S, W_z += Z dS' on this wave's d_k blocks
-#pragma unroll
-        for (int c = 0; c < NKW; ++c) {
-            const int kk = NKW * wave + c;
-#pragma unroll
-            for (int vv = 0; vv < kDVT / 16; vv += 2) {
-                const F s0 = frag_b<P>(Ss, PK, 16 * vv, 16 * kk), s1 = frag_b<P>(Ss, PK, 16 * vv + 16, 16 * kk);
-                const F d0 = frag_b<P>(dSs, PK, 16 * vv, 16 * kk), d1 = frag_b<P>(dSs, PK, 16 * vv + 16, 16 * kk);
-#pragma unroll
-                for (int mt = 0; mt < NCT; ++mt) {
-                    Wo[mt][c] = P::mma2(Wo[mt][c], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16),
-                                        s0, s1);
-                    Wp[mt][c] = P::mma2(Wp[mt][c], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16),
-                                        s0, s1);
-                    Wz[mt][c] = P::mma2(Wz[mt][c], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16),
-                                        d0, d1);
-                }
+                Ps[o] = P::from_f32(Pm[e]);
             }
         }
     }
-    __syncthreads();   // the tile buffers, T_g and L are free from here on
+    __syncthreads();
 
-    // ---- dA and dL on this wave's blocks -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
+    // ---- value contractions over all d_v: dA = dO Z^T, dL = P Z^T on this wave's lower blocks
+    f32x4 dAacc[PPW], dLacc[PPW];
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
-        const int p = wave + 4 * u;
+        dAacc[u] = dLacc[u] = zero4();
+        const int p = wave + NW * u;
+        if (p < NPAIR) {
+            int i, j;
+            tri_pair(p, i, j);
+#pragma unroll
+            for (int vv = 0; vv < NVT; vv += 2) {
+                const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
+                dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
+                                   z0, z1);
+                dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
+                                   z0, z1);
+            }
+        }
+    }
+    // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk);
+    // the B fragments S[16 vv + 4 g + i][16 kk + l % 16] come from global memory (rows other
+    // waves have just read, so mostly from L2; staging them through LDS measured no faster)
+    f32x4 Wo[NBW], Wp[NBW], Wz[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        Wo[j] = Wp[j] = Wz[j] = zero4();
+        const int blk = wave + NW * j;
+        if (NB % NW == 0 || blk < NB) {
+            const int mt = blk / NKT, kk = blk % NKT;
+#pragma unroll
+            for (int vv = 0; vv < NVT; vv += 2) {
+                const size_t o0 = static_cast<size_t>(16 * vv + 4 * g4) * DK + 16 * kk + r16;
+                const size_t o1 = o0 + static_cast<size_t>(16) * DK;
+                const F s0 = P::ld4_strided(hs + o0, DK), s1 = P::ld4_strided(hs + o1, DK);
+                const F d0 = P::ld4_strided(dhs + o0, DK), d1 = P::ld4_strided(dhs + o1, DK);
+                Wo[j] = P::mma2(Wo[j], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16), s0, s1);
+                Wp[j] = P::mma2(Wp[j], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16), s0, s1);
+                Wz[j] = P::mma2(Wz[j], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16), d0, d1);
+            }
+        }
+    }
+    __syncthreads();   // T_g, L, v, dO, Z, P are free from here on
+
+    // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int p = wave + NW * u;
         if (p < NPAIR) {
             int i, j;
             tri_pair(p, i, j);
@@ -648,63 +617,59 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
     }
     __syncthreads();   // Mq and dLb published
 
-    // ---- on this wave's d_k blocks:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K, and
+    // ---- per d_k block:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K;
     //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
-    //   dK = KT + D_r W_z + dX.
-    // The decay gradient's pair terms are row dot products of these products:
-    //   rowsum(dA o A) + rowsum(dL o beta N) = rowdot(Q, MqK) + rowdot(K, LbK),
-    //   colsum(dA o A) + colsum(dL o beta N) = rowdot(K, KT),
-    // taken from the fp32 accumulators with the exact q and k.
+    //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms are rowdot(Q, MqK) +
+    //   rowdot(K, LbK) - rowdot(K, KT) (the row and column sums of dA o A and dL o beta N
+    //   regrouped, from fp32 accumulators and the exact q and k)
     float wz = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < NCT; ++mt) {
-        const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
-        const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
-        f32x4 dlp = zero4(), dgp = zero4();
-#pragma unroll
-        for (int c = 0; c < NKW; ++c) {
-            const int kk = NKW * wave + c;
+    for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + NW * j;
+        if (NB % NW == 0 || blk < NB) {
+            const int mt = blk / NKT, kk = blk % NKT;
+            const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
+            const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
             f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
 #pragma unroll
-            for (int s = 0; s <= mt; ++s) {
-                const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
-                lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
-                mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
+            for (int s = 0; s < NCT; ++s) {
+                if (s <= mt) {
+                    const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
+                    lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
+                    mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
+                }
+                if (s >= mt) {
+                    kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
+                    kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
+                }
             }
-#pragma unroll
-            for (int s = mt; s < NCT; ++s) {
-                kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
-                kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
-            }
-            const f32x4 dX = lbk - eg * bt * Wp[mt][c];
-            const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[mt][c] - lm * bt * Wp[mt][c]) : eg * Wo[mt][c]);
-            const f32x4 dK = kt + el * Wz[mt][c] + dX;
+            const f32x4 dX = lbk - eg * bt * Wp[j];
+            const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[j] - lm * bt * Wp[j]) : eg * Wo[j]);
+            const f32x4 dK = kt + el * Wz[j] + dX;
             const f32x4 qf = P::f32(frag_b<P>(Qs, PK, 16 * mt, 16 * kk));
             const f32x4 kf = P::f32(frag_b<P>(Ks, PK, 16 * mt, 16 * kk));
-            if constexpr (HAS_L) dlp += qf * dX;
+            f32x4 dgp = zero4();
             if constexpr (HAS_A) {
                 const f32x4 xf = HAS_L ? kf + lm * qf : kf;
-                const f32x4 wzk = el * Wz[mt][c] * kf;
-                dgp += qf * mqk + kf * lbk - kf * kt + eg * (Wo[mt][c] * qf - bt * Wp[mt][c] * xf) - wzk;
+                const f32x4 wzk = el * Wz[j] * kf;
+                dgp = qf * mqk + kf * lbk - kf * kt + eg * (Wo[j] * qf - bt * Wp[j] * xf) - wzk;
                 wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
             }
+            const f32x4 dlp = HAS_L ? qf * dX : zero4();
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int o = (16 * mt + 4 * g4 + e) * PK + 16 * kk + r16;
-                Ss[o] = P::from_f32(dQ[e]);
-                dSs[o] = P::from_f32(dK[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * mt + 4 * g4 + e;
-            if constexpr (HAS_L) {
-                const float rs = sum16(dlp[e]);
-                if (r16 == 0) pdl[wave * CH + r] = rs;
-            }
-            if constexpr (HAS_A) {
-                const float rs = sum16(dgp[e]);
-                if (r16 == 0) pdg[wave * CH + r] = rs;
+                const int r = 16 * mt + 4 * g4 + e;
+                const int o = r * PK + 16 * kk + r16;
+                Qst[o] = P::from_f32(dQ[e]);
+                Kst[o] = P::from_f32(dK[e]);
+                if constexpr (HAS_L) {
+                    const float rs = sum16(dlp[e]);
+                    if (r16 == 0) pdl[wave * CH + r] += rs;
+                }
+                if constexpr (HAS_A) {
+                    const float rs = sum16(dgp[e]);
+                    if (r16 == 0) pdg[wave * CH + r] += rs;
+                }
             }
         }
     }
@@ -713,31 +678,38 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_grad_kernel(const BwdAr
         const float sd = sum64(sdot);
         if (lane == 0) {
             psc[wave] = sd;
-            psc[4 + wave] = wz;
+            psc[NW + wave] = wz;
         }
     }
     __syncthreads();
 
     // ---- stores: dQ, dK rows; per-token dbeta, dlambda, dalpha
-    for (int vi = tid; vi < CH * VPRQ; vi += kThreads) {
+    for (int vi = tid; vi < CH * VPRQ; vi += NT) {
         const int c = vi / VPRQ, cv = vi % VPRQ;
         if (c < clen) {
             const size_t off = tok(t0 + c) * DK + cv * EPV;
-            *reinterpret_cast<uint4 *>(gdq + off) = *reinterpret_cast<const uint4 *>(Ss + c * PK + cv * EPV);
-            *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(dSs + c * PK + cv * EPV);
+            *reinterpret_cast<uint4 *>(gdq + off) = *reinterpret_cast<const uint4 *>(Qst + c * PK + cv * EPV);
+            *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(Kst + c * PK + cv * EPV);
         }
     }
     if (wave == 0) {
         float db = 0.f, dl = 0.f, dg = 0.f;
         if (lane < CH) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 db += pdb[w * CH + lane];
                 dl += pdl[w * CH + lane];
                 dg += pdg[w * CH + lane];
             }
-            if (HAS_A && lane == CH - 1)
-                dg += egs[CH - 1] * (psc[0] + psc[1] + psc[2] + psc[3]) + (psc[4] + psc[5] + psc[6] + psc[7]);
+            if (HAS_A && lane == CH - 1) {
+                float sd = 0.f, wzs = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    sd += psc[w];
+                    wzs += psc[NW + w];
+                }
+                dg += egs[CH - 1] * sd + wzs;
+            }
         }
         // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
 #pragma unroll
@@ -761,8 +733,12 @@ hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || NC == 0) return err;
-    hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(kThreads), 0,
-                       stream, a);
+    if (a.dv == 128)
+        hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, 128, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(512), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, 64, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -33,23 +33,23 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
 
 namespace qd {
 
-// Gram blocks of one chunk, four waves over the lower block triangle.  Each block is
+// Gram blocks of one chunk, NW waves over the lower block triangle.  Each block is
 // computed transposed (D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c], r = 16i + l%16,
 // c = 16j + 4g + e) so a lane owns four consecutive columns of a row.  Writes
 //   L = strictly-lower(diag(beta) X K^T),  X K^T = K K^T + diag(lambda) Q K^T,
 //   A = G o lower(Q K^T),   and, when N is non-null,  N = G o strictly-lower(X K^T),
 // with G[r][c] = exp(g_r - g_c).  Blocks above the block diagonal are not written.
-template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L>
+template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int NW = 4>
 __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
                                             const float *bes, const float *lams, typename P::R *Ls,
                                             typename P::R *As, typename P::R *Ns) {
     using F = typename P::F;
     constexpr int NKT = DK / 16, NCT = CH / 16;
-    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + 3) / 4;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
     const int wave = wave_id(), lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
-        const int p = wave + 4 * u;
+        const int p = wave + NW * u;
         if (p < NPAIR) {
             int i, j;
             tri_pair(p, i, j);
@@ -82,7 +82,8 @@ __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typen
     }
 }
 
-// T = (I + L)^-1 for the strictly lower CH x CH matrix L in LDS (pitch PC), four waves.
+// T = (I + L)^-1 for the strictly lower CH x CH matrix L in LDS (pitch PC), by the first
+// four waves of the workgroup (every wave must call it: it holds the barriers).
 // The 16 x 16 diagonal blocks by forward substitution over rows (t_r = e_r -
 // sum_{j<r} L[r][j] t_j; wave w inverts block w, lane l computes column l % 16), then
 // block doubling on MFMA (T21 = -T22 L21 T11 for 16- and then 32-row halves).  Only
@@ -129,15 +130,17 @@ __device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, type
     // level 2 (CH = 64): lower-left 32x32 quadrant, one 16x16 block per wave:
     // T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
     if constexpr (NCT == 4) {
-        const int ab = 2 + (wave >> 1), cb_ = wave & 1;
-        f32x4 acc = zero4();
-        for (int m = 2; m <= ab; ++m) {
-            f32x4 x = zero4();
-            for (int kb = cb_; kb <= 1; ++kb)
-                x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
-            acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
+        if (wave < 4) {
+            const int ab = 2 + (wave >> 1), cb_ = wave & 1;
+            f32x4 acc = zero4();
+            for (int m = 2; m <= ab; ++m) {
+                f32x4 x = zero4();
+                for (int kb = cb_; kb <= 1; ++kb)
+                    x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
+                acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
+            }
+            tstore(ab, cb_, -acc);
         }
-        tstore(ab, cb_, -acc);
         __syncthreads();
     }
 }
