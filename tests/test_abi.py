@@ -101,3 +101,80 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qd, "LIB_PATH", str(tmp_path / "libqdelta.so"))
     with pytest.raises(qd.QDeltaError):
         qd.load_library()
+
+
+# ---------------------------------------------------------------- backward, QED, EDA entry points
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, alpha=FAKE * 4, beta=FAKE * 5, lam=FAKE * 6, S0=None, d_o=FAKE * 7,
+             dS_T=None, dq=FAKE * 8, dk=FAKE * 9, dv=FAKE * 10, dalpha=FAKE * 11, dbeta=FAKE * 12, dlam=FAKE * 13,
+             dS0=None, B=1, T=4, H=1, d_k=64, d_v=64, C=32, dtype=1, ws=FAKE * 64, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.qdelta_chunk_bwd(*[a[n] for n in ("q", "k", "v", "alpha", "beta", "lam", "S0", "d_o", "dS_T", "dq",
+                                                 "dk", "dv", "dalpha", "dbeta", "dlam", "dS0")],
+                                a["B"], a["T"], a["H"], a["d_k"], a["d_v"], a["C"], a["dtype"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+def test_chunk_bwd_host_side_rejections(lib):
+    assert _bwd(lib, C=64, dtype=0) == QD_ERR_UNSUPPORTED          # fp32 at C = 64
+    assert _bwd(lib, d_k=96) == QD_ERR_UNSUPPORTED
+    assert _bwd(lib, T=-1) == QD_ERR_INVALID_ARG
+    assert _bwd(lib, d_o=None) == QD_ERR_INVALID_ARG
+    assert _bwd(lib, dbeta=None) == QD_ERR_INVALID_ARG
+    assert _bwd(lib, alpha=None) == QD_ERR_INVALID_ARG             # dalpha given without alpha
+    assert _bwd(lib, lam=None) == QD_ERR_INVALID_ARG               # dlambda given without lambda
+    assert _bwd(lib, ws=None) == QD_ERR_WORKSPACE
+    assert _bwd(lib, ws_bytes=16) == QD_ERR_WORKSPACE
+    assert _bwd(lib, dq=FAKE) == QD_ERR_INVALID_ARG                # dq aliases q
+    assert _bwd(lib, dk=FAKE * 8) == QD_ERR_INVALID_ARG            # dk aliases dq
+    assert _bwd(lib, ws=FAKE * 9) == QD_ERR_INVALID_ARG            # workspace over dk
+    assert _bwd(lib, B=0) == QD_OK
+
+
+def test_chunk_bwd_workspace_formula(lib):
+    # entry states and exit-state gradients per chunk, in the element type
+    assert lib.qdelta_chunk_bwd_workspace_bytes(2, 100, 3, 64, 128, 32, 1) == 2 * 3 * 4 * 2 * 128 * 64 * 2
+    assert lib.qdelta_chunk_bwd_workspace_bytes(2, 100, 3, 64, 128, 32, 0) == 2 * 3 * 4 * 2 * 128 * 64 * 4
+    assert lib.qdelta_chunk_bwd_workspace_bytes(2, 0, 3, 64, 128, 32, 1) == 0
+    assert lib.qdelta_chunk_bwd_workspace_bytes(2, 100, 3, 64, 128, 64, 0) == 0      # unsupported
+
+
+def _qed(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, b=FAKE * 5, w=FAKE * 6, lam=FAKE * 7, S0=None, o=FAKE * 8,
+             S_T=None, B=1, T=4, H=1, d_k=64, d_v=64, C=32, dtype=1)
+    a.update(kw)
+    return lib.qdelta_qed_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["b"], a["w"], a["lam"], a["S0"], a["o"],
+                                    a["S_T"], a["B"], a["T"], a["H"], a["d_k"], a["d_v"], a["C"], a["dtype"], None)
+
+
+def test_qed_host_side_rejections(lib):
+    assert _qed(lib, C=64) == QD_ERR_UNSUPPORTED
+    assert _qed(lib, C=32, dtype=0) == QD_ERR_UNSUPPORTED
+    assert _qed(lib, lam=None) == QD_ERR_INVALID_ARG
+    assert _qed(lib, g=None) == QD_ERR_INVALID_ARG
+    assert _qed(lib, g=FAKE * 4 + 4) == QD_ERR_INVALID_ARG         # misaligned gate rows
+    assert _qed(lib, o=FAKE * 6) == QD_ERR_INVALID_ARG             # o aliases w
+    assert _qed(lib, B=0) == QD_OK
+    assert lib.qdelta_qed_step(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, None, FAKE * 64, FAKE * 8,
+                               2, 2, 64, 64, 1, None) == QD_ERR_INVALID_ARG
+    assert lib.qdelta_qed_step(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 64,
+                               FAKE * 8, 0, 2, 64, 64, 1, None) == QD_OK
+
+
+def _eda(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, e=FAKE * 4, S0=None, o=FAKE * 5, S_T=None, B=1, T=4, H=1, d_k=64,
+             d_v=64, C=32, dtype=1, ws=FAKE * 64, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.qdelta_eda_chunk_fwd(a["q"], a["k"], a["v"], a["e"], a["S0"], a["o"], a["S_T"], a["B"], a["T"],
+                                    a["H"], a["d_k"], a["d_v"], a["C"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def test_eda_host_side_rejections(lib):
+    assert _eda(lib, e=None) == QD_ERR_INVALID_ARG
+    assert _eda(lib, ws=None) == QD_ERR_WORKSPACE
+    assert _eda(lib, o=FAKE * 4) == QD_ERR_INVALID_ARG             # o aliases e
+    assert _eda(lib, C=48) == QD_ERR_UNSUPPORTED
+    assert _eda(lib, B=0) == QD_OK
+    # the interleaved sequence and its outputs: 2 B T H ((2 d_k + 2 d_v) e + 4) bytes, the last term rounded up to 16
+    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 32, 1) == 2 * 2 * 10 * 3 * ((2 * 64 + 2 * 128) * 2) + 480
+    assert lib.qdelta_eda_step(FAKE, FAKE * 2, FAKE * 3, None, FAKE * 64, FAKE * 5, 2, 2, 64, 64, 1, None) == QD_ERR_INVALID_ARG
