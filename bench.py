@@ -257,7 +257,7 @@ def main():
         eo = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
         eS = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         nws = qd.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
-        ews = torch.empty(nws, dtype=torch.uint8, device=dev)
+        ews = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         ef = lambda: qd.qdelta_eda_chunk_fwd(eq, ek, ev, ee, None, C=C, o=eo, S_T=eS, workspace=ews)
         for _ in range(args.warmup):
             ef()
@@ -283,7 +283,7 @@ def main():
         log(f"[bench] EDA chunk forward {e_ms:.4f} ms/call, {B * T / (e_ms * 1e-3) / 1e6:.2f} M tokens/s; "
             f"EDA decode {d_us:.2f} us/step, {dbytes / (d_us * 1e-6) / 1e9:.0f} GB/s")
         return {"chunk_fwd": {"workload": "Erase-then-Delta layer forward, B=8 T=4096 H=16 d_k=d_v=128 C=64, bf16 "
-                                          "q/k/e/v/o; run as DeltaNet over the interleaved 2T-token sequence",
+                                          "q/k/e/v/o; DeltaNet over the interleaved 2T-token sequence, read in place",
                               "steps": steps, "ms_per_call": e_ms, "tokens_per_s": B * T / (e_ms * 1e-3),
                               "workspace_bytes": nws, "algorithmic_bytes_per_call": ebytes,
                               "hbm_frac": ebytes / (e_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},

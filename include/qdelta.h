@@ -226,8 +226,10 @@ int qdelta_qed_step(const void *q, const void *k, const void *v,
  * [B][T][H][d_v] in the dtype's elements; S0, S_T, C, dtype and the other sizes as for
  * qdelta_chunk_fwd.  The erase is a delta step with key e, value 0 and beta 1, so the
  * chunked form is DeltaNet over the interleaved sequence e_1, k_1, e_2, k_2, ... read at
- * the k tokens: the call writes that sequence into the workspace, runs the chunk forward
- * over it and gathers o.  workspace: at least qdelta_eda_chunk_fwd_workspace_bytes
+ * the k tokens.  In bf16 at C = 32 or 64 the kernel reads that sequence in place and
+ * needs no workspace (the size query returns 0; workspace may be NULL).  Otherwise the
+ * call writes the sequence into the workspace, runs the chunk forward over it and
+ * gathers o; workspace: at least qdelta_eda_chunk_fwd_workspace_bytes
  * (2*B*T*H*((2 d_k + 2 d_v) e + 4) bytes, e = element size), 16-byte aligned, disjoint
  * from every other argument; QD_ERR_WORKSPACE otherwise.
  */

@@ -155,7 +155,7 @@ int qdelta_qed_step(const void *q, const void *k, const void *v, const float *g,
 size_t qdelta_eda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C, int dtype) {
     if (B < 0 || T < 0 || H < 0 || !qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return 0;
     if (static_cast<long long>(B) * T * H == 0) return 0;
-    return qd::eda_chunk_workspace(dtype, B, T, H, d_k, d_v);
+    return qd::eda_chunk_workspace(dtype, B, T, H, d_k, d_v, C);
 }
 
 int qdelta_eda_chunk_fwd(const void *q, const void *k, const void *v, const void *e, const float *S0, void *o,

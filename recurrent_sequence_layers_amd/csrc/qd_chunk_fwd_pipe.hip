@@ -265,8 +265,15 @@ constexpr int tile_mask(const int (&t)[4], int n) {
 // while the chunk is staged into LDS, so everything downstream is the same as without.
 // STATES: also keep every chunk's entry state S (bf16, [B][H][NC][d_v][d_k], ChunkArgs::Hs)
 // for the backward.
-template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW, bool STATES = false>
+// EDA: Erase-then-Delta, DeltaNet (beta = 1) over the interleaved sequence e_1, k_1, e_2,
+// k_2, ... read in place: chunk row 2i is an erase token (key e_i, query and value 0) and
+// row 2i + 1 the write token (k_i, q_i, v_i) of token i of the chunk's C / 2; outputs are
+// stored for the odd rows only.  The staging map gives every wave rows of one parity, so
+// the source of the key rows (e or k) is uniform per wave; the query rows of the erase
+// tokens are zeroed once and never written.
+template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW, bool STATES = false, bool EDA = false>
 struct PipeKernel {
+    static_assert(!EDA || (!HAS_A && !HAS_L && !RAW && !STATES), "Erase-then-Delta is the plain beta = 1 delta rule");
     using Lay = PipeLayout<DK, CH>;
     static constexpr int NKT = DK / 16, NKP = DK / 32;
     static constexpr int NCT = CH / 16, NCP = CH / 32;
@@ -419,13 +426,21 @@ struct PipeKernel {
         const int h = bh % args.H;
         const int T = args.T, H = args.H, dv = args.dv;
         const int dv0 = dvt * kDVT;
-        const int NC = (T + CH - 1) / CH;
-        auto chunk_len = [&](int c) { return min(CH, T - c * CH); };
+        // rows of the sequence the chunks walk (2T for the interleaved sequence), and tokens
+        // of memory per chunk
+        const int TS = EDA ? 2 * T : T;
+        constexpr int TPC = EDA ? CH / 2 : CH;
+        const int NC = (TS + CH - 1) / CH;
+        auto chunk_len = [&](int c) { return min(CH, TS - c * CH); };
+        auto chunk_tok = [&](int c) { return EDA ? chunk_len(c) / 2 : chunk_len(c); };
 
         // token 0 of this (batch, head); consecutive tokens are H rows apart
         const size_t tok0 = static_cast<size_t>(b) * T * H + h;
         const uint16_t *const qbase = static_cast<const uint16_t *>(args.q) + tok0 * DK;
         const uint16_t *const kbase = static_cast<const uint16_t *>(args.k) + tok0 * DK;
+        // key rows of this wave's staging: the erase directions for the even rows of EDA
+        const bool erase_rows = EDA && (rw & 1) == 0;
+        const uint16_t *const krows = erase_rows ? static_cast<const uint16_t *>(args.e) + tok0 * DK : kbase;
         // v == null reads as zeros and o == null drops the output (state-only passes of the
         // segmented schedule): their buffer resources get an empty range, so no branch is
         // needed in the loop and no address is formed from a null pointer
@@ -449,17 +464,25 @@ struct PipeKernel {
         // q / k: one wave instruction reads 16 / NKP whole rows; the 16 lanes of a group read
         // four consecutive rows at the four key quads of one fragment step (lane 16G + 4i + g:
         // row 4 (G / NKP) + i, quad kq(g, G % NKP)), so their fragment slots fall on distinct banks.
+        // EDA: instruction m = 4j + rw covers rows of parity m & 1 (= rw & 1), 16 / NKP of
+        // them two apart; row r is token r / 2 of the chunk.
         const int vv_row = rt / VPRV, vv_col = rt % VPRV;
         int voffQ[NVQ], ldsQ[NVQ], voffV[NVV];
 #pragma unroll
         for (int j = 0; j < NVQ; ++j) {
-            const int row = (4 * j + rw) * (16 / NKP) + 4 * (g4 / NKP) + (r16 >> 2);
+            const int m = 4 * j + rw, loc = 4 * (g4 / NKP) + (r16 >> 2);
+            const int row = EDA ? 2 * (16 / NKP) * (m >> 1) + 2 * loc + (m & 1) : m * (16 / NKP) + loc;
             const int u = g4 % NKP, g = r16 & 3;
-            voffQ[j] = row * rowQ + 16 * kq(g, u);
+            voffQ[j] = (EDA ? row >> 1 : row) * rowQ + 16 * kq(g, u);
             ldsQ[j] = qk_off(row >> 4, u, g, row & 15);
         }
+        // an offset past every buffer range: loads of it read zeros, stores to it are dropped
+        constexpr int kNoRow = 0x7ffffff0;
 #pragma unroll
-        for (int j = 0; j < NVV; ++j) voffV[j] = (vv_row + j * RJV) * rowV + vv_col * 16;
+        for (int j = 0; j < NVV; ++j) {
+            const int row = vv_row + j * RJV;
+            voffV[j] = !EDA ? row * rowV + vv_col * 16 : (row & 1) ? (row >> 1) * rowV + vv_col * 16 : kNoRow;
+        }
         const int voffG = (rt & (kWave - 1)) * rowG;
         const int ldsV = vv_row * PV + vv_col * 8;        // + j * RJV * PV
 
@@ -470,14 +493,14 @@ struct PipeKernel {
             float a, b, l;
         };
         auto gload = [&](int c, Prefetch &pf) {
-            const int clen = chunk_len(c);
-            const size_t t0 = static_cast<size_t>(c) * CH * H;
+            const int clen = chunk_tok(c);
+            const size_t t0 = static_cast<size_t>(c) * TPC * H;
             const auto rsq = buffer_rsrc(qbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
-            const auto rsk = buffer_rsrc(kbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
+            const auto rsk = buffer_rsrc(krows + t0 * DK, (clen - 1) * rowQ + DK * 2);
             const auto rsv = buffer_rsrc(vbase + (has_v ? t0 * dv : 0), has_v ? (clen - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
-                pf.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voffQ[j], 0, 0);
+                if (!erase_rows) pf.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voffQ[j], 0, 0);
                 pf.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, voffQ[j], 0, 0);
             }
 #pragma unroll
@@ -487,7 +510,9 @@ struct PipeKernel {
             pf.l = 0.f;
             if constexpr (HAS_A)
                 pf.a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.alpha + tok0 + t0, gbytes), voffG, 0, 0));
-            pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.beta + tok0 + t0, gbytes), voffG, 0, 0));
+            pf.b = 1.f;
+            if constexpr (!EDA)
+                pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.beta + tok0 + t0, gbytes), voffG, 0, 0));
             if constexpr (HAS_L)
                 pf.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.lam + tok0 + t0, gbytes), voffG, 0, 0));
         };
@@ -500,7 +525,7 @@ struct PipeKernel {
                     *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = normalise_row_segment<NKP>(pf.q[j]);
                     *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = normalise_row_segment<NKP>(pf.k[j]);
                 } else {
-                    *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
+                    if (!erase_rows) *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
                     *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
                 }
             }
@@ -525,6 +550,9 @@ struct PipeKernel {
         // pair is read by the scan's paired products and must hold zeros
         for (int i = tid; i < 3 * Lay::NCC / 8; i += kPipeThreads)
             reinterpret_cast<u32x4 *>(base + Lay::oA)[i] = u32x4{0, 0, 0, 0};
+        if constexpr (EDA)                        // query rows of the erase tokens, both slots
+            for (int i = tid; i < 2 * Lay::NQ / 8; i += kPipeThreads)
+                reinterpret_cast<u32x4 *>(base + Lay::oQ)[i] = u32x4{0, 0, 0, 0};
 
         if (NC == 0) {
             if (is_scan && args.S_T) {
@@ -755,8 +783,8 @@ struct PipeKernel {
                 // for the output stores
                 if (n + 2 < NC) rstore(n + 2, pf); // into slot n & 1, released in I3
                 if (n >= 0) {
-                    const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * CH * H * dv : 0),
-                                                 has_o ? (chunk_len(n) - 1) * rowV + kDVT * 2 : 0);
+                    const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * TPC * H * dv : 0),
+                                                 has_o ? (chunk_tok(n) - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
                     for (int j = 0; j < NVV; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),
@@ -794,6 +822,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_states_kernel(
 }
 
 template <int DK, int CH>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_eda_kernel(const ChunkArgs args) {
+    PipeKernel<DK, CH, false, false, false, false, true>::run(args);
+}
+
+template <int DK, int CH>
+hipError_t launch_pipe_eda(const ChunkArgs &a, hipStream_t stream) {
+    const int grid = a.B * a.H * a.n_dvt;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_fwd_pipe_eda_kernel<DK, CH>), dim3(grid), dim3(kPipeThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, int CH>
 hipError_t launch_pipe_states(const ChunkArgs &a, hipStream_t stream) {
     const int grid = a.B * a.H * a.n_dvt;
     if (grid == 0) return hipSuccess;
@@ -827,6 +868,11 @@ hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_chunk_fwd_pipe_eda(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
+    if (dk == 128) return C == 64 ? launch_pipe_eda<128, 64>(a, stream) : launch_pipe_eda<128, 32>(a, stream);
+    return C == 64 ? launch_pipe_eda<64, 64>(a, stream) : launch_pipe_eda<64, 32>(a, stream);
+}
 
 hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
     if (dk == 128) return C == 64 ? launch_pipe_states<128, 64>(a, stream) : launch_pipe_states<128, 32>(a, stream);

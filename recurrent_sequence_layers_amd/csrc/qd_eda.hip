@@ -7,7 +7,9 @@
 // The erase is itself a delta-rule step with key e, value 0 and beta = 1, so the layer
 // is DeltaNet (beta = 1) over the interleaved sequence e_1, k_1, e_2, k_2, ... with zero
 // values at the erase tokens, read out at the k tokens.  The chunked forward runs exactly
-// that: an interleave kernel writes the 2T-token sequence into the caller's workspace, the
+// that.  In bf16 at C = 32, 64 the eight-wave chunk kernel's EDA instance reads the
+// interleaved sequence in place (qd_chunk_fwd_pipe.hip).  The other instances build it:
+// an interleave kernel writes the 2T-token sequence into the caller's workspace, the
 // chunk forward (its alpha = 1, lambda = 0 instance) runs over it, and a gather kernel
 // keeps the outputs of the k tokens.  The decode step is its own kernel: from one read of
 // a state row, S e, S k and S q give the erased row's products through e.k and e.q.
@@ -151,7 +153,12 @@ hipError_t launch_eda_step_p(int dk, int dv, const EdaStepArgs &a, hipStream_t s
 
 }  // namespace
 
-size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv) {
+// bf16 at C = 32, 64 reads the interleaved sequence in place (no workspace); the other
+// instances build it in the workspace
+static bool eda_in_place(int dtype, int C) { return dtype == 1 && (C == 32 || C == 64); }
+
+size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv, int C) {
+    if (eda_in_place(dtype, C)) return 0;
     const size_t es = dtype == 1 ? 2 : 4;
     const size_t rows2 = 2 * static_cast<size_t>(B) * T * H;
     // q2, k2 [B][2T][H][d_k]; v2, o2 [B][2T][H][d_v]; beta2 [B][2T][H]
@@ -159,6 +166,14 @@ size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv) {
 }
 
 hipError_t launch_eda_chunk(int dtype, int dk, int C, const EdaChunkArgs &a, void *ws, hipStream_t stream) {
+    if (eda_in_place(dtype, C)) {
+        ChunkArgs f;
+        f.q = a.q; f.k = a.k; f.v = a.v; f.e = a.e;
+        f.alpha = nullptr; f.beta = nullptr; f.lam = nullptr;
+        f.S0 = a.S0; f.o = a.o; f.S_T = a.S_T;
+        f.B = a.B; f.T = a.T; f.H = a.H; f.dv = a.dv; f.n_dvt = a.dv / 64;
+        return launch_chunk_fwd_pipe_eda(dk, C, f, stream);
+    }
     const size_t es = dtype == 1 ? 2 : 4;
     const size_t rows = static_cast<size_t>(a.B) * a.T * a.H, rows2 = 2 * rows;
     unsigned char *p = static_cast<unsigned char *>(ws);

@@ -17,6 +17,7 @@ struct ChunkArgs {
     bool raw = false;               // q, k unnormalised and gates as logits (bf16 C = 32, 64 only)
     void *Hs = nullptr;             // [B][H][NC][d_v][d_k] in the element type: every chunk's entry state
                                     // (generic kernel only)
+    const void *e = nullptr;        // [B][T][H][d_k] erase directions (Erase-then-Delta instance only)
 };
 
 // Layer backward (qd_chunk_bwd.hip).  Gradients of sum(o dO) + sum(S_T dST).
@@ -82,7 +83,7 @@ struct EdaStepArgs {
     void *o;                        // [N][H][d_v]
     int N, H;
 };
-size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv);
+size_t eda_chunk_workspace(int dtype, int B, int T, int H, int dk, int dv, int C);
 hipError_t launch_eda_chunk(int dtype, int dk, int C, const EdaChunkArgs &a, void *ws, hipStream_t stream);
 hipError_t launch_eda_step(int dtype, int dk, int dv, const EdaStepArgs &a, hipStream_t stream);
 
@@ -94,6 +95,9 @@ hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t
 // the _states variant also writes ChunkArgs::Hs.
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream);
+// Erase-then-Delta over the interleaved sequence read in place (ChunkArgs::e; T real tokens;
+// beta, alpha, lam unused), bf16 C = 32, 64.
+hipError_t launch_chunk_fwd_pipe_eda(int dk, int C, const ChunkArgs &a, hipStream_t stream);
 
 // Segmented schedule (qd_segment.hip) for long sequences over few heads: the number of
 // segments P the sequence is cut into (1 = the single-pass schedule), the workspace it

@@ -162,8 +162,9 @@ def test_qed_host_side_rejections(lib):
 
 
 def _eda(lib, **kw):
+    # fp32: the instance that builds the interleaved sequence in a workspace
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, e=FAKE * 4, S0=None, o=FAKE * 5, S_T=None, B=1, T=4, H=1, d_k=64,
-             d_v=64, C=32, dtype=1, ws=FAKE * 64, ws_bytes=1 << 20)
+             d_v=64, C=32, dtype=0, ws=FAKE * 64, ws_bytes=1 << 20)
     a.update(kw)
     return lib.qdelta_eda_chunk_fwd(a["q"], a["k"], a["v"], a["e"], a["S0"], a["o"], a["S_T"], a["B"], a["T"],
                                     a["H"], a["d_k"], a["d_v"], a["C"], a["dtype"], a["ws"], a["ws_bytes"], None)
@@ -175,6 +176,11 @@ def test_eda_host_side_rejections(lib):
     assert _eda(lib, o=FAKE * 4) == QD_ERR_INVALID_ARG             # o aliases e
     assert _eda(lib, C=48) == QD_ERR_UNSUPPORTED
     assert _eda(lib, B=0) == QD_OK
+    assert _eda(lib, B=0, dtype=1, ws=None, ws_bytes=0) == QD_OK
     # the interleaved sequence and its outputs: 2 B T H ((2 d_k + 2 d_v) e + 4) bytes, the last term rounded up to 16
-    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 32, 1) == 2 * 2 * 10 * 3 * ((2 * 64 + 2 * 128) * 2) + 480
+    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 32, 0) == 2 * 2 * 10 * 3 * ((2 * 64 + 2 * 128) * 4) + 480
+    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 16, 1) == 2 * 2 * 10 * 3 * ((2 * 64 + 2 * 128) * 2) + 480
+    # bf16 at C = 32, 64 reads the interleaved sequence in place
+    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 32, 1) == 0
+    assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 128, 128, 64, 1) == 0
     assert lib.qdelta_eda_step(FAKE, FAKE * 2, FAKE * 3, None, FAKE * 64, FAKE * 5, 2, 2, 64, 64, 1, None) == QD_ERR_INVALID_ARG

@@ -79,3 +79,29 @@ def test_eda_workspace_required(qd):
     small = torch.empty(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(qd.QDeltaError, match="workspace"):
         qd.qdelta_eda_chunk_fwd(q, k, v, e, None, C=32, workspace=small)
+
+
+@pytest.mark.parametrize("T,dk,dv,C", [(1, 128, 128, 64), (31, 64, 64, 64), (32, 128, 64, 64), (33, 64, 128, 32),
+                                       (16, 128, 128, 32), (17, 64, 64, 32), (257, 128, 128, 64)])
+def test_eda_in_place_edges(qd, T, dk, dv, C):
+    """bf16 at C = 32, 64 reads the interleaved sequence in place: sequences that end inside,
+    at and just past a chunk of 2T rows, one token, and a state passed in."""
+    print(f"[eda] in place bf16 T{T} dk{dk} dv{dv} C{C}", flush=True)
+    assert qd.qdelta_eda_chunk_fwd_workspace_bytes(2, T, 3, dk, dv, C, torch.bfloat16) == 0
+    q, k, v, e, S0 = inputs.eda_inputs(2, T, 3, dk, dv, "bf16", seed=T + dk + C, s0_std=0.05)
+    o, S = qd.qdelta_eda_chunk_fwd(dev(q), dev(k), dev(v), dev(e), dev(S0), C=C)
+    torch.cuda.synchronize()
+    ro, rS = oracle.eda_fwd(q, k, v, e, S0)
+    eo, es = slice_err(o.float().cpu().numpy(), ro, (1, 3)), slice_err(S.cpu().numpy(), rS, (2, 3))
+    print(f"  max rel err o={eo:.2e} S_T={es:.2e} (bar {TOL['bf16']:g})", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_eda_in_place_empty_sequence(qd):
+    """T = 0: no output rows, and S_T is S0."""
+    print("[eda] in place bf16 T=0", flush=True)
+    q, k, v, e, S0 = inputs.eda_inputs(1, 0, 2, 128, 128, "bf16", seed=3, s0_std=0.05)
+    o, S = qd.qdelta_eda_chunk_fwd(dev(q), dev(k), dev(v), dev(e), dev(S0), C=64)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 128)
+    np.testing.assert_array_equal(S.cpu().numpy(), S0.numpy())
