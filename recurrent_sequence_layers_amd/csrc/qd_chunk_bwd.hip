@@ -17,7 +17,8 @@
 //        dZ = A^T dO + D_r K dS'^T,  dV = dR = diag(beta) T_g^T dZ,
 //        dS^T = g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR;
 //      the last dS^T is dS0;
-//   3. chunk_bwd_grad_kernel: one workgroup per chunk, independent of the others, one wave
+//   3. chunk_bwd_grad_kernel: chunks are independent of each other; a resident grid of
+//      workgroups walks them, prefetching the next chunk's rows into registers, one wave
 //      per 16 value columns; from the chunk's S and dS' (read from global memory as MFMA
 //      fragments) it recomputes R, Z, dZ, P = T_g^T dZ and the token errors
 //      U = R - N Z, and forms dQ, dK, dbeta, dlambda and dalpha:
@@ -313,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdAr
 }
 
 // ------------------------------------------------------------------ pass 3: per-chunk gradients
-// One workgroup per chunk with one wave per 16 value columns (DV / 16 waves: all value
-// columns at once).  LDS holds the chunk's q, k, v, dO rows, Z and P, and the C x C
+// One chunk at a time per workgroup, one wave per 16 value columns (DV / 16 waves: all
+// value columns at once); the grid is as large as fits the device at once.  LDS holds the chunk's q, k, v, dO rows, Z and P, and the C x C
 // matrices; the states S and dS' are read from global memory as MFMA fragments (the
 // column-local Y = X S^T and K dS'^T take each wave's 16 rows of S and dS'; the value
 // contractions W_o = dO S, W_p = P S, W_z = Z dS' take 4 x 16 blocks of them).
@@ -347,39 +348,13 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
     constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
     constexpr int NLQ = (CH * VPRQ + NT - 1) / NT, NLV = (CH * VPRV + NT - 1) / NT;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
-    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
-    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
-    R *const Vs = reinterpret_cast<R *>(smem) + Lay::oV;
-    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;    // dO
-    R *const Zs = reinterpret_cast<R *>(smem) + Lay::oZ;
-    R *const Ps = reinterpret_cast<R *>(smem) + Lay::oP;
-    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;    // diag(beta) strict(X K^T), later dLb
-    R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;
-    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;    // T, then T_g, later Mq
-    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
-    R *const Qst = Ds;                                       // dQ staging (after the value phase)
-    R *const Kst = Ds + Lay::NQ;                             // dK staging
-    float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
-    float *const egs = gs + CH;
-    float *const egls = egs + CH;
-    float *const bes = egls + CH;
-    float *const lams = bes + CH;
-    float *const als = lams + CH;
-    float *const pdb = als + CH;         // [NW][CH] per-wave row partials: dbeta
-    float *const pdl = pdb + NW * CH;    //   dlambda
-    float *const pdg = pdl + NW * CH;    //   dg
-    float *const psc = pdg + NW * CH;    // [0, NW) <dS', S> per wave, [NW, 2 NW) sum rowdot(D_r W_z, K) per wave
+    __shared__ __attribute__((aligned(16))) unsigned char smem_[Lay::bytes];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int r16 = lane & 15, g4 = lane >> 4;
     const int T = args.T, H = args.H;
     const int NC = (T + CH - 1) / CH;
-    const int n = blockIdx.x % NC;
-    const int bh = blockIdx.x / NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = n * CH;
-    const int clen = min(CH, T - t0);
+    const int total = args.B * H * NC;
 
     const R *__restrict__ gq = static_cast<const R *>(args.q);
     const R *__restrict__ gk = static_cast<const R *>(args.k);
@@ -387,22 +362,20 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
     const R *__restrict__ gdo = static_cast<const R *>(args.dO);
     R *__restrict__ gdq = static_cast<R *>(args.g_q);
     R *__restrict__ gdk = static_cast<R *>(args.g_k);
-    const R *__restrict__ hs = static_cast<const R *>(args.Hs) + (static_cast<size_t>(bh) * NC + n) * DV * DK;
-    const R *__restrict__ dhs = static_cast<const R *>(args.dHs) + (static_cast<size_t>(bh) * NC + n) * DV * DK;
-    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+    const R *__restrict__ hs0 = static_cast<const R *>(args.Hs);
+    const R *__restrict__ dhs0 = static_cast<const R *>(args.dHs);
 
-    // ---- global loads first: this wave's S^T and dS'^T fragments (S rows 16 wave + l % 16),
-    // then the chunk's q, k, v, dO rows
-    F sTf[NKT], dsTf[NKT];
-    float sdot = 0.f;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-        const size_t off = static_cast<size_t>(16 * wave + r16) * DK + 16 * t + 4 * g4;
-        sTf[t] = P::ld4(hs + off);
-        dsTf[t] = P::ld4(dhs + off);
-    }
-    {
-        uint4 xq[NLQ], xk[NLQ], xv[NLV], xd[NLV];
+    // The workgroup walks chunks it, it + gridDim.x, ...  The next chunk's q, k, v, dO rows
+    // and (wave 0) the lane's gates are prefetched into registers once the current chunk's
+    // global reads are done, so they overlap its last phases; this wave's S^T and dS'^T
+    // fragments (S rows 16 wave + l % 16) are loaded right after the rows are staged, and
+    // arrive during the Gram blocks and the inverse.
+    uint4 xq[NLQ], xk[NLQ], xv[NLV], xd[NLV];
+    float xa = 1.f, xb = 0.f, xl = 0.f;
+    auto fetch = [&](int it) {
+        const int n = it % NC, bh = it / NC, b = bh / H, h = bh % H;
+        const int t0 = n * CH, clen = min(CH, T - t0);
+        auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
 #pragma unroll
         for (int j = 0; j < NLQ; ++j) {
             const int vi = tid + NT * j;
@@ -423,6 +396,57 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 xd[j] = *reinterpret_cast<const uint4 *>(gdo + off);
             }
         }
+        if (wave == 0) {
+            const bool ok = lane < clen;
+            const size_t gi = tok(t0 + min(lane, clen - 1));
+            xa = (HAS_A && ok) ? args.alpha[gi] : 1.f;
+            xb = ok ? args.beta[gi] : 0.f;
+            xl = (HAS_L && ok) ? args.lam[gi] : 0.f;
+        }
+    };
+
+    if (static_cast<int>(blockIdx.x) < total) fetch(blockIdx.x);
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+        // Lane ids and the LDS base are rebuilt from opaque copies for every chunk rather
+        // than hoisted out of the loop: LDS addresses held across the loop do not fit the
+        // register file next to the prefetched rows (they were spilled, and the reloads
+        // waited on the state loads in flight).
+        int lid_ = threadIdx.x, zoff_ = 0;
+        asm volatile("" : "+v"(lid_), "+v"(zoff_));
+        const int tid = lid_, lane = lid_ & (kWave - 1), r16 = lane & 15, g4 = lane >> 4;
+        unsigned char *const smem = smem_ + zoff_;
+        R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
+        R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
+        R *const Vs = reinterpret_cast<R *>(smem) + Lay::oV;
+        R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;    // dO
+        R *const Zs = reinterpret_cast<R *>(smem) + Lay::oZ;
+        R *const Ps = reinterpret_cast<R *>(smem) + Lay::oP;
+        R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;    // diag(beta) strict(X K^T), later dLb
+        R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;
+        R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;    // T, then T_g, later Mq
+        R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
+        R *const Qst = Ds;                                       // dQ staging (after the value phase)
+        R *const Kst = Ds + Lay::NQ;                             // dK staging
+        float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
+        float *const egs = gs + CH;
+        float *const egls = egs + CH;
+        float *const bes = egls + CH;
+        float *const lams = bes + CH;
+        float *const als = lams + CH;
+        float *const pdb = als + CH;         // [NW][CH] per-wave row partials: dbeta
+        float *const pdl = pdb + NW * CH;    //   dlambda
+        float *const pdg = pdl + NW * CH;    //   dg
+        float *const psc = pdg + NW * CH;    // [0, NW) <dS', S> per wave, [NW, 2 NW) sum rowdot(D_r W_z, K) per wave
+
+        const int n = it % NC, bh = it / NC, b = bh / H, h = bh % H;
+        const int t0 = n * CH;
+        const int clen = min(CH, T - t0);
+        const R *__restrict__ hs = hs0 + (static_cast<size_t>(bh) * NC + n) * DV * DK;
+        const R *__restrict__ dhs = dhs0 + (static_cast<size_t>(bh) * NC + n) * DV * DK;
+        auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+        // ---- stage the prefetched rows and gates
+        float sdot = 0.f;
 #pragma unroll
         for (int j = 0; j < NLQ; ++j) {
             const int vi = tid + NT * j;
@@ -439,291 +463,322 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 *reinterpret_cast<uint4 *>(Ds + (vi / VPRV) * PV + (vi % VPRV) * EPV) = xd[j];
             }
         }
-    }
-    if (wave == 0) {
-        const bool ok = lane < clen;
-        const size_t gi = tok(t0 + min(lane, clen - 1));
-        const float a = (HAS_A && ok) ? args.alpha[gi] : 1.f;
-        float x = (HAS_A && ok) ? __logf(a) : 0.f;
+        if (wave == 0) {
+            const bool ok = lane < clen;
+            float x = (HAS_A && ok) ? __logf(xa) : 0.f;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (lane >= off) x += y;
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float glast = __shfl(x, CH - 1);
+            if (lane < CH) {
+                gs[lane] = x;
+                egs[lane] = __expf(x);
+                egls[lane] = __expf(glast - x);
+                bes[lane] = xb;
+                lams[lane] = xl;
+                als[lane] = xa;
+            }
         }
-        const float glast = __shfl(x, CH - 1);
-        if (lane < CH) {
-            gs[lane] = x;
-            egs[lane] = __expf(x);
-            egls[lane] = __expf(glast - x);
-            bes[lane] = ok ? args.beta[gi] : 0.f;
-            lams[lane] = (HAS_L && ok) ? args.lam[gi] : 0.f;
-            als[lane] = a;
+        for (int i = tid; i < 3 * NW * CH + 2 * NW; i += NT) pdb[i] = 0.f;
+        __syncthreads();
+        F sTf[NKT], dsTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            const size_t off = static_cast<size_t>(16 * wave + r16) * DK + 16 * t + 4 * g4;
+            sTf[t] = P::ld4(hs + off);
+            dsTf[t] = P::ld4(dhs + off);
         }
-    }
-    for (int i = tid; i < 3 * NW * CH + 2 * NW; i += NT) pdb[i] = 0.f;
-    __syncthreads();
 
-    // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
-    gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, NW>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
-    __syncthreads();
-    unit_lower_inverse<P, CH, PC>(Ls, Ts);
-    if constexpr (HAS_A) {
-        for (int idx = tid; idx < NPAIR * 64; idx += NT) {
-            int i, j;
-            tri_pair(idx >> 6, i, j);
-            const int r = 16 * i + ((idx >> 2) & 15);
-            const int c0 = 16 * j + 4 * (idx & 3);
-            const F tf = P::ld4(Ts + r * PC + c0);
-            const f32x4 gc = lds_f32x4(gs + c0);
-            const float gr = gs[r];
-            f32x4 tg;
+        // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
+        gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, NW>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
+        __syncthreads();
+        unit_lower_inverse<P, CH, PC>(Ls, Ts, lane);
+        if constexpr (HAS_A) {
+            for (int idx = tid; idx < NPAIR * 64; idx += NT) {
+                int i, j;
+                tri_pair(idx >> 6, i, j);
+                const int r = 16 * i + ((idx >> 2) & 15);
+                const int c0 = 16 * j + 4 * (idx & 3);
+                const F tf = P::ld4(Ts + r * PC + c0);
+                const f32x4 gc = lds_f32x4(gs + c0);
+                const float gr = gs[r];
+                f32x4 tg;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tg[e] = (c0 + e <= r) ? __expf(gr - gc[e]) * static_cast<float>(tf[e]) : 0.f;
-            P::st4(Ts + r * PC + c0, tg);
+                for (int e = 0; e < 4; ++e) tg[e] = (c0 + e <= r) ? __expf(gr - gc[e]) * static_cast<float>(tf[e]) : 0.f;
+                P::st4(Ts + r * PC + c0, tg);
+            }
+            __syncthreads();
+        }
+
+        // ---- column-local part: value columns [16 wave, 16 wave + 16)
+        {
+            f32x4 Rr[NCT], dZ[NCT];
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) {
+                f32x4 pk = zero4(), pq = zero4(), kd = zero4();
+#pragma unroll
+                for (int t = 0; t < NKT; t += 2) {
+                    const F k0 = frag<P>(Ks, PK, 16 * mt, 16 * t), k1 = frag<P>(Ks, PK, 16 * mt, 16 * t + 16);
+                    pk = P::mma2(pk, k0, k1, sTf[t], sTf[t + 1]);
+                    kd = P::mma2(kd, k0, k1, dsTf[t], dsTf[t + 1]);
+                    if constexpr (HAS_L)
+                        pq = P::mma2(pq, frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16), sTf[t],
+                                     sTf[t + 1]);
+                }
+                const f32x4 y = HAS_L ? pk + lds_f32x4(lams + 16 * mt + 4 * g4) * pq : pk;
+                const f32x4 vf = P::f32(frag_b<P>(Vs, PV, 16 * mt, 16 * wave));
+                Rr[mt] = HAS_A ? vf - lds_f32x4(egs + 16 * mt + 4 * g4) * y : vf - y;
+                dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+            }
+            if constexpr (HAS_A) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    const f32x4 a = P::f32(sTf[t]), d = P::f32(dsTf[t]);
+                    sdot += a[0] * d[0] + a[1] * d[1] + a[2] * d[2] + a[3] * d[3];
+                }
+            }
+            // Z = T_g diag(beta) R;  dZ += A^T dO
+            F bRf[NCT];
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) bRf[mt] = P::cvt(lds_f32x4(bes + 16 * mt + 4 * g4) * Rr[mt]);
+            f32x4 Z[NCT];
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) {
+                Z[mt] = zero4();
+#pragma unroll
+                for (int s = 0; s <= mt; ++s) Z[mt] = P::mma1(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), bRf[s]);
+#pragma unroll
+                for (int s = mt; s < NCT; ++s)
+                    dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
+            }
+            // P = T_g^T dZ;  U = R - N Z;  dbeta += rowdot(P, U)
+            F dZf[NCT], Zf[NCT];
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) {
+                dZf[mt] = P::cvt(dZ[mt]);
+                Zf[mt] = P::cvt(Z[mt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) {
+                f32x4 Pm = zero4();
+#pragma unroll
+                for (int s = mt; s < NCT; ++s) Pm = P::mma1(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
+                f32x4 U = Rr[mt];
+#pragma unroll
+                for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float db = sum16(Pm[e] * U[e]);
+                    const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
+                    if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = db;
+                    Zs[o] = P::from_f32(Z[mt][e]);
+                    Ps[o] = P::from_f32(Pm[e]);
+                }
+            }
         }
         __syncthreads();
-    }
 
-    // ---- column-local part: value columns [16 wave, 16 wave + 16)
-    {
-        f32x4 Rr[NCT], dZ[NCT];
+        // ---- value contractions over all d_v: dA = dO Z^T, dL = P Z^T on this wave's lower blocks
+        f32x4 dAacc[PPW], dLacc[PPW];
 #pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            f32x4 pk = zero4(), pq = zero4(), kd = zero4();
+        for (int u = 0; u < PPW; ++u) {
+            dAacc[u] = dLacc[u] = zero4();
+            const int p = wave + NW * u;
+            if (p < NPAIR) {
+                int i, j;
+                tri_pair(p, i, j);
 #pragma unroll
-            for (int t = 0; t < NKT; t += 2) {
-                const F k0 = frag<P>(Ks, PK, 16 * mt, 16 * t), k1 = frag<P>(Ks, PK, 16 * mt, 16 * t + 16);
-                pk = P::mma2(pk, k0, k1, sTf[t], sTf[t + 1]);
-                kd = P::mma2(kd, k0, k1, dsTf[t], dsTf[t + 1]);
-                if constexpr (HAS_L)
-                    pq = P::mma2(pq, frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16), sTf[t],
-                                 sTf[t + 1]);
+                for (int vv = 0; vv < NVT; vv += 2) {
+                    const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
+                    dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
+                                       z0, z1);
+                    dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
+                                       z0, z1);
+                }
             }
-            const f32x4 y = HAS_L ? pk + lds_f32x4(lams + 16 * mt + 4 * g4) * pq : pk;
-            const f32x4 vf = P::f32(frag_b<P>(Vs, PV, 16 * mt, 16 * wave));
-            Rr[mt] = HAS_A ? vf - lds_f32x4(egs + 16 * mt + 4 * g4) * y : vf - y;
-            dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+        }
+        // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk);
+        // the B fragments S[16 vv + 4 g + i][16 kk + l % 16] come from global memory (rows other
+        // waves have just read, so mostly from L2; staging them through LDS measured no faster)
+        f32x4 Wo[NBW], Wp[NBW], Wz[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            Wo[j] = Wp[j] = Wz[j] = zero4();
+            const int blk = wave + NW * j;
+            if (NB % NW == 0 || blk < NB) {
+                const int mt = blk / NKT, kk = blk % NKT;
+#pragma unroll
+                for (int vv = 0; vv < NVT; vv += 2) {
+                    const size_t o0 = static_cast<size_t>(16 * vv + 4 * g4) * DK + 16 * kk + r16;
+                    const size_t o1 = o0 + static_cast<size_t>(16) * DK;
+                    const F s0 = P::ld4_strided(hs + o0, DK), s1 = P::ld4_strided(hs + o1, DK);
+                    const F d0 = P::ld4_strided(dhs + o0, DK), d1 = P::ld4_strided(dhs + o1, DK);
+                    Wo[j] = P::mma2(Wo[j], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16), s0, s1);
+                    Wp[j] = P::mma2(Wp[j], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16), s0, s1);
+                    Wz[j] = P::mma2(Wz[j], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16), d0, d1);
+                }
+            }
+        }
+        __syncthreads();   // T_g, L, v, dO, Z, P are free from here on
+        // the next chunk's rows (this chunk's global reads are done)
+        if (it + static_cast<int>(gridDim.x) < total) fetch(it + gridDim.x);
+
+        // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
+#pragma unroll
+        for (int u = 0; u < PPW; ++u) {
+            const int p = wave + NW * u;
+            if (p < NPAIR) {
+                int i, j;
+                tri_pair(p, i, j);
+                const int c = 16 * j + r16;
+                const float gc = gs[c];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * i + 4 * g4 + e;
+                    const float G = HAS_A ? __expf(gs[r] - gc) : 1.f;
+                    const float da = (c <= r) ? dAacc[u][e] : 0.f;
+                    const float dlb = (c < r) ? -bes[r] * G * dLacc[u][e] : 0.f;
+                    Ts[r * PC + c] = P::from_f32(da * G + (HAS_L ? lams[r] * dlb : 0.f));
+                    Ls[r * PC + c] = P::from_f32(dlb);
+                }
+            }
+        }
+        __syncthreads();   // Mq and dLb published
+
+        // ---- per d_k block:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K;
+        //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
+        //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms are rowdot(Q, MqK) +
+        //   rowdot(K, LbK) - rowdot(K, KT) (the row and column sums of dA o A and dL o beta N
+        //   regrouped, from fp32 accumulators and the exact q and k)
+        float wz = 0.f;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int blk = wave + NW * j;
+            if (NB % NW == 0 || blk < NB) {
+                const int mt = blk / NKT, kk = blk % NKT;
+                const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
+                const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
+                f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
+#pragma unroll
+                for (int s = 0; s < NCT; ++s) {
+                    if (s <= mt) {
+                        const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
+                        lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
+                        mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
+                    }
+                    if (s >= mt) {
+                        kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
+                        kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
+                    }
+                }
+                const f32x4 dX = lbk - eg * bt * Wp[j];
+                const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[j] - lm * bt * Wp[j]) : eg * Wo[j]);
+                const f32x4 dK = kt + el * Wz[j] + dX;
+                const f32x4 qf = P::f32(frag_b<P>(Qs, PK, 16 * mt, 16 * kk));
+                const f32x4 kf = P::f32(frag_b<P>(Ks, PK, 16 * mt, 16 * kk));
+                f32x4 dgp = zero4();
+                if constexpr (HAS_A) {
+                    const f32x4 xf = HAS_L ? kf + lm * qf : kf;
+                    const f32x4 wzk = el * Wz[j] * kf;
+                    dgp = qf * mqk + kf * lbk - kf * kt + eg * (Wo[j] * qf - bt * Wp[j] * xf) - wzk;
+                    wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
+                }
+                const f32x4 dlp = HAS_L ? qf * dX : zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * mt + 4 * g4 + e;
+                    const int o = r * PK + 16 * kk + r16;
+                    Qst[o] = P::from_f32(dQ[e]);
+                    Kst[o] = P::from_f32(dK[e]);
+                    if constexpr (HAS_L) {
+                        const float rs = sum16(dlp[e]);
+                        if (r16 == 0) pdl[wave * CH + r] += rs;
+                    }
+                    if constexpr (HAS_A) {
+                        const float rs = sum16(dgp[e]);
+                        if (r16 == 0) pdg[wave * CH + r] += rs;
+                    }
+                }
+            }
         }
         if constexpr (HAS_A) {
-#pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                const f32x4 a = P::f32(sTf[t]), d = P::f32(dsTf[t]);
-                sdot += a[0] * d[0] + a[1] * d[1] + a[2] * d[2] + a[3] * d[3];
+            wz = sum64(wz);
+            const float sd = sum64(sdot);
+            if (lane == 0) {
+                psc[wave] = sd;
+                psc[NW + wave] = wz;
             }
         }
-        // Z = T_g diag(beta) R;  dZ += A^T dO
-        F bRf[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) bRf[mt] = P::cvt(lds_f32x4(bes + 16 * mt + 4 * g4) * Rr[mt]);
-        f32x4 Z[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            Z[mt] = zero4();
-#pragma unroll
-            for (int s = 0; s <= mt; ++s) Z[mt] = P::mma1(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), bRf[s]);
-#pragma unroll
-            for (int s = mt; s < NCT; ++s)
-                dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
-        }
-        // P = T_g^T dZ;  U = R - N Z;  dbeta += rowdot(P, U)
-        F dZf[NCT], Zf[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            dZf[mt] = P::cvt(dZ[mt]);
-            Zf[mt] = P::cvt(Z[mt]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            f32x4 Pm = zero4();
-#pragma unroll
-            for (int s = mt; s < NCT; ++s) Pm = P::mma1(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
-            f32x4 U = Rr[mt];
-#pragma unroll
-            for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float db = sum16(Pm[e] * U[e]);
-                const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
-                if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = db;
-                Zs[o] = P::from_f32(Z[mt][e]);
-                Ps[o] = P::from_f32(Pm[e]);
-            }
-        }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- value contractions over all d_v: dA = dO Z^T, dL = P Z^T on this wave's lower blocks
-    f32x4 dAacc[PPW], dLacc[PPW];
-#pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-        dAacc[u] = dLacc[u] = zero4();
-        const int p = wave + NW * u;
-        if (p < NPAIR) {
-            int i, j;
-            tri_pair(p, i, j);
-#pragma unroll
-            for (int vv = 0; vv < NVT; vv += 2) {
-                const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
-                dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
-                                   z0, z1);
-                dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
-                                   z0, z1);
+        // ---- stores: dQ, dK rows; per-token dbeta, dlambda, dalpha
+        for (int vi = tid; vi < CH * VPRQ; vi += NT) {
+            const int c = vi / VPRQ, cv = vi % VPRQ;
+            if (c < clen) {
+                const size_t off = tok(t0 + c) * DK + cv * EPV;
+                *reinterpret_cast<uint4 *>(gdq + off) = *reinterpret_cast<const uint4 *>(Qst + c * PK + cv * EPV);
+                *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(Kst + c * PK + cv * EPV);
             }
         }
-    }
-    // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk);
-    // the B fragments S[16 vv + 4 g + i][16 kk + l % 16] come from global memory (rows other
-    // waves have just read, so mostly from L2; staging them through LDS measured no faster)
-    f32x4 Wo[NBW], Wp[NBW], Wz[NBW];
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        Wo[j] = Wp[j] = Wz[j] = zero4();
-        const int blk = wave + NW * j;
-        if (NB % NW == 0 || blk < NB) {
-            const int mt = blk / NKT, kk = blk % NKT;
-#pragma unroll
-            for (int vv = 0; vv < NVT; vv += 2) {
-                const size_t o0 = static_cast<size_t>(16 * vv + 4 * g4) * DK + 16 * kk + r16;
-                const size_t o1 = o0 + static_cast<size_t>(16) * DK;
-                const F s0 = P::ld4_strided(hs + o0, DK), s1 = P::ld4_strided(hs + o1, DK);
-                const F d0 = P::ld4_strided(dhs + o0, DK), d1 = P::ld4_strided(dhs + o1, DK);
-                Wo[j] = P::mma2(Wo[j], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16), s0, s1);
-                Wp[j] = P::mma2(Wp[j], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16), s0, s1);
-                Wz[j] = P::mma2(Wz[j], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16), d0, d1);
-            }
-        }
-    }
-    __syncthreads();   // T_g, L, v, dO, Z, P are free from here on
-
-    // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
-#pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-        const int p = wave + NW * u;
-        if (p < NPAIR) {
-            int i, j;
-            tri_pair(p, i, j);
-            const int c = 16 * j + r16;
-            const float gc = gs[c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * g4 + e;
-                const float G = HAS_A ? __expf(gs[r] - gc) : 1.f;
-                const float da = (c <= r) ? dAacc[u][e] : 0.f;
-                const float dlb = (c < r) ? -bes[r] * G * dLacc[u][e] : 0.f;
-                Ts[r * PC + c] = P::from_f32(da * G + (HAS_L ? lams[r] * dlb : 0.f));
-                Ls[r * PC + c] = P::from_f32(dlb);
-            }
-        }
-    }
-    __syncthreads();   // Mq and dLb published
-
-    // ---- per d_k block:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K;
-    //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
-    //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms are rowdot(Q, MqK) +
-    //   rowdot(K, LbK) - rowdot(K, KT) (the row and column sums of dA o A and dL o beta N
-    //   regrouped, from fp32 accumulators and the exact q and k)
-    float wz = 0.f;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        const int blk = wave + NW * j;
-        if (NB % NW == 0 || blk < NB) {
-            const int mt = blk / NKT, kk = blk % NKT;
-            const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
-            const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
-            f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
-#pragma unroll
-            for (int s = 0; s < NCT; ++s) {
-                if (s <= mt) {
-                    const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
-                    lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
-                    mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
-                }
-                if (s >= mt) {
-                    kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
-                    kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
-                }
-            }
-            const f32x4 dX = lbk - eg * bt * Wp[j];
-            const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[j] - lm * bt * Wp[j]) : eg * Wo[j]);
-            const f32x4 dK = kt + el * Wz[j] + dX;
-            const f32x4 qf = P::f32(frag_b<P>(Qs, PK, 16 * mt, 16 * kk));
-            const f32x4 kf = P::f32(frag_b<P>(Ks, PK, 16 * mt, 16 * kk));
-            f32x4 dgp = zero4();
-            if constexpr (HAS_A) {
-                const f32x4 xf = HAS_L ? kf + lm * qf : kf;
-                const f32x4 wzk = el * Wz[j] * kf;
-                dgp = qf * mqk + kf * lbk - kf * kt + eg * (Wo[j] * qf - bt * Wp[j] * xf) - wzk;
-                wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
-            }
-            const f32x4 dlp = HAS_L ? qf * dX : zero4();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * mt + 4 * g4 + e;
-                const int o = r * PK + 16 * kk + r16;
-                Qst[o] = P::from_f32(dQ[e]);
-                Kst[o] = P::from_f32(dK[e]);
-                if constexpr (HAS_L) {
-                    const float rs = sum16(dlp[e]);
-                    if (r16 == 0) pdl[wave * CH + r] += rs;
-                }
-                if constexpr (HAS_A) {
-                    const float rs = sum16(dgp[e]);
-                    if (r16 == 0) pdg[wave * CH + r] += rs;
-                }
-            }
-        }
-    }
-    if constexpr (HAS_A) {
-        wz = sum64(wz);
-        const float sd = sum64(sdot);
-        if (lane == 0) {
-            psc[wave] = sd;
-            psc[NW + wave] = wz;
-        }
-    }
-    __syncthreads();
-
-    // ---- stores: dQ, dK rows; per-token dbeta, dlambda, dalpha
-    for (int vi = tid; vi < CH * VPRQ; vi += NT) {
-        const int c = vi / VPRQ, cv = vi % VPRQ;
-        if (c < clen) {
-            const size_t off = tok(t0 + c) * DK + cv * EPV;
-            *reinterpret_cast<uint4 *>(gdq + off) = *reinterpret_cast<const uint4 *>(Qst + c * PK + cv * EPV);
-            *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(Kst + c * PK + cv * EPV);
-        }
-    }
-    if (wave == 0) {
-        float db = 0.f, dl = 0.f, dg = 0.f;
-        if (lane < CH) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                db += pdb[w * CH + lane];
-                dl += pdl[w * CH + lane];
-                dg += pdg[w * CH + lane];
-            }
-            if (HAS_A && lane == CH - 1) {
-                float sd = 0.f, wzs = 0.f;
+        if (wave == 0) {
+            float db = 0.f, dl = 0.f, dg = 0.f;
+            if (lane < CH) {
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
-                    sd += psc[w];
-                    wzs += psc[NW + w];
+                    db += pdb[w * CH + lane];
+                    dl += pdl[w * CH + lane];
+                    dg += pdg[w * CH + lane];
                 }
-                dg += egs[CH - 1] * sd + wzs;
+                if (HAS_A && lane == CH - 1) {
+                    float sd = 0.f, wzs = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        sd += psc[w];
+                        wzs += psc[NW + w];
+                    }
+                    dg += egs[CH - 1] * sd + wzs;
+                }
+            }
+            // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_down(dg, off);
+                if (lane + off < kWave) dg += y;
+            }
+            if (lane < clen) {
+                const size_t gi = tok(t0 + lane);
+                args.g_beta[gi] = db;
+                if (HAS_L && args.g_lam) args.g_lam[gi] = dl;
+                if (HAS_A && args.g_alpha) args.g_alpha[gi] = dg / als[lane];
             }
         }
-        // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_down(dg, off);
-            if (lane + off < kWave) dg += y;
-        }
-        if (lane < clen) {
-            const size_t gi = tok(t0 + lane);
-            args.g_beta[gi] = db;
-            if (HAS_L && args.g_lam) args.g_lam[gi] = dl;
-            if (HAS_A && args.g_alpha) args.g_alpha[gi] = dg / als[lane];
-        }
+        __syncthreads();   // the staging buffers and row partials are reused by the next chunk
     }
+}
+
+// Persistent grid for a kernel: as many workgroups as fit on the device at once (at most
+// the number of work items), each walking items blockIdx.x, blockIdx.x + gridDim.x, ...
+// Cached per kernel and device.
+template <class Kern>
+int resident_grid(Kern kernel, int threads, long long items) {
+    constexpr int kMaxDev = 64;
+    static int cached[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+    int grid = dev >= 0 ? cached[dev] : 0;
+    if (grid == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev >= 0 ? dev : 0) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        grid = per_cu * cus;
+        if (dev >= 0) cached[dev] = grid;
+    }
+    return static_cast<int>(items < grid ? items : grid);
 }
 
 template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
@@ -733,12 +788,14 @@ hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || NC == 0) return err;
-    if (a.dv == 128)
-        hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, 128, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(512), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((chunk_bwd_grad_kernel<P, DK, CH, 64, HAS_A, HAS_L>), dim3(a.B * a.H * NC), dim3(256), 0,
-                           stream, a);
+    const long long items = static_cast<long long>(a.B) * a.H * NC;
+    if (a.dv == 128) {
+        auto kern = chunk_bwd_grad_kernel<P, DK, CH, 128, HAS_A, HAS_L>;
+        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 512, items)), dim3(512), 0, stream, a);
+    } else {
+        auto kern = chunk_bwd_grad_kernel<P, DK, CH, 64, HAS_A, HAS_L>;
+        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 256, items)), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

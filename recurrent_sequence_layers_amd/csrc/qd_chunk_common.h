@@ -89,10 +89,12 @@ __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typen
 // block doubling on MFMA (T21 = -T22 L21 T11 for 16- and then 32-row halves).  Only
 // the lower block triangle of T is written; the upper triangle of each diagonal block
 // comes out exactly zero.  Called after a barrier that publishes L; ends with one.
+// lane: the lane id (a caller inside a loop may pass an opaque copy, so the per-lane
+// constants are not hoisted out of its loop and held in registers).
 template <class P, int CH, int PC>
-__device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, typename P::R *Ts) {
+__device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, typename P::R *Ts, int lane = lane_id()) {
     constexpr int NCT = CH / 16;
-    const int wave = wave_id(), lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+    const int wave = wave_id(), r16 = lane & 15, g4 = lane >> 4;
     if (wave < NCT) {
         const int o = 16 * wave;
         const int c = r16;
