@@ -313,6 +313,353 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdAr
     }
 }
 
+// ------------------------------------------------------------------ pass 2, pipelined
+// The reverse scan as a two-stage software pipeline over the chunks: eight waves per
+// (batch, head, 64 value columns) workgroup,
+//   scan waves 0-3  the state-gradient chain of chunk n (dZ, dR, dS^T update, dV); wave w
+//                   owns value columns [16w, 16w + 16) and keeps its dS'^T slice in
+//                   registers;
+//   prep waves 4-7  the state-independent work of chunk c = n - 1 (Gram blocks, the
+//                   triangular inverse, M1).
+// A pipeline step has five intervals separated by workgroup barriers that both roles
+// execute:
+//   interval  scan (chunk n)                         prep (chunk c = n - 1)
+//   I1        prefetch chunk n - 2 (registers);      Gram blocks: L, A
+//             dZ, dR
+//   I2        dS^T update                            diagonal blocks of T
+//   I3        dV staged in LDS                       T, level 1
+//   I4        stage chunk n - 2                      T, level 2
+//   I5        dV stores; store dS' of chunk n - 1    M1 = T_g diag(beta)
+// q, k, dO, A and the gates are double-buffered by chunk parity; M1 is read by the scan in
+// I1 and rewritten by the prep in I5; L and T belong to the prep.
+template <class P, int DK, int CH>
+struct ScanPipeLayout {
+    static constexpr int PAD = 16 / P::kBytes;
+    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
+    static constexpr int NQ = CH * PK, NV = CH * PV, NCC = CH * PC;
+    static constexpr int oQ = 0, oK = oQ + 2 * NQ, oD = oK + 2 * NQ, oA = oD + 2 * NV, oM = oA + 2 * NCC;
+    static constexpr int oL = oM + NCC, oT = oL + NCC, oV = oT + NCC, nR = oV + NV;
+    static constexpr int kGates = 5;   // g, exp(g), exp(g_last - g), beta, lambda
+    static constexpr int bytes = nR * P::kBytes + 2 * kGates * CH * 4;
+    static constexpr bool fits = bytes <= 160 * 1024;
+};
+
+template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(const BwdArgs args) {
+    using R = typename P::R;
+    using F = typename P::F;
+    using Lay = ScanPipeLayout<P, DK, CH>;
+    static_assert(Lay::fits, "LDS budget of one gfx950 workgroup exceeded");
+    constexpr int NKT = DK / 16, NCT = CH / 16;
+    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
+    constexpr int PA = PC, PD = PV;                // row pitches of A, M1 and of dO
+    constexpr int EPV = 16 / P::kBytes;
+    constexpr int VPRQ = DK / EPV, VPRV = kDVT / EPV;
+    constexpr int NVQ = (CH * VPRQ + kThreads - 1) / kThreads;
+    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;
+    constexpr int NPAIR = NCT * (NCT + 1) / 2;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
+    R *const base = reinterpret_cast<R *>(smem);
+    R *const M1s = base + Lay::oM;
+    R *const Ls = base + Lay::oL;
+    R *const Ts = base + Lay::oT;
+    R *const Vst = base + Lay::oV;                  // dV staging
+    float *const gbase = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
+    auto Qb = [&](int s) { return base + Lay::oQ + s * Lay::NQ; };
+    auto Kb = [&](int s) { return base + Lay::oK + s * Lay::NQ; };
+    auto Db = [&](int s) { return base + Lay::oD + s * Lay::NV; };
+    auto Ab = [&](int s) { return base + Lay::oA + s * Lay::NCC; };
+    auto gate = [&](int s, int which) { return gbase + (s * Lay::kGates + which) * CH; };
+
+    const int tid = threadIdx.x, wave = wave_id();
+    const bool is_scan = wave < 4;
+    const int rw = wave & 3;                       // wave index within its role
+    const int rt = tid & (kThreads - 1);           // thread index within its role
+
+    const int nblk = gridDim.x;
+    int logical = blockIdx.x;
+    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int dvt = logical % args.n_dvt;
+    const int bh = logical / args.n_dvt;
+    const int b = bh / args.H, h = bh % args.H;
+    const int T = args.T, H = args.H, dv = args.dv;
+    const int dv0 = dvt * kDVT;
+    const int NC = (T + CH - 1) / CH;
+
+    const R *__restrict__ gq = static_cast<const R *>(args.q);
+    const R *__restrict__ gk = static_cast<const R *>(args.k);
+    const R *__restrict__ gdo = static_cast<const R *>(args.dO);
+    R *__restrict__ gdv = static_cast<R *>(args.g_v);
+    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+
+    // scan role: dS'^T tiles, rows d_k = 16t + 4g + i, column = this wave's value column
+    f32x4 sT[NKT];
+    {
+        const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+        const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * rw + r16) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+            sT[t] = (is_scan && args.dST) ? *reinterpret_cast<const f32x4 *>(args.dST + srow + 16 * t + 4 * g4)
+                                          : zero4();
+    }
+
+    // scan role: registers of one prefetched chunk (rows clamped to the chunk; padding rows
+    // are zeroed when staged)
+    struct Prefetch {
+        uint4 q[NVQ], k[NVQ], d[NVV];
+        float a, b, l;
+    };
+    auto gload = [&](int n, Prefetch &pf) {
+        const int t0 = n * CH;
+        const int last = min(CH, T - t0) - 1;
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = rt + kThreads * j;
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                const int c = min(vi / VPRQ, last), cv = vi % VPRQ;
+                const size_t off = tok(t0 + c) * DK + cv * EPV;
+                pf.q[j] = *reinterpret_cast<const uint4 *>(gq + off);
+                pf.k[j] = *reinterpret_cast<const uint4 *>(gk + off);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = rt + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int c = min(vi / VPRV, last), cv = vi % VPRV;
+                pf.d[j] = *reinterpret_cast<const uint4 *>(gdo + tok(t0 + c) * dv + dv0 + cv * EPV);
+            }
+        }
+        const size_t gi = tok(t0 + min(rt & (kWave - 1), last));
+        pf.a = HAS_A ? args.alpha[gi] : 1.f;
+        pf.b = args.beta[gi];
+        pf.l = HAS_L ? args.lam[gi] : 0.f;
+    };
+    auto lstore = [&](int n, const Prefetch &pf) {   // into slot n & 1
+        const int s = n & 1, clen = min(CH, T - n * CH);
+        R *Qs = Qb(s), *Ks = Kb(s), *Ds = Db(s);
+#pragma unroll
+        for (int j = 0; j < NVQ; ++j) {
+            const int vi = rt + kThreads * j;
+            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
+                const int c = vi / VPRQ, cv = vi % VPRQ;
+                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = keep_if(c < clen, pf.q[j]);
+                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = keep_if(c < clen, pf.k[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int vi = rt + kThreads * j;
+            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int c = vi / VPRV, cv = vi % VPRV;
+                *reinterpret_cast<uint4 *>(Ds + c * PD + cv * EPV) = keep_if(c < clen, pf.d[j]);
+            }
+        }
+        if (rw == 0) {
+            const int lane = lane_id();
+            const bool ok = lane < clen;
+            float x = (HAS_A && ok) ? __logf(pf.a) : 0.f;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float glast = __shfl(x, CH - 1);
+            if (lane < CH) {
+                gate(s, 0)[lane] = x;
+                gate(s, 1)[lane] = __expf(x);
+                gate(s, 2)[lane] = __expf(glast - x);
+                gate(s, 3)[lane] = ok ? pf.b : 0.f;
+                gate(s, 4)[lane] = ok ? pf.l : 0.f;
+            }
+        }
+    };
+
+    if (NC > 0 && is_scan) {
+        Prefetch pf;
+        gload(NC - 1, pf);
+        lstore(NC - 1, pf);
+    }
+    __syncthreads();
+
+    // step n: the scan on chunk n (n < NC), the prep on chunk c = n - 1 (c >= 0)
+    for (int n = NC; n >= 0; --n) {
+        const int c = n - 1;
+        const int ss = n & 1, ps = c & 1;
+        // lane ids rebuilt from an opaque copy at every step (not hoisted out of the loop)
+        int lid_ = threadIdx.x;
+        asm volatile("" : "+v"(lid_));
+        const int lane = lid_ & (kWave - 1), r16 = lane & 15, g4 = lane >> 4;
+        Prefetch pf;                               // scan: chunk n - 2, loaded in I1, staged in I4
+        f32x4 dR[NCT];                             // scan: dR = dV of chunk n, I1 to I3
+
+        // ============================================================ I1
+        if (is_scan) {
+            if (n - 2 >= 0) gload(n - 2, pf);
+            if (n < NC) {
+                const R *Ks = Kb(ss), *Ds = Db(ss), *As = Ab(ss);
+                const float *egls = gate(ss, 2);
+                F sTf[NKT];
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
+                // dZ = D_r K dS'^T + A^T dO   (A^T upper: blocks s >= mt)
+                f32x4 dZ[NCT];
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt) {
+                    f32x4 kd = zero4();
+#pragma unroll
+                    for (int t = 0; t < NKT; t += 2)
+                        kd = P::mma2(kd, frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16),
+                                     sTf[t], sTf[t + 1]);
+                    dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+#pragma unroll
+                    for (int s = mt; s < NCT; s += 2) {
+                        if (s + 1 < NCT)
+                            dZ[mt] = P::mma2(dZ[mt], frag_b<P>(As, PA, 16 * s, 16 * mt),
+                                             frag_b<P>(As, PA, 16 * s + 16, 16 * mt), frag_b<P>(Ds, PD, 16 * s, 16 * rw),
+                                             frag_b<P>(Ds, PD, 16 * s + 16, 16 * rw));
+                        else
+                            dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PA, 16 * s, 16 * mt),
+                                             frag_b<P>(Ds, PD, 16 * s, 16 * rw));
+                    }
+                }
+                // dR = M1^T dZ
+                F dZf[NCT];
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt) dZf[mt] = P::cvt(dZ[mt]);
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt) {
+                    dR[mt] = zero4();
+#pragma unroll
+                    for (int s = mt; s < NCT; s += 2) {
+                        if (s + 1 < NCT)
+                            dR[mt] = P::mma2(dR[mt], frag_b<P>(M1s, PA, 16 * s, 16 * mt),
+                                             frag_b<P>(M1s, PA, 16 * s + 16, 16 * mt), dZf[s], dZf[s + 1]);
+                        else
+                            dR[mt] = P::mma1(dR[mt], frag_b<P>(M1s, PA, 16 * s, 16 * mt), dZf[s]);
+                    }
+                }
+            }
+        } else if (c >= 0) {
+            gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, 4, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
+                                                                Ls, Ab(ps), nullptr, rw, lane);
+        }
+        __syncthreads();
+
+        // ============================================================ I2
+        if (is_scan) {
+            if (n < NC) {
+                // dS^T <- g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR
+                const R *Qs = Qb(ss), *Ks = Kb(ss), *Ds = Db(ss);
+                const float *egs = gate(ss, 1), *lams = gate(ss, 4);
+                F Ef[NCT], Ff[NCT];
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt) {
+                    const f32x4 dof = P::f32(frag_b<P>(Ds, PD, 16 * mt, 16 * rw));
+                    const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4);
+                    f32x4 e = HAS_L ? dof - lds_f32x4(lams + 16 * mt + 4 * g4) * dR[mt] : dof;
+                    f32x4 f = -dR[mt];
+                    if constexpr (HAS_A) {
+                        e = eg * e;
+                        f = eg * f;
+                    }
+                    Ef[mt] = P::cvt(e);
+                    Ff[mt] = P::cvt(f);
+                }
+                const float dlast = HAS_A ? egs[CH - 1] : 1.f;
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    f32x4 acc = sT[t] * dlast;
+#pragma unroll
+                    for (int s = 0; s < NCT; s += 2) {
+                        if (s + 1 < NCT) {
+                            acc = P::mma2(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), frag_b<P>(Qs, PK, 16 * s + 16, 16 * t),
+                                          Ef[s], Ef[s + 1]);
+                            acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t),
+                                          Ff[s], Ff[s + 1]);
+                        } else {
+                            acc = P::mma1(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), Ef[s]);
+                            acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Ff[s]);
+                        }
+                    }
+                    sT[t] = acc;
+                }
+            }
+        } else if (c >= 0) {
+            inverse_diag<P, CH, PC>(Ls, Ts, rw, lane);
+        }
+        __syncthreads();
+
+        // ============================================================ I3
+        if (is_scan) {
+            if (n < NC) {
+#pragma unroll
+                for (int mt = 0; mt < NCT; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Vst[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = P::from_f32(dR[mt][e]);
+            }
+        } else if (c >= 0) {
+            inverse_level1<P, CH, PC>(Ls, Ts, rw, lane);
+        }
+        __syncthreads();
+
+        // ============================================================ I4
+        if (is_scan) {
+            if (n - 2 >= 0) lstore(n - 2, pf);     // slot n & 1, which the scan no longer reads
+        } else if (c >= 0) {
+            inverse_level2<P, CH, PC>(Ls, Ts, rw, lane);
+        }
+        __syncthreads();
+
+        // ============================================================ I5
+        if (is_scan) {
+            if (n < NC) {                          // dV rows (staged in I3, rewritten in the next I3)
+                const int t0 = n * CH, clen = min(CH, T - t0);
+                for (int vi = rt; vi < CH * VPRV; vi += kThreads) {
+                    const int cr = vi / VPRV, cv = vi % VPRV;
+                    if (cr < clen)
+                        *reinterpret_cast<uint4 *>(gdv + tok(t0 + cr) * dv + dv0 + cv * EPV) =
+                            *reinterpret_cast<const uint4 *>(Vst + cr * PV + cv * EPV);
+                }
+            }
+            if (c >= 0) {   // gradient with respect to chunk c's exit state
+                R *dh = static_cast<R *>(args.dHs) + (static_cast<size_t>(bh) * NC + c) * dv * DK +
+                        static_cast<size_t>(dv0 + 16 * rw + r16) * DK + 4 * g4;
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) P::st4(dh + 16 * t, sT[t]);
+            }
+        } else if (c >= 0) {
+            // M1 = (H o T) diag(beta) = T_g diag(beta) (lower block triangle)
+            const float *gs = gate(ps, 0), *bes = gate(ps, 3);
+            for (int idx = rt; idx < NPAIR * 64; idx += kThreads) {
+                int i, j;
+                tri_pair(idx >> 6, i, j);
+                const int r = 16 * i + ((idx >> 2) & 15);
+                const int c0 = 16 * j + 4 * (idx & 3);
+                const F tf = P::ld4(Ts + r * PC + c0);
+                const f32x4 bc = lds_f32x4(bes + c0);
+                const f32x4 gc = lds_f32x4(gs + c0);
+                const float gr = gs[r];
+                f32x4 m1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
+                    m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+                }
+                P::st4(M1s + r * PA + c0, m1);
+            }
+        }
+        __syncthreads();
+    }
+    if (is_scan && args.g_S0) {
+        const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+        const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * rw + r16) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.g_S0 + srow + 16 * t + 4 * g4) = sT[t];
+    }
+}
+
 // ------------------------------------------------------------------ pass 3: per-chunk gradients
 // One chunk at a time per workgroup, one wave per 16 value columns (DV / 16 waves: all
 // value columns at once); the grid is as large as fits the device at once.  LDS holds the chunk's q, k, v, dO rows, Z and P, and the C x C
@@ -785,7 +1132,11 @@ template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
 hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
     const int NC = (a.T + CH - 1) / CH;
     const int g2 = a.B * a.H * a.n_dvt;
-    hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
+    if constexpr (ScanPipeLayout<P, DK, CH>::fits)
+        hipLaunchKernelGGL((chunk_bwd_scan_pipe_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(2 * kThreads), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || NC == 0) return err;
     const long long items = static_cast<long long>(a.B) * a.H * NC;

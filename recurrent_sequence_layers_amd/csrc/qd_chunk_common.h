@@ -39,14 +39,17 @@ namespace qd {
 //   L = strictly-lower(diag(beta) X K^T),  X K^T = K K^T + diag(lambda) Q K^T,
 //   A = G o lower(Q K^T),   and, when N is non-null,  N = G o strictly-lower(X K^T),
 // with G[r][c] = exp(g_r - g_c).  Blocks above the block diagonal are not written.
-template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int NW = 4>
+// wave: index of the calling wave among the NW that share the blocks; lane: its lane id.
+// PCA: the row pitch of A (PC, the pitch of L and N, by default).
+template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int NW = 4, int PCA = PC>
 __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
                                             const float *bes, const float *lams, typename P::R *Ls,
-                                            typename P::R *As, typename P::R *Ns) {
+                                            typename P::R *As, typename P::R *Ns, int wave = wave_id(),
+                                            int lane = lane_id()) {
     using F = typename P::F;
     constexpr int NKT = DK / 16, NCT = CH / 16;
     constexpr int NPAIR = NCT * (NCT + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
-    const int wave = wave_id(), lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+    const int r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
         const int p = wave + NW * u;
@@ -76,28 +79,31 @@ __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typen
                 nv[e] = (c < r) ? dec * xk : 0.f;
             }
             P::st4(Ls + r * PC + c0, lv);
-            P::st4(As + r * PC + c0, av);
+            P::st4(As + r * PCA + c0, av);
             if (Ns) P::st4(Ns + r * PC + c0, nv);
         }
     }
 }
 
-// T = (I + L)^-1 for the strictly lower CH x CH matrix L in LDS (pitch PC), by the first
-// four waves of the workgroup (every wave must call it: it holds the barriers).
-// The 16 x 16 diagonal blocks by forward substitution over rows (t_r = e_r -
-// sum_{j<r} L[r][j] t_j; wave w inverts block w, lane l computes column l % 16), then
-// block doubling on MFMA (T21 = -T22 L21 T11 for 16- and then 32-row halves).  Only
-// the lower block triangle of T is written; the upper triangle of each diagonal block
-// comes out exactly zero.  Called after a barrier that publishes L; ends with one.
-// lane: the lane id (a caller inside a loop may pass an opaque copy, so the per-lane
+// T = (I + L)^-1 for the strictly lower CH x CH matrix L in LDS (pitch PC), in three
+// stages that each read what the previous one wrote (a barrier between them):
+//   1. inverse_diag: the 16 x 16 diagonal blocks by forward substitution over rows
+//      (t_r = e_r - sum_{j<r} L[r][j] t_j; wave w < CH / 16 inverts block w, lane l
+//      computes column l % 16);
+//   2. inverse_level1: T21 = -T22 L21 T11 for the 16-row halves of each 32 x 32 block
+//      (waves w < CH / 32);
+//   3. inverse_level2 (CH = 64): the lower-left 32 x 32 quadrant, one 16 x 16 block per
+//      wave w < 4.
+// Only the lower block triangle of T is written; the upper triangle of each diagonal
+// block comes out exactly zero.  wave is the caller's index among the waves sharing the
+// work, lane its lane id (a caller inside a loop may pass opaque copies, so the per-lane
 // constants are not hoisted out of its loop and held in registers).
 template <class P, int CH, int PC>
-__device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, typename P::R *Ts, int lane = lane_id()) {
+__device__ __forceinline__ void inverse_diag(const typename P::R *Ls, typename P::R *Ts, int wave, int lane) {
     constexpr int NCT = CH / 16;
-    const int wave = wave_id(), r16 = lane & 15, g4 = lane >> 4;
     if (wave < NCT) {
         const int o = 16 * wave;
-        const int c = r16;
+        const int c = lane & 15;
         float t[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -113,24 +119,34 @@ __device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, type
             for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
         }
     }
-    __syncthreads();
-    // block (rb_, cb_) of T from an accumulator tile (rows 4g + e, column l % 16)
-    auto tstore = [&](int rb_, int cb_, f32x4 val) {
+}
+
+// block (rb, cb) of T from an accumulator tile (rows 4g + e, column l % 16)
+template <class P, int PC>
+__device__ __forceinline__ void inverse_tstore(typename P::R *Ts, int rb, int cb, f32x4 val, int lane) {
+    const int r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ts[(16 * rb_ + 4 * g4 + e) * PC + 16 * cb_ + r16] = P::from_f32(val[e]);
-    };
-    // level 1: T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
+    for (int e = 0; e < 4; ++e) Ts[(16 * rb + 4 * g4 + e) * PC + 16 * cb + r16] = P::from_f32(val[e]);
+}
+
+// T[2a+1][2a] = -T[2a+1][2a+1] L[2a+1][2a] T[2a][2a]
+template <class P, int CH, int PC>
+__device__ __forceinline__ void inverse_level1(const typename P::R *Ls, typename P::R *Ts, int wave, int lane) {
+    constexpr int NCT = CH / 16;
     if constexpr (NCT >= 2) {
         if (wave < NCT / 2) {
             const int rb_ = 2 * wave + 1, cb_ = 2 * wave;
             const f32x4 x = P::mma1(zero4(), frag<P>(Ls, PC, 16 * rb_, 16 * cb_), frag_b<P>(Ts, PC, 16 * cb_, 16 * cb_));
             const f32x4 y = P::mma1(zero4(), frag<P>(Ts, PC, 16 * rb_, 16 * rb_), P::cvt(x));
-            tstore(rb_, cb_, -y);
+            inverse_tstore<P, PC>(Ts, rb_, cb_, -y, lane);
         }
-        __syncthreads();
     }
-    // level 2 (CH = 64): lower-left 32x32 quadrant, one 16x16 block per wave:
-    // T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
+}
+
+// lower-left 32x32 quadrant: T[a][c] = -sum_{m=2..a} T[a][m] sum_{k=c..1} L[m][k] T[k][c]
+template <class P, int CH, int PC>
+__device__ __forceinline__ void inverse_level2(const typename P::R *Ls, typename P::R *Ts, int wave, int lane) {
+    constexpr int NCT = CH / 16;
     if constexpr (NCT == 4) {
         if (wave < 4) {
             const int ab = 2 + (wave >> 1), cb_ = wave & 1;
@@ -141,8 +157,26 @@ __device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, type
                     x = P::mma1(x, frag<P>(Ls, PC, 16 * m, 16 * kb), frag_b<P>(Ts, PC, 16 * kb, 16 * cb_));
                 acc = P::mma1(acc, frag<P>(Ts, PC, 16 * ab, 16 * m), P::cvt(x));
             }
-            tstore(ab, cb_, -acc);
+            inverse_tstore<P, PC>(Ts, ab, cb_, -acc, lane);
         }
+    }
+}
+
+// The three stages with the workgroup barriers between them, by the first four waves
+// (every wave must call it: it holds the barriers).  Called after a barrier that
+// publishes L; ends with one.
+template <class P, int CH, int PC>
+__device__ __forceinline__ void unit_lower_inverse(const typename P::R *Ls, typename P::R *Ts, int lane = lane_id()) {
+    constexpr int NCT = CH / 16;
+    const int wave = wave_id();
+    inverse_diag<P, CH, PC>(Ls, Ts, wave, lane);
+    __syncthreads();
+    if constexpr (NCT >= 2) {
+        inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
+        __syncthreads();
+    }
+    if constexpr (NCT == 4) {
+        inverse_level2<P, CH, PC>(Ls, Ts, wave, lane);
         __syncthreads();
     }
 }
