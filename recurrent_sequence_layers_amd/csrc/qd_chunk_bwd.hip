@@ -481,6 +481,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
         gload(NC - 1, pf);
         lstore(NC - 1, pf);
     }
+    // All loads so far (dS'^T and the first chunk) complete before the loop.  Otherwise the
+    // first use of dS'^T inside the loop is guarded, conservatively, by a wait for every
+    // outstanding load, including the prefetch issued just before it at every step.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
 
     // step n: the scan on chunk n (n < NC), the prep on chunk c = n - 1 (c >= 0)
@@ -503,28 +507,49 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                 F sTf[NKT];
 #pragma unroll
                 for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
-                // dZ = D_r K dS'^T + A^T dO   (A^T upper: blocks s >= mt)
+                // dZ = D_r K dS'^T + A^T dO (A^T upper: blocks s >= mt), then dR = M1^T dZ.
+                // Software-pipelined by hand: the fragments of row tile mt + 1 are issued
+                // before the MFMAs of tile mt, and scheduling fences keep the compiler from
+                // sinking each LDS read next to its use.
+                F Df[NCT];                             // dO blocks (s, this wave's columns)
+#pragma unroll
+                for (int s2 = 0; s2 < NCT; ++s2) Df[s2] = frag_b<P>(Ds, PD, 16 * s2, 16 * rw);
+                F kf[2][NKT], af[2][NCT];
+                auto load_mt = [&](int mt, F(&k)[NKT], F(&a)[NCT]) {
+#pragma unroll
+                    for (int t = 0; t < NKT; ++t) k[t] = frag<P>(Ks, PK, 16 * mt, 16 * t);
+#pragma unroll
+                    for (int s2 = 0; s2 < NCT; ++s2)
+                        if (s2 >= mt) a[s2] = frag_b<P>(As, PA, 16 * s2, 16 * mt);
+                };
+                load_mt(0, kf[0], af[0]);
+                F mf[NCT][NCT];                        // M1 blocks (s, mt), s >= mt, issued with the last tile
                 f32x4 dZ[NCT];
 #pragma unroll
                 for (int mt = 0; mt < NCT; ++mt) {
+                    if (mt + 1 < NCT) {
+                        load_mt(mt + 1, kf[(mt + 1) & 1], af[(mt + 1) & 1]);
+                    } else {
+#pragma unroll
+                        for (int m2 = 0; m2 < NCT; ++m2)
+#pragma unroll
+                            for (int s2 = m2; s2 < NCT; ++s2) mf[m2][s2] = frag_b<P>(M1s, PA, 16 * s2, 16 * m2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                     f32x4 kd = zero4();
 #pragma unroll
-                    for (int t = 0; t < NKT; t += 2)
-                        kd = P::mma2(kd, frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16),
-                                     sTf[t], sTf[t + 1]);
-                    dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
+                    for (int t = 0; t < NKT; t += 2) kd = P::mma2(kd, kf[mt & 1][t], kf[mt & 1][t + 1], sTf[t], sTf[t + 1]);
+                    f32x4 z = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
 #pragma unroll
-                    for (int s = mt; s < NCT; s += 2) {
-                        if (s + 1 < NCT)
-                            dZ[mt] = P::mma2(dZ[mt], frag_b<P>(As, PA, 16 * s, 16 * mt),
-                                             frag_b<P>(As, PA, 16 * s + 16, 16 * mt), frag_b<P>(Ds, PD, 16 * s, 16 * rw),
-                                             frag_b<P>(Ds, PD, 16 * s + 16, 16 * rw));
+                    for (int s2 = mt; s2 < NCT; s2 += 2) {
+                        if (s2 + 1 < NCT)
+                            z = P::mma2(z, af[mt & 1][s2], af[mt & 1][s2 + 1], Df[s2], Df[s2 + 1]);
                         else
-                            dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PA, 16 * s, 16 * mt),
-                                             frag_b<P>(Ds, PD, 16 * s, 16 * rw));
+                            z = P::mma1(z, af[mt & 1][s2], Df[s2]);
                     }
+                    dZ[mt] = z;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // dR = M1^T dZ
                 F dZf[NCT];
 #pragma unroll
                 for (int mt = 0; mt < NCT; ++mt) dZf[mt] = P::cvt(dZ[mt]);
@@ -532,12 +557,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                 for (int mt = 0; mt < NCT; ++mt) {
                     dR[mt] = zero4();
 #pragma unroll
-                    for (int s = mt; s < NCT; s += 2) {
-                        if (s + 1 < NCT)
-                            dR[mt] = P::mma2(dR[mt], frag_b<P>(M1s, PA, 16 * s, 16 * mt),
-                                             frag_b<P>(M1s, PA, 16 * s + 16, 16 * mt), dZf[s], dZf[s + 1]);
+                    for (int s2 = mt; s2 < NCT; s2 += 2) {
+                        if (s2 + 1 < NCT)
+                            dR[mt] = P::mma2(dR[mt], mf[mt][s2], mf[mt][s2 + 1], dZf[s2], dZf[s2 + 1]);
                         else
-                            dR[mt] = P::mma1(dR[mt], frag_b<P>(M1s, PA, 16 * s, 16 * mt), dZf[s]);
+                            dR[mt] = P::mma1(dR[mt], mf[mt][s2], dZf[s2]);
                     }
                 }
             }
@@ -568,22 +592,34 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                     Ff[mt] = P::cvt(f);
                 }
                 const float dlast = HAS_A ? egs[CH - 1] : 1.f;
+                // the transposed q and k fragments of key tile t + 1 are issued before the
+                // MFMAs of tile t
+                F qf[2][NCT], kf[2][NCT];
+                auto load_t = [&](int t, F(&qq)[NCT], F(&kk)[NCT]) {
+#pragma unroll
+                    for (int s2 = 0; s2 < NCT; ++s2) {
+                        qq[s2] = frag_b<P>(Qs, PK, 16 * s2, 16 * t);
+                        kk[s2] = frag_b<P>(Ks, PK, 16 * s2, 16 * t);
+                    }
+                };
+                load_t(0, qf[0], kf[0]);
 #pragma unroll
                 for (int t = 0; t < NKT; ++t) {
+                    if (t + 1 < NKT) load_t(t + 1, qf[(t + 1) & 1], kf[(t + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
                     f32x4 acc = sT[t] * dlast;
 #pragma unroll
-                    for (int s = 0; s < NCT; s += 2) {
-                        if (s + 1 < NCT) {
-                            acc = P::mma2(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), frag_b<P>(Qs, PK, 16 * s + 16, 16 * t),
-                                          Ef[s], Ef[s + 1]);
-                            acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t),
-                                          Ff[s], Ff[s + 1]);
+                    for (int s2 = 0; s2 < NCT; s2 += 2) {
+                        if (s2 + 1 < NCT) {
+                            acc = P::mma2(acc, qf[t & 1][s2], qf[t & 1][s2 + 1], Ef[s2], Ef[s2 + 1]);
+                            acc = P::mma2(acc, kf[t & 1][s2], kf[t & 1][s2 + 1], Ff[s2], Ff[s2 + 1]);
                         } else {
-                            acc = P::mma1(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), Ef[s]);
-                            acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Ff[s]);
+                            acc = P::mma1(acc, qf[t & 1][s2], Ef[s2]);
+                            acc = P::mma1(acc, kf[t & 1][s2], Ff[s2]);
                         }
                     }
                     sT[t] = acc;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else if (c >= 0) {

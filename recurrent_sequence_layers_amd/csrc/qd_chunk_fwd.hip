@@ -197,6 +197,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
 
     const int NC = (T + CH - 1) / CH;
     if (NC > 0) gload(0);
+    // The state and the first chunk's loads complete before the loop.  Otherwise the first
+    // use of the state inside the loop is guarded, conservatively, by a wait for every
+    // outstanding load, including the next chunk's prefetch.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * CH;
