@@ -37,6 +37,7 @@ namespace qd {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kChunkThreads = 512;   // chunk kernel: eight waves, four of them on the state
 constexpr int kLanesPerRow = 8;
 constexpr int kDVT = 64;
 
@@ -150,7 +151,7 @@ struct QedLayout {
 };
 
 template <class P, int DK, int CH>
-__global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkArgs args) {
+__global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedChunkArgs args) {
     using R = typename P::R;
     using F = typename P::F;
     using Lay = QedLayout<P, DK, CH>;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
     // staging threads per chunk row (each takes at least one 16-byte vector of q and k) and
     // key columns per staging thread; threads beyond CH * TPR stage nothing
     constexpr int VMIN = EPV > 4 ? EPV : 4;
-    constexpr int TPR = (kThreads / CH < DK / VMIN) ? kThreads / CH : DK / VMIN;
+    constexpr int NT = kChunkThreads;
+    constexpr int TPR = (NT / CH < DK / VMIN) ? NT / CH : DK / VMIN;
     constexpr int CPT = DK / TPR;
     static_assert(CPT % 4 == 0 && CPT <= 32, "staging split");
     constexpr int NPAIR = NCT * (NCT + 1) / 2;
@@ -202,11 +204,14 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
     R *__restrict__ go = static_cast<R *>(args.o);
     auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
 
+    // waves 0-3 own value columns [16 wave, 16 wave + 16) and their slice of S^T; the other
+    // waves take part in the state-independent work only
+    const bool state_wave = wave < 4;
     f32x4 sT[NKT];
-    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * wave + r16) * DK;
+    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * (wave & 3) + r16) * DK;
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
-        sT[t] = args.S0 ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
+        sT[t] = (state_wave && args.S0) ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
 
     // staging thread -> (row sr, key columns [sc0, sc0 + CPT)); the next chunk's raw rows are
     // loaded into registers while the current chunk computes (rows past the end are clamped
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
     const bool stager = sr < CH;
     constexpr int QV = CPT / EPV;                  // 16-byte vectors of q or k per staging thread
     constexpr int GV = CPT / 4;                    // float4 of g or b per staging thread
-    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;   // v vectors per thread
+    constexpr int NVV = (CH * VPRV + NT - 1) / NT;               // v vectors per thread
     constexpr int WPV = EPV / 4;                   // float4 of w per v vector
     uint4 rq[QV], rk[QV], rv[NVV];
     f32x4 rg[GV], rb[GV], rw[NVV][WPV];
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
         }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+            const int vi = tid + NT * j;
+            if (CH * VPRV % NT == 0 || vi < CH * VPRV) {
                 const size_t off = tok(t0 + min(vi / VPRV, last)) * dv + dv0 + (vi % VPRV) * EPV;
                 rv[j] = *reinterpret_cast<const uint4 *>(gv + off);
 #pragma unroll
@@ -291,8 +296,8 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) {
-                const int vi = tid + kThreads * j;
-                if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
+                const int vi = tid + NT * j;
+                if (CH * VPRV % NT == 0 || vi < CH * VPRV) {
                     const int c = vi / VPRV, cv = vi % VPRV;
                     const R *e = reinterpret_cast<const R *>(&rv[j]);
 #pragma unroll
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
         __syncthreads();
         // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0): the
         // column is read into registers, summed, and written back
-        for (int c = tid; c < DK; c += kThreads) {
+        for (int c = tid; c < DK; c += NT) {
             float col[CH];
 #pragma unroll
             for (int t = 0; t < CH; ++t) col[t] = Gs[t * PF + c];
@@ -374,59 +379,61 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
         __syncthreads();
         unit_lower_inverse<P, CH, PC>(Ls, Ts);
 
-        // ---- this wave's 16 value columns
-        F sTf[NKT];
+        // ---- this wave's 16 value columns (state waves)
+        if (state_wave) {
+            F sTf[NKT];
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
-        F Ef[NCT];
+            for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
+            F Ef[NCT];
 #pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            f32x4 y = zero4();
+            for (int mt = 0; mt < NCT; ++mt) {
+                f32x4 y = zero4();
 #pragma unroll
-            for (int t = 0; t < NKT; t += 2)
-                y = P::mma2(y, frag<P>(Ats, PK, 16 * mt, 16 * t), frag<P>(Ats, PK, 16 * mt, 16 * t + 16), sTf[t],
-                            sTf[t + 1]);
-            f32x4 wv;
+                for (int t = 0; t < NKT; t += 2)
+                    y = P::mma2(y, frag<P>(Ats, PK, 16 * mt, 16 * t), frag<P>(Ats, PK, 16 * mt, 16 * t + 16), sTf[t],
+                                sTf[t + 1]);
+                f32x4 wv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = WVs[(16 * mt + 4 * g4 + e) * PW + 16 * wave + r16];
-            Ef[mt] = P::cvt(wv - y);
-        }
-        f32x4 Rr[NCT];
-        F Rf[NCT];
+                for (int e = 0; e < 4; ++e) wv[e] = WVs[(16 * mt + 4 * g4 + e) * PW + 16 * wave + r16];
+                Ef[mt] = P::cvt(wv - y);
+            }
+            f32x4 Rr[NCT];
+            F Rf[NCT];
 #pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            Rr[mt] = zero4();
+            for (int mt = 0; mt < NCT; ++mt) {
+                Rr[mt] = zero4();
 #pragma unroll
-            for (int s = 0; s <= mt; ++s) Rr[mt] = P::mma1(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), Ef[s]);
-            Rf[mt] = P::cvt(Rr[mt]);
-        }
-        f32x4 O[NCT];
+                for (int s = 0; s <= mt; ++s) Rr[mt] = P::mma1(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), Ef[s]);
+                Rf[mt] = P::cvt(Rr[mt]);
+            }
+            f32x4 O[NCT];
 #pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            O[mt] = zero4();
+            for (int mt = 0; mt < NCT; ++mt) {
+                O[mt] = zero4();
 #pragma unroll
-            for (int t = 0; t < NKT; t += 2)
-                O[mt] = P::mma2(O[mt], frag<P>(Qts, PK, 16 * mt, 16 * t), frag<P>(Qts, PK, 16 * mt, 16 * t + 16),
-                                sTf[t], sTf[t + 1]);
+                for (int t = 0; t < NKT; t += 2)
+                    O[mt] = P::mma2(O[mt], frag<P>(Qts, PK, 16 * mt, 16 * t), frag<P>(Qts, PK, 16 * mt, 16 * t + 16),
+                                    sTf[t], sTf[t + 1]);
 #pragma unroll
-            for (int s = 0; s <= mt; ++s) O[mt] = P::mma1(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), Rf[s]);
-        }
-        // S^T <- diag(exp Gm_C) S^T + Kh^T R
+                for (int s = 0; s <= mt; ++s) O[mt] = P::mma1(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), Rf[s]);
+            }
+            // S^T <- diag(exp Gm_C) S^T + Kh^T R
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            f32x4 acc = lds_f32x4(eGC + 16 * t + 4 * g4) * sT[t];
+            for (int t = 0; t < NKT; ++t) {
+                f32x4 acc = lds_f32x4(eGC + 16 * t + 4 * g4) * sT[t];
 #pragma unroll
-            for (int s = 0; s < NCT; ++s) acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
-            sT[t] = acc;
-        }
-        // output rows through LDS
+                for (int s = 0; s < NCT; ++s) acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
+                sT[t] = acc;
+            }
+            // output rows through LDS
 #pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
+            for (int mt = 0; mt < NCT; ++mt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(O[mt][e]);
+                for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(O[mt][e]);
+            }
         }
         __syncthreads();
-        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
+        for (int vi = tid; vi < CH * VPRV; vi += NT) {
             const int c = vi / VPRV, cv = vi % VPRV;
             if (c < clen)
                 *reinterpret_cast<uint4 *>(go + tok(t0 + c) * dv + dv0 + cv * EPV) =
@@ -434,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void qed_chunk_kernel(const QedChunkAr
         }
         __syncthreads();   // the next chunk's staging rewrites every buffer read above
     }
-    if (args.S_T) {
+    if (state_wave && args.S_T) {
 #pragma unroll
         for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.S_T + srow + 16 * t + 4 * g4) = sT[t];
     }
@@ -460,7 +467,7 @@ template <class P, int DK, int CH>
 hipError_t launch_qed_chunk_typed(const QedChunkArgs &a, hipStream_t stream) {
     const int grid = a.B * a.H * a.n_dvt;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((qed_chunk_kernel<P, DK, CH>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qed_chunk_kernel<P, DK, CH>), dim3(grid), dim3(kChunkThreads), 0, stream, a);
     return hipGetLastError();
 }
 
