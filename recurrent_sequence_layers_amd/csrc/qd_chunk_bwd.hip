@@ -951,14 +951,17 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 f32x4 U = Rr[mt];
 #pragma unroll
                 for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+                f32x4 db;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float db = sum16(Pm[e] * U[e]);
+                    db[e] = sum16(Pm[e] * U[e]);
                     const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
-                    if (r16 == 0) pdb[wave * CH + 16 * mt + 4 * g4 + e] = db;
                     Zs[o] = P::from_f32(Z[mt][e]);
                     Ps[o] = P::from_f32(Pm[e]);
                 }
+                // lane r16 < 4 of each 16-lane group stores row 16 mt + 4 g + r16
+                const float x01 = (r16 & 1) ? db[1] : db[0], x23 = (r16 & 1) ? db[3] : db[2];
+                if (r16 < 4) pdb[wave * CH + 16 * mt + 4 * g4 + r16] = (r16 & 2) ? x23 : x01;
             }
         }
         __syncthreads();
@@ -1071,17 +1074,37 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 const f32x4 dlp = HAS_L ? qf * dX : zero4();
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * mt + 4 * g4 + e;
-                    const int o = r * PK + 16 * kk + r16;
+                    const int o = (16 * mt + 4 * g4 + e) * PK + 16 * kk + r16;
                     Qst[o] = P::from_f32(dQ[e]);
                     Kst[o] = P::from_f32(dK[e]);
-                    if constexpr (HAS_L) {
-                        const float rs = sum16(dlp[e]);
-                        if (r16 == 0) pdl[wave * CH + r] += rs;
+                }
+                // row sums over this wave's 16 key columns; lane r16 < 4 of each 16-lane group
+                // stores row 16 mt + 4 g + r16.  When every wave owns one key tile (NW a multiple
+                // of NKT), each (wave, row) partial is written once and needs no read.
+                constexpr bool kOnce = NW % NKT == 0;
+                const int pr = wave * CH + 16 * mt + 4 * g4 + r16;
+                auto pick = [&](f32x4 v) {
+                    const float x01 = (r16 & 1) ? v[1] : v[0], x23 = (r16 & 1) ? v[3] : v[2];
+                    return (r16 & 2) ? x23 : x01;
+                };
+                if constexpr (HAS_L) {
+                    f32x4 rs;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rs[e] = sum16(dlp[e]);
+                    const float v = pick(rs);
+                    if (r16 < 4) {
+                        if constexpr (kOnce) pdl[pr] = v;
+                        else pdl[pr] += v;
                     }
-                    if constexpr (HAS_A) {
-                        const float rs = sum16(dgp[e]);
-                        if (r16 == 0) pdg[wave * CH + r] += rs;
+                }
+                if constexpr (HAS_A) {
+                    f32x4 rs;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rs[e] = sum16(dgp[e]);
+                    const float v = pick(rs);
+                    if (r16 < 4) {
+                        if constexpr (kOnce) pdg[pr] = v;
+                        else pdg[pr] += v;
                     }
                 }
             }
