@@ -929,12 +929,24 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             f32x4 Z[NCT];
 #pragma unroll
             for (int mt = 0; mt < NCT; ++mt) {
+                // contractions over the chunk's positions, two 16-position blocks per MFMA
                 Z[mt] = zero4();
 #pragma unroll
-                for (int s = 0; s <= mt; ++s) Z[mt] = P::mma1(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), bRf[s]);
+                for (int s = 0; s <= mt; s += 2) {
+                    if (s + 1 <= mt)
+                        Z[mt] = P::mma2(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), frag<P>(Ts, PC, 16 * mt, 16 * s + 16),
+                                        bRf[s], bRf[s + 1]);
+                    else
+                        Z[mt] = P::mma1(Z[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), bRf[s]);
+                }
 #pragma unroll
-                for (int s = mt; s < NCT; ++s)
-                    dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
+                for (int s = mt; s < NCT; s += 2) {
+                    if (s + 1 < NCT)
+                        dZ[mt] = P::mma2(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(As, PC, 16 * s + 16, 16 * mt),
+                                         frag_b<P>(Ds, PV, 16 * s, 16 * wave), frag_b<P>(Ds, PV, 16 * s + 16, 16 * wave));
+                    else
+                        dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
+                }
             }
             // P = T_g^T dZ;  U = R - N Z;  dbeta += rowdot(P, U)
             F dZf[NCT], Zf[NCT];
@@ -947,10 +959,22 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             for (int mt = 0; mt < NCT; ++mt) {
                 f32x4 Pm = zero4();
 #pragma unroll
-                for (int s = mt; s < NCT; ++s) Pm = P::mma1(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
+                for (int s = mt; s < NCT; s += 2) {
+                    if (s + 1 < NCT)
+                        Pm = P::mma2(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Ts, PC, 16 * s + 16, 16 * mt), dZf[s],
+                                     dZf[s + 1]);
+                    else
+                        Pm = P::mma1(Pm, frag_b<P>(Ts, PC, 16 * s, 16 * mt), dZf[s]);
+                }
                 f32x4 U = Rr[mt];
 #pragma unroll
-                for (int s = 0; s <= mt; ++s) U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+                for (int s = 0; s <= mt; s += 2) {
+                    if (s + 1 <= mt)
+                        U = P::mma2(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s + 16)),
+                                    Zf[s], Zf[s + 1]);
+                    else
+                        U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+                }
                 f32x4 db;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1046,15 +1070,30 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 const int mt = blk / NKT, kk = blk % NKT;
                 const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
                 const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
+                // contractions over the chunk's positions, two 16-position blocks per MFMA:
+                // s <= mt for Mq K and dLb K, s >= mt for Mq^T Q + dLb^T K
                 f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
 #pragma unroll
-                for (int s = 0; s < NCT; ++s) {
-                    if (s <= mt) {
+                for (int s = 0; s < NCT; s += 2) {
+                    if (s + 1 <= mt) {
+                        const F kb0 = frag_b<P>(Ks, PK, 16 * s, 16 * kk), kb1 = frag_b<P>(Ks, PK, 16 * s + 16, 16 * kk);
+                        lbk = P::mma2(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), frag<P>(Ls, PC, 16 * mt, 16 * s + 16), kb0, kb1);
+                        mqk = P::mma2(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), frag<P>(Ts, PC, 16 * mt, 16 * s + 16), kb0, kb1);
+                    } else if (s <= mt) {
                         const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
                         lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
                         mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
                     }
-                    if (s >= mt) {
+                }
+#pragma unroll
+                for (int s = 0; s < NCT; ++s) {
+                    if (s < mt || (s - mt) % 2 != 0) continue;     // pairs (s, s + 1) from s = mt
+                    if (s + 1 < NCT) {
+                        kt = P::mma2(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Ts, PC, 16 * s + 16, 16 * mt),
+                                     frag_b<P>(Qs, PK, 16 * s, 16 * kk), frag_b<P>(Qs, PK, 16 * s + 16, 16 * kk));
+                        kt = P::mma2(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ls, PC, 16 * s + 16, 16 * mt),
+                                     frag_b<P>(Ks, PK, 16 * s, 16 * kk), frag_b<P>(Ks, PK, 16 * s + 16, 16 * kk));
+                    } else {
                         kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
                         kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
                     }
