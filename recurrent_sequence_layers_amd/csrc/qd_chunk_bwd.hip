@@ -9,9 +9,9 @@
 //     Y = X S^T,  R = V - D_g Y,  Z = T_g diag(beta) R,  O = D_g Q S^T + A Z,
 //     S'^T = g_C S^T + K^T D_r Z.
 // Three passes:
-//   1. the forward over the chunks, keeping every chunk's entry state S^T (generic
-//      forward kernel, no output);
-//   2. chunk_bwd_scan_kernel, the reverse scan: one workgroup per (batch, head, 64 value
+//   1. the forward over the chunks, keeping every chunk's entry state S^T (the states
+//      variant of the forward kernel, no output);
+//   2. chunk_bwd_scan_pipe_kernel, the reverse scan: one workgroup per (batch, head, 64 value
 //      columns) walks the chunks last to first holding the exit-state gradient dS'^T,
 //      stores it per chunk, and writes dV:
 //        dZ = A^T dO + D_r K dS'^T,  dV = dR = diag(beta) T_g^T dZ,
@@ -50,269 +50,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kDVT = 64;  // value columns per tile
 
-// ------------------------------------------------------------------ pass 2: reverse scan
-template <class P, int DK, int CH>
-struct ScanLayout {
-    static constexpr int PAD = 16 / P::kBytes;
-    static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
-    static constexpr int NQ = CH * PK, NV = CH * PV, NCC = CH * PC;
-    static constexpr int NT = (NV > NCC) ? NV : NCC;  // T buffer doubles as dV staging
-    static constexpr int oQ = 0, oK = oQ + NQ, oD = oK + NQ, oL = oD + NV, oT = oL + NCC, oA = oT + NT;
-    static constexpr int nR = oA + NCC;
-    static constexpr int bytes = nR * P::kBytes + 5 * CH * 4;
-    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
-};
-
-template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
-__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_scan_kernel(const BwdArgs args) {
-    using R = typename P::R;
-    using F = typename P::F;
-    using Lay = ScanLayout<P, DK, CH>;
-    constexpr int NKT = DK / 16, NCT = CH / 16;
-    constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
-    constexpr int EPV = 16 / P::kBytes;
-    constexpr int VPRQ = DK / EPV, VPRV = kDVT / EPV;
-    constexpr int NVQ = (CH * VPRQ + kThreads - 1) / kThreads;
-    constexpr int NVV = (CH * VPRV + kThreads - 1) / kThreads;
-    constexpr int NPAIR = NCT * (NCT + 1) / 2;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
-    R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
-    R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
-    R *const Ds = reinterpret_cast<R *>(smem) + Lay::oD;   // dO tile
-    R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;   // L, later M1 = T_g diag(beta)
-    R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;   // T, later dV staging
-    R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
-    float *const gs = reinterpret_cast<float *>(smem + Lay::nR * P::kBytes);
-    float *const egs = gs + CH;
-    float *const egls = egs + CH;
-    float *const bes = egls + CH;
-    float *const lams = bes + CH;
-
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int r16 = lane & 15, g4 = lane >> 4;
-
-    const int nblk = gridDim.x;
-    int logical = blockIdx.x;
-    if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int dvt = logical % args.n_dvt;
-    const int bh = logical / args.n_dvt;
-    const int b = bh / args.H, h = bh % args.H;
-    const int T = args.T, H = args.H, dv = args.dv;
-    const int dv0 = dvt * kDVT;
-
-    const R *__restrict__ gq = static_cast<const R *>(args.q);
-    const R *__restrict__ gk = static_cast<const R *>(args.k);
-    const R *__restrict__ gdo = static_cast<const R *>(args.dO);
-    R *__restrict__ gdv = static_cast<R *>(args.g_v);
-    auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
-
-    // dS'^T tiles: rows d_k = 16t + 4g + i, column = this wave's value column
-    f32x4 sT[NKT];
-    const size_t srow = ((static_cast<size_t>(b) * H + h) * dv + dv0 + 16 * wave + r16) * DK;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-        sT[t] = args.dST ? *reinterpret_cast<const f32x4 *>(args.dST + srow + 16 * t + 4 * g4) : zero4();
-
-    uint4 rq[NVQ], rk[NVQ], rd[NVV];
-    float ra = 1.f, rb = 0.f, rl = 0.f;
-    auto gload = [&](int n) {
-        const int t0 = n * CH;
-        const int last = min(CH, T - t0) - 1;
-#pragma unroll
-        for (int j = 0; j < NVQ; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
-                const int c = min(vi / VPRQ, last), cv = vi % VPRQ;
-                const size_t off = tok(t0 + c) * DK + cv * EPV;
-                rq[j] = *reinterpret_cast<const uint4 *>(gq + off);
-                rk[j] = *reinterpret_cast<const uint4 *>(gk + off);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
-                const int c = min(vi / VPRV, last), cv = vi % VPRV;
-                rd[j] = *reinterpret_cast<const uint4 *>(gdo + tok(t0 + c) * dv + dv0 + cv * EPV);
-            }
-        }
-        const size_t gi = tok(t0 + min(tid & (kWave - 1), last));
-        if constexpr (HAS_A) ra = args.alpha[gi];
-        rb = args.beta[gi];
-        if constexpr (HAS_L) rl = args.lam[gi];
-    };
-    auto lstore = [&](int clen) {
-#pragma unroll
-        for (int j = 0; j < NVQ; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRQ % kThreads == 0 || vi < CH * VPRQ) {
-                const int c = vi / VPRQ, cv = vi % VPRQ;
-                *reinterpret_cast<uint4 *>(Qs + c * PK + cv * EPV) = keep_if(c < clen, rq[j]);
-                *reinterpret_cast<uint4 *>(Ks + c * PK + cv * EPV) = keep_if(c < clen, rk[j]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int vi = tid + kThreads * j;
-            if (CH * VPRV % kThreads == 0 || vi < CH * VPRV) {
-                const int c = vi / VPRV, cv = vi % VPRV;
-                *reinterpret_cast<uint4 *>(Ds + c * PV + cv * EPV) = keep_if(c < clen, rd[j]);
-            }
-        }
-        if (wave == 0) {
-            const bool ok = lane < clen;
-            float x = (HAS_A && ok) ? __logf(ra) : 0.f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, CH - 1);
-            if (lane < CH) {
-                gs[lane] = x;
-                egs[lane] = __expf(x);
-                egls[lane] = __expf(glast - x);
-                bes[lane] = ok ? rb : 0.f;
-                lams[lane] = ok ? rl : 0.f;
-            }
-        }
-    };
-
-    const int NC = (T + CH - 1) / CH;
-    if (NC > 0) gload(NC - 1);
-    for (int n = NC - 1; n >= 0; --n) {
-        const int t0 = n * CH;
-        const int clen = min(CH, T - t0);
-        {   // gradient with respect to chunk n's exit state
-            R *dh = static_cast<R *>(args.dHs) + (static_cast<size_t>(bh) * NC + n) * dv * DK +
-                    static_cast<size_t>(dv0 + 16 * wave + r16) * DK + 4 * g4;
-#pragma unroll
-            for (int t = 0; t < NKT; ++t) P::st4(dh + 16 * t, sT[t]);
-        }
-        lstore(clen);
-        if (n > 0) gload(n - 1);
-        __syncthreads();
-
-        gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, nullptr);
-        __syncthreads();
-        unit_lower_inverse<P, CH, PC>(Ls, Ts);
-
-        // M1 = (H o T) diag(beta) = T_g diag(beta), in place of L (lower block triangle)
-        for (int idx = tid; idx < NPAIR * 64; idx += kThreads) {
-            int i, j;
-            tri_pair(idx >> 6, i, j);
-            const int r = 16 * i + ((idx >> 2) & 15);
-            const int c0 = 16 * j + 4 * (idx & 3);
-            const F tf = P::ld4(Ts + r * PC + c0);
-            const f32x4 bc = lds_f32x4(bes + c0);
-            const f32x4 gc = lds_f32x4(gs + c0);
-            const float gr = gs[r];
-            f32x4 m1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
-                m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
-            }
-            P::st4(Ls + r * PC + c0, m1);
-        }
-        __syncthreads();
-
-        // ---- this wave's 16 value columns
-        F sTf[NKT];
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
-        // dZ = D_r K dS'^T + A^T dO   (A^T upper: blocks s >= mt)
-        f32x4 dZ[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            f32x4 kd = zero4();
-#pragma unroll
-            for (int t = 0; t < NKT; t += 2)
-                kd = P::mma2(kd, frag<P>(Ks, PK, 16 * mt, 16 * t), frag<P>(Ks, PK, 16 * mt, 16 * t + 16), sTf[t],
-                             sTf[t + 1]);
-            dZ[mt] = HAS_A ? lds_f32x4(egls + 16 * mt + 4 * g4) * kd : kd;
-#pragma unroll
-            for (int s = mt; s < NCT; s += 2) {
-                if (s + 1 < NCT)
-                    dZ[mt] = P::mma2(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(As, PC, 16 * s + 16, 16 * mt),
-                                     frag_b<P>(Ds, PV, 16 * s, 16 * wave), frag_b<P>(Ds, PV, 16 * s + 16, 16 * wave));
-                else
-                    dZ[mt] = P::mma1(dZ[mt], frag_b<P>(As, PC, 16 * s, 16 * mt), frag_b<P>(Ds, PV, 16 * s, 16 * wave));
-            }
-        }
-        // dR = M1^T dZ
-        F dZf[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) dZf[mt] = P::cvt(dZ[mt]);
-        f32x4 dR[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            dR[mt] = zero4();
-#pragma unroll
-            for (int s = mt; s < NCT; s += 2) {
-                if (s + 1 < NCT)
-                    dR[mt] = P::mma2(dR[mt], frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ls, PC, 16 * s + 16, 16 * mt),
-                                     dZf[s], dZf[s + 1]);
-                else
-                    dR[mt] = P::mma1(dR[mt], frag_b<P>(Ls, PC, 16 * s, 16 * mt), dZf[s]);
-            }
-        }
-        // dS^T <- g_C dS'^T + Q^T D_g (dO - diag(lambda) dR) - K^T D_g dR
-        F Ef[NCT], Ff[NCT];
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-            const f32x4 dof = P::f32(frag_b<P>(Ds, PV, 16 * mt, 16 * wave));
-            const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4);
-            f32x4 e = HAS_L ? dof - lds_f32x4(lams + 16 * mt + 4 * g4) * dR[mt] : dof;
-            f32x4 f = -dR[mt];
-            if constexpr (HAS_A) {
-                e = eg * e;
-                f = eg * f;
-            }
-            Ef[mt] = P::cvt(e);
-            Ff[mt] = P::cvt(f);
-        }
-        const float dlast = HAS_A ? egs[CH - 1] : 1.f;
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            f32x4 acc = sT[t] * dlast;
-#pragma unroll
-            for (int s = 0; s < NCT; s += 2) {
-                if (s + 1 < NCT) {
-                    acc = P::mma2(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), frag_b<P>(Qs, PK, 16 * s + 16, 16 * t), Ef[s],
-                                  Ef[s + 1]);
-                    acc = P::mma2(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), frag_b<P>(Ks, PK, 16 * s + 16, 16 * t), Ff[s],
-                                  Ff[s + 1]);
-                } else {
-                    acc = P::mma1(acc, frag_b<P>(Qs, PK, 16 * s, 16 * t), Ef[s]);
-                    acc = P::mma1(acc, frag_b<P>(Ks, PK, 16 * s, 16 * t), Ff[s]);
-                }
-            }
-            sT[t] = acc;
-        }
-        // dV: stage (the T buffer is dead after the M1 build), then coalesced row stores
-#pragma unroll
-        for (int mt = 0; mt < NCT; ++mt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ts[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(dR[mt][e]);
-        }
-        __syncthreads();
-        for (int vi = tid; vi < CH * VPRV; vi += kThreads) {
-            const int c = vi / VPRV, cv = vi % VPRV;
-            if (c < clen)
-                *reinterpret_cast<uint4 *>(gdv + tok(t0 + c) * dv + dv0 + cv * EPV) =
-                    *reinterpret_cast<const uint4 *>(Ts + c * PV + cv * EPV);
-        }
-        // the next chunk's LDS writes (q, k, dO, gates) do not touch the staging buffer,
-        // and the T writes that reuse it are two barriers away
-    }
-    if (args.g_S0) {
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4 *>(args.g_S0 + srow + 16 * t + 4 * g4) = sT[t];
-    }
-}
-
 // ------------------------------------------------------------------ pass 2, pipelined
 // The reverse scan as a two-stage software pipeline over the chunks: eight waves per
 // (batch, head, 64 value columns) workgroup,
@@ -341,7 +78,6 @@ struct ScanPipeLayout {
     static constexpr int oL = oM + NCC, oT = oL + NCC, oV = oT + NCC, nR = oV + NV;
     static constexpr int kGates = 5;   // g, exp(g), exp(g_last - g), beta, lambda
     static constexpr int bytes = nR * P::kBytes + 2 * kGates * CH * 4;
-    static constexpr bool fits = bytes <= 160 * 1024;
 };
 
 template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
@@ -349,7 +85,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
     using R = typename P::R;
     using F = typename P::F;
     using Lay = ScanPipeLayout<P, DK, CH>;
-    static_assert(Lay::fits, "LDS budget of one gfx950 workgroup exceeded");
+    static_assert(Lay::bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
     constexpr int NKT = DK / 16, NCT = CH / 16;
     constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV;
     constexpr int PA = PC, PD = PV;                // row pitches of A, M1 and of dO
@@ -1230,11 +966,7 @@ template <class P, int DK, int CH, bool HAS_A, bool HAS_L>
 hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
     const int NC = (a.T + CH - 1) / CH;
     const int g2 = a.B * a.H * a.n_dvt;
-    if constexpr (ScanPipeLayout<P, DK, CH>::fits)
-        hipLaunchKernelGGL((chunk_bwd_scan_pipe_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(2 * kThreads), 0, stream,
-                           a);
-    else
-        hipLaunchKernelGGL((chunk_bwd_scan_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((chunk_bwd_scan_pipe_kernel<P, DK, CH, HAS_A, HAS_L>), dim3(g2), dim3(2 * kThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || NC == 0) return err;
     const long long items = static_cast<long long>(a.B) * a.H * NC;
