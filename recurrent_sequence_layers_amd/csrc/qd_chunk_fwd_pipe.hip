@@ -263,8 +263,8 @@ constexpr int tile_mask(const int (&t)[4], int n) {
 
 // RAW: q and k arrive unnormalised and alpha, beta, lambda as logits; both are mapped
 // while the chunk is staged into LDS, so everything downstream is the same as without.
-// STATES: also keep every chunk's entry state S (bf16, [B][H][NC][d_v][d_k], ChunkArgs::Hs)
-// for the backward.
+// STATES: no output (nothing of O is formed); keep every chunk's entry state S (bf16,
+// [B][H][NC][d_v][d_k], ChunkArgs::Hs, when not null) for the backward.
 // EDA: Erase-then-Delta, DeltaNet (beta = 1) over the interleaved sequence e_1, k_1, e_2,
 // k_2, ... read in place: chunk row 2i is an erase token (key e_i, query and value 0) and
 // row 2i + 1 the write token (k_i, q_i, v_i) of token i of the chunk's C / 2; outputs are
@@ -587,7 +587,7 @@ struct PipeKernel {
             // ============================================================ I1
             if (is_scan) {
                 if (n >= 0) {
-                    if constexpr (STATES) {   // chunk n's entry state, rounded to bf16
+                    if (STATES && args.Hs) {   // chunk n's entry state, rounded to bf16
                         uint16_t *hs = static_cast<uint16_t *>(args.Hs) +
                                        ((static_cast<size_t>(bh) * NC + n) * dv + dv0 + 16 * rw + r16) * DK;
 #pragma unroll
@@ -647,10 +647,13 @@ struct PipeKernel {
                     }
                     // Yg = -D_g (K S^T + diag(lambda) Q S^T); the A fragments of O are issued here
                     bf16x8 af[NCT][NCP];
+                    if constexpr (!STATES) {
 #pragma unroll
-                    for (int m = 0; m < NCT; ++m)
+                        for (int m = 0; m < NCT; ++m)
 #pragma unroll
-                        for (int u = 0; u <= (m >> 1); ++u) af[m][u] = lds8(As + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
+                            for (int u = 0; u <= (m >> 1); ++u)
+                                af[m][u] = lds8(As + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
+                    }
                     bf16x4 Yg[NCT];
 #pragma unroll
                     for (int mt = 0; mt < NCT; ++mt) {
@@ -678,13 +681,16 @@ struct PipeKernel {
                         Zd[mt] = HAS_A ? Bf16::cvt(lds_f32x4(egl + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
                     }
                     // O = D_g Q S^T + A Z, staged for the row stores of I4
+                    if constexpr (!STATES) {
 #pragma unroll
-                    for (int mt = 0; mt < NCT; ++mt) {
-                        f32x4 o = HAS_A ? lds_f32x4(eg + 16 * mt + 4 * g4) * PQ[mt] : PQ[mt];
+                        for (int mt = 0; mt < NCT; ++mt) {
+                            f32x4 o = HAS_A ? lds_f32x4(eg + 16 * mt + 4 * g4) * PQ[mt] : PQ[mt];
 #pragma unroll
-                        for (int u = 0; u <= (mt >> 1); ++u) o = mfma32(af[mt][u], cat8(Zf[2 * u], Zf[2 * u + 1]), o);
+                            for (int u = 0; u <= (mt >> 1); ++u) o = mfma32(af[mt][u], cat8(Zf[2 * u], Zf[2 * u + 1]), o);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = Bf16::from_f32(o[e]);
+                            for (int e = 0; e < 4; ++e)
+                                Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = Bf16::from_f32(o[e]);
+                        }
                     }
                 }
             } else if (c < NC) {
@@ -782,7 +788,7 @@ struct PipeKernel {
                 // stage chunk n + 2 first: its wait for the prefetch would otherwise also wait
                 // for the output stores
                 if (n + 2 < NC) rstore(n + 2, pf); // into slot n & 1, released in I3
-                if (n >= 0) {
+                if (!STATES && n >= 0) {
                     const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * TPC * H * dv : 0),
                                                  has_o ? (chunk_tok(n) - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
@@ -880,6 +886,9 @@ hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipSt
 }
 
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
+    // no output wanted (the state-only passes of the segmented schedule): the instance
+    // that forms nothing of O, with no entry states kept when a.Hs is null
+    if (!a.raw && a.o == nullptr) return launch_chunk_fwd_pipe_states(dk, C, a, stream);
     if (dk == 128) {
         switch (C) {
             case 32: return launch_pipe_typed<128, 32>(a, stream);
