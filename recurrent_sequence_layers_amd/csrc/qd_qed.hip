@@ -349,8 +349,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             const int rref = (J < I) ? 16 * I : 16 * I + 8;
             const int tr = 16 * I + r16, tc = 16 * J + r16;       // this lane's row and column token
             f32x4 lacc = zero4(), macc = zero4();
-#pragma unroll
-            for (int s = 0; s < NKT; ++s) {
+            // scaled operands of one 16-channel step: row a and q, column k
+            auto step = [&](int s, F &fa, F &fq, F &fk) {
                 const int c0 = 16 * s + 4 * g4;
                 const f32x4 gr = *reinterpret_cast<const f32x4 *>(Gs + rref * PF + c0);
                 const f32x4 gt = *reinterpret_cast<const f32x4 *>(Gs + tr * PF + c0);
@@ -364,9 +364,17 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                     ea[i] = __expf(gt[i] - gr[i]);
                     ek[i] = __expf(gr[i] - gj[i]);
                 }
-                const F kb = P::cvt(xk * ek);
-                lacc = P::mma1(lacc, P::cvt(xa * ea), kb);
-                macc = P::mma1(macc, P::cvt(xq * ea), kb);
+                fa = P::cvt(xa * ea);
+                fq = P::cvt(xq * ea);
+                fk = P::cvt(xk * ek);
+            };
+#pragma unroll
+            for (int s = 0; s < NKT; s += 2) {        // two steps per MFMA
+                F a0, q0, k0, a1, q1, k1;
+                step(s, a0, q0, k0);
+                step(s + 1, a1, q1, k1);
+                lacc = P::mma2(lacc, a0, a1, k0, k1);
+                macc = P::mma2(macc, q0, q1, k0, k1);
             }
             // accumulator: rows 16 I + 4 g + e, column 16 J + l % 16
 #pragma unroll
@@ -403,7 +411,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             for (int mt = 0; mt < NCT; ++mt) {
                 Rr[mt] = zero4();
 #pragma unroll
-                for (int s = 0; s <= mt; ++s) Rr[mt] = P::mma1(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), Ef[s]);
+                for (int s = 0; s <= mt; s += 2) {   // two 16-position blocks per MFMA
+                    if (s + 1 <= mt)
+                        Rr[mt] = P::mma2(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), frag<P>(Ts, PC, 16 * mt, 16 * s + 16),
+                                         Ef[s], Ef[s + 1]);
+                    else
+                        Rr[mt] = P::mma1(Rr[mt], frag<P>(Ts, PC, 16 * mt, 16 * s), Ef[s]);
+                }
                 Rf[mt] = P::cvt(Rr[mt]);
             }
             f32x4 O[NCT];
@@ -415,14 +429,26 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                     O[mt] = P::mma2(O[mt], frag<P>(Qts, PK, 16 * mt, 16 * t), frag<P>(Qts, PK, 16 * mt, 16 * t + 16),
                                     sTf[t], sTf[t + 1]);
 #pragma unroll
-                for (int s = 0; s <= mt; ++s) O[mt] = P::mma1(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), Rf[s]);
+                for (int s = 0; s <= mt; s += 2) {
+                    if (s + 1 <= mt)
+                        O[mt] = P::mma2(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), frag<P>(Ms, PC, 16 * mt, 16 * s + 16), Rf[s],
+                                        Rf[s + 1]);
+                    else
+                        O[mt] = P::mma1(O[mt], frag<P>(Ms, PC, 16 * mt, 16 * s), Rf[s]);
+                }
             }
             // S^T <- diag(exp Gm_C) S^T + Kh^T R
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 f32x4 acc = lds_f32x4(eGC + 16 * t + 4 * g4) * sT[t];
 #pragma unroll
-                for (int s = 0; s < NCT; ++s) acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
+                for (int s = 0; s < NCT; s += 2) {
+                    if (s + 1 < NCT)
+                        acc = P::mma2(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), frag_b<P>(Khs, PK, 16 * s + 16, 16 * t), Rf[s],
+                                      Rf[s + 1]);
+                    else
+                        acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
+                }
                 sT[t] = acc;
             }
             // output rows through LDS
