@@ -40,6 +40,8 @@
 // accumulation) and the same Gram and triangular-inverse steps as the forward.  A short
 // last chunk is padded with alpha = 1, beta = 0 and zero q, k, v, dO rows, which adds
 // nothing to any gradient.
+#include <atomic>
+
 #include "qd_chunk_common.h"
 #include "qd_device.h"
 #include "qd_internal.h"
@@ -945,10 +947,10 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
 template <class Kern>
 int resident_grid(Kern kernel, int threads, long long items) {
     constexpr int kMaxDev = 64;
-    static int cached[kMaxDev] = {};
+    static std::atomic<int> cached[kMaxDev];       // zero-initialised; 0 = not yet known
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-    int grid = dev >= 0 ? cached[dev] : 0;
+    int grid = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
     if (grid == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
@@ -957,7 +959,7 @@ int resident_grid(Kern kernel, int threads, long long items) {
             cus < 1)
             cus = 256;
         grid = per_cu * cus;
-        if (dev >= 0) cached[dev] = grid;
+        if (dev >= 0) cached[dev].store(grid, std::memory_order_relaxed);
     }
     return static_cast<int>(items < grid ? items : grid);
 }
