@@ -163,7 +163,7 @@ def main():
                          "byte counters are scaled against")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(requested --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -69,7 +69,7 @@ def _fwd(lib, q, k, v, a, be, la, S0):
 
 
 def _checks(lib):
-    """Return the list of reference checks that fail for this build."""
+    """Return the list of reference checks that fail for the oracle library lib."""
     failed = []
     r = np.random.default_rng(99)
     T, dk, dv = 12, 5, 4
