@@ -13,7 +13,9 @@ headline figure, and the layer backward (qdelta_chunk_bwd, all three passes) is 
 the headline workload with dO ~ N(0, 1); the QED / GDN-2 variant (per-channel decay,
 vector gates) is timed at the headline shapes (C = 32) and as a decode step, and so is
 Erase-then-Delta (C = 64).  Kernel
-durations come from HIP events recorded on the stream the kernels run on.
+durations come from HIP events recorded on the stream the kernels run on, after W
+untimed warm-up calls (default 200: the GPU's clocks take about 120 back-to-back chunk
+calls to settle).
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -145,7 +147,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks ramp up over the first ~120 back-to-back chunk calls (about 25 ms):
+    # 0.24 ms per call at first, 0.205 ms from there on; the default warm-up covers that
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
