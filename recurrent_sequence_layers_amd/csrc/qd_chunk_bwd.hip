@@ -198,12 +198,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
             const int lane = lane_id();
             const bool ok = lane < clen;
             float x = (HAS_A && ok) ? __logf(pf.a) : 0.f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, CH - 1);
+            x = wave_inclusive_sum(x);
+            const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
             if (lane < CH) {
                 gate(s, 0)[lane] = x;
                 gate(s, 1)[lane] = __expf(x);
@@ -587,12 +583,8 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         if (wave == 0) {
             const bool ok = lane < clen;
             float x = (HAS_A && ok) ? __logf(xa) : 0.f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, CH - 1);
+            x = wave_inclusive_sum(x);
+            const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
             if (lane < CH) {
                 gs[lane] = x;
                 egs[lane] = __expf(x);

@@ -179,12 +179,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(const ChunkArgs 
             // inclusive prefix sum of log(alpha) over the chunk (padding rows add 0)
             const bool ok = lane < clen;
             float x = (HAS_A && ok) ? __logf(ra) : 0.f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, CH - 1);
+            x = wave_inclusive_sum(x);
+            const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
             if (lane < CH) {
                 gs[lane] = x;
                 egs[lane] = __expf(x);

@@ -144,6 +144,22 @@ __device__ __forceinline__ typename P::F frag_b(const typename P::R *m, int pitc
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts and row
+// broadcasts (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_src<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_src<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_src<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_src<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_src<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_src<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 __device__ __forceinline__ f32x4 lds_f32x4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 }  // namespace qd
