@@ -596,17 +596,19 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         }
         for (int i = tid; i < 3 * NW * CH + 2 * NW; i += NT) pdb[i] = 0.f;
         __syncthreads();
-        F sTf[NKT], dsTf[NKT];
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            const size_t off = static_cast<size_t>(16 * wave + r16) * DK + 16 * t + 4 * g4;
-            sTf[t] = P::ld4(hs + off);
-            dsTf[t] = P::ld4(dhs + off);
-        }
 
         // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
         gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, NW>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
         __syncthreads();
+        // this wave's 16 rows of S and dS', as B operands in octet order (one 16-byte load
+        // per lane and 32 keys; the key fragments they meet are read in the same order)
+        F sTf[NKT], dsTf[NKT];
+#pragma unroll
+        for (int t = 0; t < NKT; t += 2) {
+            const size_t off = static_cast<size_t>(16 * wave + r16) * DK + 16 * t + 8 * g4;
+            P::ld8(hs + off, sTf[t], sTf[t + 1]);
+            P::ld8(dhs + off, dsTf[t], dsTf[t + 1]);
+        }
         unit_lower_inverse<P, CH, PC>(Ls, Ts, lane);
         if constexpr (HAS_A) {
             for (int idx = tid; idx < NPAIR * 64; idx += NT) {
@@ -633,12 +635,15 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 f32x4 pk = zero4(), pq = zero4(), kd = zero4();
 #pragma unroll
                 for (int t = 0; t < NKT; t += 2) {
-                    const F k0 = frag<P>(Ks, PK, 16 * mt, 16 * t), k1 = frag<P>(Ks, PK, 16 * mt, 16 * t + 16);
+                    F k0, k1;
+                    frag_oct<P>(Ks, PK, 16 * mt, 16 * t, k0, k1, lane);
                     pk = P::mma2(pk, k0, k1, sTf[t], sTf[t + 1]);
                     kd = P::mma2(kd, k0, k1, dsTf[t], dsTf[t + 1]);
-                    if constexpr (HAS_L)
-                        pq = P::mma2(pq, frag<P>(Qs, PK, 16 * mt, 16 * t), frag<P>(Qs, PK, 16 * mt, 16 * t + 16), sTf[t],
-                                     sTf[t + 1]);
+                    if constexpr (HAS_L) {
+                        F q0, q1;
+                        frag_oct<P>(Qs, PK, 16 * mt, 16 * t, q0, q1, lane);
+                        pq = P::mma2(pq, q0, q1, sTf[t], sTf[t + 1]);
+                    }
                 }
                 const f32x4 y = HAS_L ? pk + lds_f32x4(lams + 16 * mt + 4 * g4) * pq : pk;
                 const f32x4 vf = P::f32(frag_b<P>(Vs, PV, 16 * mt, 16 * wave));

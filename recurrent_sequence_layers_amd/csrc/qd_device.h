@@ -58,6 +58,12 @@ struct Bf16 {
     __device__ __forceinline__ static void st4(R *p, f32x4 a) {
         *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, cvt(a));
     }
+    // 8 consecutive elements (p 16-byte aligned) as two halves, one 16-byte access
+    __device__ __forceinline__ static void ld8(const R *p, F &lo, F &hi) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        lo = __builtin_bit_cast(bf16x4, make_uint2(u.x, u.y));
+        hi = __builtin_bit_cast(bf16x4, make_uint2(u.z, u.w));
+    }
     // acc += [A0 A1](16 x 32) [B0; B1](32 x 16)
     __device__ __forceinline__ static f32x4 mma2(f32x4 acc, F a0, F a1, F b0, F b1) {
         bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -91,6 +97,10 @@ struct F32 {
         return r;
     }
     __device__ __forceinline__ static void st4(R *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
+    __device__ __forceinline__ static void ld8(const R *p, F &lo, F &hi) {
+        lo = ld4(p);
+        hi = ld4(p + 4);
+    }
     __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -110,6 +120,18 @@ template <class P>
 __device__ __forceinline__ typename P::F frag(const typename P::R *m, int pitch, int row0, int col0) {
     const int l = lane_id();
     return P::ld4(m + (row0 + (l & 15)) * pitch + col0 + 4 * (l >> 4));
+}
+
+// The two halves of a lane's slice of a paired (32-position) product in octet order:
+// lane l takes M[row0 + l%16][col0 + 8(l/16) .. +7], lo = +0..3 and hi = +4..7, in one
+// 16-byte access.  Pairing frag at col0 and col0 + 16 gives lane group g the positions
+// 4g..4g+3 and 16+4g..16+4g+3 instead; either order contracts the same 32 positions, as
+// long as both operands of a product use it.  The element offset of each row start and
+// col0 must keep 16-byte alignment.
+template <class P>
+__device__ __forceinline__ void frag_oct(const typename P::R *m, int pitch, int row0, int col0, typename P::F &lo,
+                                         typename P::F &hi, int lane) {
+    P::ld8(m + (row0 + (lane & 15)) * pitch + col0 + 8 * (lane >> 4), lo, hi);
 }
 
 // Fragment of the transpose of the block of a row-major matrix at (row0, col0),
