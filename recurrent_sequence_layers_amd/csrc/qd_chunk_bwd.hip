@@ -736,17 +736,19 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 tri_pair(p, i, j);
 #pragma unroll
                 for (int vv = 0; vv < NVT; vv += 2) {
-                    const F z0 = frag<P>(Zs, PV, 16 * j, 16 * vv), z1 = frag<P>(Zs, PV, 16 * j, 16 * vv + 16);
-                    dAacc[u] = P::mma2(dAacc[u], frag<P>(Ds, PV, 16 * i, 16 * vv), frag<P>(Ds, PV, 16 * i, 16 * vv + 16),
-                                       z0, z1);
-                    dLacc[u] = P::mma2(dLacc[u], frag<P>(Ps, PV, 16 * i, 16 * vv), frag<P>(Ps, PV, 16 * i, 16 * vv + 16),
-                                       z0, z1);
+                    F z0, z1, a0, a1, b0, b1;
+                    frag_oct<P>(Zs, PV, 16 * j, 16 * vv, z0, z1, lane);
+                    frag_oct<P>(Ds, PV, 16 * i, 16 * vv, a0, a1, lane);
+                    frag_oct<P>(Ps, PV, 16 * i, 16 * vv, b0, b1, lane);
+                    dAacc[u] = P::mma2(dAacc[u], a0, a1, z0, z1);
+                    dLacc[u] = P::mma2(dLacc[u], b0, b1, z0, z1);
                 }
             }
         }
-        // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk);
-        // the B fragments S[16 vv + 4 g + i][16 kk + l % 16] come from global memory (rows other
-        // waves have just read, so mostly from L2; staging them through LDS measured no faster)
+        // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk),
+        // contracted over the value columns in octet order; the B fragments
+        // S[16 vv + 8 g + i][16 kk + l % 16], i = 0..7, come from global memory (rows other waves
+        // have just read, so mostly from L2; staging them through LDS measured no faster)
         f32x4 Wo[NBW], Wp[NBW], Wz[NBW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
@@ -756,13 +758,17 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 const int mt = blk / NKT, kk = blk % NKT;
 #pragma unroll
                 for (int vv = 0; vv < NVT; vv += 2) {
-                    const size_t o0 = static_cast<size_t>(16 * vv + 4 * g4) * DK + 16 * kk + r16;
-                    const size_t o1 = o0 + static_cast<size_t>(16) * DK;
+                    const size_t o0 = static_cast<size_t>(16 * vv + 8 * g4) * DK + 16 * kk + r16;
+                    const size_t o1 = o0 + static_cast<size_t>(4) * DK;
                     const F s0 = P::ld4_strided(hs + o0, DK), s1 = P::ld4_strided(hs + o1, DK);
                     const F d0 = P::ld4_strided(dhs + o0, DK), d1 = P::ld4_strided(dhs + o1, DK);
-                    Wo[j] = P::mma2(Wo[j], frag<P>(Ds, PV, 16 * mt, 16 * vv), frag<P>(Ds, PV, 16 * mt, 16 * vv + 16), s0, s1);
-                    Wp[j] = P::mma2(Wp[j], frag<P>(Ps, PV, 16 * mt, 16 * vv), frag<P>(Ps, PV, 16 * mt, 16 * vv + 16), s0, s1);
-                    Wz[j] = P::mma2(Wz[j], frag<P>(Zs, PV, 16 * mt, 16 * vv), frag<P>(Zs, PV, 16 * mt, 16 * vv + 16), d0, d1);
+                    F a0, a1, b0, b1, c0, c1;
+                    frag_oct<P>(Ds, PV, 16 * mt, 16 * vv, a0, a1, lane);
+                    frag_oct<P>(Ps, PV, 16 * mt, 16 * vv, b0, b1, lane);
+                    frag_oct<P>(Zs, PV, 16 * mt, 16 * vv, c0, c1, lane);
+                    Wo[j] = P::mma2(Wo[j], a0, a1, s0, s1);
+                    Wp[j] = P::mma2(Wp[j], b0, b1, s0, s1);
+                    Wz[j] = P::mma2(Wz[j], c0, c1, d0, d1);
                 }
             }
         }
