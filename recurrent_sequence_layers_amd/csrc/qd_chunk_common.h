@@ -57,12 +57,15 @@ __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typen
             int i, j;
             tri_pair(p, i, j);
             f32x4 gq_ = zero4(), gk_ = zero4();
+            // key contraction in octet order: one 16-byte LDS read per lane and operand
 #pragma unroll
             for (int s = 0; s < NKT; s += 2) {
-                const F a0 = frag<P>(Ks, PK, 16 * j, 16 * s);
-                const F a1 = frag<P>(Ks, PK, 16 * j, 16 * s + 16);
-                gq_ = P::mma2(gq_, a0, a1, frag<P>(Qs, PK, 16 * i, 16 * s), frag<P>(Qs, PK, 16 * i, 16 * s + 16));
-                gk_ = P::mma2(gk_, a0, a1, frag<P>(Ks, PK, 16 * i, 16 * s), frag<P>(Ks, PK, 16 * i, 16 * s + 16));
+                F a0, a1, q0, q1, k0, k1;
+                frag_oct<P>(Ks, PK, 16 * j, 16 * s, a0, a1, lane);
+                frag_oct<P>(Qs, PK, 16 * i, 16 * s, q0, q1, lane);
+                frag_oct<P>(Ks, PK, 16 * i, 16 * s, k0, k1, lane);
+                gq_ = P::mma2(gq_, a0, a1, q0, q1);
+                gk_ = P::mma2(gk_, a0, a1, k0, k1);
             }
             const int r = 16 * i + r16;
             const int c0 = 16 * j + 4 * g4;
