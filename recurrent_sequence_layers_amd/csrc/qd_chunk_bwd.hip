@@ -402,22 +402,28 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
         } else if (c >= 0) {
             // M1 = (H o T) diag(beta) = T_g diag(beta) (lower block triangle)
             const float *gs = gate(ps, 0), *bes = gate(ps, 3);
-            for (int idx = rt; idx < NPAIR * 64; idx += kThreads) {
+            // eight consecutive columns of one row per item (16-byte LDS accesses)
+            for (int idx = rt; idx < NPAIR * 32; idx += kThreads) {
                 int i, j;
-                tri_pair(idx >> 6, i, j);
-                const int r = 16 * i + ((idx >> 2) & 15);
-                const int c0 = 16 * j + 4 * (idx & 3);
-                const F tf = P::ld4(Ts + r * PC + c0);
-                const f32x4 bc = lds_f32x4(bes + c0);
-                const f32x4 gc = lds_f32x4(gs + c0);
+                tri_pair(idx >> 5, i, j);
+                const int r = 16 * i + ((idx >> 1) & 15);
+                const int c0 = 16 * j + 8 * (idx & 1);
+                F tf[2];
+                P::ld8(Ts + r * PC + c0, tf[0], tf[1]);
                 const float gr = gs[r];
-                f32x4 m1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float tb = (c0 + e <= r) ? static_cast<float>(tf[e]) * bc[e] : 0.f;
-                    m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ch = c0 + 4 * hh;
+                    const f32x4 bc = lds_f32x4(bes + ch);
+                    const f32x4 gc = lds_f32x4(gs + ch);
+                    f32x4 m1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float tb = (ch + e <= r) ? static_cast<float>(tf[hh][e]) * bc[e] : 0.f;
+                        m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+                    }
+                    P::st4(M1s + r * PA + ch, m1);
                 }
-                P::st4(M1s + r * PA + c0, m1);
             }
         }
         __syncthreads();
