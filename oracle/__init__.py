@@ -14,13 +14,13 @@ Contents
   * ``qed_fwd``     -- the QED / GDN-2 recurrence with per-channel decay and vector
                        erase and write gates (the QED reading notes §2.1-2.2; C, fp64).
   * ``eda_fwd``     -- Erase-then-Delta: erase along e, then a delta write along k (the
-                       EDA explainer's two-step pseudo-code; C, fp64).
+                       EDA explainer's core method, as one composed map; C, fp64).
   * ``chunk_form``  -- the chunkwise WY/UT-transform algebra in fp64 numpy
                        (module ``oracle.chunk_form``), used to pin that the
                        chunked algebra reproduces the recurrence.
 
-Source of the rule: the Q-Delta reading notes, §2.4 (boxed gated update and the
-teaching pseudo-code); state convention S in R^{d_v x d_k} from §2.1.
+Source of the rule: the Q-Delta reading notes, §2.4 (the boxed gated update,
+evaluated row by row); state convention S in R^{d_v x d_k} from §2.1.
 """
 import ctypes
 import os

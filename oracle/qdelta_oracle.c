@@ -3,26 +3,26 @@
  * check and the benchmark's CPU-baseline leg load this library; the product
  * path never does.  It shares no code, header or helper with the HIP library.
  *
- * What it computes: the token-by-token gated Q-Delta recurrence, exactly as the
- * Q-Delta reading notes state it (page "Q-Delta: Beyond Key-Value Associative
- * State Evolution" reading notes, section 2.4 "Q-Delta 的逐步计算", the boxed
- * gated update and its teaching pseudo-code):
+ * What it computes: the gated Q-Delta recurrence token by token, from the boxed
+ * update on the Q-Delta reading notes page ("Q-Delta: Beyond Key-Value
+ * Associative State Evolution" reading notes, section 2.4, boxed equation):
  *
- *     x_t       = k_t + lambda_t q_t            (mixed read direction, §2.1 table)
- *     S_prior   = alpha_t S_{t-1}               (decay first)
- *     err_t     = v_t - S_prior x_t             (error read along x_t)
- *     S_t       = S_prior + beta_t err_t k_t^T  (rank-one write along k_t)
- *     o_t       = S_t q_t                       (read-out uses the updated state)
+ *     S_t = alpha_t S_{t-1} (I - beta_t x_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,         with x_t = k_t + lambda_t q_t  (section 2.1 table).
  *
- * State convention (same page, §2.1 table): S is d_v x d_k, so the prediction
- * along a key is S k and the read-out is S q.  In memory a state is row-major
- * [d_v][d_k] (row = value index, column = key index).
+ * State convention (same page, section 2.1 table): S is d_v x d_k, so S k is the
+ * value predicted for key k.  In memory a state is row-major [d_v][d_k] (row =
+ * value index, column = key index).
  *
- * The transition acts on S from the right (S_prior (I - beta x k^T)), so each row
- * of S evolves on its own: row i only sees v_t[i].  The loops below therefore run
- * the row loop outside the time loop and hand independent rows to OpenMP
- * threads.  Within a row the arithmetic is the pseudo-code above, step for step,
- * in fp64, with no reassociation beyond plain left-to-right dot products.
+ * The transition multiplies S from the right, so row i of the state, s (length
+ * d_k), is mapped on its own:
+ *
+ *     s  ->  alpha s - alpha beta (s . x) k + beta v_i k
+ *
+ * (the matrix equation restricted to one row; only v_t[i] enters).  The code
+ * evaluates exactly this expression per row, in fp64, with plain left-to-right
+ * dot products, then reads out o_t[i] = s . q from the updated row.  The loops run
+ * the row loop outside the time loop and hand independent rows to OpenMP threads.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see build_oracle.py).
  */
@@ -32,22 +32,25 @@
 #include <string.h>
 #include <omp.h>
 
-/* Advance one row s (length dk) by one token.
- *   read  : direction the error is read along (x_t for Q-Delta)
- *   write : direction the correction is written along (k_t for Q-Delta)
- * Returns the post-update read-out s . q (the row's entry of o_t = S_t q_t). */
-static double advance_row(double *s, const double *read, const double *write,
-                          const double *q, double v_i, double alpha, double beta,
-                          int dk)
+static double dot(const double *a, const double *b, int n)
 {
+    double acc = 0.0;
     int j;
-    double pred = 0.0, err, out = 0.0;
-    for (j = 0; j < dk; ++j) s[j] = alpha * s[j];          /* S_prior = alpha S   */
-    for (j = 0; j < dk; ++j) pred += s[j] * read[j];       /* (S_prior x)_i       */
-    err = v_i - pred;                                      /* error_i             */
-    for (j = 0; j < dk; ++j) s[j] = s[j] + beta * err * write[j]; /* + beta err k^T */
-    for (j = 0; j < dk; ++j) out += s[j] * q[j];           /* o_i = (S_t q)_i     */
-    return out;
+    for (j = 0; j < n; ++j) acc += a[j] * b[j];
+    return acc;
+}
+
+/* Row form of the boxed update for one state row s (length dk), in place:
+ *     s <- alpha (s - beta (s . read) write) + beta v_i write
+ * i.e. s (alpha (I - beta read write^T)) + beta v_i write^T.  Q-Delta has
+ * read = x_t and write = k_t. */
+static void gated_row_update(double *s, const double *read, const double *write,
+                             double v_i, double alpha, double beta, int dk)
+{
+    const double s_read = dot(s, read, dk);                     /* (S_{t-1} x_t)_i */
+    int j;
+    for (j = 0; j < dk; ++j)
+        s[j] = alpha * (s[j] - beta * s_read * write[j]) + beta * v_i * write[j];
 }
 
 /* One step with an explicit read direction and write direction, for a single
@@ -62,8 +65,9 @@ void oracle_step_rw(double *S, const double *read, const double *write,
 {
     int i;
     for (i = 0; i < dv; ++i) {
-        double out = advance_row(S + (size_t)i * dk, read, write, q, v[i], alpha, beta, dk);
-        if (o) o[i] = out;
+        double *s = S + (size_t)i * dk;
+        gated_row_update(s, read, write, v[i], alpha, beta, dk);
+        if (o) o[i] = dot(s, q, dk);                           /* read-out from S_t */
     }
 }
 
@@ -104,10 +108,9 @@ int oracle_qdelta_fwd(const double *q, const double *k, const double *v,
             double a = alpha ? alpha[tok] : 1.0;
             double be = beta[tok];
             double la = lam ? lam[tok] : 0.0;
-            double out;
             for (j = 0; j < dk; ++j) x[j] = kt[j] + la * qt[j];   /* x_t = k_t + lambda_t q_t */
-            out = advance_row(s, x, kt, qt, v[tok * dv + i], a, be, dk);
-            if (o) o[tok * dv + i] = out;
+            gated_row_update(s, x, kt, v[tok * dv + i], a, be, dk);
+            if (o) o[tok * dv + i] = dot(s, qt, dk);          /* o_t = S_t q_t */
         }
     }
     return 0;
@@ -135,11 +138,12 @@ int oracle_qdelta_step(const double *q, const double *k, const double *v,
         const double *kt = k + nh * dk;
         double a = alpha ? alpha[nh] : 1.0;
         double la = lam ? lam[nh] : 0.0;
-        double x[1024], out;
+        double *s = S + (nh * dv + i) * dk;
+        double x[1024];
         int j;
         for (j = 0; j < dk; ++j) x[j] = kt[j] + la * qt[j];
-        out = advance_row(S + (nh * dv + i) * dk, x, kt, qt, v[nh * dv + i], a, beta[nh], dk);
-        if (o) o[nh * dv + i] = out;
+        gated_row_update(s, x, kt, v[nh * dv + i], a, beta[nh], dk);
+        if (o) o[nh * dv + i] = dot(s, qt, dk);
     }
     return 0;
 }
@@ -170,14 +174,13 @@ int oracle_max_threads(void) { return omp_get_max_threads(); }
  */
 #define ORACLE_BWD_SEG 64
 
-/* S <- alpha S + beta (v - alpha S x) k^T for one (dv x dk) state (the same step as
- * advance_row, written for a whole state). */
+/* The boxed update for one whole (dv x dk) state, row by row. */
 static void step_state(double *S, const double *x, const double *kt, const double *vt,
                        double a, double be, int dk, int dv)
 {
     int i;
     for (i = 0; i < dv; ++i)
-        advance_row(S + (size_t)i * dk, x, kt, kt, vt[i], a, be, dk);
+        gated_row_update(S + (size_t)i * dk, x, kt, vt[i], a, be, dk);
 }
 
 /* Backward of oracle_qdelta_fwd for the loss sum(o * dO) + sum(S_T * dST).
@@ -374,14 +377,15 @@ int oracle_qed_fwd(const double *q, const double *k, const double *v,
 }
 
 /* ------------------------------------------------------------------ EDA
- * Erase-then-Delta (page "Erase-then-Delta Attention" explainer, core method, the
- * two-step pseudo-code), in this file's d_v x d_k convention (the page's K x V memory
- * transposed).  Per token, with a unit erase direction e:
+ * Erase-then-Delta (page "Erase-then-Delta Attention" explainer, core method), in
+ * this file's d_v x d_k convention (the page's K x V memory transposed).  Per token,
+ * with a unit erase direction e, the page's erase (remove the state's component along
+ * e) followed by its delta write along k with no beta composes to one map:
  *
- *     S <- S - (S e) e^T                   (step 1: zero the component along e)
- *     S <- S + (v - S k) k^T               (step 2: delta write along k; no beta)
- *     o  = S q                             (read-out from the updated state)
+ *     S_t = S_{t-1} (I - e e^T)(I - k k^T) + v k^T,      o_t = S_t q.
  *
+ * Row form, expanding the product of the two projectors:
+ *     s -> s - (s . e) e + (v_i - s . k + (s . e)(e . k)) k.
  * Rows of S evolve independently. */
 int oracle_eda_fwd(const double *q, const double *k, const double *v, const double *e,
                    const double *S0, double *o, double *S_T,
@@ -406,14 +410,10 @@ int oracle_eda_fwd(const double *q, const double *k, const double *v, const doub
         for (t = 0; t < T; ++t) {
             size_t tok = ((size_t)bb * T + t) * H + h;
             const double *qt = q + tok * dk, *kt = k + tok * dk, *et = e + tok * dk;
-            double se = 0.0, sk = 0.0, err, out = 0.0;
-            for (j = 0; j < dk; ++j) se += s[j] * et[j];               /* (S e)_i */
-            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];        /* step 1   */
-            for (j = 0; j < dk; ++j) sk += s[j] * kt[j];               /* (S k)_i */
-            err = v[tok * dv + i] - sk;
-            for (j = 0; j < dk; ++j) s[j] = s[j] + err * kt[j];       /* step 2   */
-            for (j = 0; j < dk; ++j) out += s[j] * qt[j];
-            if (o) o[tok * dv + i] = out;
+            const double se = dot(s, et, dk), sk = dot(s, kt, dk), ek = dot(et, kt, dk);
+            const double coef_k = v[tok * dv + i] - sk + se * ek;
+            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j] + coef_k * kt[j];
+            if (o) o[tok * dv + i] = dot(s, qt, dk);
         }
     }
     return 0;

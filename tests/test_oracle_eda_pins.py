@@ -79,22 +79,17 @@ def test_eda_is_deltanet_on_the_interleaved_sequence(eda=oracle.eda_fwd):
 
 
 EDA_MUTANTS = {
-    "write_before_erase": ("for (j = 0; j < dk; ++j) se += s[j] * et[j];               /* (S e)_i */\n"
-                           "            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];        /* step 1   */\n"
-                           "            for (j = 0; j < dk; ++j) sk += s[j] * kt[j];               /* (S k)_i */\n"
-                           "            err = v[tok * dv + i] - sk;\n"
-                           "            for (j = 0; j < dk; ++j) s[j] = s[j] + err * kt[j];       /* step 2   */",
-                           "for (j = 0; j < dk; ++j) sk += s[j] * kt[j];\n"
-                           "            err = v[tok * dv + i] - sk;\n"
-                           "            for (j = 0; j < dk; ++j) s[j] = s[j] + err * kt[j];\n"
-                           "            for (j = 0; j < dk; ++j) se += s[j] * et[j];\n"
-                           "            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];"),
-    "erase_along_k": ("s[j] = s[j] - se * et[j];", "s[j] = s[j] - se * kt[j];"),
-    "error_from_pre_erase_state": ("for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];        /* step 1   */\n"
-                                   "            for (j = 0; j < dk; ++j) sk += s[j] * kt[j];",
-                                   "for (j = 0; j < dk; ++j) sk += s[j] * kt[j];\n"
-                                   "            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j];"),
-    "half_erase": ("s[j] = s[j] - se * et[j];", "s[j] = s[j] - 0.5 * se * et[j];"),
+    # the write applied first, then the erase: S (I - k k^T) + v k^T, then times (I - e e^T)
+    "write_before_erase": ("            const double coef_k = v[tok * dv + i] - sk + se * ek;\n"
+                           "            for (j = 0; j < dk; ++j) s[j] = s[j] - se * et[j] + coef_k * kt[j];",
+                           "            const double coef_k = v[tok * dv + i] - sk;\n"
+                           "            for (j = 0; j < dk; ++j) s[j] = s[j] + coef_k * kt[j];\n"
+                           "            { const double se2 = dot(s, et, dk); for (j = 0; j < dk; ++j) s[j] -= se2 * et[j]; }"),
+    "erase_along_k": ("s[j] = s[j] - se * et[j]", "s[j] = s[j] - se * kt[j]"),
+    # the delta write's error read from the state before the erase (the cross term dropped)
+    "error_from_pre_erase_state": ("v[tok * dv + i] - sk + se * ek;", "v[tok * dv + i] - sk;"),
+    "cross_term_sign": ("v[tok * dv + i] - sk + se * ek;", "v[tok * dv + i] - sk - se * ek;"),
+    "half_erase": ("s[j] = s[j] - se * et[j]", "s[j] = s[j] - 0.5 * se * et[j]"),
 }
 
 

@@ -17,26 +17,25 @@ GOLDEN = os.path.join(ROOT, "tests", "golden", "qed_2d_example.json")
 _dp = ctypes.POINTER(ctypes.c_double)
 
 MUTANTS = {
-    "feedback_not_decayed": [
-        ("    for (j = 0; j < dk; ++j) s[j] = alpha * s[j];          /* S_prior = alpha S   */\n"
-         "    for (j = 0; j < dk; ++j) pred += s[j] * read[j];       /* (S_prior x)_i       */\n",
-         "    for (j = 0; j < dk; ++j) pred += s[j] * read[j];\n"
-         "    for (j = 0; j < dk; ++j) s[j] = alpha * s[j];\n")],
-    "write_term_decayed": [("s[j] + beta * err * write[j]", "s[j] + alpha * beta * err * write[j]")],
+    # the decay multiplies the whole transition: dropping it from the feedback term
+    "feedback_not_decayed": [("alpha * (s[j] - beta * s_read * write[j])", "alpha * s[j] - beta * s_read * write[j]")],
+    "write_term_decayed": [("+ beta * v_i * write[j]", "+ alpha * beta * v_i * write[j]")],
     "lambda_sign": [("x[j] = kt[j] + la * qt[j];   /* x_t", "x[j] = kt[j] - la * qt[j];   /* x_t")],
     "lambda_dropped": [("x[j] = kt[j] + la * qt[j];   /* x_t", "x[j] = kt[j] + 0.0 * la * qt[j];   /* x_t")],
     "lambda_normalised": [("x[j] = kt[j] + la * qt[j];   /* x_t",
                            "x[j] = (kt[j] + la * qt[j]) / (1.0 + la);   /* x_t")],
-    "write_along_x": [("advance_row(s, x, kt, qt,", "advance_row(s, x, x, qt,")],
-    "read_along_k": [("advance_row(s, x, kt, qt,", "advance_row(s, kt, kt, qt,")],
-    "readout_along_read_dir": [("out += s[j] * q[j];", "out += s[j] * read[j];")],
-    "error_sign": [("err = v_i - pred;", "err = pred - v_i;")],
+    "write_along_x": [("gated_row_update(s, x, kt, v[tok * dv + i]", "gated_row_update(s, x, x, v[tok * dv + i]")],
+    "read_along_k": [("gated_row_update(s, x, kt, v[tok * dv + i]", "gated_row_update(s, kt, kt, v[tok * dv + i]")],
+    "readout_along_read_dir": [("o[tok * dv + i] = dot(s, qt, dk);          /* o_t",
+                                "o[tok * dv + i] = dot(s, x, dk);          /* o_t"),
+                               ("if (o) o[i] = dot(s, q, dk);", "if (o) o[i] = dot(s, read, dk);")],
+    "feedback_sign": [("(s[j] - beta * s_read * write[j])", "(s[j] + beta * s_read * write[j])")],
     "readout_before_write": [
-        ("    for (j = 0; j < dk; ++j) s[j] = s[j] + beta * err * write[j]; /* + beta err k^T */\n"
-         "    for (j = 0; j < dk; ++j) out += s[j] * q[j];           /* o_i = (S_t q)_i     */\n",
-         "    for (j = 0; j < dk; ++j) out += s[j] * q[j];\n"
-         "    for (j = 0; j < dk; ++j) s[j] = s[j] + beta * err * write[j];\n")],
-    "beta_dropped": [("s[j] + beta * err * write[j]", "s[j] + err * write[j]")],
+        ("            gated_row_update(s, x, kt, v[tok * dv + i], a, be, dk);\n"
+         "            if (o) o[tok * dv + i] = dot(s, qt, dk);          /* o_t = S_t q_t */\n",
+         "            if (o) o[tok * dv + i] = dot(s, qt, dk);\n"
+         "            gated_row_update(s, x, kt, v[tok * dv + i], a, be, dk);\n")],
+    "beta_dropped": [("+ beta * v_i * write[j]", "+ v_i * write[j]")],
 }
 
 
