@@ -22,10 +22,13 @@
  * [N][H][d_v], gates [N][H], S [N][H][d_v][d_k].
  *
  * Ownership and execution: the caller owns every buffer.  All pointers except
- * `stream` are device pointers.  The library allocates no device memory, keeps no
- * mutable global state, and enqueues its kernels asynchronously on `stream` (a
- * hipStream_t; NULL means the default stream); nothing synchronises.  Buffers must
- * stay valid until the work on `stream` completes.
+ * `stream` are device pointers.  The library allocates no device memory and
+ * enqueues its kernels asynchronously on `stream` (a hipStream_t; NULL means the
+ * default stream); nothing synchronises.  Buffers must stay valid until the work on
+ * `stream` completes.  Its only process-wide state is a host-side cache, per device,
+ * of the compute-unit count and of the backward gradient kernels' occupancy: each
+ * entry is filled once, on the first call on that device, with atomic stores, so
+ * calls from several host threads are safe.
  *
  * Errors: arguments are checked on the host before anything is enqueued; a
  * failed check returns a status and enqueues nothing.  A launch failure returns

@@ -2,7 +2,9 @@
 
 Argument marshalling only: every step of the layer runs in the HIP kernels behind
 the C ABI declared in ``include/qdelta.h``.  PyTorch supplies device memory and the
-current HIP stream.  If the library is not built, the functions raise; there is no
+HIP stream: every wrapper takes ``stream=None`` (torch's current stream) or a
+``torch.cuda.Stream``, enqueues the kernels on it and allocates any output or workspace
+it creates while that stream is current.  If the library is not built, the functions raise; there is no
 fallback path.
 
     qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C=64, o=None, S_T=None)
@@ -110,6 +112,19 @@ def _check(t, name, dtype=None, shape=None):
         raise QDeltaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _launch_stream(stream, device):
+    """The stream the kernels are enqueued on: torch's current stream, or the given
+    torch.cuda.Stream.  Wrappers allocate their outputs and workspaces while that stream
+    is current, so the caching allocator ties those blocks to it: a workspace released on
+    return is handed out again only to work ordered after these kernels."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if not isinstance(stream, torch.cuda.Stream):
+        raise QDeltaError("stream must be a torch.cuda.Stream or None")
+    return stream
+
+
 def _raise(rc, fn):
     if rc != 0:
         raise QDeltaError(f"{fn}: {qdelta_status_string(rc)} (status {rc})")
@@ -128,31 +143,31 @@ def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_
     the layer's normalisation and gate maps run inside the kernel)."""
     import torch
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
-    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
-        _check(g, name, torch.float32, (B, T, H))
-    _check(S0, "S0", torch.float32, (B, H, dv, dk))
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (B, T, H, dv))
-    if S_T is None and want_state:
-        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
-    code = _dtype_code(dt)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    ws = lib.qdelta_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
-    if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    fn = lib.qdelta_chunk_fwd_raw if raw else lib.qdelta_chunk_fwd
-    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
-            _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_chunk_fwd_raw" if raw else "qdelta_chunk_fwd")
-    return o, S_T
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+        for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+            _check(g, name, torch.float32, (B, T, H))
+        _check(S0, "S0", torch.float32, (B, H, dv, dk))
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (B, T, H, dv))
+        if S_T is None and want_state:
+            S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+        _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+        code = _dtype_code(dt)
+        ws = lib.qdelta_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
+        if ws and workspace is None:
+            workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+        fn = lib.qdelta_chunk_fwd_raw if raw else lib.qdelta_chunk_fwd
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
+                _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_chunk_fwd_raw" if raw else "qdelta_chunk_fwd")
+        return o, S_T
 
 
 def qdelta_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:
@@ -169,42 +184,42 @@ def qdelta_chunk_bwd(q, k, v, alpha, beta, lam, S0, d_o, dS_T=None, C: int = 64,
     buffer of at least qdelta_chunk_bwd_workspace_bytes(...) bytes (allocated when None)."""
     import torch
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    dev = q.device
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
-    _check(d_o, "d_o", dt, (B, T, H, dv))
-    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
-        _check(g, name, torch.float32, (B, T, H))
-    _check(S0, "S0", torch.float32, (B, H, dv, dk))
-    _check(dS_T, "dS_T", torch.float32, (B, H, dv, dk))
-    out = dict(out or {})
-    shapes = dict(dq=((B, T, H, dk), dt), dk=((B, T, H, dk), dt), dv=((B, T, H, dv), dt),
-                  dbeta=((B, T, H), torch.float32), dalpha=((B, T, H), torch.float32),
-                  dlam=((B, T, H), torch.float32), dS0=((B, H, dv, dk), torch.float32))
-    wanted = dict(dq=True, dk=True, dv=True, dbeta=True, dalpha=alpha is not None, dlam=lam is not None,
-                  dS0=want_dS0)
-    for name, (shape, dtype) in shapes.items():
-        if not wanted[name]:
-            out[name] = None
-            continue
-        if out.get(name) is None:
-            out[name] = torch.empty(shape, dtype=dtype, device=dev)
-        _check(out[name], name, dtype, shape)
-    code = _dtype_code(dt)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    ws = lib.qdelta_chunk_bwd_workspace_bytes(B, T, H, dk, dv, C, code)
-    if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    rc = lib.qdelta_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0), _ptr(d_o),
-                              _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
-                              _ptr(out["dbeta"]), _ptr(out["dlam"]), _ptr(out["dS0"]), B, T, H, dk, dv, int(C), code,
-                              ws_ptr, ws_bytes, ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_chunk_bwd")
-    return out
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        dev = q.device
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+        _check(d_o, "d_o", dt, (B, T, H, dv))
+        for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+            _check(g, name, torch.float32, (B, T, H))
+        _check(S0, "S0", torch.float32, (B, H, dv, dk))
+        _check(dS_T, "dS_T", torch.float32, (B, H, dv, dk))
+        out = dict(out or {})
+        shapes = dict(dq=((B, T, H, dk), dt), dk=((B, T, H, dk), dt), dv=((B, T, H, dv), dt),
+                      dbeta=((B, T, H), torch.float32), dalpha=((B, T, H), torch.float32),
+                      dlam=((B, T, H), torch.float32), dS0=((B, H, dv, dk), torch.float32))
+        wanted = dict(dq=True, dk=True, dv=True, dbeta=True, dalpha=alpha is not None, dlam=lam is not None,
+                      dS0=want_dS0)
+        for name, (shape, dtype) in shapes.items():
+            if not wanted[name]:
+                out[name] = None
+                continue
+            if out.get(name) is None:
+                out[name] = torch.empty(shape, dtype=dtype, device=dev)
+            _check(out[name], name, dtype, shape)
+        code = _dtype_code(dt)
+        ws = lib.qdelta_chunk_bwd_workspace_bytes(B, T, H, dk, dv, C, code)
+        if ws and workspace is None:
+            workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+        rc = lib.qdelta_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0), _ptr(d_o),
+                                  _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                                  _ptr(out["dbeta"]), _ptr(out["dlam"]), _ptr(out["dS0"]), B, T, H, dk, dv, int(C), code,
+                                  ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_chunk_bwd")
+        return out
 
 
 def qdelta_qed_chunk_fwd(q, k, v, g, b, w, lam_h, S0=None, C: int = 32, o=None, S_T=None, want_state=True,
@@ -213,25 +228,25 @@ def qdelta_qed_chunk_fwd(q, k, v, g, b, w, lam_h, S0=None, C: int = 32, o=None, 
     [B,T,H,d_k], w [B,T,H,d_v], lam_h [H], S0 [B,H,d_v,d_k] fp32.  Returns (o, S_T)."""
     import torch
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
-    _check(g, "g", torch.float32, (B, T, H, dk)); _check(b, "b", torch.float32, (B, T, H, dk))
-    _check(w, "w", torch.float32, (B, T, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
-    _check(S0, "S0", torch.float32, (B, H, dv, dk))
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (B, T, H, dv))
-    if S_T is None and want_state:
-        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.qdelta_qed_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S0),
-                                  _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), _dtype_code(dt), ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_qed_chunk_fwd")
-    return o, S_T
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+        _check(g, "g", torch.float32, (B, T, H, dk)); _check(b, "b", torch.float32, (B, T, H, dk))
+        _check(w, "w", torch.float32, (B, T, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
+        _check(S0, "S0", torch.float32, (B, H, dv, dk))
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (B, T, H, dv))
+        if S_T is None and want_state:
+            S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+        _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+        rc = lib.qdelta_qed_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S0),
+                                      _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), _dtype_code(dt), ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_qed_chunk_fwd")
+        return o, S_T
 
 
 def qdelta_qed_step(q, k, v, g, b, w, lam_h, S, o=None, stream=None):
@@ -239,22 +254,22 @@ def qdelta_qed_step(q, k, v, g, b, w, lam_h, S, o=None, stream=None):
     lam_h [H] fp32; S [N,H,d_v,d_k] fp32 updated in place.  Returns o [N,H,d_v]."""
     import torch
     lib = load_library()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
-    _check(g, "g", torch.float32, (N, H, dk)); _check(b, "b", torch.float32, (N, H, dk))
-    _check(w, "w", torch.float32, (N, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
-    _check(S, "S", torch.float32, (N, H, dv, dk))
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (N, H, dv))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.qdelta_qed_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S), _ptr(o),
-                             N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_qed_step")
-    return o
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        N, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+        _check(g, "g", torch.float32, (N, H, dk)); _check(b, "b", torch.float32, (N, H, dk))
+        _check(w, "w", torch.float32, (N, H, dv)); _check(lam_h, "lam_h", torch.float32, (H,))
+        _check(S, "S", torch.float32, (N, H, dv, dk))
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (N, H, dv))
+        rc = lib.qdelta_qed_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(lam_h), _ptr(S), _ptr(o),
+                                 N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_qed_step")
+        return o
 
 
 def qdelta_eda_chunk_fwd(q, k, v, e, S0=None, C: int = 64, o=None, S_T=None, want_state=True, workspace=None,
@@ -264,28 +279,28 @@ def qdelta_eda_chunk_fwd(q, k, v, e, S0=None, C: int = 64, o=None, S_T=None, wan
     qdelta_eda_chunk_fwd_workspace_bytes(...) bytes (allocated here when None)."""
     import torch
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
-    _check(S0, "S0", torch.float32, (B, H, dv, dk))
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (B, T, H, dv))
-    if S_T is None and want_state:
-        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
-    code = _dtype_code(dt)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    ws = lib.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
-    if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    rc = lib.qdelta_eda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
-                                  int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_eda_chunk_fwd")
-    return o, S_T
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+        _check(S0, "S0", torch.float32, (B, H, dv, dk))
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (B, T, H, dv))
+        if S_T is None and want_state:
+            S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+        _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+        code = _dtype_code(dt)
+        ws = lib.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, code)
+        if ws and workspace is None:
+            workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+        rc = lib.qdelta_eda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                      int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_eda_chunk_fwd")
+        return o, S_T
 
 
 def qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:
@@ -297,20 +312,20 @@ def qdelta_eda_step(q, k, v, e, S, o=None, stream=None):
     updated in place.  Returns o [N,H,d_v]."""
     import torch
     lib = load_library()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (N, H, dv))
-    _check(S, "S", torch.float32, (N, H, dv, dk))
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (N, H, dv))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.qdelta_eda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S), _ptr(o), N, H, dk, dv, _dtype_code(dt),
-                             ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_eda_step")
-    return o
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        N, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(e, "e", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+        _check(S, "S", torch.float32, (N, H, dv, dk))
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (N, H, dv))
+        rc = lib.qdelta_eda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(S), _ptr(o), N, H, dk, dv, _dtype_code(dt),
+                                 ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_eda_step")
+        return o
 
 
 def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None, raw: bool = False):
@@ -320,20 +335,20 @@ def qdelta_step(q, k, v, alpha, beta, lam, S, o=None, stream=None, raw: bool = F
     raw: q and k unnormalised and the gates as logits (qdelta_step_raw)."""
     import torch
     lib = load_library()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
-    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
-        _check(g, name, torch.float32, (N, H))
-    _check(S, "S", torch.float32, (N, H, dv, dk))
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _check(o, "o", dt, (N, H, dv))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    fn = lib.qdelta_step_raw if raw else lib.qdelta_step
-    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S), _ptr(o),
-            N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(stream))
-    _raise(rc, "qdelta_step_raw" if raw else "qdelta_step")
-    return o
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        N, H, dk = q.shape
+        dv = v.shape[-1]
+        dt = q.dtype
+        _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (N, H, dv))
+        for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+            _check(g, name, torch.float32, (N, H))
+        _check(S, "S", torch.float32, (N, H, dv, dk))
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _check(o, "o", dt, (N, H, dv))
+        fn = lib.qdelta_step_raw if raw else lib.qdelta_step
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S), _ptr(o),
+                N, H, dk, dv, _dtype_code(dt), ctypes.c_void_p(s.cuda_stream))
+        _raise(rc, "qdelta_step_raw" if raw else "qdelta_step")
+        return o

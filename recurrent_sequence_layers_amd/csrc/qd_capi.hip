@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace {
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -14,6 +16,27 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Buf {
+    const void *p;
+    size_t n;
+};
+
+// Every output must be disjoint from every input and from every other output.  The one
+// exception is the in-place state update: the output `same_out` may be exactly the input
+// `same_in` (same address; a partial overlap is still rejected).
+bool disjoint(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs, const void *same_in = nullptr,
+              const void *same_out = nullptr) {
+    for (const Buf &o : outs) {
+        for (const Buf &i : ins) {
+            if (same_in && o.p == same_out && i.p == same_in && o.p == i.p) continue;
+            if (overlaps(o.p, o.n, i.p, i.n)) return false;
+        }
+        for (const Buf &o2 : outs)
+            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return false;
+    }
+    return true;
+}
 
 }  // namespace
 
@@ -67,18 +90,11 @@ int qdelta_chunk_bwd(const void *q, const void *k, const void *v, const float *a
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, v_bytes = static_cast<size_t>(ntok) * d_v * es;
     const size_t g_bytes = static_cast<size_t>(ntok) * 4, st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
-    const struct { const void *p; size_t n; } ins[] = {
-        {q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {alpha, g_bytes}, {beta, g_bytes}, {lambda, g_bytes},
-        {S0, st_bytes}, {d_o, v_bytes}, {dS_T, st_bytes}};
-    const struct { const void *p; size_t n; } outs[] = {
-        {dq, qk_bytes}, {dk, qk_bytes}, {dv, v_bytes}, {dalpha, g_bytes}, {dbeta, g_bytes}, {dlambda, g_bytes},
-        {dS0, st_bytes}, {workspace, need}};
-    for (const auto &o : outs) {
-        for (const auto &i : ins)
-            if (overlaps(o.p, o.n, i.p, i.n)) return QD_ERR_INVALID_ARG;
-        for (const auto &o2 : outs)
-            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return QD_ERR_INVALID_ARG;
-    }
+    if (!disjoint({{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {alpha, g_bytes}, {beta, g_bytes}, {lambda, g_bytes},
+                   {S0, st_bytes}, {d_o, v_bytes}, {dS_T, st_bytes}},
+                  {{dq, qk_bytes}, {dk, qk_bytes}, {dv, v_bytes}, {dalpha, g_bytes}, {dbeta, g_bytes}, {dlambda, g_bytes},
+                   {dS0, st_bytes}, {workspace, need}}))
+        return QD_ERR_INVALID_ARG;
 
     qd::BwdArgs a;
     a.q = q; a.k = k; a.v = v;
@@ -112,12 +128,10 @@ int qdelta_qed_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const size_t o_bytes = static_cast<size_t>(ntok) * d_v * es, st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
     const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, gb_bytes = static_cast<size_t>(ntok) * d_k * 4;
     const size_t w_bytes = static_cast<size_t>(ntok) * d_v * 4;
-    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {v, o_bytes}, {g, gb_bytes},
-                                                      {b, gb_bytes}, {w, w_bytes}, {lambda_h, H * sizeof(float)}};
-    for (const auto &i : ins)
-        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S_T, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
-    if (overlaps(o, o_bytes, S0, st_bytes) || overlaps(o, o_bytes, S_T, st_bytes)) return QD_ERR_INVALID_ARG;
-    if (S_T && S0 && S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)) return QD_ERR_INVALID_ARG;
+    if (!disjoint({{q, qk_bytes}, {k, qk_bytes}, {v, o_bytes}, {g, gb_bytes}, {b, gb_bytes}, {w, w_bytes},
+                   {lambda_h, H * sizeof(float)}, {S0, st_bytes}},
+                  {{o, o_bytes}, {S_T, st_bytes}}, S0, S_T))
+        return QD_ERR_INVALID_ARG;
     qd::QedChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w; a.lam_h = lambda_h;
     a.S0 = S0; a.o = o; a.S_T = S_T;
@@ -138,13 +152,11 @@ int qdelta_qed_step(const void *q, const void *k, const void *v, const float *g,
     if (!aligned16(S) || !aligned16(g) || !aligned16(b)) return QD_ERR_INVALID_ARG;
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t st_bytes = static_cast<size_t>(nh) * d_v * d_k * 4, o_bytes = static_cast<size_t>(nh) * d_v * es;
-    const struct { const void *p; size_t n; } ins[] = {
-        {q, static_cast<size_t>(nh) * d_k * es}, {k, static_cast<size_t>(nh) * d_k * es}, {v, o_bytes},
-        {g, static_cast<size_t>(nh) * d_k * 4}, {b, static_cast<size_t>(nh) * d_k * 4},
-        {w, static_cast<size_t>(nh) * d_v * 4}, {lambda_h, H * sizeof(float)}};
-    for (const auto &i : ins)
-        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
-    if (overlaps(o, o_bytes, S, st_bytes)) return QD_ERR_INVALID_ARG;
+    if (!disjoint({{q, static_cast<size_t>(nh) * d_k * es}, {k, static_cast<size_t>(nh) * d_k * es}, {v, o_bytes},
+                   {g, static_cast<size_t>(nh) * d_k * 4}, {b, static_cast<size_t>(nh) * d_k * 4},
+                   {w, static_cast<size_t>(nh) * d_v * 4}, {lambda_h, H * sizeof(float)}},
+                  {{o, o_bytes}, {S, st_bytes}}))
+        return QD_ERR_INVALID_ARG;
     qd::QedStepArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w; a.lam_h = lambda_h;
     a.S = S; a.o = o; a.N = N; a.H = H;
@@ -176,12 +188,8 @@ int qdelta_eda_chunk_fwd(const void *q, const void *k, const void *v, const void
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, o_bytes = static_cast<size_t>(ntok) * d_v * es;
     const size_t st_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
-    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes},
-                                                      {S0, st_bytes}};
-    for (const auto &i : ins)
-        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(workspace, need, i.p, i.n)) return QD_ERR_INVALID_ARG;
-    if (overlaps(workspace, need, o, o_bytes) || overlaps(workspace, need, S_T, st_bytes) ||
-        overlaps(o, o_bytes, S_T, st_bytes) || (S_T && S0 && S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)))
+    if (!disjoint({{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes}, {S0, st_bytes}},
+                  {{o, o_bytes}, {S_T, st_bytes}, {workspace, need}}, S0, S_T))
         return QD_ERR_INVALID_ARG;
     qd::EdaChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.e = e; a.S0 = S0; a.o = o; a.S_T = S_T;
@@ -202,10 +210,8 @@ int qdelta_eda_step(const void *q, const void *k, const void *v, const void *e, 
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t st_bytes = static_cast<size_t>(nh) * d_v * d_k * 4, o_bytes = static_cast<size_t>(nh) * d_v * es;
     const size_t qk_bytes = static_cast<size_t>(nh) * d_k * es;
-    const struct { const void *p; size_t n; } ins[] = {{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes}};
-    for (const auto &i : ins)
-        if (overlaps(o, o_bytes, i.p, i.n) || overlaps(S, st_bytes, i.p, i.n)) return QD_ERR_INVALID_ARG;
-    if (overlaps(o, o_bytes, S, st_bytes)) return QD_ERR_INVALID_ARG;
+    if (!disjoint({{q, qk_bytes}, {k, qk_bytes}, {e, qk_bytes}, {v, o_bytes}}, {{o, o_bytes}, {S, st_bytes}}))
+        return QD_ERR_INVALID_ARG;
     qd::EdaStepArgs a;
     a.q = q; a.k = k; a.v = v; a.e = e; a.S = S; a.o = o; a.N = N; a.H = H;
     const hipError_t err = qd::launch_eda_step(dtype, d_k, d_v, a, static_cast<hipStream_t>(stream));
@@ -234,13 +240,16 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, c
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t state_bytes = static_cast<size_t>(bh) * d_v * d_k * 4;
     const size_t o_bytes = static_cast<size_t>(ntok) * d_v * es;
-    // outputs must not overlap inputs (S_T == S0 exactly is the allowed in-place case)
-    if (overlaps(o, o_bytes, q, static_cast<size_t>(ntok) * d_k * es) ||
-        overlaps(o, o_bytes, k, static_cast<size_t>(ntok) * d_k * es) ||
-        overlaps(o, o_bytes, v, o_bytes) || overlaps(o, o_bytes, S_T, state_bytes) ||
-        overlaps(o, o_bytes, S0, state_bytes))
+    const size_t qk_bytes = static_cast<size_t>(ntok) * d_k * es, g_bytes = static_cast<size_t>(ntok) * 4;
+    const int P = qd::chunk_fwd_segments(dtype, B, T, H, d_k, d_v, C);
+    const size_t need = qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
+    if (need > 0 && (!workspace || !aligned16(workspace))) return QD_ERR_WORKSPACE;
+    // outputs (and the workspace) disjoint from inputs and each other; S_T == S0 exactly is
+    // the allowed in-place case
+    if (!disjoint({{q, qk_bytes}, {k, qk_bytes}, {v, o_bytes}, {alpha, g_bytes}, {beta, g_bytes}, {lambda, g_bytes},
+                   {S0, state_bytes}},
+                  {{o, o_bytes}, {S_T, state_bytes}, {need > 0 ? workspace : nullptr, need}}, S0, S_T))
         return QD_ERR_INVALID_ARG;
-    if (S_T && S0 && S_T != S0 && overlaps(S_T, state_bytes, S0, state_bytes)) return QD_ERR_INVALID_ARG;
 
     qd::ChunkArgs a;
     a.q = q; a.k = k; a.v = v;
@@ -249,16 +258,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, c
     a.B = B; a.T = T; a.H = H; a.dv = d_v;
     a.n_dvt = d_v / 64;
     a.raw = raw;
-    const int P = qd::chunk_fwd_segments(dtype, B, T, H, d_k, d_v, C);
     hipError_t err;
     if (P > 1) {
-        const size_t need = qd::chunk_fwd_segment_workspace(B, T, H, d_k, d_v, P);
-        if (!workspace || !aligned16(workspace)) return QD_ERR_WORKSPACE;
-        if (overlaps(workspace, need, q, static_cast<size_t>(ntok) * d_k * es) ||
-            overlaps(workspace, need, k, static_cast<size_t>(ntok) * d_k * es) ||
-            overlaps(workspace, need, v, o_bytes) || overlaps(workspace, need, o, o_bytes) ||
-            overlaps(workspace, need, S0, state_bytes) || overlaps(workspace, need, S_T, state_bytes))
-            return QD_ERR_INVALID_ARG;
         err = qd::launch_chunk_fwd_segmented(dtype, d_k, C, a, P, workspace, static_cast<hipStream_t>(stream));
     } else {
         err = qd::launch_chunk_fwd(dtype, d_k, C, a, static_cast<hipStream_t>(stream));
@@ -278,10 +279,10 @@ int step(const void *q, const void *k, const void *v, const float *alpha, const 
     const size_t es = dtype == QD_BF16 ? 2 : 4;
     const size_t state_bytes = static_cast<size_t>(nh) * d_v * d_k * 4;
     const size_t o_bytes = static_cast<size_t>(nh) * d_v * es;
-    if (overlaps(o, o_bytes, S, state_bytes) || overlaps(o, o_bytes, q, static_cast<size_t>(nh) * d_k * es) ||
-        overlaps(o, o_bytes, k, static_cast<size_t>(nh) * d_k * es) || overlaps(o, o_bytes, v, o_bytes) ||
-        overlaps(S, state_bytes, q, static_cast<size_t>(nh) * d_k * es) ||
-        overlaps(S, state_bytes, k, static_cast<size_t>(nh) * d_k * es) || overlaps(S, state_bytes, v, o_bytes))
+    const size_t g_bytes = static_cast<size_t>(nh) * 4;
+    if (!disjoint({{q, static_cast<size_t>(nh) * d_k * es}, {k, static_cast<size_t>(nh) * d_k * es}, {v, o_bytes},
+                   {alpha, g_bytes}, {beta, g_bytes}, {lambda, g_bytes}},
+                  {{o, o_bytes}, {S, state_bytes}}))
         return QD_ERR_INVALID_ARG;
 
     qd::StepArgs a;

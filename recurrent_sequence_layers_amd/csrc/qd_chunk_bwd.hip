@@ -952,23 +952,21 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
 
 // Persistent grid for a kernel: as many workgroups as fit on the device at once (at most
 // the number of work items), each walking items blockIdx.x, blockIdx.x + gridDim.x, ...
-// Cached per kernel and device.
+// The occupancy figure is cached per device in `cache`, which each kernel instantiation
+// owns (a function-local static of its launcher), so instantiations of different block
+// size or register use never share an entry.
 template <class Kern>
-int resident_grid(Kern kernel, int threads, long long items) {
-    constexpr int kMaxDev = 64;
-    static std::atomic<int> cached[kMaxDev];       // zero-initialised; 0 = not yet known
+int resident_grid(Kern kernel, int threads, long long items, std::atomic<int> (&cache)[kMaxDevices]) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-    int grid = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+    int grid = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
     if (grid == 0) {
-        int per_cu = 0, cus = 0;
+        int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
             per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev >= 0 ? dev : 0) != hipSuccess ||
-            cus < 1)
-            cus = 256;
-        grid = per_cu * cus;
-        if (dev >= 0) cached[dev].store(grid, std::memory_order_relaxed);
+        const int cus = device_cu_count();
+        grid = per_cu * (cus > 0 ? cus : 256);
+        if (dev >= 0) cache[dev].store(grid, std::memory_order_relaxed);
     }
     return static_cast<int>(items < grid ? items : grid);
 }
@@ -982,11 +980,13 @@ hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
     if (err != hipSuccess || NC == 0) return err;
     const long long items = static_cast<long long>(a.B) * a.H * NC;
     if (a.dv == 128) {
+        static std::atomic<int> cache[kMaxDevices];   // this instantiation's occupancy, per device
         auto kern = chunk_bwd_grad_kernel<P, DK, CH, 128, HAS_A, HAS_L>;
-        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 512, items)), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 512, items, cache)), dim3(512), 0, stream, a);
     } else {
+        static std::atomic<int> cache[kMaxDevices];
         auto kern = chunk_bwd_grad_kernel<P, DK, CH, 64, HAS_A, HAS_L>;
-        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 256, items)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(kern, dim3(resident_grid(kern, 256, items, cache)), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -5,6 +5,14 @@
 
 namespace qd {
 
+// Devices the host-side caches have an entry for (device ids at or above it are simply
+// not cached).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, read once per device and cached (0 if the query
+// fails).  Sizes the segmented schedule and the backward's persistent grid.
+int device_cu_count();
+
 struct ChunkArgs {
     const void *q, *k, *v;          // [B][T][H][d_k] / [B][T][H][d_v], element type per dtype;
                                     // v may be null (read as zeros) for the bf16 C = 32, 64 kernel

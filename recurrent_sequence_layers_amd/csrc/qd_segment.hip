@@ -19,6 +19,8 @@
 #include "qd_device.h"
 #include "qd_internal.h"
 
+#include <atomic>
+
 namespace qd {
 namespace {
 
@@ -83,20 +85,29 @@ __global__ __launch_bounds__(256) void segment_propagate_kernel(const float *S0,
     }
 }
 
-int compute_units() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+}  // namespace
+
+int device_cu_count() {
+    // the library's one host-side cache: the compute-unit count of each device, read
+    // once per device (an attribute that cannot change while the process runs)
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int n = cached[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
-
-}  // namespace
 
 int chunk_fwd_segments(int dtype, int B, int T, int H, int dk, int dv, int C) {
     // the state-only passes use the bf16 eight-wave kernel (null v and o)
     if (dtype != 1 || (C != 32 && C != 64) || B <= 0 || H <= 0 || T <= 0) return 1;
     const long long units = static_cast<long long>(B) * H * (dv > dk ? dv : dk) / 64;
-    const int cus = compute_units();
+    const int cus = device_cu_count();
     int P = 1;
     while (P < 16 && units * 2 * P <= cus && T % (2 * P * C) == 0 && T / (2 * P * C) >= 8) P *= 2;
     return P;

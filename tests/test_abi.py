@@ -184,3 +184,23 @@ def test_eda_host_side_rejections(lib):
     assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 64, 128, 32, 1) == 0
     assert lib.qdelta_eda_chunk_fwd_workspace_bytes(2, 10, 3, 128, 128, 64, 1) == 0
     assert lib.qdelta_eda_step(FAKE, FAKE * 2, FAKE * 3, None, FAKE * 64, FAKE * 5, 2, 2, 64, 64, 1, None) == QD_ERR_INVALID_ARG
+
+
+def test_gate_arrays_are_part_of_the_disjointness_check(lib):
+    """Every entry point checks each output against every input, the gate arrays
+    included; a partial overlap with the state is rejected too."""
+    # chunk forward: S_T over alpha, o over lambda, S_T over beta
+    assert _fwd(lib, alpha=FAKE * 6, S_T=FAKE * 6) == QD_ERR_INVALID_ARG
+    assert _fwd(lib, lam=FAKE * 7, o=FAKE * 7) == QD_ERR_INVALID_ARG
+    assert _fwd(lib, S_T=FAKE * 4 - 1024) == QD_ERR_INVALID_ARG       # the state's span covers beta
+    # decode step: the state over a gate, the output over a gate
+    assert _step(lib, alpha=FAKE * 64 + 64) == QD_ERR_INVALID_ARG
+    assert _step(lib, lam=FAKE * 5) == QD_ERR_INVALID_ARG
+    # backward: the workspace over beta
+    assert _bwd(lib, ws=FAKE * 5) == QD_ERR_INVALID_ARG
+    # QED: S_T over the erase gate, and a partial overlap of S_T with S0
+    assert _qed(lib, S_T=FAKE * 5) == QD_ERR_INVALID_ARG
+    assert _qed(lib, S0=FAKE * 64, S_T=FAKE * 64 + 16) == QD_ERR_INVALID_ARG
+    # EDA: the workspace over S0, S_T over q
+    assert _eda(lib, S0=FAKE * 32, ws=FAKE * 32) == QD_ERR_INVALID_ARG
+    assert _eda(lib, S_T=FAKE) == QD_ERR_INVALID_ARG

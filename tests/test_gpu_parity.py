@@ -408,3 +408,39 @@ def test_raw_chunk_unsupported_configurations(qd):
     q, k, v, a, b, l = raw_inputs(1, 64, 1, 64, 64, "bf16", seed=1)
     with pytest.raises(qd.QDeltaError, match="unsupported"):
         qd.qdelta_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), l.cuda(), C=16, raw=True)
+
+
+def test_side_stream_internal_allocations(qd):
+    """Calls on a side stream: the wrappers allocate the segmented schedule's workspace,
+    the backward's workspace and the outputs while that stream is current, so blocks
+    released on return cannot be handed to work on the current stream while the kernels
+    still run.  Results equal those of the same calls on the current stream, bitwise,
+    with allocation churn on the current stream in between."""
+    B, T, H, d, C = 1, 8192, 2, 128, 64
+    print(f"side stream: segmented forward B={B} T={T} H={H} d={d}, then a backward", flush=True)
+    x = inputs.chunk_inputs(B, T, H, d, d, "bf16", seed=91, s0_std=0.05, device="cuda")
+    o_ref, S_ref = qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=C)
+    dO, _ = inputs.upstream_grads(1, 300, 2, d, d, "bf16", seed=92, device="cuda")
+    xs = inputs.chunk_inputs(1, 300, 2, d, d, "bf16", seed=93, s0_std=0.05, device="cuda")
+    g_ref = qd.qdelta_chunk_bwd(xs.q, xs.k, xs.v, xs.alpha, xs.beta, xs.lam, xs.S0, dO, None, C=C)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    results = []
+    for _ in range(3):
+        results.append(qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=C, stream=side))
+        results.append(qd.qdelta_chunk_bwd(xs.q, xs.k, xs.v, xs.alpha, xs.beta, xs.lam, xs.S0, dO, None, C=C,
+                                           stream=side))
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xFF)                       # current-stream work on freshly allocated blocks
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for r in results:
+        if isinstance(r, dict):
+            for n, t in r.items():
+                assert (t is None) == (g_ref[n] is None) and (t is None or torch.equal(t, g_ref[n])), n
+        else:
+            assert torch.equal(r[0], o_ref) and torch.equal(r[1], S_ref)
+    with pytest.raises(qd.QDeltaError, match="stream"):
+        qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, x.S0, C=C, stream=side.cuda_stream)
