@@ -63,7 +63,8 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
 
 
 def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="random",
-                 s0_std=None, device="cpu", gates_as_none=False, key_corr=0.0) -> ChunkInputs:
+                 s0_std=None, device="cpu", gates_as_none=False, key_corr=0.0,
+                 alpha_logit_mean=-4.0) -> ChunkInputs:
     """Inputs for the layer forward, layout q,k [B,T,H,dk], v [B,T,H,dv],
     gates [B,T,H], S0 [B,H,dv,dk].
 
@@ -75,7 +76,11 @@ def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="ran
     key_corr: weight of one shared N(0, 1) direction per (batch, head) added to every
     q and k before normalisation (drawn last, so the other draws do not shift); at 2
     the keys of a head have mean pairwise cosine about 0.8, at 3 about 0.9, a stress
-    case for the triangular solve."""
+    case for the triangular solve.
+    alpha_logit_mean: mean of the decay logit a, alpha = exp(-softplus(a)).  The default
+    -4 gives alpha about 0.98; +1 gives strong decay (median about 0.27, down to about
+    0.05 at two standard deviations), so a 64-token chunk's cumulative decay reaches the
+    bottom of the fp32 range."""
     dt = _DT[dtype]
     g = _generator(seed, device)
     f = dict(generator=g, device=device, dtype=torch.float32)
@@ -83,7 +88,7 @@ def chunk_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lam="random", alpha="ran
     k = torch.randn(B, T, H, dk, **f)
     v = torch.randn(B, T, H, dv, **f)
     beta_logit = torch.randn(B, T, H, **f)
-    alpha_logit = torch.randn(B, T, H, **f) - 4.0
+    alpha_logit = torch.randn(B, T, H, **f) + float(alpha_logit_mean)
     lam_logit = torch.randn(B, T, H, **f)
     S0 = (torch.randn(B, H, dv, dk, **f) * float(s0_std)) if s0_std else None
     if key_corr:
@@ -190,10 +195,10 @@ def decode_state(N, H, dk, dv, s0_std=0.02, seed=0, device="cpu") -> torch.Tenso
     return (torch.randn(N, H, dv, dk, generator=g, device=device) * float(s0_std)).contiguous()
 
 
-def decode_tokens(steps, N, H, dk, dv, dtype="bf16", seed=0, device="cpu"):
+def decode_tokens(steps, N, H, dk, dv, dtype="bf16", seed=0, device="cpu", alpha_logit_mean=-4.0):
     """Per-step decode inputs for `steps` consecutive tokens: q,k [steps,N,H,dk],
     v [steps,N,H,dv], alpha, beta, lam [steps,N,H].  Same distributions as
-    ``chunk_inputs``."""
+    ``chunk_inputs`` (alpha_logit_mean likewise)."""
     dt = _DT[dtype]
     g = _generator(seed, device)
     f = dict(generator=g, device=device, dtype=torch.float32)
@@ -201,6 +206,6 @@ def decode_tokens(steps, N, H, dk, dv, dtype="bf16", seed=0, device="cpu"):
     k = _unit(torch.randn(steps, N, H, dk, **f)).to(dt).contiguous()
     v = torch.randn(steps, N, H, dv, **f).to(dt).contiguous()
     beta = torch.sigmoid(torch.randn(steps, N, H, **f)).contiguous()
-    alpha = torch.exp(-torch.nn.functional.softplus(torch.randn(steps, N, H, **f) - 4.0)).contiguous()
+    alpha = torch.exp(-torch.nn.functional.softplus(torch.randn(steps, N, H, **f) + float(alpha_logit_mean))).contiguous()
     lam = torch.sigmoid(torch.randn(steps, N, H, **f)).contiguous()
     return q, k, v, alpha, beta, lam
