@@ -5,17 +5,21 @@
 One timed step is one call of the chunked layer forward over the 1.3B-layer-shaped
 workload (B=8, T=4096, H=16, d_k=d_v=128, C=64, bf16 q/k/v/o, fp32 gates and
 state, S0 = 0), inputs resident in HBM.  The value is tokens/s (B*T per step).
-In the same run the decode step is timed on 256 sequences x 16 heads (fp32 state
-resident, one token per call) and reported as achieved HBM GB/s, and the layer is
-timed with lambda = 0 (Gated DeltaNet), with lambda = 0 and alpha = 1 (DeltaNet), and
-on the long-context workload (B=1, T=65536, S0 given), each reported beside the
-headline figure, and the layer backward (qdelta_chunk_bwd, all three passes) is timed on
-the headline workload with dO ~ N(0, 1); the QED / GDN-2 variant (per-channel decay,
-vector gates) is timed at the headline shapes (C = 32) and as a decode step, and so is
-Erase-then-Delta (C = 64).  Kernel
-durations come from HIP events recorded on the stream the kernels run on, after W
-untimed warm-up calls (default 200: the GPU's clocks take about 120 back-to-back chunk
-calls to settle).
+
+Order of a full run:
+  1. the fp64 oracle on the host cores over the headline inputs (cpu_baseline; the GPU
+     is idle meanwhile); its outputs give the headline's whole-tensor parity error;
+  2. the other workloads, each timed on its own: the tiny fp32 layer (B1 T256 H1 d64,
+     launch latency), lambda = 0 (Gated DeltaNet), lambda = 0 and alpha = 1 (DeltaNet),
+     the long-context layer (B1 T65536 H16, S0 given, segmented schedule), the layer
+     backward, the QED / GDN-2 and Erase-then-Delta variants, the fused prologue, the
+     decode step on 256 sequences x 16 heads (268 MB state) and on 1024 x 16 (1.07 GB,
+     four times the 256 MB Infinity Cache, so that its rate is DRAM bandwidth);
+  3. the headline: W untimed warm-up calls, then exactly K timed calls.
+The headline comes last so that its K calls run at the clocks the GPU holds under
+sustained load: from idle, MI355X takes about 120 back-to-back calls (25 ms) to ramp
+up, and a short warm-up alone would time the ramp.  Kernel durations come from HIP
+events recorded on the stream the kernels run on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -60,6 +64,25 @@ def counter_traffic(name, sources):
     return int(d["hbm_bytes_per_launch"])
 
 
+def counter_mfma(name, sources, ms_per_launch):
+    """MFMA evidence for the chunk kernel from the committed rocprofv3 counter summary (hash
+    gated like the traffic): the bf16 MFMA operations the kernel executed per launch
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP), their rate at this run's launch time as a
+    fraction of the bf16 peak, and the MFMA pipes' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES
+    over every SIMD's cycles of the profiled launch).  None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    m = d.get("mfma")
+    if d.get("kernel_source_sha") != source_sha(sources) or not m:
+        return None
+    flops = float(m["executed_flops_per_launch"])
+    return {"executed_flops_per_launch": flops,
+            "executed_frac_of_peak": flops / (ms_per_launch * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "busy_frac": m["busy_frac"], "source": f"profiles/{name}_counters.json"}
+
+
 def chunk_algorithmic(B, T, H, dk, dv, C, es):
     """Single-pass bytes and the pages' dense-product FLOP count for one forward call."""
     toks = B * T * H
@@ -97,18 +120,22 @@ def time_region(torch, fn, steps):
 
 
 def cpu_baseline(torch, x, budget_s=10.0):
-    """The fp64 oracle on whole batch rows of the same workload until ~budget_s spent."""
+    """The fp64 oracle on whole batch rows of the headline workload until ~budget_s spent
+    (the whole workload takes about 1 s on 16 threads).  Returns the baseline record and
+    the oracle's o and S_T for the rows it ran, which the headline's parity check uses."""
     import numpy as np
     import oracle
     B, T, H = x.beta.shape
     f = lambda t: None if t is None else np.ascontiguousarray(t.detach().cpu().double().numpy())
-    total, rows = 0.0, 0
+    total, rows, o_ref, s_ref = 0.0, 0, [], []
     for b in range(B):
         sl = slice(b, b + 1)
         args = [f(t[sl]) if t is not None else None for t in (x.q, x.k, x.v, x.alpha, x.beta, x.lam)]
         t0 = time.perf_counter()
-        oracle.qdelta_fwd(*args, None)
+        o, S = oracle.qdelta_fwd(*args, None)
         total += time.perf_counter() - t0
+        o_ref.append(o)
+        s_ref.append(S)
         rows += 1
         if total >= budget_s:
             break
@@ -122,10 +149,20 @@ def cpu_baseline(torch, x, budget_s=10.0):
         oracle.qdelta_fwd(tx.q, tx.k, tx.v, tx.alpha, tx.beta, tx.lam, None, nthreads=1)
         reps += 1
     one = reps * tw["B"] * tw["T"] / (time.perf_counter() - t0)
-    return {"value": rows * T / total, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{rows} of {B} batch rows x {T} tokens x {H} heads of the same workload "
-                      f"({rows * T * H} token-heads, {total:.2f} s, fp64 recurrence, OpenMP over state rows)",
-            "host": host, "one_thread_tiny_fp32_tokens_per_s": one}
+    rec = {"value": rows * T / total, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+           "sample": f"{rows} of {B} batch rows x {T} tokens x {H} heads of the same workload "
+                     f"({rows * T * H} token-heads, {total:.2f} s, fp64 recurrence, OpenMP over state rows)",
+           "host": host, "one_thread_tiny_fp32_tokens_per_s": one}
+    return rec, (np.concatenate(o_ref), np.concatenate(s_ref))
+
+
+def max_rel_err(y, ref, axes):
+    """max over (batch, head) slices of max|y - ref| / max|ref| (the parity metric)."""
+    import numpy as np
+    y = np.asarray(y, dtype=np.float64)
+    num = np.abs(y - ref).max(axis=axes)
+    den = np.abs(ref).max(axis=axes)
+    return float((num / np.where(den == 0, 1.0, den)).max())
 
 
 def _cpu_model():
@@ -147,14 +184,19 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU's clocks ramp up over the first ~120 back-to-back chunk calls (about 25 ms):
-    # 0.24 ms per call at first, 0.205 ms from there on; the default warm-up covers that
+    # from idle the GPU's clocks ramp up over the first ~120 back-to-back chunk calls
+    # (about 25 ms); in a full run the other workloads, timed first, cover that
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the Gated DeltaNet, DeltaNet and long-context timings (used for the "
-                         "profiled runs, so that per-kernel statistics cover the headline workload only)")
+                    help="time only the headline forward and the 256 x 16 decode step (the profiled runs, "
+                         "so that per-kernel statistics cover the headline workload only)")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the long-context forward (B1 T65536 H16, segmented schedule; profiled runs "
+                         "of its five launches)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode step, on 256 x 16 and on 1024 x 16 heads (profiled runs)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the layer backward on the headline workload (profiled runs of its kernels)")
     ap.add_argument("--qed-only", action="store_true",
@@ -190,10 +232,49 @@ def main():
     name = "layer_1p3b_bf16"
     w = inputs.WORKLOADS[name]
     B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
-    log(f"[bench] generating {name} on device")
-    x = inputs.workload_inputs(name, seed=args.seed, device="cuda")
 
-    def backward_run(steps):
+    def chunk_variant(vname, vsteps, warm):
+        """One of the chunk-forward workloads, timed on its own: ms per call, tokens/s,
+        the roofline fractions and the time ratio to the headline (filled in later)."""
+        vw = inputs.WORKLOADS[vname]
+        vB, vT, vH, vdk, vdv, vC = vw["B"], vw["T"], vw["H"], vw["dk"], vw["dv"], vw["C"]
+        es = 4 if vw["dtype"] == "f32" else 2
+        log(f"[bench] generating {vname} on device")
+        vx = inputs.workload_inputs(vname, seed=args.seed, device="cuda", gates_as_none=True)
+        vo = torch.empty((vB, vT, vH, vdv), dtype=vx.q.dtype, device=dev)
+        vS = torch.empty((vB, vH, vdv, vdk), dtype=torch.float32, device=dev)
+        nws = qd.qdelta_chunk_fwd_workspace_bytes(vB, vT, vH, vdk, vdv, vC, vx.q.dtype)
+        vws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None   # allocated outside the timing
+        vf = lambda: qd.qdelta_chunk_fwd(vx.q, vx.k, vx.v, vx.alpha, vx.beta, vx.lam, vx.S0, C=vC,
+                                         o=vo, S_T=vS, workspace=vws)
+        for _ in range(warm):
+            vf()
+        torch.cuda.synchronize()
+        v_s, _ = time_region(torch, vf, vsteps)
+        v_ms = v_s / vsteps * 1e3
+        vbytes, vflops = chunk_algorithmic(vB, vT, vH, vdk, vdv, vC, es)
+        vbytes -= vB * vT * vH * 4 * ((vx.lam is None) + (vx.alpha is None))   # gates not read
+        vbytes += 0 if vx.S0 is None else vB * vH * vdv * vdk * 4
+        rec = {"B": vB, "T": vT, "H": vH, "d_k": vdk, "d_v": vdv, "C": vC, "dtype": vw["dtype"],
+               "lambda": "0" if vx.lam is None else "sigmoid draw",
+               "alpha": "1" if vx.alpha is None else "exp(-softplus) draw",
+               "S0": None if vx.S0 is None else "N(0, 0.02)", "steps": vsteps,
+               "ms_per_call": v_ms, "tokens_per_s": vB * vT / (v_ms * 1e-3),
+               "algorithmic_bytes_per_call": vbytes, "algorithmic_flops_per_call": vflops,
+               "hbm_frac": vbytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "tflops": vflops / (v_ms * 1e-3) / 1e12,
+               "mfma_frac": vflops / (v_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "us_per_chunk_step": v_ms * 1e3 / ((vT + vC - 1) // vC),
+               "schedule": (f"segmented ({nws} B workspace)" if nws else "single pass")}
+        if vw["dtype"] == "f32":
+            rec["mfma_frac_note"] = "fp32 inputs run on fp32 MFMA; the fraction is still taken against the bf16 peak"
+        log(f"[bench] {vname}: {v_ms:.4f} ms/call, {vB * vT / (v_ms * 1e-3) / 1e6:.2f} M tokens/s, "
+            f"{rec['tflops']:.1f} TFLOP/s")
+        del vx, vo, vS, vws
+        torch.cuda.synchronize()
+        return rec
+
+    def backward_run(x, steps):
         """The layer backward on the headline workload: dO ~ N(0, 1), dS_T = 0, S0 = 0."""
         dO, _ = inputs.upstream_grads(B, T, H, dk, dv, "bf16", seed=args.seed + 5, device="cuda")
         nws = qd.qdelta_chunk_bwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
@@ -236,6 +317,7 @@ def main():
         Sd = sx.S0.clone()
         od = torch.empty((N, Hd, dv), dtype=torch.bfloat16, device=dev)
         toks_d = [tuple(t[:, i].contiguous() for t in (sx.q, sx.k, sx.v, sx.g, sx.b, sx.w)) for i in range(dsteps)]
+
         def decode():
             for tq, tk, tv, tg, tb, tw in toks_d:
                 qd.qdelta_qed_step(tq, tk, tv, tg, tb, tw, sx.lam_h, Sd, o=od)
@@ -277,6 +359,7 @@ def main():
         Sd = S0.clone()
         od = torch.empty((N, Hd, dv), dtype=torch.bfloat16, device=dev)
         toks_d = [tuple(t[:, i].contiguous() for t in (sq, sk, sv, se)) for i in range(dsteps)]
+
         def decode():
             for tq, tk, tv, te in toks_d:
                 qd.qdelta_eda_step(tq, tk, tv, te, Sd, o=od)
@@ -295,17 +378,115 @@ def main():
                                 "steps": dsteps, "us_per_step": d_us, "algorithmic_bytes_per_step": dbytes,
                                 "hbm_frac": dbytes / (d_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
+    def raw_run(x, steps):
+        """The headline layer through the fused prologue: unnormalised q, k and gate logits
+        (qdelta_chunk_fwd_raw), against the headline call on prepared inputs."""
+        g = torch.Generator(device=dev).manual_seed(args.seed + 3)
+        rq = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
+        rk = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
+        ra = torch.randn(B, T, H, generator=g, device=dev) - 4.0
+        rb = torch.randn(B, T, H, generator=g, device=dev)
+        rl = torch.randn(B, T, H, generator=g, device=dev)
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        rf = lambda: qd.qdelta_chunk_fwd(rq, rk, x.v, ra, rb, rl, None, C=C, o=o, S_T=S_T, raw=True)
+        for _ in range(args.warmup):
+            rf()
+        torch.cuda.synchronize()
+        r_s, _ = time_region(torch, rf, steps)
+        r_ms = r_s / steps * 1e3
+        sep = 2 * B * T * H * dk * 2 * 2 + 3 * B * T * H * 4 * 2
+        log(f"[bench] layer_1p3b raw prologue: {r_ms:.4f} ms/call")
+        del rq, rk, ra, rb, rl, o, S_T
+        return {"B": B, "T": T, "H": H, "inputs": "q, k unnormalised; alpha, beta, lambda as logits",
+                "steps": steps, "ms_per_call": r_ms, "tokens_per_s": B * T / (r_ms * 1e-3),
+                "separate_prologue_pass_bytes": sep, "separate_prologue_pass_us_at_peak": sep / (PEAK_HBM_GBS * 1e3)}
+
+    def decode_run(N, D, seed):
+        """D consecutive decode steps on N sequences x 16 heads, fp32 state resident in HBM;
+        the per-step inputs are generated on the device beforehand."""
+        dw = inputs.WORKLOADS["decode_256x16"]
+        Hd, dkd, dvd = dw["H"], dw["dk"], dw["dv"]
+        log(f"[bench] generating decode inputs: {N} x {Hd} heads, {D} steps")
+        dq, dk_, dv_, da, db, dl = inputs.decode_tokens(D, N, Hd, dkd, dvd, dw["dtype"], seed=seed, device="cuda")
+        S = inputs.decode_state(N, Hd, dkd, dvd, s0_std=dw["s0_std"], seed=seed + 1, device="cuda")
+        od = torch.empty((N, Hd, dvd), dtype=torch.bfloat16, device=dev)
+        lib = qd.load_library()
+        import ctypes
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        ptr = lambda t, i: ctypes.c_void_p(t[i].data_ptr())
+        calls = [(ptr(dq, i), ptr(dk_, i), ptr(dv_, i), ptr(da, i), ptr(db, i), ptr(dl, i)) for i in range(D)]
+        Sp, op = ctypes.c_void_p(S.data_ptr()), ctypes.c_void_p(od.data_ptr())
+
+        def run():
+            for c in calls:
+                rc = lib.qdelta_step(c[0], c[1], c[2], c[3], c[4], c[5], Sp, op, N, Hd, dkd, dvd, 1, stream)
+                if rc:
+                    raise RuntimeError(qd.qdelta_status_string(rc))
+
+        run()                                      # warm-up pass over all steps
+        d_s, d_wall = time_region(torch, run, 1)
+        us = d_s / D * 1e6
+        dbytes = step_algorithmic(N, Hd, dkd, dvd, 2)
+        gbs = dbytes / (us * 1e-6) / 1e9
+        log(f"[bench] decode {N}x{Hd}: {us:.2f} us/step, {gbs:.0f} GB/s algorithmic, "
+            f"{N * Hd / (us * 1e-6) / 1e6:.2f} M token-heads/s")
+        del dq, dk_, dv_, da, db, dl, S, od
+        torch.cuda.synchronize()
+        return {"workload": f"{N} sequences x {Hd} heads, d_k=d_v={dkd}, fp32 state resident "
+                            f"({N * Hd * dkd * dvd * 4 / 1e6:.0f} MB), bf16 q/k/v/o, {D} consecutive steps",
+                "steps": D, "us_per_step": us, "token_heads_per_s": N * Hd / (us * 1e-6),
+                "state_bytes": N * Hd * dkd * dvd * 4, "wall_s": d_wall,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": dbytes}}
+
+    # ---------------------------------------------------------------- profiled single modes
     if args.eda_only:
         print(json.dumps({"eda": eda_run(args.steps, 200)}), flush=True)
         return
-
     if args.qed_only:
         print(json.dumps({"qed": qed_run(args.steps, 200)}), flush=True)
         return
-
-    if args.backward_only:
-        print(json.dumps({"backward": backward_run(args.steps)}), flush=True)
+    if args.decode_only:
+        print(json.dumps({"decode_256x16": decode_run(256, args.decode_steps, args.seed + 1),
+                          "decode_1024x16": decode_run(1024, 200, args.seed + 11)}), flush=True)
         return
+    if args.long_only:
+        print(json.dumps({"long_64k_bf16": chunk_variant("long_64k_bf16", args.steps, max(1, min(args.warmup, 20)))}),
+              flush=True)
+        return
+
+    log(f"[bench] generating {name} on device")
+    x = inputs.workload_inputs(name, seed=args.seed, device="cuda")
+    if args.backward_only:
+        print(json.dumps({"backward": backward_run(x, args.steps)}), flush=True)
+        return
+
+    # ---------------------------------------------------------------- 1. the oracle on the host
+    cpu, ref = None, None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores (cpu_baseline)")
+        cpu, ref = cpu_baseline(torch, x)
+        log(f"[bench] oracle {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+
+    # ---------------------------------------------------------------- 2. the other workloads
+    variants = {}
+    if not args.headline_only:
+        variants["tiny_fp32"] = chunk_variant("tiny_fp32", 200, 50)
+        variants["tiny_fp32"]["us_per_call"] = variants["tiny_fp32"]["ms_per_call"] * 1e3
+        variants["tiny_fp32"]["bound"] = "launch latency (one workgroup, four chunks)"
+        for vname in ("gdn_bf16", "deltanet_bf16"):
+            variants[vname] = chunk_variant(vname, args.steps, min(args.warmup, 50))
+        variants["long_64k_bf16"] = chunk_variant("long_64k_bf16", 10, 3)
+        variants["layer_1p3b_backward"] = backward_run(x, max(5, args.steps // 5))
+        variants["qed_gdn2"] = qed_run(args.steps, 200)
+        variants["erase_then_delta"] = eda_run(args.steps, 200)
+        variants["layer_1p3b_raw_prologue"] = raw_run(x, args.steps)
+    decode = decode_run(256, args.decode_steps, args.seed + 1)
+    if not args.headline_only:
+        variants["decode_1024x16_beyond_infinity_cache"] = decode_run(1024, 200, args.seed + 11)
+
+    # ---------------------------------------------------------------- 3. the headline
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     fwd = lambda: qd.qdelta_chunk_fwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, C=C, o=o, S_T=S_T)
@@ -321,115 +502,24 @@ def main():
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     log(f"[bench] chunk forward {ms_per_step:.4f} ms/step, {tokens_per_s / 1e6:.2f} M tokens/s, "
         f"{ach_gbs:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+    for v in variants.values():
+        for rec in ([v] if "ms_per_call" in v else [r for r in v.values() if isinstance(r, dict)]):
+            if "ms_per_call" in rec:
+                rec["time_ratio_to_headline"] = rec["ms_per_call"] / ms_per_step
 
-    # ---- the same layer with lambda = 0 (Gated DeltaNet) and lambda = 0, alpha = 1 (DeltaNet),
-    # gates passed as NULL so the specialised kernel instances run; and the long-context
-    # workload (B=1, T=65536, S0 given, S_T returned): reported beside the headline figure
-    variants = {}
-    for vname, vsteps in (() if args.headline_only else
-                          (("gdn_bf16", args.steps), ("deltanet_bf16", args.steps), ("long_64k_bf16", 5))):
-        vw = inputs.WORKLOADS[vname]
-        vB, vT, vH = vw["B"], vw["T"], vw["H"]
-        log(f"[bench] generating {vname} on device")
-        vx = inputs.workload_inputs(vname, seed=args.seed, device="cuda", gates_as_none=True)
-        vo = torch.empty((vB, vT, vH, vw["dv"]), dtype=torch.bfloat16, device=dev)
-        vS = torch.empty((vB, vH, vw["dv"], vw["dk"]), dtype=torch.float32, device=dev)
-        nws = qd.qdelta_chunk_fwd_workspace_bytes(vB, vT, vH, vw["dk"], vw["dv"], vw["C"], torch.bfloat16)
-        vws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None   # allocated outside the timing
-        vf = lambda: qd.qdelta_chunk_fwd(vx.q, vx.k, vx.v, vx.alpha, vx.beta, vx.lam, vx.S0, C=vw["C"],
-                                         o=vo, S_T=vS, workspace=vws)
-        for _ in range(max(1, min(args.warmup, vsteps))):
-            vf()
-        torch.cuda.synchronize()
-        v_s, _ = time_region(torch, vf, vsteps)
-        v_ms = v_s / vsteps * 1e3
-        vbytes, vflops = chunk_algorithmic(vB, vT, vH, vw["dk"], vw["dv"], vw["C"], 2)
-        vbytes -= vB * vT * vH * 4 * ((vx.lam is None) + (vx.alpha is None))   # gates not read
-        vbytes += 0 if vx.S0 is None else vB * vH * vw["dv"] * vw["dk"] * 4
-        variants[vname] = {"B": vB, "T": vT, "H": vH, "lambda": "0" if vx.lam is None else "sigmoid draw",
-                           "alpha": "1" if vx.alpha is None else "exp(-softplus) draw",
-                           "S0": None if vx.S0 is None else "N(0, 0.02)", "steps": vsteps,
-                           "ms_per_call": v_ms, "tokens_per_s": vB * vT / (v_ms * 1e-3),
-                           "hbm_frac": vbytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                           "time_ratio_to_headline": v_ms / ms_per_step,
-                           "us_per_chunk_step": v_ms * 1e3 / ((vT + vw["C"] - 1) // vw["C"]),
-                           "schedule": (f"segmented ({nws} B workspace)" if nws else "single pass")}
-        log(f"[bench] {vname}: {v_ms:.4f} ms/call, {vB * vT / (v_ms * 1e-3) / 1e6:.2f} M tokens/s, "
-            f"{v_ms / ms_per_step:.3f} x the headline time")
-        del vx, vo, vS, vws
-    torch.cuda.synchronize()
-    if not args.headline_only:
-        bwd = backward_run(max(5, args.steps // 5))
-        bwd["time_ratio_to_headline"] = bwd["ms_per_call"] / ms_per_step
-        variants["layer_1p3b_backward"] = bwd
-        qed = qed_run(args.steps, 200)
-        qed["chunk_fwd"]["time_ratio_to_headline"] = qed["chunk_fwd"]["ms_per_call"] / ms_per_step
-        variants["qed_gdn2"] = qed
-        eda = eda_run(args.steps, 200)
-        eda["chunk_fwd"]["time_ratio_to_headline"] = eda["chunk_fwd"]["ms_per_call"] / ms_per_step
-        variants["erase_then_delta"] = eda
-        # the headline layer through the fused prologue: unnormalised q, k and gate logits
-        # (qdelta_chunk_fwd_raw), against the headline call on prepared inputs
-        g = torch.Generator(device=dev).manual_seed(args.seed + 3)
-        rq = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
-        rk = torch.randn(B, T, H, dk, generator=g, device=dev).to(torch.bfloat16)
-        ra = torch.randn(B, T, H, generator=g, device=dev) - 4.0
-        rb = torch.randn(B, T, H, generator=g, device=dev)
-        rl = torch.randn(B, T, H, generator=g, device=dev)
-        rf = lambda: qd.qdelta_chunk_fwd(rq, rk, x.v, ra, rb, rl, None, C=C, o=o, S_T=S_T, raw=True)
-        for _ in range(args.warmup):
-            rf()
-        torch.cuda.synchronize()
-        r_s, _ = time_region(torch, rf, args.steps)
-        r_ms = r_s / args.steps * 1e3
-        variants["layer_1p3b_raw_prologue"] = {
-            "B": B, "T": T, "H": H, "inputs": "q, k unnormalised; alpha, beta, lambda as logits",
-            "steps": args.steps, "ms_per_call": r_ms, "tokens_per_s": B * T / (r_ms * 1e-3),
-            "time_ratio_to_headline": r_ms / ms_per_step,
-            "separate_prologue_pass_bytes": 2 * B * T * H * dk * 2 * 2 + 3 * B * T * H * 4 * 2,
-            "separate_prologue_pass_us_at_peak": (2 * B * T * H * dk * 2 * 2 + 3 * B * T * H * 4 * 2)
-                                                 / (PEAK_HBM_GBS * 1e3)}
-        log(f"[bench] layer_1p3b raw prologue: {r_ms:.4f} ms/call, {r_ms / ms_per_step:.3f} x the headline time")
-        del rq, rk, ra, rb, rl
-
-    # ---- decode step: 256 sequences x 16 heads, fp32 state resident, D consecutive steps
-    dw = inputs.WORKLOADS["decode_256x16"]
-    N, Hd, dkd, dvd = dw["N"], dw["H"], dw["dk"], dw["dv"]
-    D = args.decode_steps
-    log(f"[bench] generating decode inputs for {D} steps")
-    dq, dk_, dv_, da, db, dl = inputs.decode_tokens(D, N, Hd, dkd, dvd, dw["dtype"], seed=args.seed + 1,
-                                                    device="cuda")
-    S = inputs.decode_state(N, Hd, dkd, dvd, s0_std=dw["s0_std"], seed=args.seed + 2, device="cuda")
-    od = torch.empty((N, Hd, dvd), dtype=torch.bfloat16, device=dev)
-    lib = qd.load_library()
-    import ctypes
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    ptr = lambda t, i: ctypes.c_void_p(t[i].data_ptr())
-    calls = [(ptr(dq, i), ptr(dk_, i), ptr(dv_, i), ptr(da, i), ptr(db, i), ptr(dl, i)) for i in range(D)]
-    Sp, op = ctypes.c_void_p(S.data_ptr()), ctypes.c_void_p(od.data_ptr())
-
-    def decode_run():
-        for c in calls:
-            rc = lib.qdelta_step(c[0], c[1], c[2], c[3], c[4], c[5], Sp, op, N, Hd, dkd, dvd, 1, stream)
-            if rc:
-                raise RuntimeError(qd.qdelta_status_string(rc))
-
-    decode_run()                                   # warm-up pass over all steps
-    dec_s, dec_wall = time_region(torch, decode_run, 1)
-    us_per_step = dec_s / D * 1e6
-    dec_bytes = step_algorithmic(N, Hd, dkd, dvd, 2)
-    dec_gbs = dec_bytes / (us_per_step * 1e-6) / 1e9
-    log(f"[bench] decode {us_per_step:.2f} us/step, {dec_gbs:.0f} GB/s algorithmic, "
-        f"{N * Hd / (us_per_step * 1e-6) / 1e6:.2f} M token-heads/s")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on the host cores (cpu_baseline)")
-        cpu = cpu_baseline(torch, x)
-        log(f"[bench] oracle {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+    parity = None
+    if ref is not None:
+        o_ref, s_ref = ref
+        rows = o_ref.shape[0]
+        parity = {"o_max_rel_err": max_rel_err(o[:rows].float().cpu().numpy(), o_ref, (1, 3)),
+                  "S_T_max_rel_err": max_rel_err(S_T[:rows].cpu().numpy(), s_ref, (2, 3)),
+                  "bar": 2e-2, "slices": f"{rows * H} of {B * H} (batch, head) slices, whole",
+                  "metric": "max over (batch, head) slices of max|y - y_ref| / max|y_ref|, fp64 oracle"}
+        log(f"[bench] parity vs the fp64 oracle: o {parity['o_max_rel_err']:.2e}, S_T {parity['S_T_max_rel_err']:.2e}")
 
     traffic = counter_traffic("chunk_fwd_layer_1p3b", CHUNK_KERNEL_SOURCES)
-    dec_traffic = counter_traffic("step_decode_256x16", STEP_KERNEL_SOURCES)
+    mfma_counters = counter_mfma("chunk_fwd_layer_1p3b", CHUNK_KERNEL_SOURCES, ms_per_step)
+    decode["roofline"]["traffic"] = counter_traffic("step_decode_256x16", STEP_KERNEL_SOURCES)
     out = {
         "metric": "Q-Delta chunk-fwd tokens/s + MFMA util (B8 T4096 H16 d128); decode HBM GB/s",
         "value": tokens_per_s,
@@ -452,16 +542,12 @@ def main():
                      "kernel": "chunk_fwd_pipe_kernel<128,64,true,true,false>",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
-                 "algorithmic_flops_per_launch": alg_flops},
-        "decode": {"workload": "256 sequences x 16 heads, d_k=d_v=128, fp32 state resident, bf16 q/k/v/o, "
-                               f"{D} consecutive steps",
-                   "us_per_step": us_per_step, "token_heads_per_s": N * Hd / (us_per_step * 1e-6),
-                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": dec_gbs / PEAK_HBM_GBS, "traffic": dec_traffic,
-                                "algorithmic_bytes_per_launch": dec_bytes}},
+                 "algorithmic_flops_per_launch": alg_flops, "counters": mfma_counters},
+        "parity": parity,
+        "decode": decode,
         "other_workloads": variants,
         "cpu_baseline": cpu,
-        "timing": {"chunk_wall_s": wall_s, "decode_wall_s": dec_wall},
+        "timing": {"chunk_wall_s": wall_s},
     }
     print(json.dumps(out), flush=True)
 
