@@ -25,10 +25,11 @@
  * `stream` are device pointers.  The library allocates no device memory and
  * enqueues its kernels asynchronously on `stream` (a hipStream_t; NULL means the
  * default stream); nothing synchronises.  Buffers must stay valid until the work on
- * `stream` completes.  Its only process-wide state is a host-side cache, per device,
- * of the compute-unit count and of the backward gradient kernels' occupancy: each
- * entry is filled once, on the first call on that device, with atomic stores, so
- * calls from several host threads are safe.
+ * `stream` completes.  Process-wide state: a host-side cache, per device, of the
+ * compute-unit count and of the backward gradient kernels' occupancy (each entry filled
+ * once, on the first call on that device, with atomic stores, so calls from several
+ * host threads are safe); and the device scratch array of qdelta_chunk_fwd_noalloc
+ * (see there), the only entry point that uses it.
  *
  * Errors: arguments are checked on the host before anything is enqueued; a
  * failed check returns a status and enqueues nothing.  A launch failure returns
@@ -44,14 +45,15 @@
 extern "C" {
 #endif
 
-#define QDELTA_ABI_VERSION 5
+#define QDELTA_ABI_VERSION 6
 
 typedef enum qd_status {
     QD_OK = 0,
     QD_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, aliasing not allowed */
     QD_ERR_UNSUPPORTED = 2,   /* d_k, d_v, C or dtype outside the supported set            */
     QD_ERR_WORKSPACE = 3,     /* workspace smaller than qdelta_chunk_fwd_workspace_bytes    */
-    QD_ERR_HIP = 4            /* the HIP runtime reported an error at launch                */
+    QD_ERR_HIP = 4,           /* the HIP runtime reported an error at launch                */
+    QD_ERR_SCRATCH_LIMIT = 5  /* qdelta_chunk_fwd_noalloc: sizes need more than its scratch */
 } qd_status;
 
 typedef enum qd_dtype {
@@ -118,6 +120,28 @@ int qdelta_step(const void *q, const void *k, const void *v,
                 const float *alpha, const float *beta, const float *lambda,
                 float *S, void *o, int N, int H, int d_k, int d_v, int dtype,
                 void *stream);
+
+/*
+ * qdelta_chunk_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Arguments, results,
+ * layouts, aliasing rules and status codes are those of qdelta_chunk_fwd, without the
+ * workspace: where the sizes call for the segmented schedule (qdelta_chunk_fwd_workspace_bytes
+ * non-zero), its workspace is a scratch array of QDELTA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends, set up on the first call on that
+ * device.  The call itself allocates nothing.
+ *   - Sizes whose workspace would exceed QDELTA_NOALLOC_SCRATCH_BYTES return
+ *     QD_ERR_SCRATCH_LIMIT and enqueue nothing (B = 1, T = 65536, H = 16, d = 128 needs 25.2 MB).
+ *   - Every call on a GPU uses that GPU's one scratch array: calls that may overlap in time
+ *     on one device (different streams, different host threads without ordering) race and
+ *     give wrong results; calls ordered on one stream are safe.
+ *   - QD_ERR_HIP if the scratch's device address cannot be obtained.
+ */
+#define QDELTA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int qdelta_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, const float *lambda,
+                             const float *S0, void *o, float *S_T,
+                             int B, int T, int H, int d_k, int d_v, int C, int dtype,
+                             void *stream);
 
 /*
  * The same two calls with the layer's prologue fused in (the layer of the Q-Delta

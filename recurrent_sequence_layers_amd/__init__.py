@@ -22,6 +22,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqdelta.so")
 
 QD_F32, QD_BF16 = 0, 1
+# bytes of device scratch qdelta_chunk_fwd_noalloc holds per device (QDELTA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 _lib = None
 
 
@@ -47,6 +49,8 @@ def load_library():
     lib.qdelta_chunk_fwd_workspace_bytes.argtypes = [i] * 7
     lib.qdelta_chunk_fwd.restype = i
     lib.qdelta_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
+    lib.qdelta_chunk_fwd_noalloc.restype = i
+    lib.qdelta_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp]
     lib.qdelta_chunk_fwd_raw.restype = i
     lib.qdelta_chunk_fwd_raw.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
     lib.qdelta_step.restype = i
@@ -168,6 +172,33 @@ def qdelta_chunk_fwd(q, k, v, alpha, beta, lam, S0=None, C: int = 64, o=None, S_
                 _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), code, ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
         _raise(rc, "qdelta_chunk_fwd_raw" if raw else "qdelta_chunk_fwd")
         return o, S_T
+
+
+def qdelta_chunk_fwd_noalloc(q, k, v, alpha, beta, lam, S0, o, S_T, C: int = 64, stream=None):
+    """qdelta_chunk_fwd for callers that cannot allocate: o and S_T (or None) are supplied
+    by the caller and nothing is allocated, here or in the library; the segmented schedule,
+    when the sizes call for it, runs in the library's per-device scratch (calls that overlap
+    in time on one GPU race on it).  Raises when the sizes need more than
+    NOALLOC_SCRATCH_BYTES of it."""
+    import torch
+    lib = load_library()
+    s = _launch_stream(stream, q.device)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt, q.shape); _check(v, "v", dt, (B, T, H, dv))
+    for name, g in (("alpha", alpha), ("beta", beta), ("lam", lam)):
+        _check(g, name, torch.float32, (B, T, H))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if o is None:
+        raise QDeltaError("qdelta_chunk_fwd_noalloc: o must be supplied (nothing is allocated)")
+    _check(o, "o", dt, (B, T, H, dv))
+    _check(S_T, "S_T", torch.float32, (B, H, dv, dk))
+    rc = lib.qdelta_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(lam), _ptr(S0),
+                                      _ptr(o), _ptr(S_T), B, T, H, dk, dv, int(C), _dtype_code(dt),
+                                      ctypes.c_void_p(s.cuda_stream))
+    _raise(rc, "qdelta_chunk_fwd_noalloc")
+    return o, S_T
 
 
 def qdelta_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype) -> int:

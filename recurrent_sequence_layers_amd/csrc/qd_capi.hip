@@ -5,7 +5,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 namespace {
 
@@ -38,6 +40,35 @@ bool disjoint(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs, c
     return true;
 }
 
+// ---- scratch of qdelta_chunk_fwd_noalloc
+// The segmented schedule's workspace (transition maps, offsets and entry states of the
+// segments) for callers that cannot allocate: a file-scope device array that every GPU the
+// library runs on holds until the process ends.  Host code never passes the symbol itself
+// (on the host it is only a stand-in); it uses the device address hipGetSymbolAddress
+// returns for the current device, taken once per device and kept below.  Nothing in it
+// needs to start at zero: the schedule writes every byte it later reads (the identity fill
+// of the maps, the offsets' zero entry states, the propagation).  Calls that overlap in time
+// on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[QDELTA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[qd::kMaxDevices];
+
+// Device address of the current device's scratch array, or null if it cannot be had.
+void *device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= qd::kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,6 +82,8 @@ const char *qdelta_status_string(int status) {
         case QD_ERR_UNSUPPORTED: return "unsupported size or dtype (d_k, d_v in {64,128}; C in {16,32,64}; fp32 or bf16)";
         case QD_ERR_WORKSPACE: return "workspace too small";
         case QD_ERR_HIP: return "HIP runtime error at launch";
+        case QD_ERR_SCRATCH_LIMIT:
+            return "sizes need more than the 32 MiB scratch qdelta_chunk_fwd_noalloc holds per device";
         default: return "unknown status";
     }
 }
@@ -222,12 +255,25 @@ int qdelta_eda_step(const void *q, const void *k, const void *v, const void *e, 
 
 namespace {
 
+// noalloc: the workspace arguments are ignored and the segmented schedule, when the sizes
+// call for it, runs in the library's per-device scratch array instead.
 int chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
               const float *lambda, const float *S0, void *o, float *S_T, int B, int T, int H, int d_k, int d_v,
-              int C, int dtype, void *workspace, size_t ws_bytes, void *stream, bool raw) {
+              int C, int dtype, void *workspace, size_t ws_bytes, void *stream, bool raw, bool noalloc = false) {
     if (B < 0 || T < 0 || H < 0) return QD_ERR_INVALID_ARG;
     if (!qd::chunk_fwd_supported(dtype, d_k, d_v, C)) return QD_ERR_UNSUPPORTED;
     if (raw && (dtype != QD_BF16 || (C != 32 && C != 64))) return QD_ERR_UNSUPPORTED;
+    if (noalloc) {
+        workspace = nullptr;
+        ws_bytes = 0;
+        const size_t need = qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype);
+        if (need > QDELTA_NOALLOC_SCRATCH_BYTES) return QD_ERR_SCRATCH_LIMIT;
+        if (need > 0 && static_cast<long long>(B) * H > 0) {
+            workspace = device_scratch();
+            if (!workspace) return QD_ERR_HIP;
+            ws_bytes = QDELTA_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     if (ws_bytes < qdelta_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, C, dtype)) return QD_ERR_WORKSPACE;
     const long long bh = static_cast<long long>(B) * H;
     if (bh == 0) return QD_OK;
@@ -311,6 +357,13 @@ int qdelta_chunk_fwd_raw(const void *q, const void *k, const void *v, const floa
                          void *stream) {
     return chunk_fwd(q, k, v, alpha_logit, beta_logit, lambda_logit, S0, o, S_T, B, T, H, d_k, d_v, C, dtype,
                      workspace, ws_bytes, stream, true);
+}
+
+int qdelta_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                             const float *lambda, const float *S0, void *o, float *S_T, int B, int T, int H, int d_k,
+                             int d_v, int C, int dtype, void *stream) {
+    return chunk_fwd(q, k, v, alpha, beta, lambda, S0, o, S_T, B, T, H, d_k, d_v, C, dtype, nullptr, 0, stream, false,
+                     true);
 }
 
 int qdelta_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,

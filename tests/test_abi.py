@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qdelta.h")
 
-QD_OK, QD_ERR_INVALID_ARG, QD_ERR_UNSUPPORTED, QD_ERR_WORKSPACE, QD_ERR_HIP = range(5)
+QD_OK, QD_ERR_INVALID_ARG, QD_ERR_UNSUPPORTED, QD_ERR_WORKSPACE, QD_ERR_HIP, QD_ERR_SCRATCH_LIMIT = range(6)
 
 
 def declared_functions():
@@ -41,8 +41,8 @@ def test_version_and_status_strings(lib):
     hdr = open(HEADER).read()
     ver = int(re.search(r"#define QDELTA_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.qdelta_abi_version() == ver
-    for s in range(5):
-        assert lib.qdelta_status_string(s)
+    for s in range(6):
+        assert lib.qdelta_status_string(s) and b"unknown" not in lib.qdelta_status_string(s)
     assert b"unknown" in lib.qdelta_status_string(99)
     assert lib.qdelta_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1) == 0
 
