@@ -31,7 +31,8 @@
 //             S^T update, first half of the keys     of level 2; block doubling, level 1
 //   I3        S^T update, second half                -
 //   I4        stage chunk n + 2 in LDS; gate         block doubling, level 2 (C = 64)
-//             prefix sums; store O
+//             tables (each scan wave writes part
+//             of them); store O
 //
 // LDS layouts (bf16 unless noted):
 //   q, k slots [2][C x d_k] in fragment order (see frag_slot);
@@ -515,16 +516,26 @@ struct PipeKernel {
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
-            if (rw == 0) {                        // gates of the chunk, lane = position
+            // gates of the chunk, lane = position; every scan wave holds them and writes part
+            // of the tables (wave 0: g and beta, 1: exp(g), 2: exp(g_last - g), 3: lambda)
+            {
                 const bool ok = lane < chunk_len(c);
-                const float la = RAW ? log_decay_from_logit(pf.a) : __logf(pf.a);
-                const float x = wave_inclusive_sum((HAS_A && ok) ? la : 0.f);
-                const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
-                if (lane < CH) {
-                    gate(s, 0)[lane] = x;
-                    gate(s, 1)[lane] = __expf(x);
-                    gate(s, 2)[lane] = __expf(glast - x);
-                    gate(s, 3)[lane] = ok ? (RAW ? sigmoid_f(pf.b) : pf.b) : 0.f;
+                if (rw <= 2) {
+                    const float la = RAW ? log_decay_from_logit(pf.a) : __logf(pf.a);
+                    const float x = wave_inclusive_sum((HAS_A && ok) ? la : 0.f);
+                    if (lane < CH) {
+                        if (rw == 0) {
+                            gate(s, 0)[lane] = x;
+                            gate(s, 3)[lane] = ok ? (RAW ? sigmoid_f(pf.b) : pf.b) : 0.f;
+                        } else if (rw == 1) {
+                            gate(s, 1)[lane] = __expf(x);
+                        } else {
+                            const float glast =
+                                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
+                            gate(s, 2)[lane] = __expf(glast - x);
+                        }
+                    }
+                } else if (lane < CH) {
                     gate(s, 4)[lane] = ok ? ((RAW && HAS_L) ? sigmoid_f(pf.l) : pf.l) : 0.f;
                 }
             }

@@ -35,53 +35,55 @@ __global__ __launch_bounds__(256) void identity_fill_kernel(float *M, int dk, si
 // Entry states of the segments and the exit state of the sequence, for rows
 // [R * blockIdx.y, R * blockIdx.y + R) of S for (batch, head) blockIdx.x:
 //   S <- S0 (or 0); for p: S_in[b P + p] = S; S <- S M[b P + p] + G[b P + p];  S_T = S.
-// M is streamed through LDS 32 rows at a time; each thread owns DK / 32 columns of one row.
+// The whole of M[b P + p] sits in LDS for step p while the next segment's map is already
+// on its way into registers, so each step waits on one barrier, not on a global load;
+// each thread owns DK / 32 columns of one row and sums over the rows of M in order.
 template <int DK>
 __global__ __launch_bounds__(256) void segment_propagate_kernel(const float *S0, const float *M, const float *G,
                                                                 float *Sin, float *S_T, int P, int H, int dv) {
-    constexpr int R = 8, CPT = DK / 32;
+    constexpr int R = 8, CPT = DK / 32, NV = DK * DK / 4 / 256;
     __shared__ __attribute__((aligned(16))) float Ss[R][DK];
-    __shared__ __attribute__((aligned(16))) float Ms[32][DK];
+    __shared__ __attribute__((aligned(16))) float Ms[DK][DK];
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     const int r0 = R * blockIdx.y;
     const int t = threadIdx.x, row = t / 32, c0 = (t % 32) * CPT;
-    {
-        const size_t off = ((static_cast<size_t>(bh)) * dv + r0 + row) * DK + c0;
+    const size_t off0 = ((static_cast<size_t>(bh)) * dv + r0 + row) * DK + c0;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) Ss[row][c0 + c] = S0 ? S0[off + c] : 0.f;
-    }
-    __syncthreads();
+    for (int c = 0; c < CPT; ++c) Ss[row][c0 + c] = S0 ? S0[off0 + c] : 0.f;
+    auto seg = [&](int p) { return static_cast<size_t>(b * P + p) * H + h; };
+    f32x4 mv[NV];                                  // the next map, in flight
+    auto load_map = [&](int p) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(M + seg(p) * DK * DK);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) mv[j] = src[t + 256 * j];
+    };
+    load_map(0);
     for (int p = 0; p < P; ++p) {
-        const size_t seg = static_cast<size_t>(b * P + p) * H + h;
-        const size_t off = (seg * dv + r0 + row) * DK + c0;
+        const size_t off = (seg(p) * dv + r0 + row) * DK + c0;
         float acc[CPT];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            Sin[off + c] = Ss[row][c0 + c];
-            acc[c] = G[off + c];
-        }
-        const float *Mp = M + seg * DK * DK;
-        for (int js = 0; js < DK / 32; ++js) {
-            __syncthreads();                           // previous slice consumed
-            for (int i = t; i < 32 * DK / 4; i += 256)
-                reinterpret_cast<f32x4 *>(&Ms[0][0])[i] = reinterpret_cast<const f32x4 *>(Mp + 32 * js * DK)[i];
-            __syncthreads();
-#pragma unroll 8
-            for (int i = 0; i < 32; ++i) {
-                const float s = Ss[row][32 * js + i];
+        for (int c = 0; c < CPT; ++c) acc[c] = G[off + c];
+        __syncthreads();                           // S of this step written; the previous map consumed
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[c] += s * Ms[i][c0 + c];
-            }
+        for (int j = 0; j < NV; ++j) reinterpret_cast<f32x4 *>(&Ms[0][0])[t + 256 * j] = mv[j];
+        if (p + 1 < P) load_map(p + 1);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Sin[off + c] = Ss[row][c0 + c];
+        __syncthreads();
+#pragma unroll 8
+        for (int i = 0; i < DK; ++i) {
+            const float sv = Ss[row][i];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] += sv * Ms[i][c0 + c];
         }
-        __syncthreads();                               // every thread has read Ss
+        __syncthreads();                           // every thread has read S
 #pragma unroll
         for (int c = 0; c < CPT; ++c) Ss[row][c0 + c] = acc[c];
-        __syncthreads();
     }
+    __syncthreads();
     if (S_T) {
-        const size_t off = ((static_cast<size_t>(bh)) * dv + r0 + row) * DK + c0;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) S_T[off + c] = Ss[row][c0 + c];
+        for (int c = 0; c < CPT; ++c) S_T[off0 + c] = Ss[row][c0 + c];
     }
 }
 
