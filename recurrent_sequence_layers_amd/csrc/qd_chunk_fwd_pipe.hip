@@ -20,19 +20,27 @@
 //   prep waves 4-7  state-independent work of chunk c = n + 1 (Gram blocks, L_g, A,
 //                   the UT-transform solve, M1).
 //
-// Every SIMD hosts one wave of each role.  A pipeline step has four intervals
-// separated by workgroup barriers that both roles execute:
+// Every SIMD hosts one wave of each role.  Each role runs its own loop over the chunks,
+// with the same four workgroup barriers per step, so that each role's registers are
+// allocated for its own code alone.  A step has four intervals:
 //
 //   interval  scan (chunk n)                         prep (chunk c = n + 1)
-//   I1        Y, Z, O (O staged in LDS)              Gram blocks on MFMA; A and L_g written;
-//                                                    each wave inverts its diagonal 16x16
-//                                                    block of T_g in registers
-//   I2        fetch chunk n + 2 (registers);         M1 of the diagonal blocks; Gram blocks
-//             S^T update, first half of the keys     of level 2; block doubling, level 1
-//   I3        S^T update, second half                -
-//   I4        stage chunk n + 2 in LDS; gate         block doubling, level 2 (C = 64)
-//             tables (each scan wave writes part
-//             of them); store O
+//   I1        fetch q, v of chunk n + 2; Y from the  the wave's diagonal Gram block on MFMA,
+//             S^T products formed a step ahead;      A and L_g written, its 16x16 block of
+//             Z, O (O staged in LDS)                 T_g inverted in registers
+//   I2        stage q, v of chunk n + 2 (chunk n's   M1 of the diagonal blocks; the six
+//             V was last read in I1, its Q a step    off-diagonal Gram blocks
+//             earlier); fetch k of chunk n + 2;
+//             S^T update over the first half of
+//             the keys, then K S^T and Q S^T of
+//             chunk n + 1 over those keys
+//   I3        the same over the second half          block doubling, level 1 (waves 6, 7)
+//   I4        stage k and the gate tables of chunk   block doubling, level 2 (C = 64)
+//             n + 2 (each scan wave writes part of
+//             the tables); store O
+//
+// Forming K S^T and Q S^T of chunk n + 1 as each key pair of its entry state becomes
+// final takes that contraction off the path from one chunk's Z to the next chunk's Z.
 //
 // LDS layouts (bf16 unless noted):
 //   q, k slots [2][C x d_k] in fragment order (see frag_slot);
@@ -229,14 +237,16 @@ struct PipeLayout {
 // are formed in I2.
 template <int NCT, int P, int PH>
 struct GramPlan { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<4, 0, 1> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 0, 1> { static constexpr int n = 1; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
 template <> struct GramPlan<4, 1, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
-template <> struct GramPlan<4, 2, 1> { static constexpr int n = 2; static constexpr int i[4] = {2, 3, 0, 0}, j[4] = {2, 2, 0, 0}; };
+template <> struct GramPlan<4, 2, 1> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {2, 0, 0, 0}; };
 template <> struct GramPlan<4, 3, 1> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {3, 0, 0, 0}; };
-template <> struct GramPlan<4, 0, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<4, 1, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
-template <> struct GramPlan<4, 2, 2> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
-template <> struct GramPlan<4, 3, 2> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<4, 0, 2> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 1, 2> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {2, 0, 0, 0}; };
+template <> struct GramPlan<4, 2, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 3, 2> { static constexpr int n = 1; static constexpr int i[4] = {2, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
+template <> struct GramPlan<4, 0, 3> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlan<4, 1, 3> { static constexpr int n = 1; static constexpr int i[4] = {3, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
 template <> struct GramPlan<2, 0, 1> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
 template <> struct GramPlan<2, 1, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
 
@@ -471,25 +481,34 @@ struct PipeKernel {
         const int voffG = (rt & (kWave - 1)) * rowG;
         const int ldsV = vv_row * PV + vv_col * 8;        // + j * RJV * PV
 
-        // registers of one prefetched chunk; declared per pipeline step so that they are
-        // not carried around the loop (and so not live in the prep role's code)
-        struct Prefetch {
-            u32x4 q[NVQ], k[NVQ], v[NVV];
+        // Staging of a chunk c into LDS slot c & 1, in two parts with their own registers.
+        // q and v: loaded in I1 and written in I2 (the scan reads chunk n's V only in I1 and
+        // its Q not at all: its Q S^T is formed a step ahead); k and the gates: loaded in I2
+        // and written in I4, once the state update has read chunk n's K and the gate tables.
+        struct PrefQV {
+            u32x4 q[NVQ], v[NVV];
+        };
+        struct PrefK {
+            u32x4 k[NVQ];
             float a, b, l;
         };
-        auto gload = [&](int c, Prefetch &pf) {
+        auto gload_qv = [&](int c, PrefQV &pf) {
             const int clen = chunk_tok(c);
             const size_t t0 = static_cast<size_t>(c) * TPC * H;
             const auto rsq = buffer_rsrc(qbase + t0 * DK, (clen - 1) * rowQ + DK * 2);
-            const auto rsk = buffer_rsrc(krows + t0 * DK, (clen - 1) * rowQ + DK * 2);
             const auto rsv = buffer_rsrc(vbase + (has_v ? t0 * dv : 0), has_v ? (clen - 1) * rowV + kDVT * 2 : 0);
 #pragma unroll
-            for (int j = 0; j < NVQ; ++j) {
+            for (int j = 0; j < NVQ; ++j)
                 if (!erase_rows) pf.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voffQ[j], 0, 0);
-                pf.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, voffQ[j], 0, 0);
-            }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) pf.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voffV[j], 0, 0);
+        };
+        auto gload_k = [&](int c, PrefK &pf) {
+            const int clen = chunk_tok(c);
+            const size_t t0 = static_cast<size_t>(c) * TPC * H;
+            const auto rsk = buffer_rsrc(krows + t0 * DK, (clen - 1) * rowQ + DK * 2);
+#pragma unroll
+            for (int j = 0; j < NVQ; ++j) pf.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, voffQ[j], 0, 0);
             const int gbytes = (clen - 1) * rowG + 4;
             pf.a = 1.f;
             pf.l = 0.f;
@@ -501,21 +520,31 @@ struct PipeKernel {
             if constexpr (HAS_L)
                 pf.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(args.lam + tok0 + t0, gbytes), voffG, 0, 0));
         };
-        auto rstore = [&](int c, const Prefetch &pf) {   // stage chunk c into LDS slot c & 1
+        auto rstore_qv = [&](int c, const PrefQV &pf) {
             const int s = c & 1;
-            uint16_t *Qs = Qb(s), *Ks = Kb(s), *Vs = Vb(s);
+            uint16_t *Qs = Qb(s), *Vs = Vb(s);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
                 if constexpr (RAW) {
                     *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = normalise_row_segment<NKP>(pf.q[j]);
-                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = normalise_row_segment<NKP>(pf.k[j]);
                 } else {
                     if (!erase_rows) *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
-                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
                 }
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
+        };
+        auto rstore_k = [&](int c, const PrefK &pf) {
+            const int s = c & 1;
+            uint16_t *Ks = Kb(s);
+#pragma unroll
+            for (int j = 0; j < NVQ; ++j) {
+                if constexpr (RAW) {
+                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = normalise_row_segment<NKP>(pf.k[j]);
+                } else {
+                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
+                }
+            }
             // gates of the chunk, lane = position; every scan wave holds them and writes part
             // of the tables (wave 0: g and beta, 1: exp(g), 2: exp(g_last - g), 3: lambda)
             {
@@ -559,28 +588,93 @@ struct PipeKernel {
         }
 
         if (is_scan) {
-            Prefetch pf;
-            gload(0, pf);
-            rstore(0, pf);
+            PrefQV pq0;
+            PrefK pk0;
+            gload_qv(0, pq0);
+            gload_k(0, pk0);
+            rstore_qv(0, pq0);
+            rstore_k(0, pk0);
         }
         __syncthreads();
 
-        for (int n = -1; n < NC; ++n) {
-            const int c = n + 1;                  // the prep role's chunk
-            const int ss = n & 1;                 // scan slot (n >= 0)
-            const int ps = c & 1;                 // prep slot
-            // lane-dependent LDS addresses are rebuilt from an opaque copy of the thread id at
-            // every step rather than hoisted out of the loop: held across the loop they would
-            // not fit the register file next to the state
-            int lid_ = threadIdx.x;
-            asm volatile("" : "+v"(lid_));
-            const int lane = lid_ & (kWave - 1), r16 = lane & 15, g4 = lane >> 4, tri = r16 >> 2, trp = r16 & 3;
-            Prefetch pf;                          // scan: chunk n + 2, loaded in I1, staged in I4
-            bf16x4 Zd[NCT];                       // scan: exp(g_last - g) Z, from I1 to I2/I3
-            f32x4 tdiag;                          // prep: the wave's diagonal block of T_g, I1 to I2
+        // The two roles run separate loops with the same four barriers per step, so each
+        // role's registers are allocated for its own code: the scan's state and look-ahead
+        // products are not live through the prep's code, nor the prep's through the scan's.
+        if (is_scan) {
+            // K S^T and Q S^T of the chunk the next step's I1 processes, formed in I2 and I3
+            // as the key tiles of that chunk's entry state become final
+            f32x4 PK_[NCT], PQ[NCT];
+            for (int n = -1; n < NC; ++n) {
+                const int c = n + 1;              // the chunk whose S^T products are formed ahead
+                const int ss = n & 1;             // slot of chunk n
+                const int ps = c & 1;             // slot of chunk c
+                const int tri = r16 >> 2, trp = r16 & 3;
+                PrefQV pfqv;                      // q, v of chunk n + 2, loaded in I1, staged in I2
+                PrefK pfk;                        // k and gates of chunk n + 2, loaded in I2, staged in I4
+                bf16x4 Zd[NCT];                   // exp(g_last - g) Z, from I1 to I2/I3
 
-            // ============================================================ I1
-            if (is_scan) {
+                // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z for key tiles [t_lo, t_hi).
+                // Output row m of tile 2u + hh is key 8 kq(m/4, u) + 4hh + m%4, read from K with
+                // the transpose read: lane (g, 4i + p) reads keys 8 kq(p, u) + 4hh.. of position
+                // 32s + 4g + i (and + 16), matching the pairing of Zd[2s], Zd[2s + 1].
+                auto state_update = [&](int t_lo, int t_hi) {
+                    const uint16_t *Ks = Kb(ss);
+                    const float dlast = HAS_A ? gate(ss, 1)[CH - 1] : 1.f;
+                    bf16x8 zp[NCP];
+    #pragma unroll
+                    for (int s = 0; s < NCP; ++s) zp[s] = cat8(Zd[2 * s], Zd[2 * s + 1]);
+                    bf16x8 kf[2][NCP];
+                    auto load = [&](int t, bf16x8(&dst)[NCP]) {
+                        // keys 8 kq(trp, t / 2) + 4 (t & 1) .. + 3 of positions 32 s + 4 g4 + tri
+                        // and 16 later: slot (trp, 4 g4 + tri) of blocks (2 s, t / 2), (2 s + 1, t / 2)
+    #pragma unroll
+                        for (int s = 0; s < NCP; ++s) {
+                            const uint16_t *p = Ks + qk_off(2 * s, t >> 1, trp, 4 * g4 + tri) + 4 * (t & 1);
+                            dst[s] = cat8(lds_tr(p), lds_tr(p + NKP * 512));
+                        }
+                    };
+                    load(t_lo, kf[0]);
+    #pragma unroll
+                    for (int t = 0; t < NKT; ++t) {
+                        if (t < t_lo || t >= t_hi) continue;
+                        if (t + 1 < t_hi) load(t + 1, kf[(t + 1 - t_lo) & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        f32x4 acc = sT[t] * dlast;
+    #pragma unroll
+                        for (int s = 0; s < NCP; ++s) acc = mfma32(kf[(t - t_lo) & 1][s], zp[s], acc);
+                        sT[t] = acc;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+
+                // K S^T and Q S^T of chunk c (slot ps) over the key pairs [u_lo, u_hi), from the
+                // state tiles the update has just made final (its entry state); the contraction
+                // runs over the pairs in order, so the sums are those of one pass over the keys
+                auto lookahead = [&](int u_lo, int u_hi) {
+                    const uint16_t *Qn = Qb(ps), *Kn = Kb(ps);
+    #pragma unroll
+                    for (int u = 0; u < NKP; ++u) {
+                        if (u < u_lo || u >= u_hi) continue;
+                        const bf16x8 sf = cat8(Bf16::cvt(sT[2 * u]), Bf16::cvt(sT[2 * u + 1]));
+                        bf16x8 fk[NCT], fq[NCT];
+    #pragma unroll
+                        for (int mt = 0; mt < NCT; ++mt) {
+                            const int off = qk_off(mt, u, g4, r16);
+                            fk[mt] = lds8(Kn + off);
+                            if (!STATES || HAS_L) fq[mt] = lds8(Qn + off);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                        for (int mt = 0; mt < NCT; ++mt) {
+                            PK_[mt] = mfma32(fk[mt], sf, PK_[mt]);
+                            if (!STATES || HAS_L) PQ[mt] = mfma32(fq[mt], sf, PQ[mt]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+
+                // ======================================================== I1
+                if (n + 2 < NC) gload_qv(n + 2, pfqv);   // slot n & 1: its Q is no longer read
                 if (n >= 0) {
                     if (STATES && args.Hs) {   // chunk n's entry state, rounded to bf16
                         uint16_t *hs = static_cast<uint16_t *>(args.Hs) +
@@ -589,57 +683,21 @@ struct PipeKernel {
                         for (int t = 0; t < NKT; ++t)
                             *reinterpret_cast<bf16x4 *>(hs + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = Bf16::cvt(sT[t]);
                     }
-                    // Software-pipelined by hand: the fragments of the next tile are issued
-                    // before the MFMAs of the current one, and scheduling fences keep the
-                    // compiler from sinking each LDS read next to its use.
-                    const uint16_t *Qs = Qb(ss), *Ks = Kb(ss), *Vs = Vb(ss), *As = Ab(ss);
+                    const uint16_t *Vs = Vb(ss), *As = Ab(ss);
                     const float *lam_s = gate(ss, 4), *eg = gate(ss, 1), *egl = gate(ss, 2);
-                    bf16x8 fk[2][NKP], fq[2][NKP];
-                    auto load_qk = [&](int mt, bf16x8(&k)[NKP], bf16x8(&q)[NKP]) {
-#pragma unroll
-                        for (int u = 0; u < NKP; ++u) {
-                            const int off = qk_off(mt, u, g4, r16);
-                            k[u] = lds8(Ks + off);
-                            q[u] = lds8(Qs + off);
-                        }
-                    };
-                    load_qk(0, fk[0], fq[0]);
-                    bf16x8 sTf[NKP];
-#pragma unroll
-                    for (int u = 0; u < NKP; ++u) sTf[u] = cat8(Bf16::cvt(sT[2 * u]), Bf16::cvt(sT[2 * u + 1]));
+                    // operands of Z: V as the paired B operand (positions 32u + 4g + i and
+                    // 32u + 16 + 4g + i) and the M1 fragments
                     bf16x8 Vf[NCP], m1f[NCT][NCP];
-                    f32x4 PK_[NCT], PQ[NCT];
-                    __builtin_amdgcn_sched_barrier(0);
-                    // K S^T and Q S^T
 #pragma unroll
-                    for (int mt = 0; mt < NCT; ++mt) {
-                        if (mt + 1 < NCT) {
-                            load_qk(mt + 1, fk[(mt + 1) & 1], fq[(mt + 1) & 1]);
-                        } else {
-                            // operands of Z: V as the paired B operand (positions 32u + 4g + i
-                            // and 32u + 16 + 4g + i) and the M1 fragments
-#pragma unroll
-                            for (int u = 0; u < NCP; ++u) {
-                                const uint16_t *p = Vs + (32 * u + 4 * g4 + tri) * PV + 16 * rw + 4 * trp;
-                                Vf[u] = cat8(lds_tr(p), lds_tr(p + 16 * PV));
-                            }
-#pragma unroll
-                            for (int m = 0; m < NCT; ++m)
-#pragma unroll
-                                for (int u = 0; u <= (m >> 1); ++u)
-                                    m1f[m][u] = lds8(M1s + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        f32x4 pk = zero4(), pq = zero4();
-#pragma unroll
-                        for (int u = 0; u < NKP; ++u) {
-                            pk = mfma32(fk[mt & 1][u], sTf[u], pk);
-                            pq = mfma32(fq[mt & 1][u], sTf[u], pq);
-                        }
-                        PK_[mt] = pk;
-                        PQ[mt] = pq;
-                        __builtin_amdgcn_sched_barrier(0);
+                    for (int u = 0; u < NCP; ++u) {
+                        const uint16_t *p = Vs + (32 * u + 4 * g4 + tri) * PV + 16 * rw + 4 * trp;
+                        Vf[u] = cat8(lds_tr(p), lds_tr(p + 16 * PV));
                     }
+#pragma unroll
+                    for (int m = 0; m < NCT; ++m)
+#pragma unroll
+                        for (int u = 0; u <= (m >> 1); ++u)
+                            m1f[m][u] = lds8(M1s + (m * NCP + u) * 512 + 8 * frag_slot(g4, r16));
                     // Yg = -D_g (K S^T + diag(lambda) Q S^T); the A fragments of O are issued here
                     bf16x8 af[NCT][NCP];
                     if constexpr (!STATES) {
@@ -688,7 +746,49 @@ struct PipeKernel {
                         }
                     }
                 }
-            } else if (c < NC) {
+                __syncthreads();
+
+                // ======================================================== I2
+                if (n + 2 < NC) rstore_qv(n + 2, pfqv);  // V of chunk n was read in I1
+                if (n + 2 < NC) gload_k(n + 2, pfk);
+                if (n >= 0) state_update(0, NKT / 2);
+                if (c < NC) {
+#pragma unroll
+                    for (int mt = 0; mt < NCT; ++mt) PK_[mt] = PQ[mt] = zero4();
+                    lookahead(0, NKP / 2);
+                }
+                __syncthreads();
+
+                // ======================================================== I3
+                if (n >= 0) state_update(NKT / 2, NKT);
+                if (c < NC) lookahead(NKP / 2, NKP);
+                __syncthreads();
+
+                // ======================================================== I4
+                if (n + 2 < NC) rstore_k(n + 2, pfk);    // K and gates of chunk n were read up to I3
+                if (!STATES && n >= 0) {
+                    const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * TPC * H * dv : 0),
+                                                 has_o ? (chunk_tok(n) - 1) * rowV + kDVT * 2 : 0);
+#pragma unroll
+                    for (int j = 0; j < NVV; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),
+                                                               rso, voffV[j], 0, 0);
+                }
+                __syncthreads();
+            }
+            if (args.S_T) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+                    *reinterpret_cast<f32x4 *>(args.S_T + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = sT[t];
+            }
+        } else {
+            for (int n = -1; n < NC; ++n) {
+                const int c = n + 1;              // the prep role's chunk
+                const int ps = c & 1;             // its slot
+                const int tri = r16 >> 2, trp = r16 & 3;
+                f32x4 tdiag;                      // the wave's diagonal block of T_g, I1 to I2
+                // ======================================================== I1
+                if (c < NC) {
                 const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
                 uint16_t *As = Ab(ps);
                 const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
@@ -698,48 +798,10 @@ struct PipeKernel {
                     case 2: gram<2, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
                     default: gram<3, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
                 }
-            }
-            __syncthreads();
-
-            // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) Z for key tiles [t_lo, t_hi).
-            // Output row m of tile 2u + hh is key 8 kq(m/4, u) + 4hh + m%4, read from K with
-            // the transpose read: lane (g, 4i + p) reads keys 8 kq(p, u) + 4hh.. of position
-            // 32s + 4g + i (and + 16), matching the pairing of Zd[2s], Zd[2s + 1].
-            auto state_update = [&](int t_lo, int t_hi) {
-                const uint16_t *Ks = Kb(ss);
-                const float dlast = HAS_A ? gate(ss, 1)[CH - 1] : 1.f;
-                bf16x8 zp[NCP];
-#pragma unroll
-                for (int s = 0; s < NCP; ++s) zp[s] = cat8(Zd[2 * s], Zd[2 * s + 1]);
-                bf16x8 kf[2][NCP];
-                auto load = [&](int t, bf16x8(&dst)[NCP]) {
-                    // keys 8 kq(trp, t / 2) + 4 (t & 1) .. + 3 of positions 32 s + 4 g4 + tri
-                    // and 16 later: slot (trp, 4 g4 + tri) of blocks (2 s, t / 2), (2 s + 1, t / 2)
-#pragma unroll
-                    for (int s = 0; s < NCP; ++s) {
-                        const uint16_t *p = Ks + qk_off(2 * s, t >> 1, trp, 4 * g4 + tri) + 4 * (t & 1);
-                        dst[s] = cat8(lds_tr(p), lds_tr(p + NKP * 512));
-                    }
-                };
-                load(t_lo, kf[0]);
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) {
-                    if (t < t_lo || t >= t_hi) continue;
-                    if (t + 1 < t_hi) load(t + 1, kf[(t + 1 - t_lo) & 1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    f32x4 acc = sT[t] * dlast;
-#pragma unroll
-                    for (int s = 0; s < NCP; ++s) acc = mfma32(kf[(t - t_lo) & 1][s], zp[s], acc);
-                    sT[t] = acc;
-                    __builtin_amdgcn_sched_barrier(0);
                 }
-            };
-
-            // ============================================================ I2
-            if (is_scan) {
-                if (n + 2 < NC) gload(n + 2, pf); // staged in I4, after this slot is released
-                if (n >= 0) state_update(0, NKT / 2);
-            } else if (c < NC) {
+                __syncthreads();
+                // ======================================================== I2
+                if (c < NC) {
                 if (rw < NCT) {                   // M1 of this wave's diagonal block
                     const int o = 16 * rw;
                     const float bc = gate(ps, 3)[o + r16];
@@ -757,9 +819,19 @@ struct PipeKernel {
                         default: gram<3, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
                     }
                 }
-                if (rw < NCT / 2) {
-                    // T_g[2a+1][2a] = -T_g[2a+1][2a+1] L_g[2a+1][2a] T_g[2a][2a]
-                    const int aa = 2 * rw, bb = 2 * rw + 1;
+                }
+                __syncthreads();
+                // ======================================================== I3
+                if (c < NC && rw < 2) {
+                    const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
+                    uint16_t *As = Ab(ps);
+                    const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
+                    if (rw == 0) gram<0, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag);
+                    else gram<1, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag);
+                }
+                if (c < NC && rw >= 2 && rw - 2 < NCT / 2) {
+                    // block doubling, level 1: T_g[2a+1][2a] = -T_g[2a+1][2a+1] L_g[2a+1][2a] T_g[2a][2a]
+                    const int aa = 2 * (rw - 2), bb = aa + 1;
                     const f32x4 x = mfma16(lds4(Lgs + (16 * bb + r16) * PC + 16 * aa + 4 * g4),
                                            lds4(Tds + (16 * aa + r16) * PC + 16 * aa + 4 * g4), zero4());
                     const f32x4 y = mfma16(lds_tr(Tds + (16 * bb + 4 * g4 + tri) * PC + 16 * bb + 4 * trp), Bf16::cvt(x),
@@ -769,45 +841,20 @@ struct PipeKernel {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) M1s[cc_off<CH>(16 * bb + 4 * g4 + e, 16 * aa + r16)] = Bf16::from_f32(-y[e] * bc);
                 }
-            }
-            __syncthreads();
-
-            // ============================================================ I3
-            if (is_scan) {
-                if (n >= 0) state_update(NKT / 2, NKT);
-            }
-            __syncthreads();
-
-            // ============================================================ I4
-            if (is_scan) {
-                // stage chunk n + 2 first: its wait for the prefetch would otherwise also wait
-                // for the output stores
-                if (n + 2 < NC) rstore(n + 2, pf); // into slot n & 1, released in I3
-                if (!STATES && n >= 0) {
-                    const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * TPC * H * dv : 0),
-                                                 has_o ? (chunk_tok(n) - 1) * rowV + kDVT * 2 : 0);
-#pragma unroll
-                    for (int j = 0; j < NVV; ++j)
-                        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(Os + ldsV + j * RJV * PV),
-                                                               rso, voffV[j], 0, 0);
-                }
-            } else if constexpr (NCT == 4) {
-                if (c < NC) {
+                __syncthreads();
+                // ======================================================== I4
+                if constexpr (NCT == 4) {
+                    if (c < NC) {
                     switch (rw) {
                         case 0: level2<2, 0>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
                         case 1: level2<2, 1>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
                         case 2: level2<3, 0>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
                         default: level2<3, 1>(Lgs, Tds, M1s, gate(ps, 3), lane); break;
                     }
+                    }
                 }
+                __syncthreads();
             }
-            __syncthreads();
-        }
-
-        if (is_scan && args.S_T) {
-#pragma unroll
-            for (int t = 0; t < NKT; ++t)
-                *reinterpret_cast<f32x4 *>(args.S_T + srow + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = sT[t];
         }
     }
 };
