@@ -37,10 +37,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    src = os.path.join(os.path.dirname(LIB), "qdelta_oracle.c")
-    if (not os.path.exists(LIB)) or os.path.getmtime(LIB) < os.path.getmtime(src):
-        build()
-    lib = ctypes.CDLL(LIB)
+    override = os.environ.get("ORACLE_LIB")      # a separately built copy (the sanitizer test)
+    if override:
+        lib = ctypes.CDLL(override)
+    else:
+        src = os.path.join(os.path.dirname(LIB), "qdelta_oracle.c")
+        if (not os.path.exists(LIB)) or os.path.getmtime(LIB) < os.path.getmtime(src):
+            build()
+        lib = ctypes.CDLL(LIB)
     lib.oracle_qdelta_fwd.restype = ctypes.c_int
     lib.oracle_qdelta_fwd.argtypes = [_dp] * 9 + [ctypes.c_int] * 6
     lib.oracle_qdelta_step.restype = ctypes.c_int

@@ -24,6 +24,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out: str, verbose: bool = False, src: str = SRC) -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer, every report
+    fatal, for the sanitizer test (loaded through ORACLE_LIB with the runtimes preloaded)."""
+    cc = os.environ.get("ORACLE_CC", "gcc")
+    cmd = [cc, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", out, src, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     sys.exit(0)
