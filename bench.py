@@ -13,6 +13,7 @@ Order of a full run:
      launch latency), lambda = 0 (Gated DeltaNet), lambda = 0 and alpha = 1 (DeltaNet),
      the decode step on 256 sequences x 16 heads (268 MB state) and on 1024 x 16
      (1.07 GB, four times the 256 MB Infinity Cache, so that its rate is DRAM bandwidth),
+     a plain 2 GiB device copy and fill (`hbm_practical`, context for the HBM fractions),
      the long-context layer (B1 T65536 H16, S0 given, segmented schedule), the layer
      backward, the QED / GDN-2 and Erase-then-Delta variants, the fused prologue;
   3. the headline: W untimed warm-up calls, then exactly K timed calls.
@@ -442,6 +443,26 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": dbytes}}
 
+    def hbm_practical():
+        """What plain device-memory traffic reaches in the same run, as context for the HBM
+        fractions: a 2 GiB device-to-device copy (the runtime's own copy kernel; read plus
+        write) and a 2 GiB fill (write only), beyond the 256 MB Infinity Cache."""
+        n = 2 ** 29                                  # fp32 elements: 2 GiB
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        c_s, _ = time_region(torch, lambda: b.copy_(a), 10)
+        f_s, _ = time_region(torch, lambda: b.fill_(2.0), 10)
+        del a, b
+        torch.cuda.synchronize()
+        copy_gbs, fill_gbs = 2 * 4 * n * 10 / c_s / 1e9, 4 * n * 10 / f_s / 1e9
+        log(f"[bench] device copy 2 GiB: {copy_gbs:.0f} GB/s (read + write); fill: {fill_gbs:.0f} GB/s")
+        return {"device_copy_2gib_gbs": copy_gbs, "fill_2gib_gbs": fill_gbs,
+                "note": "plain device copy (read + write) and fill (write) of 2 GiB in the same run, "
+                        "for the HBM fractions' context; the fractions themselves use the 8 TB/s peak"}
+
     # ---------------------------------------------------------------- profiled single modes
     if args.eda_only:
         print(json.dumps({"eda": eda_run(args.steps, 200)}), flush=True)
@@ -482,8 +503,10 @@ def main():
     # the decode runs stream the whole HBM for tens of milliseconds; chunk-kernel work follows
     # them before the headline, so its clocks are those of the chunk kernels' own load
     decode = decode_run(256, args.decode_steps, args.seed + 1)
+    practical = None
     if not args.headline_only:
         variants["decode_1024x16_beyond_infinity_cache"] = decode_run(1024, 200, args.seed + 11)
+        practical = hbm_practical()
         variants["long_64k_bf16"] = chunk_variant("long_64k_bf16", 10, 3)
         variants["layer_1p3b_backward"] = backward_run(x, max(5, args.steps // 5))
         variants["qed_gdn2"] = qed_run(args.steps, 200)
@@ -549,6 +572,7 @@ def main():
                  "algorithmic_flops_per_launch": alg_flops, "counters": mfma_counters},
         "parity": parity,
         "decode": decode,
+        "hbm_practical": practical,
         "other_workloads": variants,
         "cpu_baseline": cpu,
         "timing": {"chunk_wall_s": wall_s},
