@@ -62,15 +62,100 @@ constexpr int kDVT = 64;  // value columns per tile
 //                   triangular inverse, M1).
 // A pipeline step has five intervals separated by workgroup barriers that both roles
 // execute:
-//   interval  scan (chunk n)                         prep (chunk c = n - 1)
-//   I1        prefetch chunk n - 2 (registers);      Gram blocks: L, A
-//             dZ, dR
-//   I2        dS^T update                            diagonal blocks of T
-//   I3        dV staged in LDS                       T, level 1
+//   interval  scan (chunk n)                         prep (chunk c = n - 1), C = 64
+//   I1        prefetch chunk n - 2 (registers);      Gram blocks (L, A): each wave its
+//             dZ, dR                                 diagonal block and one of (1,0), (3,2),
+//                                                    (2,0), (2,1)
+//   I2        dS^T update                            wave 4: the four diagonal blocks of T;
+//                                                    waves 6, 7: Gram blocks (3,0), (3,1)
+//   I3        dV staged in LDS                       T, level 1 (waves 4, 5); M1 of the
+//                                                    diagonal blocks (waves 6, 7)
 //   I4        stage chunk n - 2                      T, level 2
-//   I5        dV stores; store dS' of chunk n - 1    M1 = T_g diag(beta)
-// q, k, dO, A and the gates are double-buffered by chunk parity; M1 is read by the scan in
-// I1 and rewritten by the prep in I5; L and T belong to the prep.
+//   I5        dV stores; store dS' of chunk n - 1    M1 = T_g diag(beta) below the diagonal
+// At C = 16 and 32 the prep forms every Gram block in I1, the diagonal blocks of T in I2
+// and all of M1 in I5.  q, k, dO, A and the gates are double-buffered by chunk parity; M1
+// is read by the scan in I1 and rewritten by the prep in I3 and I5; L and T belong to the
+// prep.
+// One Gram block pair (i, j), j <= i, of gram_blocks: L, A (and N when non-null) for block
+// (i, j).  The reverse scan's prep role schedules the pairs itself.
+template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int PCA = PC>
+__device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
+                                          const float *bes, const float *lams, typename P::R *Ls, typename P::R *As,
+                                          int i, int j, int lane) {
+    using F = typename P::F;
+    constexpr int NKT = DK / 16;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    f32x4 gq_ = zero4(), gk_ = zero4();
+#pragma unroll
+    for (int s = 0; s < NKT; s += 2) {
+        F a0, a1, q0, q1, k0, k1;
+        frag_oct<P>(Ks, PK, 16 * j, 16 * s, a0, a1, lane);
+        frag_oct<P>(Qs, PK, 16 * i, 16 * s, q0, q1, lane);
+        frag_oct<P>(Ks, PK, 16 * i, 16 * s, k0, k1, lane);
+        gq_ = P::mma2(gq_, a0, a1, q0, q1);
+        gk_ = P::mma2(gk_, a0, a1, k0, k1);
+    }
+    const int r = 16 * i + r16;
+    const int c0 = 16 * j + 4 * g4;
+    const float lr = lams[r], br = bes[r], gr = gs[r];
+    const f32x4 gc = lds_f32x4(gs + c0);
+    f32x4 lv, av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = c0 + e;
+        const float xk = HAS_L ? gk_[e] + lr * gq_[e] : gk_[e];
+        const float dec = HAS_A ? __expf(gr - gc[e]) : 1.f;
+        lv[e] = (c < r) ? br * xk : 0.f;
+        av[e] = (c <= r) ? dec * gq_[e] : 0.f;
+    }
+    P::st4(Ls + r * PC + c0, lv);
+    P::st4(As + r * PCA + c0, av);
+}
+
+// The four 16 x 16 diagonal blocks of T = (I + L)^-1 (C = 64) on one wave: lane group g
+// inverts block g by forward substitution over rows, lane l computing column l % 16.  The
+// next row of L is read while the current one is substituted, and each row's sum runs as
+// two interleaved partial sums.
+template <class P, int PC>
+__device__ __forceinline__ void inverse_diag4(const typename P::R *Ls, typename P::R *Ts, int lane) {
+    static_assert(P::kBytes == 2, "bf16 rows: two 16-byte reads each");
+    const int o = 16 * (lane >> 4);
+    const int c = lane & 15;
+    const typename P::R *row0 = Ls + o * PC + o;
+    float t[16];
+    uint4 cur[2], nxt[2];
+    cur[0] = *reinterpret_cast<const uint4 *>(row0);
+    cur[1] = *reinterpret_cast<const uint4 *>(row0 + 8);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r + 1 < 16) {
+            nxt[0] = *reinterpret_cast<const uint4 *>(row0 + (r + 1) * PC);
+            nxt[1] = *reinterpret_cast<const uint4 *>(row0 + (r + 1) * PC + 8);
+        }
+        float lr[16];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const uint32_t w[4] = {cur[v].x, cur[v].y, cur[v].z, cur[v].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                lr[8 * v + 2 * u] = __builtin_bit_cast(float, w[u] << 16);
+                lr[8 * v + 2 * u + 1] = __builtin_bit_cast(float, w[u] & 0xffff0000u);
+            }
+        }
+        float a0 = (r == c) ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < r; ++jj) {
+            if (jj & 1) a1 -= lr[jj] * t[jj];
+            else a0 -= lr[jj] * t[jj];
+        }
+        t[r] = a0 + a1;
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
+}
+
 template <class P, int DK, int CH>
 struct ScanPipeLayout {
     static constexpr int PAD = 16 / P::kBytes;
@@ -210,6 +295,31 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
         }
     };
 
+    // M1 = T_g diag(beta) for eight consecutive columns of one row of block (i, j): item
+    // sub in [0, 32) takes row 16 i + sub / 2 and columns 16 j + 8 (sub & 1) .. + 7 (16-byte
+    // LDS accesses)
+    auto m1_item = [&](int ps, int i, int j, int sub) {
+        const float *gs = gate(ps, 0), *bes = gate(ps, 3);
+        const int r = 16 * i + (sub >> 1);
+        const int c0 = 16 * j + 8 * (sub & 1);
+        F tf[2];
+        P::ld8(Ts + r * PC + c0, tf[0], tf[1]);
+        const float gr = gs[r];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ch = c0 + 4 * hh;
+            const f32x4 bc = lds_f32x4(bes + ch);
+            const f32x4 gc = lds_f32x4(gs + ch);
+            f32x4 m1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float tb = (ch + e <= r) ? static_cast<float>(tf[hh][e]) * bc[e] : 0.f;
+                m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
+            }
+            P::st4(M1s + r * PA + ch, m1);
+        }
+    };
+
     if (NC > 0 && is_scan) {
         Prefetch pf;
         gload(NC - 1, pf);
@@ -300,8 +410,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                 }
             }
         } else if (c >= 0) {
-            gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, 4, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
-                                                                Ls, Ab(ps), nullptr, rw, lane);
+            if constexpr (NCT == 4) {
+                // two Gram pairs per wave: its diagonal block and one the inverse's levels read;
+                // the last two pairs (3, 0) and (3, 1) follow in I2
+                const int pi = rw == 0 ? 1 : rw == 1 ? 3 : 2, pj = rw == 0 ? 0 : rw == 1 ? 2 : rw - 2;
+                gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
+                                                              Ls, Ab(ps), rw, rw, lane);
+                gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
+                                                              Ls, Ab(ps), pi, pj, lane);
+            } else {
+                gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, 4, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3),
+                                                                    gate(ps, 4), Ls, Ab(ps), nullptr, rw, lane);
+            }
         }
         __syncthreads();
 
@@ -357,7 +477,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                 }
             }
         } else if (c >= 0) {
-            inverse_diag<P, CH, PC>(Ls, Ts, rw, lane);
+            if constexpr (NCT == 4) {
+                if (rw == 0) inverse_diag4<P, PC>(Ls, Ts, lane);   // (bf16: C = 64 is bf16 only)
+                else if (rw >= 2)
+                    gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3),
+                                                                  gate(ps, 4), Ls, Ab(ps), 3, rw - 2, lane);
+            } else {
+                inverse_diag<P, CH, PC>(Ls, Ts, rw, lane);
+            }
         }
         __syncthreads();
 
@@ -371,6 +498,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
             }
         } else if (c >= 0) {
             inverse_level1<P, CH, PC>(Ls, Ts, rw, lane);
+            if constexpr (NCT == 4) {                  // M1 of the diagonal blocks, final since I2
+                if (rw >= 2) m1_item(ps, rt - 128 >> 5, rt - 128 >> 5, rt & 31);
+            }
         }
         __syncthreads();
 
@@ -401,28 +531,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
             }
         } else if (c >= 0) {
             // M1 = (H o T) diag(beta) = T_g diag(beta) (lower block triangle)
-            const float *gs = gate(ps, 0), *bes = gate(ps, 3);
-            // eight consecutive columns of one row per item (16-byte LDS accesses)
-            for (int idx = rt; idx < NPAIR * 32; idx += kThreads) {
-                int i, j;
-                tri_pair(idx >> 5, i, j);
-                const int r = 16 * i + ((idx >> 1) & 15);
-                const int c0 = 16 * j + 8 * (idx & 1);
-                F tf[2];
-                P::ld8(Ts + r * PC + c0, tf[0], tf[1]);
-                const float gr = gs[r];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int ch = c0 + 4 * hh;
-                    const f32x4 bc = lds_f32x4(bes + ch);
-                    const f32x4 gc = lds_f32x4(gs + ch);
-                    f32x4 m1;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float tb = (ch + e <= r) ? static_cast<float>(tf[hh][e]) * bc[e] : 0.f;
-                        m1[e] = HAS_A ? __expf(gr - gc[e]) * tb : tb;
-                    }
-                    P::st4(M1s + r * PA + ch, m1);
+            if constexpr (NCT == 4) {                  // the six blocks below the diagonal
+                if (rt < 192) {
+                    const int pr = rt >> 5;            // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                    const int i = pr == 0 ? 1 : pr < 3 ? 2 : 3, j = pr == 0 ? 0 : pr < 3 ? pr - 1 : pr - 3;
+                    m1_item(ps, i, j, rt & 31);
+                }
+            } else {
+                for (int idx = rt; idx < NPAIR * 32; idx += kThreads) {
+                    int i, j;
+                    tri_pair(idx >> 5, i, j);
+                    m1_item(ps, i, j, idx & 31);
                 }
             }
         }
@@ -914,36 +1033,34 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 *reinterpret_cast<uint4 *>(gdk + off) = *reinterpret_cast<const uint4 *>(Kst + c * PK + cv * EPV);
             }
         }
-        if (wave == 0) {
-            float db = 0.f, dl = 0.f, dg = 0.f;
+        // per-token sums of the waves' row partials, one quantity per wave: wave 0 dbeta,
+        // wave 1 dlambda, wave 2 dalpha (its reverse cumulative sum over the chunk from a
+        // DPP prefix sum: the total minus the prefix before the row)
+        if (wave <= 2) {
+            const float *part = wave == 0 ? pdb : wave == 1 ? pdl : pdg;
+            float x = 0.f;
             if (lane < CH) {
 #pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    db += pdb[w * CH + lane];
-                    dl += pdl[w * CH + lane];
-                    dg += pdg[w * CH + lane];
-                }
-                if (HAS_A && lane == CH - 1) {
+                for (int w = 0; w < NW; ++w) x += part[w * CH + lane];
+            }
+            if (wave == 0) {
+                if (lane < clen) args.g_beta[tok(t0 + lane)] = x;
+            } else if (wave == 1) {
+                if (HAS_L && args.g_lam && lane < clen) args.g_lam[tok(t0 + lane)] = x;
+            } else if constexpr (HAS_A) {
+                if (lane == CH - 1) {
                     float sd = 0.f, wzs = 0.f;
 #pragma unroll
                     for (int w = 0; w < NW; ++w) {
                         sd += psc[w];
                         wzs += psc[NW + w];
                     }
-                    dg += egs[CH - 1] * sd + wzs;
+                    x += egs[CH - 1] * sd + wzs;
                 }
-            }
-            // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_down(dg, off);
-                if (lane + off < kWave) dg += y;
-            }
-            if (lane < clen) {
-                const size_t gi = tok(t0 + lane);
-                args.g_beta[gi] = db;
-                if (HAS_L && args.g_lam) args.g_lam[gi] = dl;
-                if (HAS_A && args.g_alpha) args.g_alpha[gi] = dg / als[lane];
+                // dlog(alpha_t) = sum over the chunk's rows s >= t of dg_s
+                const float inc = wave_inclusive_sum(x);
+                const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inc), kWave - 1));
+                if (args.g_alpha && lane < clen) args.g_alpha[tok(t0 + lane)] = (tot - inc + x) / als[lane];
             }
         }
         __syncthreads();   // the staging buffers and row partials are reused by the next chunk
