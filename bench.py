@@ -529,6 +529,20 @@ def main():
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     log(f"[bench] chunk forward {ms_per_step:.4f} ms/step, {tokens_per_s / 1e6:.2f} M tokens/s, "
         f"{ach_gbs:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+    # after the timed region: the same K calls once more, each between its own pair of HIP
+    # events, for the median and the extremes of a single launch
+    s_cur = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(s_cur)
+        fwd()
+        e1.record(s_cur)
+    torch.cuda.synchronize()
+    per_launch = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    launch_stats = {"median_us": per_launch[len(per_launch) // 2], "min_us": per_launch[0], "max_us": per_launch[-1],
+                    "launches": len(per_launch),
+                    "note": "a second pass of K calls after the timed region, one event pair per call"}
+    log(f"[bench] per launch: median {launch_stats['median_us']:.1f} us, min {launch_stats['min_us']:.1f} us")
     for v in variants.values():
         for rec in ([v] if "ms_per_call" in v else [r for r in v.values() if isinstance(r, dict)]):
             if "ms_per_call" in rec:
@@ -575,7 +589,7 @@ def main():
         "hbm_practical": practical,
         "other_workloads": variants,
         "cpu_baseline": cpu,
-        "timing": {"chunk_wall_s": wall_s},
+        "timing": {"chunk_wall_s": wall_s, "per_launch": launch_stats},
     }
     print(json.dumps(out), flush=True)
 
