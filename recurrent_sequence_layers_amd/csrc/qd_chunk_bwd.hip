@@ -871,9 +871,11 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             }
         }
         // W_o = dO S, W_p = P S, W_z = Z dS' on this wave's d_k blocks (block index mt * NKT + kk),
-        // contracted over the value columns in octet order; the B fragments
-        // S[16 vv + 8 g + i][16 kk + l % 16], i = 0..7, come from global memory (rows other waves
-        // have just read, so mostly from L2; staging them through LDS measured no faster)
+        // contracted over the value columns in octet order, and formed transposed (S^T dO^T, ...):
+        // lane (g, n) gets row 16 mt + n and the four keys 16 kk + 4 g .. + 3, the layout of the
+        // per-d_k-block phase below.  The fragments S[16 vv + 8 g + i][16 kk + l % 16], i = 0..7,
+        // come from global memory (rows other waves have just read, so mostly from L2; staging
+        // them through LDS measured no faster)
         f32x4 Wo[NBW], Wp[NBW], Wz[NBW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
@@ -891,9 +893,9 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                     frag_oct<P>(Ds, PV, 16 * mt, 16 * vv, a0, a1, lane);
                     frag_oct<P>(Ps, PV, 16 * mt, 16 * vv, b0, b1, lane);
                     frag_oct<P>(Zs, PV, 16 * mt, 16 * vv, c0, c1, lane);
-                    Wo[j] = P::mma2(Wo[j], a0, a1, s0, s1);
-                    Wp[j] = P::mma2(Wp[j], b0, b1, s0, s1);
-                    Wz[j] = P::mma2(Wz[j], c0, c1, d0, d1);
+                    Wo[j] = P::mma2(Wo[j], s0, s1, a0, a1);
+                    Wp[j] = P::mma2(Wp[j], s0, s1, b0, b1);
+                    Wz[j] = P::mma2(Wz[j], d0, d1, c0, c1);
                 }
             }
         }
@@ -927,15 +929,19 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
         //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms are rowdot(Q, MqK) +
         //   rowdot(K, LbK) - rowdot(K, KT) (the row and column sums of dA o A and dL o beta N
-        //   regrouped, from fp32 accumulators and the exact q and k)
+        //   regrouped, from fp32 accumulators and the exact q and k).
+        //   Every product is formed transposed (K^T Mq^T, ...), so lane (g, n) holds row
+        //   16 mt + n and keys 16 kk + 4 g .. + 3: the row's gates are one value per lane, its
+        //   sums over the block's keys are the lane's four plus two cross-group shuffles, and
+        //   dQ and dK leave as one 8-byte store per lane.
         float wz = 0.f;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int blk = wave + NW * j;
             if (NB % NW == 0 || blk < NB) {
                 const int mt = blk / NKT, kk = blk % NKT;
-                const f32x4 eg = lds_f32x4(egs + 16 * mt + 4 * g4), el = lds_f32x4(egls + 16 * mt + 4 * g4);
-                const f32x4 bt = lds_f32x4(bes + 16 * mt + 4 * g4), lm = lds_f32x4(lams + 16 * mt + 4 * g4);
+                const int row = 16 * mt + r16;
+                const float eg = egs[row], el = egls[row], bt = bes[row], lm = lams[row];
                 // contractions over the chunk's positions, two 16-position blocks per MFMA:
                 // s <= mt for Mq K and dLb K, s >= mt for Mq^T Q + dLb^T K
                 f32x4 mqk = zero4(), lbk = zero4(), kt = zero4();
@@ -943,32 +949,32 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 for (int s = 0; s < NCT; s += 2) {
                     if (s + 1 <= mt) {
                         const F kb0 = frag_b<P>(Ks, PK, 16 * s, 16 * kk), kb1 = frag_b<P>(Ks, PK, 16 * s + 16, 16 * kk);
-                        lbk = P::mma2(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), frag<P>(Ls, PC, 16 * mt, 16 * s + 16), kb0, kb1);
-                        mqk = P::mma2(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), frag<P>(Ts, PC, 16 * mt, 16 * s + 16), kb0, kb1);
+                        lbk = P::mma2(lbk, kb0, kb1, frag<P>(Ls, PC, 16 * mt, 16 * s), frag<P>(Ls, PC, 16 * mt, 16 * s + 16));
+                        mqk = P::mma2(mqk, kb0, kb1, frag<P>(Ts, PC, 16 * mt, 16 * s), frag<P>(Ts, PC, 16 * mt, 16 * s + 16));
                     } else if (s <= mt) {
                         const F kb = frag_b<P>(Ks, PK, 16 * s, 16 * kk);
-                        lbk = P::mma1(lbk, frag<P>(Ls, PC, 16 * mt, 16 * s), kb);
-                        mqk = P::mma1(mqk, frag<P>(Ts, PC, 16 * mt, 16 * s), kb);
+                        lbk = P::mma1(lbk, kb, frag<P>(Ls, PC, 16 * mt, 16 * s));
+                        mqk = P::mma1(mqk, kb, frag<P>(Ts, PC, 16 * mt, 16 * s));
                     }
                 }
 #pragma unroll
                 for (int s = 0; s < NCT; ++s) {
                     if (s < mt || (s - mt) % 2 != 0) continue;     // pairs (s, s + 1) from s = mt
                     if (s + 1 < NCT) {
-                        kt = P::mma2(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Ts, PC, 16 * s + 16, 16 * mt),
-                                     frag_b<P>(Qs, PK, 16 * s, 16 * kk), frag_b<P>(Qs, PK, 16 * s + 16, 16 * kk));
-                        kt = P::mma2(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ls, PC, 16 * s + 16, 16 * mt),
-                                     frag_b<P>(Ks, PK, 16 * s, 16 * kk), frag_b<P>(Ks, PK, 16 * s + 16, 16 * kk));
+                        kt = P::mma2(kt, frag_b<P>(Qs, PK, 16 * s, 16 * kk), frag_b<P>(Qs, PK, 16 * s + 16, 16 * kk),
+                                     frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Ts, PC, 16 * s + 16, 16 * mt));
+                        kt = P::mma2(kt, frag_b<P>(Ks, PK, 16 * s, 16 * kk), frag_b<P>(Ks, PK, 16 * s + 16, 16 * kk),
+                                     frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ls, PC, 16 * s + 16, 16 * mt));
                     } else {
-                        kt = P::mma1(kt, frag_b<P>(Ts, PC, 16 * s, 16 * mt), frag_b<P>(Qs, PK, 16 * s, 16 * kk));
-                        kt = P::mma1(kt, frag_b<P>(Ls, PC, 16 * s, 16 * mt), frag_b<P>(Ks, PK, 16 * s, 16 * kk));
+                        kt = P::mma1(kt, frag_b<P>(Qs, PK, 16 * s, 16 * kk), frag_b<P>(Ts, PC, 16 * s, 16 * mt));
+                        kt = P::mma1(kt, frag_b<P>(Ks, PK, 16 * s, 16 * kk), frag_b<P>(Ls, PC, 16 * s, 16 * mt));
                     }
                 }
-                const f32x4 dX = lbk - eg * bt * Wp[j];
-                const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[j] - lm * bt * Wp[j]) : eg * Wo[j]);
+                const f32x4 dX = lbk - (eg * bt) * Wp[j];
+                const f32x4 dQ = mqk + (HAS_L ? eg * (Wo[j] - (lm * bt) * Wp[j]) : eg * Wo[j]);
                 const f32x4 dK = kt + el * Wz[j] + dX;
-                const f32x4 qf = P::f32(frag_b<P>(Qs, PK, 16 * mt, 16 * kk));
-                const f32x4 kf = P::f32(frag_b<P>(Ks, PK, 16 * mt, 16 * kk));
+                const f32x4 qf = P::f32(frag<P>(Qs, PK, 16 * mt, 16 * kk));
+                const f32x4 kf = P::f32(frag<P>(Ks, PK, 16 * mt, 16 * kk));
                 f32x4 dgp = zero4();
                 if constexpr (HAS_A) {
                     const f32x4 xf = HAS_L ? kf + lm * qf : kf;
@@ -977,37 +983,29 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                     wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
                 }
                 const f32x4 dlp = HAS_L ? qf * dX : zero4();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int o = (16 * mt + 4 * g4 + e) * PK + 16 * kk + r16;
-                    Qst[o] = P::from_f32(dQ[e]);
-                    Kst[o] = P::from_f32(dK[e]);
-                }
-                // row sums over this wave's 16 key columns; lane r16 < 4 of each 16-lane group
-                // stores row 16 mt + 4 g + r16.  When every wave owns one key tile (NW a multiple
-                // of NKT), each (wave, row) partial is written once and needs no read.
+                P::st4(Qst + row * PK + 16 * kk + 4 * g4, dQ);
+                P::st4(Kst + row * PK + 16 * kk + 4 * g4, dK);
+                // row sums over this wave's 16 key columns: the lane's four, then the four lane
+                // groups; lanes of group 0 store row 16 mt + n.  When every wave owns one key
+                // tile (NW a multiple of NKT), each (wave, row) partial is written once.
                 constexpr bool kOnce = NW % NKT == 0;
-                const int pr = wave * CH + 16 * mt + 4 * g4 + r16;
-                auto pick = [&](f32x4 v) {
-                    const float x01 = (r16 & 1) ? v[1] : v[0], x23 = (r16 & 1) ? v[3] : v[2];
-                    return (r16 & 2) ? x23 : x01;
+                const int pr = wave * CH + row;
+                auto rowsum = [&](f32x4 v) {
+                    float x = (v[0] + v[1]) + (v[2] + v[3]);
+                    x += __shfl_xor(x, 16);
+                    x += __shfl_xor(x, 32);
+                    return x;
                 };
                 if constexpr (HAS_L) {
-                    f32x4 rs;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rs[e] = sum16(dlp[e]);
-                    const float v = pick(rs);
-                    if (r16 < 4) {
+                    const float v = rowsum(dlp);
+                    if (g4 == 0) {
                         if constexpr (kOnce) pdl[pr] = v;
                         else pdl[pr] += v;
                     }
                 }
                 if constexpr (HAS_A) {
-                    f32x4 rs;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rs[e] = sum16(dgp[e]);
-                    const float v = pick(rs);
-                    if (r16 < 4) {
+                    const float v = rowsum(dgp);
+                    if (g4 == 0) {
                         if constexpr (kOnce) pdg[pr] = v;
                         else pdg[pr] += v;
                     }
