@@ -561,6 +561,23 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
 // matrices; the states S and dS' are read from global memory as MFMA fragments (the
 // column-local Y = X S^T and K dS'^T take each wave's 16 rows of S and dS'; the value
 // contractions W_o = dO S, W_p = P S, W_z = Z dS' take 4 x 16 blocks of them).
+// Four row sums at once.  x holds rows 4g + e (e = 0..3) of the 16 columns a 16-lane group
+// spans (the MFMA accumulator layout); lane n of the group gets the sum over the group's
+// lanes of row 4g + quad_row(n).  Two exchanges inside each quad leave every lane one of
+// the four pair-then-quad partial sums, and two row rotations add the group's four quads:
+// five DPP moves for the four sums.
+__device__ __forceinline__ int quad_row(int n) { return 2 * (n & 1) + ((n >> 1) & 1); }
+__device__ __forceinline__ float rowsum4x16(f32x4 x, int n) {
+    const bool b0 = n & 1, b1 = n & 2;
+    // lanes n and n ^ 1: even lanes keep rows 0 and 1, odd lanes rows 2 and 3
+    const float y0 = (b0 ? x[2] : x[0]) + dpp_mov<0xb1>(b0 ? x[0] : x[2]);
+    const float y1 = (b0 ? x[3] : x[1]) + dpp_mov<0xb1>(b0 ? x[1] : x[3]);
+    // lanes n and n ^ 2: bit 1 clear keeps the first, set the second
+    const float z = (b1 ? y1 : y0) + dpp_mov<0x4e>(b1 ? y0 : y1);
+    const float z4 = z + dpp_mov<0x124>(z);          // row_ror:4
+    return z4 + dpp_mov<0x128>(z4);                  // row_ror:8
+}
+
 template <class P, int DK, int CH, int DV>
 struct GradLayout {
     static constexpr int NW = DV / 16;
@@ -664,7 +681,7 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         R *const Zs = reinterpret_cast<R *>(smem) + Lay::oZ;
         R *const Ps = reinterpret_cast<R *>(smem) + Lay::oP;
         R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;    // diag(beta) strict(X K^T), later dLb
-        R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;
+        R *const Ns = reinterpret_cast<R *>(smem) + Lay::oN;    // -N
         R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;    // T, then T_g, later Mq
         R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
         R *const Qst = Ds;                                       // dQ staging (after the value phase)
@@ -830,27 +847,28 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
 #pragma unroll
                 for (int s = 0; s <= mt; s += 2) {
                     if (s + 1 <= mt)
-                        U = P::mma2(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s + 16)),
+                        U = P::mma2(U, frag<P>(Ns, PC, 16 * mt, 16 * s), frag<P>(Ns, PC, 16 * mt, 16 * s + 16),
                                     Zf[s], Zf[s + 1]);
                     else
-                        U = P::mma1(U, P::neg(frag<P>(Ns, PC, 16 * mt, 16 * s)), Zf[s]);
+                        U = P::mma1(U, frag<P>(Ns, PC, 16 * mt, 16 * s), Zf[s]);
                 }
-                f32x4 db;
+                f32x4 pu;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    db[e] = sum16(Pm[e] * U[e]);
+                    pu[e] = Pm[e] * U[e];
                     const int o = (16 * mt + 4 * g4 + e) * PV + 16 * wave + r16;
                     Zs[o] = P::from_f32(Z[mt][e]);
                     Ps[o] = P::from_f32(Pm[e]);
                 }
-                // lane r16 < 4 of each 16-lane group stores row 16 mt + 4 g + r16
-                const float x01 = (r16 & 1) ? db[1] : db[0], x23 = (r16 & 1) ? db[3] : db[2];
-                if (r16 < 4) pdb[wave * CH + 16 * mt + 4 * g4 + r16] = (r16 & 2) ? x23 : x01;
+                // lane r16 < 4 of each 16-lane group stores row 16 mt + 4 g + quad_row(r16)
+                const float db = rowsum4x16(pu, r16);
+                if (r16 < 4) pdb[wave * CH + 16 * mt + 4 * g4 + quad_row(r16)] = db;
             }
         }
         __syncthreads();
 
-        // ---- value contractions over all d_v: dA = dO Z^T, dL = P Z^T on this wave's lower blocks
+        // ---- value contractions over all d_v: dA = dO Z^T, dL = P Z^T on this wave's lower blocks,
+        // formed transposed (Z dO^T, Z P^T): lane (g, n) gets row 16 i + n, columns 16 j + 4 g .. + 3
         f32x4 dAacc[PPW], dLacc[PPW];
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
@@ -865,8 +883,8 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                     frag_oct<P>(Zs, PV, 16 * j, 16 * vv, z0, z1, lane);
                     frag_oct<P>(Ds, PV, 16 * i, 16 * vv, a0, a1, lane);
                     frag_oct<P>(Ps, PV, 16 * i, 16 * vv, b0, b1, lane);
-                    dAacc[u] = P::mma2(dAacc[u], a0, a1, z0, z1);
-                    dLacc[u] = P::mma2(dLacc[u], b0, b1, z0, z1);
+                    dAacc[u] = P::mma2(dAacc[u], z0, z1, a0, a1);
+                    dLacc[u] = P::mma2(dLacc[u], z0, z1, b0, b1);
                 }
             }
         }
@@ -903,33 +921,40 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         // the next chunk's rows (this chunk's global reads are done)
         if (it + static_cast<int>(gridDim.x) < total) fetch(it + gridDim.x);
 
-        // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL)
+        // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL); each lane
+        // has one row and four consecutive columns, stored with one 8-byte write per matrix
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
             const int p = wave + NW * u;
             if (p < NPAIR) {
                 int i, j;
                 tri_pair(p, i, j);
-                const int c = 16 * j + r16;
-                const float gc = gs[c];
+                const int r = 16 * i + r16;
+                const int c0 = 16 * j + 4 * g4;
+                const float gr = gs[r], br = bes[r], lr = lams[r];
+                const f32x4 gc = lds_f32x4(gs + c0);
+                f32x4 mq, lb;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * i + 4 * g4 + e;
-                    const float G = HAS_A ? __expf(gs[r] - gc) : 1.f;
+                    const int c = c0 + e;
+                    const float G = HAS_A ? __expf(gr - gc[e]) : 1.f;
                     const float da = (c <= r) ? dAacc[u][e] : 0.f;
-                    const float dlb = (c < r) ? -bes[r] * G * dLacc[u][e] : 0.f;
-                    Ts[r * PC + c] = P::from_f32(da * G + (HAS_L ? lams[r] * dlb : 0.f));
-                    Ls[r * PC + c] = P::from_f32(dlb);
+                    const float dlb = (c < r) ? -br * G * dLacc[u][e] : 0.f;
+                    mq[e] = da * G + (HAS_L ? lr * dlb : 0.f);
+                    lb[e] = dlb;
                 }
+                P::st4(Ts + r * PC + c0, mq);
+                P::st4(Ls + r * PC + c0, lb);
             }
         }
         __syncthreads();   // Mq and dLb published
 
         // ---- per d_k block:  MqK = Mq K,  LbK = dLb K,  KT = Mq^T Q + dLb^T K;
         //   dX = LbK - D_g diag(beta) W_p,  dQ = MqK + D_g (W_o - diag(lambda beta) W_p),
-        //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms are rowdot(Q, MqK) +
+        //   dK = KT + D_r W_z + dX;  the decay gradient's pair terms, rowdot(Q, MqK) +
         //   rowdot(K, LbK) - rowdot(K, KT) (the row and column sums of dA o A and dL o beta N
-        //   regrouped, from fp32 accumulators and the exact q and k).
+        //   regrouped, from fp32 accumulators and the exact q and k), together with its W
+        //   terms, come to rowdot(Q, dQ) + rowdot(K, 2 dX - dK).
         //   Every product is formed transposed (K^T Mq^T, ...), so lane (g, n) holds row
         //   16 mt + n and keys 16 kk + 4 g .. + 3: the row's gates are one value per lane, its
         //   sums over the block's keys are the lane's four plus two cross-group shuffles, and
@@ -977,9 +1002,10 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 const f32x4 kf = P::f32(frag<P>(Ks, PK, 16 * mt, 16 * kk));
                 f32x4 dgp = zero4();
                 if constexpr (HAS_A) {
-                    const f32x4 xf = HAS_L ? kf + lm * qf : kf;
+                    // the pair terms plus rowdot(D_g W_o, Q) - rowdot(D_g diag(beta) W_p, X) -
+                    // rowdot(D_r W_z, K), regrouped as rowdot(Q, dQ) + rowdot(K, 2 dX - dK)
                     const f32x4 wzk = el * Wz[j] * kf;
-                    dgp = qf * mqk + kf * lbk - kf * kt + eg * (Wo[j] * qf - bt * Wp[j] * xf) - wzk;
+                    dgp = qf * dQ + kf * (2.f * dX - dK);
                     wz += wzk[0] + wzk[1] + wzk[2] + wzk[3];
                 }
                 const f32x4 dlp = HAS_L ? qf * dX : zero4();

@@ -37,7 +37,8 @@ namespace qd {
 // computed transposed (D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c], r = 16i + l%16,
 // c = 16j + 4g + e) so a lane owns four consecutive columns of a row.  Writes
 //   L = strictly-lower(diag(beta) X K^T),  X K^T = K K^T + diag(lambda) Q K^T,
-//   A = G o lower(Q K^T),   and, when N is non-null,  N = G o strictly-lower(X K^T),
+//   A = G o lower(Q K^T),   and, when Ns is non-null,  Ns = -N, N = G o strictly-lower(X K^T)
+//   (stored negated: its one reader subtracts N Z),
 // with G[r][c] = exp(g_r - g_c).  Blocks above the block diagonal are not written.
 // wave: index of the calling wave among the NW that share the blocks; lane: its lane id.
 // PCA: the row pitch of A (PC, the pitch of L and N, by default).
@@ -79,7 +80,7 @@ __device__ __forceinline__ void gram_blocks(const typename P::R *Qs, const typen
                 const float dec = HAS_A ? __expf(gr - gc[e]) : 1.f;
                 lv[e] = (c < r) ? br * xk : 0.f;
                 av[e] = (c <= r) ? dec * gq_[e] : 0.f;
-                nv[e] = (c < r) ? dec * xk : 0.f;
+                nv[e] = (c < r) ? -dec * xk : 0.f;
             }
             P::st4(Ls + r * PC + c0, lv);
             P::st4(As + r * PCA + c0, av);

@@ -44,7 +44,6 @@ struct Bf16 {
     }
     __device__ __forceinline__ static F cvt(f32x4 a) { return __builtin_convertvector(a, bf16x4); }
     __device__ __forceinline__ static f32x4 f32(F a) { return __builtin_convertvector(a, f32x4); }
-    __device__ __forceinline__ static F neg(F a) { return -a; }
     __device__ __forceinline__ static F ld4(const R *p) {      // 4 consecutive elements
         return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(p));
     }
@@ -89,7 +88,6 @@ struct F32 {
     __device__ __forceinline__ static R from_f32(float x) { return x; }
     __device__ __forceinline__ static F cvt(f32x4 a) { return a; }
     __device__ __forceinline__ static f32x4 f32(F a) { return a; }
-    __device__ __forceinline__ static F neg(F a) { return -a; }
     __device__ __forceinline__ static F ld4(const R *p) { return *reinterpret_cast<const f32x4 *>(p); }
     __device__ __forceinline__ static F ld4_strided(const R *p, int stride) {
         f32x4 r;

@@ -330,6 +330,10 @@ def kernel_form_bwd(q, k, v, alpha, beta, lam, S0, dO, dST, C):
                 assert np.allclose(regrouped, pair, rtol=1e-9, atol=1e-12 * max(1.0, np.abs(pair).max()))
                 dg = (pair
                       + np.einsum("tj,tj->t", Dg[:, None] * Wo, Q) - np.einsum("tj,tj->t", Dg[:, None] * Wr, X) - wz)
+                # and the whole per-row sum from the gradients the kernel forms anyway:
+                # rowdot(Q, dQ) + rowdot(K, 2 dX - dK)
+                short = rd(Q, dQ) + rd(K, 2.0 * dX - dK)
+                assert np.allclose(short, dg, rtol=1e-9, atol=1e-12 * max(1.0, np.abs(dg).max()))
                 dg[-1] += c["gC"] * (dSp * S).sum() + wz.sum()
                 out["dq"][b, c["sl"], h] = dQ
                 out["dk"][b, c["sl"], h] = dK
