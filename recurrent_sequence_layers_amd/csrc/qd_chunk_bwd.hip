@@ -64,10 +64,10 @@ constexpr int kDVT = 64;  // value columns per tile
 // execute:
 //   interval  scan (chunk n)                         prep (chunk c = n - 1), C = 64
 //   I1        prefetch chunk n - 2 (registers);      Gram blocks (L, A): each wave its
-//             dZ, dR                                 diagonal block and one of (1,0), (3,2),
+//             dZ, dR                                 diagonal block, whose T it inverts in
+//                                                    registers, and one of (1,0), (3,2),
 //                                                    (2,0), (2,1)
-//   I2        dS^T update                            wave 4: the four diagonal blocks of T;
-//                                                    waves 6, 7: Gram blocks (3,0), (3,1)
+//   I2        dS^T update                            waves 6, 7: Gram blocks (3,0), (3,1)
 //   I3        dV staged in LDS                       T, level 1 (waves 4, 5); M1 of the
 //                                                    diagonal blocks (waves 6, 7)
 //   I4        stage chunk n - 2                      T, level 2
@@ -76,12 +76,16 @@ constexpr int kDVT = 64;  // value columns per tile
 // and all of M1 in I5.  q, k, dO, A and the gates are double-buffered by chunk parity; M1
 // is read by the scan in I1 and rewritten by the prep in I3 and I5; L and T belong to the
 // prep.
-// One Gram block pair (i, j), j <= i, of gram_blocks: L, A (and N when non-null) for block
-// (i, j).  The reverse scan's prep role schedules the pairs itself.
+// One Gram block pair (i, j), j <= i, of gram_blocks: L, A (and -N when Ns is non-null) for
+// block (i, j); the callers schedule the pairs themselves.  For a diagonal block and a
+// non-null Ts the lane's row of L is already in the MFMA A-operand layout, and the block's
+// inverse (I + L)^-1 is formed at once in registers, with fp32 products, from L rounded as
+// stored, and written to Ts.
 template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int PCA = PC>
 __device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
                                           const float *bes, const float *lams, typename P::R *Ls, typename P::R *As,
-                                          int i, int j, int lane) {
+                                          int i, int j, int lane, typename P::R *Ns = nullptr,
+                                          typename P::R *Ts = nullptr) {
     using F = typename P::F;
     constexpr int NKT = DK / 16;
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -99,7 +103,7 @@ __device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typenam
     const int c0 = 16 * j + 4 * g4;
     const float lr = lams[r], br = bes[r], gr = gs[r];
     const f32x4 gc = lds_f32x4(gs + c0);
-    f32x4 lv, av;
+    f32x4 lv, av, nv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = c0 + e;
@@ -107,53 +111,18 @@ __device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typenam
         const float dec = HAS_A ? __expf(gr - gc[e]) : 1.f;
         lv[e] = (c < r) ? br * xk : 0.f;
         av[e] = (c <= r) ? dec * gq_[e] : 0.f;
+        nv[e] = (c < r) ? -dec * xk : 0.f;
     }
     P::st4(Ls + r * PC + c0, lv);
     P::st4(As + r * PCA + c0, av);
-}
-
-// The four 16 x 16 diagonal blocks of T = (I + L)^-1 (C = 64) on one wave: lane group g
-// inverts block g by forward substitution over rows, lane l computing column l % 16.  The
-// next row of L is read while the current one is substituted, and each row's sum runs as
-// two interleaved partial sums.
-template <class P, int PC>
-__device__ __forceinline__ void inverse_diag4(const typename P::R *Ls, typename P::R *Ts, int lane) {
-    static_assert(P::kBytes == 2, "bf16 rows: two 16-byte reads each");
-    const int o = 16 * (lane >> 4);
-    const int c = lane & 15;
-    const typename P::R *row0 = Ls + o * PC + o;
-    float t[16];
-    uint4 cur[2], nxt[2];
-    cur[0] = *reinterpret_cast<const uint4 *>(row0);
-    cur[1] = *reinterpret_cast<const uint4 *>(row0 + 8);
+    if (Ns) P::st4(Ns + r * PC + c0, nv);
+    if (Ts && i == j) {
+        // the inverse of L as stored (rounded to the element type), the matrix the block
+        // doubling's off-diagonal blocks also read
+        const f32x4 t = invert_unit_lower16<F32>(P::f32(P::cvt(lv)), g4, r16);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r + 1 < 16) {
-            nxt[0] = *reinterpret_cast<const uint4 *>(row0 + (r + 1) * PC);
-            nxt[1] = *reinterpret_cast<const uint4 *>(row0 + (r + 1) * PC + 8);
-        }
-        float lr[16];
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const uint32_t w[4] = {cur[v].x, cur[v].y, cur[v].z, cur[v].w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                lr[8 * v + 2 * u] = __builtin_bit_cast(float, w[u] << 16);
-                lr[8 * v + 2 * u + 1] = __builtin_bit_cast(float, w[u] & 0xffff0000u);
-            }
-        }
-        float a0 = (r == c) ? 1.f : 0.f, a1 = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < r; ++jj) {
-            if (jj & 1) a1 -= lr[jj] * t[jj];
-            else a0 -= lr[jj] * t[jj];
-        }
-        t[r] = a0 + a1;
-        cur[0] = nxt[0];
-        cur[1] = nxt[1];
+        for (int e = 0; e < 4; ++e) Ts[(16 * i + 4 * g4 + e) * PC + 16 * i + r16] = P::from_f32(t[e]);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Ts[(o + r) * PC + o + c] = P::from_f32(t[r]);
 }
 
 template <class P, int DK, int CH>
@@ -415,7 +384,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                 // the last two pairs (3, 0) and (3, 1) follow in I2
                 const int pi = rw == 0 ? 1 : rw == 1 ? 3 : 2, pj = rw == 0 ? 0 : rw == 1 ? 2 : rw - 2;
                 gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
-                                                              Ls, Ab(ps), rw, rw, lane);
+                                                              Ls, Ab(ps), rw, rw, lane, nullptr, Ts);
                 gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3), gate(ps, 4),
                                                               Ls, Ab(ps), pi, pj, lane);
             } else {
@@ -478,8 +447,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
             }
         } else if (c >= 0) {
             if constexpr (NCT == 4) {
-                if (rw == 0) inverse_diag4<P, PC>(Ls, Ts, lane);   // (bf16: C = 64 is bf16 only)
-                else if (rw >= 2)
+                if (rw >= 2)
                     gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L, PA>(Qb(ps), Kb(ps), gate(ps, 0), gate(ps, 3),
                                                                   gate(ps, 4), Ls, Ab(ps), 3, rw - 2, lane);
             } else {
@@ -739,8 +707,21 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         for (int i = tid; i < 3 * NW * CH + 2 * NW; i += NT) pdb[i] = 0.f;
         __syncthreads();
 
-        // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place
-        gram_blocks<P, DK, CH, PK, PC, HAS_A, HAS_L, NW>(Qs, Ks, gs, bes, lams, Ls, As, Ns);
+        // ---- L, A, N; T = (I + L)^-1; T_g = H o T in place.  Waves 0 .. NCT - 1 form their
+        // diagonal block and invert it in registers; the blocks below the diagonal go to the
+        // other waves (round-robin over all waves when there are no others)
+        if (wave < NCT)
+            gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, wave, wave, lane, Ns, Ts);
+        constexpr int NOFF = NPAIR - NCT;
+#pragma unroll
+        for (int q = 0; q < NOFF; ++q) {
+            if (wave == (NW > NCT ? NCT + q % (NW - NCT) : q % NW)) {
+                int i = 1;
+                while (i * (i + 1) / 2 <= q) ++i;
+                gram_pair<P, DK, CH, PK, PC, HAS_A, HAS_L>(Qs, Ks, gs, bes, lams, Ls, As, i, q - i * (i - 1) / 2, lane,
+                                                           Ns, nullptr);
+            }
+        }
         __syncthreads();
         // this wave's 16 rows of S and dS', as B operands in octet order (one 16-byte load
         // per lane and 32 keys; the key fragments they meet are read in the same order)
@@ -751,7 +732,15 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             P::ld8(hs + off, sTf[t], sTf[t + 1]);
             P::ld8(dhs + off, dsTf[t], dsTf[t + 1]);
         }
-        unit_lower_inverse<P, CH, PC>(Ls, Ts, lane);
+        // the two block-doubling levels of the inverse (the diagonal blocks are done)
+        if constexpr (NCT >= 2) {
+            inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
+            __syncthreads();
+        }
+        if constexpr (NCT == 4) {
+            inverse_level2<P, CH, PC>(Ls, Ts, wave, lane);
+            __syncthreads();
+        }
         if constexpr (HAS_A) {
             for (int idx = tid; idx < NPAIR * 64; idx += NT) {
                 int i, j;

@@ -33,6 +33,56 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
 
 namespace qd {
 
+// Value of lane k of each group of four lanes (DPP quad permutation).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
+}
+
+// Inverse T of a 16x16 unit lower triangular block I + L, stable block forward substitution:
+//   4x4 diagonal blocks inverted in registers (lanes 4j.. of a quad hold rows j),
+//   then T21 = -T22 L21 T11 twice (4 -> 8 -> 16) on MFMA.
+// In: lv = L[m][4g + e] (lane g = l/16, m = l%16; the MFMA A-operand layout of L, fp32).
+// Out: T[4g + e][n] (n = l%16; the accumulator layout).  Both layouts of every partial
+// inverse are produced by multiplying in both orders, so no LDS transposes are needed.
+// Q: the products' element policy: Bf16 rounds every operand of the substitution to bf16
+// (the forward kernel), F32 keeps them in fp32 on the fp32 MFMA (the backward, whose
+// reverse scan carries the error of T from chunk to chunk).
+template <class Q>
+__device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
+    auto prod = [](f32x4 a, f32x4 b) { return Q::mma1(zero4(), Q::cvt(a), Q::cvt(b)); };
+    // 4x4 diagonal blocks.  In the quad of lanes (g, 4g .. 4g+3), lane j holds row j of D
+    // (D = the block's strictly lower part); the others hold rows of off-diagonal blocks.
+    const int j = m & 3;
+    const bool diag = (m >> 2) == g;
+    const float d10 = quad_bcast<1>(lv[0]);
+    const float d20 = quad_bcast<2>(lv[0]), d21 = quad_bcast<2>(lv[1]);
+    const float d30 = quad_bcast<3>(lv[0]), d31 = quad_bcast<3>(lv[1]), d32 = quad_bcast<3>(lv[2]);
+    // row j of D^-1 (A layout: lane (g, m) gets T4[m][4g + e])
+    f32x4 ra;
+    ra[0] = (j == 0) ? 1.f : -lv[0] + lv[1] * d10 + lv[2] * (d20 - d21 * d10);
+    ra[1] = (j == 1) ? 1.f : -lv[1] + lv[2] * d21;
+    ra[2] = (j == 2) ? 1.f : -lv[2];
+    ra[3] = (j == 3) ? 1.f : 0.f;
+    // column j of D^-1 (B layout: lane (g, n) gets T4[4g + e][n])
+    f32x4 cb;
+    cb[0] = (j == 0) ? 1.f : 0.f;
+    cb[1] = ((j == 1) ? 1.f : 0.f) - d10 * cb[0];
+    cb[2] = ((j == 2) ? 1.f : 0.f) - d20 * cb[0] - d21 * cb[1];
+    cb[3] = ((j == 3) ? 1.f : 0.f) - d30 * cb[0] - d31 * cb[1] - d32 * cb[2];
+    const f32x4 A4 = diag ? ra : zero4(), B4 = diag ? cb : zero4();
+    // 4 -> 8: L restricted to 4x4 blocks (1,0) and (3,2)
+    const f32x4 Lm4 = ((m >> 2) == g + 1 && (g & 1) == 0) ? lv : zero4();
+    const f32x4 X = prod(Lm4, B4);                   // L' T4
+    const f32x4 Y = prod(A4, X);                     // T4 L' T4
+    const f32x4 Yt = prod(X, A4);                    // (T4 L' T4)^T
+    const f32x4 B8 = B4 - Y, A8 = A4 - Yt;
+    // 8 -> 16: L restricted to rows 8..15, columns 0..7
+    const f32x4 Lm8 = (m >= 8 && g < 2) ? lv : zero4();
+    const f32x4 X2 = prod(Lm8, B8);
+    return B8 - prod(A8, X2);
+}
+
 // Gram blocks of one chunk, NW waves over the lower block triangle.  Each block is
 // computed transposed (D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c], r = 16i + l%16,
 // c = 16j + 4g + e) so a lane owns four consecutive columns of a row.  Writes

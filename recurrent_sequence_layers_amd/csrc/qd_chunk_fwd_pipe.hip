@@ -56,6 +56,7 @@
 // the range check returns zeros for rows past the end of the sequence and drops
 // their stores, so the tail chunk needs no clamping or masking (it is padded with
 // q = k = v = 0, beta = 0, alpha = 1, which leaves the state and valid outputs alone).
+#include "qd_chunk_common.h"
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -97,12 +98,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-// Value of lane k of each group of four lanes (DPP quad permutation).
-template <int K>
-__device__ __forceinline__ float quad_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
-}
-
 // Layer prologue of the raw entry point (the layer of the Q-Delta reading notes §1 and
 // §3.1 normalises q and k and maps the gate logits): row segment of a staging lane,
 // 8 bf16 of one q or k row, L2-normalised over the row, q / sqrt(|q|^2 + 1e-6).  The
@@ -137,51 +132,6 @@ __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf
 // log(alpha) = -softplus(a) = -(max(a, 0) + log(1 + exp(-|a|)))
 __device__ __forceinline__ float log_decay_from_logit(float a) {
     return -(fmaxf(a, 0.f) + __logf(1.f + __expf(-fabsf(a))));
-}
-
-// acc + A B for fp32 fragments a (A operand) and b (B operand), rounded to bf16 like
-// every other operand of the block doubling
-__device__ __forceinline__ f32x4 mfma_bf(f32x4 a, f32x4 b, f32x4 acc) {
-    return mfma16(Bf16::cvt(a), Bf16::cvt(b), acc);
-}
-
-// Inverse T of a 16x16 unit lower triangular block I + L, stable block forward substitution:
-//   4x4 diagonal blocks inverted in registers (lanes 4j.. of a quad hold rows j),
-//   then T21 = -T22 L21 T11 twice (4 -> 8 -> 16) on MFMA.
-// In: lv = L[m][4g + e] (lane g = l/16, m = l%16; the MFMA A-operand layout of L, fp32).
-// Out: T[4g + e][n] (n = l%16; the accumulator layout).  Both layouts of every partial
-// inverse are produced by multiplying in both orders, so no LDS transposes are needed.
-__device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
-    // 4x4 diagonal blocks.  In the quad of lanes (g, 4g .. 4g+3), lane j holds row j of D
-    // (D = the block's strictly lower part); the others hold rows of off-diagonal blocks.
-    const int j = m & 3;
-    const bool diag = (m >> 2) == g;
-    const float d10 = quad_bcast<1>(lv[0]);
-    const float d20 = quad_bcast<2>(lv[0]), d21 = quad_bcast<2>(lv[1]);
-    const float d30 = quad_bcast<3>(lv[0]), d31 = quad_bcast<3>(lv[1]), d32 = quad_bcast<3>(lv[2]);
-    // row j of D^-1 (A layout: lane (g, m) gets T4[m][4g + e])
-    f32x4 ra;
-    ra[0] = (j == 0) ? 1.f : -lv[0] + lv[1] * d10 + lv[2] * (d20 - d21 * d10);
-    ra[1] = (j == 1) ? 1.f : -lv[1] + lv[2] * d21;
-    ra[2] = (j == 2) ? 1.f : -lv[2];
-    ra[3] = (j == 3) ? 1.f : 0.f;
-    // column j of D^-1 (B layout: lane (g, n) gets T4[4g + e][n])
-    f32x4 cb;
-    cb[0] = (j == 0) ? 1.f : 0.f;
-    cb[1] = ((j == 1) ? 1.f : 0.f) - d10 * cb[0];
-    cb[2] = ((j == 2) ? 1.f : 0.f) - d20 * cb[0] - d21 * cb[1];
-    cb[3] = ((j == 3) ? 1.f : 0.f) - d30 * cb[0] - d31 * cb[1] - d32 * cb[2];
-    const f32x4 A4 = diag ? ra : zero4(), B4 = diag ? cb : zero4();
-    // 4 -> 8: L restricted to 4x4 blocks (1,0) and (3,2)
-    const f32x4 Lm4 = ((m >> 2) == g + 1 && (g & 1) == 0) ? lv : zero4();
-    const f32x4 X = mfma_bf(Lm4, B4, zero4());        // L' T4
-    const f32x4 Y = mfma_bf(A4, X, zero4());          // T4 L' T4
-    const f32x4 Yt = mfma_bf(X, A4, zero4());         // (T4 L' T4)^T
-    const f32x4 B8 = B4 - Y, A8 = A4 - Yt;
-    // 8 -> 16: L restricted to rows 8..15, columns 0..7
-    const f32x4 Lm8 = (m >= 8 && g < 2) ? lv : zero4();
-    const f32x4 X2 = mfma_bf(Lm8, B8, zero4());
-    return B8 - mfma_bf(A8, X2, zero4());
 }
 
 // Fragment-order layout.  A 16 x 32 tile of an MFMA operand (16 rows, 32 contraction
@@ -339,7 +289,7 @@ struct PipeKernel {
                 }
                 sts4(As + cc_off<CH>(r, c0), av);
                 if (i == j) {
-                    tdiag = invert_unit_lower16(lv, g4, r16);
+                    tdiag = invert_unit_lower16<Bf16>(lv, g4, r16);
                     sts4(Td + (16 * i + r16) * PC + 16 * i + 4 * g4, tdiag);   // T_g[16i + 4g + e][16i + n]
                 } else {
                     sts4(Lg + r * PC + c0, lv);
