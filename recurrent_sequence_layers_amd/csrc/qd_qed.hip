@@ -368,24 +368,42 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                 fq = P::cvt(xq * ea);
                 fk = P::cvt(xk * ek);
             };
+            // formed transposed (K A^T, K Q^T): lane (g, n) gets row 16 I + n and the columns
+            // 16 J + 4 g .. + 3, the MFMA A-operand layout of the block
 #pragma unroll
             for (int s = 0; s < NKT; s += 2) {        // two steps per MFMA
                 F a0, q0, k0, a1, q1, k1;
                 step(s, a0, q0, k0);
                 step(s + 1, a1, q1, k1);
-                lacc = P::mma2(lacc, a0, a1, k0, k1);
-                macc = P::mma2(macc, q0, q1, k0, k1);
+                lacc = P::mma2(lacc, k0, k1, a0, a1);
+                macc = P::mma2(macc, k0, k1, q0, q1);
             }
-            // accumulator: rows 16 I + 4 g + e, column 16 J + l % 16
+            const int r = 16 * I + r16, c0 = 16 * J + 4 * g4;
+            f32x4 lv, mv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * I + 4 * g4 + e, c = 16 * J + r16;
-                Ls[r * PC + c] = P::from_f32(c < r ? lacc[e] : 0.f);
-                Ms[r * PC + c] = P::from_f32(c <= r ? macc[e] : 0.f);
+                lv[e] = (c0 + e < r) ? lacc[e] : 0.f;
+                mv[e] = (c0 + e <= r) ? macc[e] : 0.f;
+            }
+            P::st4(Ls + r * PC + c0, lv);
+            P::st4(Ms + r * PC + c0, mv);
+            if (I == J) {
+                // the diagonal block's inverse (I + L)^-1 at once, in registers (fp32 products,
+                // from L rounded as stored, like the block doubling's reads)
+                const f32x4 t = invert_unit_lower16<F32>(P::f32(P::cvt(lv)), g4, r16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ts[(16 * I + 4 * g4 + e) * PC + 16 * I + r16] = P::from_f32(t[e]);
             }
         }
         __syncthreads();
-        unit_lower_inverse<P, CH, PC>(Ls, Ts);
+        if constexpr (NCT >= 2) {                      // the block doubling (C = 32: one level)
+            inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
+            __syncthreads();
+        }
+        if constexpr (NCT == 4) {
+            inverse_level2<P, CH, PC>(Ls, Ts, wave, lane);
+            __syncthreads();
+        }
 
         // ---- this wave's 16 value columns (state waves)
         if (state_wave) {
