@@ -79,8 +79,8 @@ constexpr int kDVT = 64;  // value columns per tile
 // One Gram block pair (i, j), j <= i, of gram_blocks: L, A (and -N when Ns is non-null) for
 // block (i, j); the callers schedule the pairs themselves.  For a diagonal block and a
 // non-null Ts the lane's row of L is already in the MFMA A-operand layout, and the block's
-// inverse (I + L)^-1 is formed at once in registers, with fp32 products, from L rounded as
-// stored, and written to Ts.
+// inverse (I + L)^-1 is formed at once in registers, with products of about fp32 accuracy
+// (split bf16 for bf16 data), from L rounded as stored, and written to Ts.
 template <class P, int DK, int CH, int PK, int PC, bool HAS_A, bool HAS_L, int PCA = PC>
 __device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typename P::R *Ks, const float *gs,
                                           const float *bes, const float *lams, typename P::R *Ls, typename P::R *As,
@@ -119,7 +119,7 @@ __device__ __forceinline__ void gram_pair(const typename P::R *Qs, const typenam
     if (Ts && i == j) {
         // the inverse of L as stored (rounded to the element type), the matrix the block
         // doubling's off-diagonal blocks also read
-        const f32x4 t = invert_unit_lower16<F32>(P::f32(P::cvt(lv)), g4, r16);
+        const f32x4 t = invert_unit_lower16<typename AccurateInv<P>::Q>(P::f32(P::cvt(lv)), g4, r16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Ts[(16 * i + 4 * g4 + e) * PC + 16 * i + r16] = P::from_f32(t[e]);
     }

@@ -39,6 +39,26 @@ __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
 }
 
+// Products with fp32-like accuracy on the bf16 MFMA: each operand is split into a bf16
+// head and a bf16 tail (a = hi + lo to about 2^-16 relative), and a b is formed as
+// (hi_a + lo_a) hi_b + (hi_a + lo_a) lo_b, the two halves of each 16x16x32 instruction
+// carrying the head and the tail of a.  Two MFMAs per 16x16x16 product, against four
+// 16x16x4 fp32 MFMAs.
+struct Bf16Split {
+    struct F {
+        bf16x4 hi, lo;
+    };
+    __device__ __forceinline__ static F cvt(f32x4 a) {
+        F r;
+        r.hi = Bf16::cvt(a);
+        r.lo = Bf16::cvt(a - Bf16::f32(r.hi));
+        return r;
+    }
+    __device__ __forceinline__ static f32x4 mma1(f32x4 acc, F a, F b) {
+        return Bf16::mma2(Bf16::mma2(acc, a.hi, a.lo, b.hi, b.hi), a.hi, a.lo, b.lo, b.lo);
+    }
+};
+
 // Inverse T of a 16x16 unit lower triangular block I + L, stable block forward substitution:
 //   4x4 diagonal blocks inverted in registers (lanes 4j.. of a quad hold rows j),
 //   then T21 = -T22 L21 T11 twice (4 -> 8 -> 16) on MFMA.
@@ -46,8 +66,9 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // Out: T[4g + e][n] (n = l%16; the accumulator layout).  Both layouts of every partial
 // inverse are produced by multiplying in both orders, so no LDS transposes are needed.
 // Q: the products' element policy: Bf16 rounds every operand of the substitution to bf16
-// (the forward kernel), F32 keeps them in fp32 on the fp32 MFMA (the backward, whose
-// reverse scan carries the error of T from chunk to chunk).
+// (the Q-Delta forward), Bf16Split keeps about 16 bits of each operand on the bf16 MFMA
+// (the QED forward and the bf16 backward, whose reverse scan carries the error of T from
+// chunk to chunk), F32 computes in fp32 on the fp32 MFMA (fp32 inputs).
 template <class Q>
 __device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
     auto prod = [](f32x4 a, f32x4 b) { return Q::mma1(zero4(), Q::cvt(a), Q::cvt(b)); };
@@ -82,6 +103,17 @@ __device__ __forceinline__ f32x4 invert_unit_lower16(f32x4 lv, int g, int m) {
     const f32x4 X2 = prod(Lm8, B8);
     return B8 - prod(A8, X2);
 }
+
+// The accurate policy for a kernel's element type: split bf16 products for bf16 data, fp32
+// products for fp32 data.
+template <class P>
+struct AccurateInv {
+    using Q = Bf16Split;
+};
+template <>
+struct AccurateInv<F32> {
+    using Q = F32;
+};
 
 // Gram blocks of one chunk, NW waves over the lower block triangle.  Each block is
 // computed transposed (D = K_j Q_i^T gives D[c][r] = (Q K^T)[r][c], r = 16i + l%16,

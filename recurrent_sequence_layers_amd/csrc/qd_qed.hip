@@ -141,9 +141,10 @@ struct QedLayout {
     static constexpr int oQ = 0, oK = oQ + NQ, oA = oK + NQ, oAt = oA + NQ, oQt = oAt + NQ, oKh = oQt + NQ;
     static constexpr int oL = oKh + NQ, oM = oL + NCC, oT = oM + NCC, oO = oT + NCC;
     static constexpr int nR = oO + CH * PV;
-    // fp32 arrays: Gm (cumulative log decay), w . v tile, exp(Gm_C)
-    static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + CH * PW;
-    static constexpr int nF = fE + DK;
+    // fp32 arrays: Gm (cumulative log decay), w . v tile, exp(Gm_C), and the partial L and M
+    // block sums of each wave (one f32x4 per lane and matrix)
+    static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + CH * PW, fP = fE + DK;
+    static constexpr int nF = fP + (kChunkThreads / kWave) * 2 * 64 * 4;
     static constexpr int bytes = ((nR * P::kBytes + 15) / 16) * 16 + nF * 4;
     static_assert((PK * P::kBytes) % 16 == 0 && (PC * P::kBytes) % 16 == 0 && (PV * P::kBytes) % 16 == 0,
                   "row pitches keep 16-byte alignment");
@@ -167,7 +168,23 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
     constexpr int CPT = DK / TPR;
     static_assert(CPT % 4 == 0 && CPT <= 32, "staging split");
     constexpr int NPAIR = NCT * (NCT + 1) / 2;
-    static_assert(NPAIR <= 4, "one 16 x 16 block pair per wave");
+    // The key contraction of each 16 x 16 block pair is cut into units of 32 channels (one
+    // MFMA each).  With twelve units (C = 32, d_k = 128), waves 0-3 take two units each (block
+    // pairs 0 and 1) and waves 4-7 one each (pair 2), three units per SIMD; otherwise wave w
+    // takes unit w.  One wave of each pair sums the others' partial blocks: with twelve units
+    // waves 0, 2 and 5, so that the two diagonal pairs, which are inverted next, sit on
+    // different SIMDs (wave w runs on SIMD w mod 4); otherwise the pair's first wave.
+    constexpr int NU = NKT / 2, NUNITS = NPAIR * NU, NWAVE = kChunkThreads / kWave;
+    static_assert(NUNITS == 12 || NUNITS <= NWAVE, "block-pair units");
+    auto ubeg = [](int w) { return NUNITS == 12 ? (w < 4 ? 2 * w : 4 + w) : w; };
+    auto uend = [](int w) { return NUNITS == 12 ? (w < 4 ? 2 * w + 2 : 5 + w) : (w < NUNITS ? w + 1 : w); };
+    auto combiner = [](int w) {
+        return NUNITS == 12 ? (w == 0 || w == 2 || w == 5) : (w < NUNITS && w % NU == 0);
+    };
+    // threads of the per-channel decay sums: the last d_k threads (the state waves issue the
+    // next chunk's loads meanwhile, the other waves during the state-dependent part)
+    constexpr int CS0 = kChunkThreads - DK;
+    static_assert(CS0 >= kChunkThreads / 2, "the decay sums run on waves that hold no state");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
     R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
@@ -184,6 +201,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
     float *const Gs = fbase + Lay::fG;
     float *const WVs = fbase + Lay::fW;
     float *const eGC = fbase + Lay::fE;
+    f32x4 *const Part = reinterpret_cast<f32x4 *>(fbase + Lay::fP);   // [wave][L, M][lane]
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -310,11 +328,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                 }
             }
         }
-        if (n + 1 < NC) gload(n + 1);
         __syncthreads();
         // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0): the
         // column is read into registers, summed, and written back
-        for (int c = tid; c < DK; c += NT) {
+        if (state_wave && n + 1 < NC) gload(n + 1);
+        for (int c = tid - CS0; c >= 0 && c < DK; c += NT) {
             float col[CH];
 #pragma unroll
             for (int t = 0; t < CH; ++t) col[t] = Gs[t * PF + c];
@@ -342,13 +360,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             P::st4(Qts + sr * PK + sc0 + c, qt);
             P::st4(Khs + sr * PK + sc0 + c, kh);
         }
-        // ---- L and M blocks, one 16 x 16 block pair per wave, from scaled fragments
-        if (wave < NPAIR) {
-            int I, J;
-            tri_pair(wave, I, J);
+        // ---- L and M blocks, unit by unit (see ubeg / uend)
+        f32x4 lacc = zero4(), macc = zero4();
+        const int u0 = ubeg(wave), u1 = uend(wave);
+        const int pr = u0 / NU;                        // this wave's block pair
+        int I, J;
+        tri_pair(pr < NPAIR ? pr : 0, I, J);
+        if (u0 < u1) {
             const int rref = (J < I) ? 16 * I : 16 * I + 8;
             const int tr = 16 * I + r16, tc = 16 * J + r16;       // this lane's row and column token
-            f32x4 lacc = zero4(), macc = zero4();
             // scaled operands of one 16-channel step: row a and q, column k
             auto step = [&](int s, F &fa, F &fq, F &fk) {
                 const int c0 = 16 * s + 4 * g4;
@@ -371,12 +391,29 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             // formed transposed (K A^T, K Q^T): lane (g, n) gets row 16 I + n and the columns
             // 16 J + 4 g .. + 3, the MFMA A-operand layout of the block
 #pragma unroll
-            for (int s = 0; s < NKT; s += 2) {        // two steps per MFMA
-                F a0, q0, k0, a1, q1, k1;
-                step(s, a0, q0, k0);
-                step(s + 1, a1, q1, k1);
-                lacc = P::mma2(lacc, k0, k1, a0, a1);
-                macc = P::mma2(macc, k0, k1, q0, q1);
+            for (int u = 0; u < 2; ++u) {
+                if (u0 + u < u1) {
+                    const int s = 2 * ((u0 + u) % NU);      // two 16-channel steps per unit
+                    F a0, q0, k0, a1, q1, k1;
+                    step(s, a0, q0, k0);
+                    step(s + 1, a1, q1, k1);
+                    lacc = P::mma2(lacc, k0, k1, a0, a1);
+                    macc = P::mma2(macc, k0, k1, q0, q1);
+                }
+            }
+            if (!combiner(wave)) {                     // hand the partial blocks over
+                Part[(2 * wave) * 64 + lane] = lacc;
+                Part[(2 * wave + 1) * 64 + lane] = macc;
+            }
+        }
+        __syncthreads();
+        if (combiner(wave)) {
+#pragma unroll
+            for (int w2 = 0; w2 < NWAVE; ++w2) {
+                if (w2 != wave && ubeg(w2) < uend(w2) && ubeg(w2) / NU == pr) {
+                    lacc += Part[(2 * w2) * 64 + lane];
+                    macc += Part[(2 * w2 + 1) * 64 + lane];
+                }
             }
             const int r = 16 * I + r16, c0 = 16 * J + 4 * g4;
             f32x4 lv, mv;
@@ -388,9 +425,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             P::st4(Ls + r * PC + c0, lv);
             P::st4(Ms + r * PC + c0, mv);
             if (I == J) {
-                // the diagonal block's inverse (I + L)^-1 at once, in registers (fp32 products,
-                // from L rounded as stored, like the block doubling's reads)
-                const f32x4 t = invert_unit_lower16<F32>(P::f32(P::cvt(lv)), g4, r16);
+                // the diagonal block's inverse (I + L)^-1 at once, in registers (products of
+                // about fp32 accuracy, from L rounded as stored, like the block doubling's reads)
+                const f32x4 t = invert_unit_lower16<typename AccurateInv<P>::Q>(P::f32(P::cvt(lv)), g4, r16);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Ts[(16 * I + 4 * g4 + e) * PC + 16 * I + r16] = P::from_f32(t[e]);
             }
@@ -405,7 +442,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             __syncthreads();
         }
 
-        // ---- this wave's 16 value columns (state waves)
+        // ---- this wave's 16 value columns (state waves); the other waves issue the next
+        // chunk's loads meanwhile
+        if (!state_wave && n + 1 < NC) gload(n + 1);
         if (state_wave) {
             F sTf[NKT];
 #pragma unroll
