@@ -26,9 +26,11 @@
 //   the diagonal r is the first token of the row block (every factor <= 1); for a
 //   diagonal block r is its ninth token, so a factor exceeds 1 by at most eight tokens of
 //   decay.  That is the kernel's domain: exp(-(g_s + ... + g_{s+7})) must stay within the
-//   fp32 range (per-token log decays above about -11).  T = (I + L)^-1 uses the shared
-//   blocked inverse; the state-dependent part is the generic forward's, one wave per 16
-//   value columns holding S^T in MFMA accumulators.
+//   fp32 range (per-token log decays above about -11).  T = (I + L)^-1: the diagonal
+//   16 x 16 blocks inverted in registers, then the shared block doubling.  The state-
+//   dependent part runs on waves 0-3, one wave per 16 value columns holding S^T in MFMA
+//   accumulators, one chunk behind the state-independent part (a two-stage pipeline: the
+//   decayed operands, w . v and exp(Gm_C) are double-buffered in LDS).
 #include "qd_chunk_common.h"
 #include "qd_device.h"
 #include "qd_internal.h"
@@ -40,6 +42,11 @@ constexpr int kThreads = 256;
 constexpr int kChunkThreads = 512;   // chunk kernel: eight waves, four of them on the state
 constexpr int kLanesPerRow = 8;
 constexpr int kDVT = 64;
+
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the transcendental unit (results below the normal range flush to zero, as the
+// natural-base form does)
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float group8_sum(float x) {
     x += __shfl_xor(x, 1, kLanesPerRow);
@@ -137,19 +144,40 @@ struct QedLayout {
     static constexpr int PK = DK + PAD, PC = CH + PAD, PV = kDVT + PAD;
     static constexpr int PF = DK + 4, PW = kDVT + 4;     // fp32 pitches
     static constexpr int NQ = CH * PK, NCC = CH * PC;
-    // element-type arrays: q, k, a; the decayed At, Qt, Kh; L, M, T; O staging
-    static constexpr int oQ = 0, oK = oQ + NQ, oA = oK + NQ, oAt = oA + NQ, oQt = oAt + NQ, oKh = oQt + NQ;
-    static constexpr int oL = oKh + NQ, oM = oL + NCC, oT = oM + NCC, oO = oT + NCC;
+    // element-type arrays: q, k, a; the decayed At, Qt, Kh, two buffers each (the chunk being
+    // prepared and the chunk on the state); L, M, T; O staging
+    static constexpr int oQ = 0, oK = oQ + NQ, oA = oK + NQ, oAt = oA + NQ, oQt = oAt + 2 * NQ, oKh = oQt + 2 * NQ;
+    static constexpr int oL = oKh + 2 * NQ, oM = oL + NCC, oT = oM + NCC, oO = oT + NCC;
     static constexpr int nR = oO + CH * PV;
-    // fp32 arrays: Gm (cumulative log decay), w . v tile, exp(Gm_C), and the partial L and M
-    // block sums of each wave (one f32x4 per lane and matrix)
-    static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + CH * PW, fP = fE + DK;
-    static constexpr int nF = fP + (kChunkThreads / kWave) * 2 * 64 * 4;
+    // fp32 arrays: Gm (cumulative log decay, base 2); the w . v tile and exp(Gm_C), two buffers each;
+    // three slots of partial L and M blocks (one f32x4 per lane and matrix)
+    static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + 2 * CH * PW, fP = fE + 2 * DK;
+    static constexpr int nF = fP + 3 * 2 * 64 * 4;
     static constexpr int bytes = ((nR * P::kBytes + 15) / 16) * 16 + nF * 4;
     static_assert((PK * P::kBytes) % 16 == 0 && (PC * P::kBytes) % 16 == 0 && (PV * P::kBytes) % 16 == 0,
                   "row pitches keep 16-byte alignment");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
+
+// The key contraction of each 16 x 16 block pair of L and M is cut into NU units of 32
+// channels (one MFMA each), computed by waves 4-7.  C = 32 (three pairs): wave 4, 5 and 7
+// take all units but the last of pair 0, 1 and 2 and sum that pair, wave 6 takes the last
+// unit of every pair (the diagonal pairs 0 and 2 are summed and inverted on different SIMDs;
+// wave w runs on SIMD w mod 4).  C = 16 (one pair): unit k on wave 4 + k, summed by wave 4.
+template <int NPAIR>
+__device__ constexpr int qed_pair_sum_wave(int p) {
+    return NPAIR == 3 ? (p == 0 ? 4 : (p == 1 ? 5 : 7)) : 4;
+}
+template <int NPAIR, int NU>
+__device__ constexpr int qed_unit_wave(int p, int k) {
+    return NPAIR == 3 ? (k < NU - 1 ? qed_pair_sum_wave<NPAIR>(p) : 6) : 4 + k;
+}
+// partial-block slot of wave w's share of pair p (every wave that holds a share it does not
+// sum itself has one slot per pair)
+template <int NPAIR>
+__device__ constexpr int qed_part_slot(int w, int p) {
+    return NPAIR == 3 ? p : w - 5;
+}
 
 template <class P, int DK, int CH>
 __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedChunkArgs args) {
@@ -168,40 +196,26 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
     constexpr int CPT = DK / TPR;
     static_assert(CPT % 4 == 0 && CPT <= 32, "staging split");
     constexpr int NPAIR = NCT * (NCT + 1) / 2;
-    // The key contraction of each 16 x 16 block pair is cut into units of 32 channels (one
-    // MFMA each).  With twelve units (C = 32, d_k = 128), waves 0-3 take two units each (block
-    // pairs 0 and 1) and waves 4-7 one each (pair 2), three units per SIMD; otherwise wave w
-    // takes unit w.  One wave of each pair sums the others' partial blocks: with twelve units
-    // waves 0, 2 and 5, so that the two diagonal pairs, which are inverted next, sit on
-    // different SIMDs (wave w runs on SIMD w mod 4); otherwise the pair's first wave.
-    constexpr int NU = NKT / 2, NUNITS = NPAIR * NU, NWAVE = kChunkThreads / kWave;
-    static_assert(NUNITS == 12 || NUNITS <= NWAVE, "block-pair units");
-    auto ubeg = [](int w) { return NUNITS == 12 ? (w < 4 ? 2 * w : 4 + w) : w; };
-    auto uend = [](int w) { return NUNITS == 12 ? (w < 4 ? 2 * w + 2 : 5 + w) : (w < NUNITS ? w + 1 : w); };
-    auto combiner = [](int w) {
-        return NUNITS == 12 ? (w == 0 || w == 2 || w == 5) : (w < NUNITS && w % NU == 0);
-    };
-    // threads of the per-channel decay sums: the last d_k threads (the state waves issue the
-    // next chunk's loads meanwhile, the other waves during the state-dependent part)
-    constexpr int CS0 = kChunkThreads - DK;
-    static_assert(CS0 >= kChunkThreads / 2, "the decay sums run on waves that hold no state");
+    constexpr int NU = NKT / 2;                    // 32-channel units per block pair
+    static_assert((NPAIR == 1 || NPAIR == 3) && NU >= 2 && NU <= 4, "C = 16 or 32, d_k = 64 or 128");
+    static_assert(2 * DK <= kChunkThreads / 2, "the decay sums run on the state waves");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
     R *const Qs = reinterpret_cast<R *>(smem) + Lay::oQ;
     R *const Ks = reinterpret_cast<R *>(smem) + Lay::oK;
     R *const As = reinterpret_cast<R *>(smem) + Lay::oA;
-    R *const Ats = reinterpret_cast<R *>(smem) + Lay::oAt;
-    R *const Qts = reinterpret_cast<R *>(smem) + Lay::oQt;
-    R *const Khs = reinterpret_cast<R *>(smem) + Lay::oKh;
+    R *const Ats0 = reinterpret_cast<R *>(smem) + Lay::oAt;   // [2][CH][PK]
+    R *const Qts0 = reinterpret_cast<R *>(smem) + Lay::oQt;
+    R *const Khs0 = reinterpret_cast<R *>(smem) + Lay::oKh;
     R *const Ls = reinterpret_cast<R *>(smem) + Lay::oL;
     R *const Ms = reinterpret_cast<R *>(smem) + Lay::oM;
     R *const Ts = reinterpret_cast<R *>(smem) + Lay::oT;
     R *const Os = reinterpret_cast<R *>(smem) + Lay::oO;
     float *const fbase = reinterpret_cast<float *>(smem + ((Lay::nR * P::kBytes + 15) / 16) * 16);
     float *const Gs = fbase + Lay::fG;
-    float *const WVs = fbase + Lay::fW;
-    float *const eGC = fbase + Lay::fE;
-    f32x4 *const Part = reinterpret_cast<f32x4 *>(fbase + Lay::fP);   // [wave][L, M][lane]
+    float *const WVs0 = fbase + Lay::fW;          // [2][CH][PW]
+    float *const eGC0 = fbase + Lay::fE;          // [2][DK]
+    f32x4 *const Part = reinterpret_cast<f32x4 *>(fbase + Lay::fP);   // [slot][L, M][lane]
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -230,32 +244,37 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
         sT[t] = (state_wave && args.S0) ? *reinterpret_cast<const f32x4 *>(args.S0 + srow + 16 * t + 4 * g4) : zero4();
+    // settle the entry state here: inside the chunk loop the state registers are written by
+    // MFMAs only, and the first product of each step should not wait for the memory counter
+    // (which by then also counts the previous step's output stores)
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) asm volatile("" : : "v"(sT[t]));
 
-    // staging thread -> (row sr, key columns [sc0, sc0 + CPT)); the next chunk's raw rows are
+    // staging thread -> (row sr, key columns sc0 + 4 TPR j + [0, 4), j < CPT / 4): the TPR
+    // threads of a row read each 4-column group of q, k, g and b as one contiguous run, so a
+    // load instruction touches no cache line it does not fill.  The next chunk's raw rows are
     // loaded into registers while the current chunk computes (rows past the end are clamped
-    // to the last valid row when loaded and zeroed when staged)
-    const int sr = tid / TPR, sc0 = (tid % TPR) * CPT;
+    // to the last valid row when loaded and zeroed when staged).
+    const int sr = tid / TPR, sc0 = (tid % TPR) * 4;
     const bool stager = sr < CH;
-    constexpr int QV = CPT / EPV;                  // 16-byte vectors of q or k per staging thread
-    constexpr int GV = CPT / 4;                    // float4 of g or b per staging thread
+    constexpr int GV = CPT / 4;                    // 4-column groups per staging thread
+    auto scol = [&](int j) { return sc0 + 4 * TPR * j; };
     constexpr int NVV = (CH * VPRV + NT - 1) / NT;               // v vectors per thread
     constexpr int WPV = EPV / 4;                   // float4 of w per v vector
-    uint4 rq[QV], rk[QV], rv[NVV];
+    F rq[GV], rk[GV];
+    uint4 rv[NVV];
     f32x4 rg[GV], rb[GV], rw[NVV][WPV];
     auto gload = [&](int n) {
         const int t0 = n * CH;
         const int last = min(CH, T - t0) - 1;
         if (stager) {
-            const size_t base = tok(t0 + min(sr, last)) * DK + sc0;
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                rq[j] = *reinterpret_cast<const uint4 *>(gq + base + j * EPV);
-                rk[j] = *reinterpret_cast<const uint4 *>(gk + base + j * EPV);
-            }
+            const size_t base = tok(t0 + min(sr, last)) * DK;
 #pragma unroll
             for (int j = 0; j < GV; ++j) {
-                rg[j] = *reinterpret_cast<const f32x4 *>(args.g + base + 4 * j);
-                rb[j] = *reinterpret_cast<const f32x4 *>(args.b + base + 4 * j);
+                rq[j] = P::ld4(gq + base + scol(j));
+                rk[j] = P::ld4(gk + base + scol(j));
+                rg[j] = *reinterpret_cast<const f32x4 *>(args.g + base + scol(j));
+                rb[j] = *reinterpret_cast<const f32x4 *>(args.b + base + scol(j));
             }
         }
 #pragma unroll
@@ -270,24 +289,39 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
         }
     };
 
+    // Two-stage pipeline over the chunks: step n prepares chunk n (everything that does not
+    // depend on the state) while the state waves run the state-dependent part of chunk n - 1
+    // from the buffers chunk n - 1 was prepared into.  Per step, with a barrier after each:
+    //   P0  stage chunk n (all waves)
+    //   P1  per-channel decay sums (state waves); waves 4-7 load chunk n + 1
+    //   P2  decayed operands (all waves), L and M units (waves 4-7) | state part of chunk n - 1
+    //   P3  L and M summed, masked, stored, diagonal blocks inverted | chunk n + 1 loaded and
+    //       chunk n - 1's output stored (state waves)
+    //   P4  block doubling (C = 32)
     const int NC = (T + CH - 1) / CH;
     if (NC > 0) gload(0);
-    for (int n = 0; n < NC; ++n) {
+    for (int n = 0; n <= NC; ++n) {
+        const bool prep = n < NC;
+        const int buf = n & 1;
+        R *const Ats = Ats0 + buf * Lay::NQ;
+        R *const Qts = Qts0 + buf * Lay::NQ;
+        R *const Khs = Khs0 + buf * Lay::NQ;
+        float *const WVs = WVs0 + buf * CH * PW;
+        float *const eGC = eGC0 + buf * DK;
         const int t0 = n * CH;
         const int clen = min(CH, T - t0);
         const bool ok = sr < clen;   // (false for the threads that stage nothing)
 
-        // ---- stage: q, k, a = b.k + lambda (b.q - k (k . b.q)), raw g; w . v tile
+        // ---- P0: stage q, k, a = b.k + lambda (b.q - k (k . b.q)), raw g; w . v tile
         float qf[CPT], kf[CPT], af[CPT];
-        {
+        if (prep) {
 #pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                const R *eq = reinterpret_cast<const R *>(&rq[j]);
-                const R *ek = reinterpret_cast<const R *>(&rk[j]);
+            for (int j = 0; j < GV; ++j) {
+                const f32x4 q4 = P::f32(rq[j]), k4 = P::f32(rk[j]);
 #pragma unroll
-                for (int u = 0; u < EPV; ++u) {
-                    qf[j * EPV + u] = ok ? P::to_f32(eq[u]) : 0.f;
-                    kf[j * EPV + u] = ok ? P::to_f32(ek[u]) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    qf[4 * j + i] = ok ? q4[i] : 0.f;
+                    kf[4 * j + i] = ok ? k4[i] : 0.f;
                 }
             }
             float ku = 0.f;
@@ -299,17 +333,23 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
 #pragma unroll
             for (int c = 0; c < CPT; ++c) af[c] = rb[c / 4][c % 4] * kf[c] + lam * af[c];
             // the TPR threads of a row are consecutive lanes of one wave
+            if constexpr (TPR == 16) {
+                ku = sum16(ku);
+            } else {
 #pragma unroll
-            for (int off = 1; off < TPR; off <<= 1) ku += __shfl_xor(ku, off, TPR);
+                for (int off = 1; off < TPR; off <<= 1) ku += __shfl_xor(ku, off, TPR);
+            }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) af[c] -= lam * ku * kf[c];
             if (stager) {
 #pragma unroll
-                for (int c = 0; c < CPT; c += 4) {
-                    P::st4(Qs + sr * PK + sc0 + c, f32x4{qf[c], qf[c + 1], qf[c + 2], qf[c + 3]});
-                    P::st4(Ks + sr * PK + sc0 + c, f32x4{kf[c], kf[c + 1], kf[c + 2], kf[c + 3]});
-                    P::st4(As + sr * PK + sc0 + c, f32x4{af[c], af[c + 1], af[c + 2], af[c + 3]});
-                    *reinterpret_cast<f32x4 *>(Gs + sr * PF + sc0 + c) = ok ? rg[c / 4] : zero4();
+                for (int j = 0; j < GV; ++j) {
+                    const int c = 4 * j;
+                    P::st4(Qs + sr * PK + scol(j), f32x4{qf[c], qf[c + 1], qf[c + 2], qf[c + 3]});
+                    P::st4(Ks + sr * PK + scol(j), f32x4{kf[c], kf[c + 1], kf[c + 2], kf[c + 3]});
+                    P::st4(As + sr * PK + scol(j), f32x4{af[c], af[c + 1], af[c + 2], af[c + 3]});
+                    // log decays in base 2 (g log2 e): every decay factor below is one exp2
+                    *reinterpret_cast<f32x4 *>(Gs + sr * PF + scol(j)) = ok ? rg[j] * kLog2e : zero4();
                 }
             }
 #pragma unroll
@@ -327,125 +367,37 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                     }
                 }
             }
-        }
-        __syncthreads();
-        // ---- Gm = per-channel cumulative sum of g over the chunk (padding rows add 0): the
-        // column is read into registers, summed, and written back
-        if (state_wave && n + 1 < NC) gload(n + 1);
-        for (int c = tid - CS0; c >= 0 && c < DK; c += NT) {
-            float col[CH];
-#pragma unroll
-            for (int t = 0; t < CH; ++t) col[t] = Gs[t * PF + c];
-#pragma unroll
-            for (int t = 1; t < CH; ++t) col[t] += col[t - 1];
-#pragma unroll
-            for (int t = 0; t < CH; ++t) Gs[t * PF + c] = col[t];
-            eGC[c] = __expf(col[CH - 1]);
-        }
-        __syncthreads();
-        // ---- decayed operands: At = a . exp(Gm_t), Qt = q . exp(Gm_t), Kh = k . exp(Gm_C - Gm_t)
-#pragma unroll
-        for (int c = 0; c < (stager ? CPT : 0); c += 4) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gs + sr * PF + sc0 + c);
-            const f32x4 gC = *reinterpret_cast<const f32x4 *>(Gs + (CH - 1) * PF + sc0 + c);
-            f32x4 at, qt, kh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = __expf(gm[i]);
-                at[i] = af[c + i] * e;
-                qt[i] = qf[c + i] * e;
-                kh[i] = kf[c + i] * __expf(gC[i] - gm[i]);
-            }
-            P::st4(Ats + sr * PK + sc0 + c, at);
-            P::st4(Qts + sr * PK + sc0 + c, qt);
-            P::st4(Khs + sr * PK + sc0 + c, kh);
-        }
-        // ---- L and M blocks, unit by unit (see ubeg / uend)
-        f32x4 lacc = zero4(), macc = zero4();
-        const int u0 = ubeg(wave), u1 = uend(wave);
-        const int pr = u0 / NU;                        // this wave's block pair
-        int I, J;
-        tri_pair(pr < NPAIR ? pr : 0, I, J);
-        if (u0 < u1) {
-            const int rref = (J < I) ? 16 * I : 16 * I + 8;
-            const int tr = 16 * I + r16, tc = 16 * J + r16;       // this lane's row and column token
-            // scaled operands of one 16-channel step: row a and q, column k
-            auto step = [&](int s, F &fa, F &fq, F &fk) {
-                const int c0 = 16 * s + 4 * g4;
-                const f32x4 gr = *reinterpret_cast<const f32x4 *>(Gs + rref * PF + c0);
-                const f32x4 gt = *reinterpret_cast<const f32x4 *>(Gs + tr * PF + c0);
-                const f32x4 gj = *reinterpret_cast<const f32x4 *>(Gs + tc * PF + c0);
-                const f32x4 xa = P::f32(P::ld4(As + tr * PK + c0));
-                const f32x4 xq = P::f32(P::ld4(Qs + tr * PK + c0));
-                const f32x4 xk = P::f32(P::ld4(Ks + tc * PK + c0));
-                f32x4 ea, ek;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ea[i] = __expf(gt[i] - gr[i]);
-                    ek[i] = __expf(gr[i] - gj[i]);
-                }
-                fa = P::cvt(xa * ea);
-                fq = P::cvt(xq * ea);
-                fk = P::cvt(xk * ek);
-            };
-            // formed transposed (K A^T, K Q^T): lane (g, n) gets row 16 I + n and the columns
-            // 16 J + 4 g .. + 3, the MFMA A-operand layout of the block
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (u0 + u < u1) {
-                    const int s = 2 * ((u0 + u) % NU);      // two 16-channel steps per unit
-                    F a0, q0, k0, a1, q1, k1;
-                    step(s, a0, q0, k0);
-                    step(s + 1, a1, q1, k1);
-                    lacc = P::mma2(lacc, k0, k1, a0, a1);
-                    macc = P::mma2(macc, k0, k1, q0, q1);
-                }
-            }
-            if (!combiner(wave)) {                     // hand the partial blocks over
-                Part[(2 * wave) * 64 + lane] = lacc;
-                Part[(2 * wave + 1) * 64 + lane] = macc;
-            }
-        }
-        __syncthreads();
-        if (combiner(wave)) {
-#pragma unroll
-            for (int w2 = 0; w2 < NWAVE; ++w2) {
-                if (w2 != wave && ubeg(w2) < uend(w2) && ubeg(w2) / NU == pr) {
-                    lacc += Part[(2 * w2) * 64 + lane];
-                    macc += Part[(2 * w2 + 1) * 64 + lane];
-                }
-            }
-            const int r = 16 * I + r16, c0 = 16 * J + 4 * g4;
-            f32x4 lv, mv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lv[e] = (c0 + e < r) ? lacc[e] : 0.f;
-                mv[e] = (c0 + e <= r) ? macc[e] : 0.f;
-            }
-            P::st4(Ls + r * PC + c0, lv);
-            P::st4(Ms + r * PC + c0, mv);
-            if (I == J) {
-                // the diagonal block's inverse (I + L)^-1 at once, in registers (products of
-                // about fp32 accuracy, from L rounded as stored, like the block doubling's reads)
-                const f32x4 t = invert_unit_lower16<typename AccurateInv<P>::Q>(P::f32(P::cvt(lv)), g4, r16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Ts[(16 * I + 4 * g4 + e) * PC + 16 * I + r16] = P::from_f32(t[e]);
-            }
-        }
-        __syncthreads();
-        if constexpr (NCT >= 2) {                      // the block doubling (C = 32: one level)
-            inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
             __syncthreads();
-        }
-        if constexpr (NCT == 4) {
-            inverse_level2<P, CH, PC>(Ls, Ts, wave, lane);
+            // ---- P1: Gm = per-channel cumulative sum of g over the chunk (padding rows add 0).
+            // Lanes l and l + 32 of a state wave take the two halves of channel 32 w + l % 32:
+            // each sums its half in registers, the second adds the first's total.
+            if (!state_wave && n + 1 < NC) gload(n + 1);
+            if (tid < 2 * DK) {
+                constexpr int HC = CH / 2;
+                const int c = 32 * (tid >> 6) + (lane & 31), h = lane >> 5;
+                float col[HC];
+#pragma unroll
+                for (int t = 0; t < HC; ++t) col[t] = Gs[(HC * h + t) * PF + c];
+#pragma unroll
+                for (int t = 1; t < HC; ++t) col[t] += col[t - 1];
+                const float first = __shfl_xor(col[HC - 1], 32);
+                const float add = h ? first : 0.f;
+#pragma unroll
+                for (int t = 0; t < HC; ++t) Gs[(HC * h + t) * PF + c] = col[t] + add;
+                if (h) eGC[c] = exp2f_fast(col[HC - 1] + add);
+            }
             __syncthreads();
         }
 
-        // ---- this wave's 16 value columns (state waves); the other waves issue the next
-        // chunk's loads meanwhile
-        if (!state_wave && n + 1 < NC) gload(n + 1);
-        if (state_wave) {
+        // ---- P2, state waves: the state-dependent part of chunk n - 1 (this wave's 16 value
+        // columns)
+        if (state_wave && n > 0) {
+            const int pb = buf ^ 1;
+            const R *const pAt = Ats0 + pb * Lay::NQ;
+            const R *const pQt = Qts0 + pb * Lay::NQ;
+            const R *const pKh = Khs0 + pb * Lay::NQ;
+            const float *const pWV = WVs0 + pb * CH * PW;
+            const float *const peGC = eGC0 + pb * DK;
             F sTf[NKT];
 #pragma unroll
             for (int t = 0; t < NKT; ++t) sTf[t] = P::cvt(sT[t]);
@@ -455,11 +407,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                 f32x4 y = zero4();
 #pragma unroll
                 for (int t = 0; t < NKT; t += 2)
-                    y = P::mma2(y, frag<P>(Ats, PK, 16 * mt, 16 * t), frag<P>(Ats, PK, 16 * mt, 16 * t + 16), sTf[t],
+                    y = P::mma2(y, frag<P>(pAt, PK, 16 * mt, 16 * t), frag<P>(pAt, PK, 16 * mt, 16 * t + 16), sTf[t],
                                 sTf[t + 1]);
                 f32x4 wv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) wv[e] = WVs[(16 * mt + 4 * g4 + e) * PW + 16 * wave + r16];
+                for (int e = 0; e < 4; ++e) wv[e] = pWV[(16 * mt + 4 * g4 + e) * PW + 16 * wave + r16];
                 Ef[mt] = P::cvt(wv - y);
             }
             f32x4 Rr[NCT];
@@ -483,7 +435,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                 O[mt] = zero4();
 #pragma unroll
                 for (int t = 0; t < NKT; t += 2)
-                    O[mt] = P::mma2(O[mt], frag<P>(Qts, PK, 16 * mt, 16 * t), frag<P>(Qts, PK, 16 * mt, 16 * t + 16),
+                    O[mt] = P::mma2(O[mt], frag<P>(pQt, PK, 16 * mt, 16 * t), frag<P>(pQt, PK, 16 * mt, 16 * t + 16),
                                     sTf[t], sTf[t + 1]);
 #pragma unroll
                 for (int s = 0; s <= mt; s += 2) {
@@ -497,14 +449,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
             // S^T <- diag(exp Gm_C) S^T + Kh^T R
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
-                f32x4 acc = lds_f32x4(eGC + 16 * t + 4 * g4) * sT[t];
+                f32x4 acc = lds_f32x4(peGC + 16 * t + 4 * g4) * sT[t];
 #pragma unroll
                 for (int s = 0; s < NCT; s += 2) {
                     if (s + 1 < NCT)
-                        acc = P::mma2(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), frag_b<P>(Khs, PK, 16 * s + 16, 16 * t), Rf[s],
+                        acc = P::mma2(acc, frag_b<P>(pKh, PK, 16 * s, 16 * t), frag_b<P>(pKh, PK, 16 * s + 16, 16 * t), Rf[s],
                                       Rf[s + 1]);
                     else
-                        acc = P::mma1(acc, frag_b<P>(Khs, PK, 16 * s, 16 * t), Rf[s]);
+                        acc = P::mma1(acc, frag_b<P>(pKh, PK, 16 * s, 16 * t), Rf[s]);
                 }
                 sT[t] = acc;
             }
@@ -515,14 +467,145 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
                 for (int e = 0; e < 4; ++e) Os[(16 * mt + 4 * g4 + e) * PV + 16 * wave + r16] = P::from_f32(O[mt][e]);
             }
         }
-        __syncthreads();
-        for (int vi = tid; vi < CH * VPRV; vi += NT) {
-            const int c = vi / VPRV, cv = vi % VPRV;
-            if (c < clen)
-                *reinterpret_cast<uint4 *>(go + tok(t0 + c) * dv + dv0 + cv * EPV) =
-                    *reinterpret_cast<const uint4 *>(Os + c * PV + cv * EPV);
+        // ---- P2, chunk n: decayed operands At = a . exp(Gm_t), Qt = q . exp(Gm_t),
+        // Kh = k . exp(Gm_C - Gm_t); the L and M units
+        f32x4 lacc[NPAIR], macc[NPAIR];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) lacc[p] = macc[p] = zero4();
+        if (prep) {
+#pragma unroll
+            for (int j = 0; j < (stager ? GV : 0); ++j) {
+                const int c = 4 * j;
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gs + sr * PF + scol(j));
+                const f32x4 gC = *reinterpret_cast<const f32x4 *>(Gs + (CH - 1) * PF + scol(j));
+                f32x4 at, qt, kh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp2f_fast(gm[i]);
+                    at[i] = af[c + i] * e;
+                    qt[i] = qf[c + i] * e;
+                    kh[i] = kf[c + i] * exp2f_fast(gC[i] - gm[i]);
+                }
+                P::st4(Ats + sr * PK + scol(j), at);
+                P::st4(Qts + sr * PK + scol(j), qt);
+                P::st4(Khs + sr * PK + scol(j), kh);
+            }
+            if (!state_wave) {
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    int I, J;
+                    tri_pair(p, I, J);
+                    const int rref = (J < I) ? 16 * I : 16 * I + 8;
+                    const int tr = 16 * I + r16, tc = 16 * J + r16;   // this lane's row and column token
+                    // scaled operands of one 16-channel step: row a and q, column k
+                    auto step = [&](int st, F &fa, F &fq, F &fk) {
+                        const int c0 = 16 * st + 4 * g4;
+                        const f32x4 gr = *reinterpret_cast<const f32x4 *>(Gs + rref * PF + c0);
+                        const f32x4 gt = *reinterpret_cast<const f32x4 *>(Gs + tr * PF + c0);
+                        const f32x4 gj = *reinterpret_cast<const f32x4 *>(Gs + tc * PF + c0);
+                        const f32x4 xa = P::f32(P::ld4(As + tr * PK + c0));
+                        const f32x4 xq = P::f32(P::ld4(Qs + tr * PK + c0));
+                        const f32x4 xk = P::f32(P::ld4(Ks + tc * PK + c0));
+                        f32x4 ea, ek;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            ea[i] = exp2f_fast(gt[i] - gr[i]);
+                            ek[i] = exp2f_fast(gr[i] - gj[i]);
+                        }
+                        fa = P::cvt(xa * ea);
+                        fq = P::cvt(xq * ea);
+                        fk = P::cvt(xk * ek);
+                    };
+                    // formed transposed (K A^T, K Q^T): lane (g, n) gets row 16 I + n and the
+                    // columns 16 J + 4 g .. + 3, the MFMA A-operand layout of the block
+#pragma unroll
+                    for (int k = 0; k < NU; ++k) {
+                        if (qed_unit_wave<NPAIR, NU>(p, k) == wave) {
+                            F a0, q0, k0, a1, q1, k1;
+                            step(2 * k, a0, q0, k0);
+                            step(2 * k + 1, a1, q1, k1);
+                            lacc[p] = P::mma2(lacc[p], k0, k1, a0, a1);
+                            macc[p] = P::mma2(macc[p], k0, k1, q0, q1);
+                        }
+                    }
+                }
+                // hand over the shares this wave does not sum itself
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    bool mine = false;
+#pragma unroll
+                    for (int k = 0; k < NU; ++k) mine = mine || qed_unit_wave<NPAIR, NU>(p, k) == wave;
+                    if (mine && wave != qed_pair_sum_wave<NPAIR>(p)) {
+                        const int sl = qed_part_slot<NPAIR>(wave, p);
+                        Part[(2 * sl) * 64 + lane] = lacc[p];
+                        Part[(2 * sl + 1) * 64 + lane] = macc[p];
+                    }
+                }
+            }
         }
-        __syncthreads();   // the next chunk's staging rewrites every buffer read above
+        __syncthreads();
+
+        // ---- P3: L and M summed, masked and stored, diagonal blocks inverted | output of
+        // chunk n - 1, loads of chunk n + 1
+        if (prep && !state_wave) {
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) {
+                if (wave == qed_pair_sum_wave<NPAIR>(p)) {
+                    f32x4 lsum = lacc[p], msum = macc[p];
+#pragma unroll
+                    for (int k = 0; k < NU; ++k) {
+                        const int w2 = qed_unit_wave<NPAIR, NU>(p, k);
+                        bool first = true;                 // count each other wave once
+#pragma unroll
+                        for (int k2 = 0; k2 < k; ++k2) first = first && qed_unit_wave<NPAIR, NU>(p, k2) != w2;
+                        if (w2 != wave && first) {
+                            const int sl = qed_part_slot<NPAIR>(w2, p);
+                            lsum += Part[(2 * sl) * 64 + lane];
+                            msum += Part[(2 * sl + 1) * 64 + lane];
+                        }
+                    }
+                    int I, J;
+                    tri_pair(p, I, J);
+                    const int r = 16 * I + r16, c0 = 16 * J + 4 * g4;
+                    f32x4 lv, mv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lv[e] = (c0 + e < r) ? lsum[e] : 0.f;
+                        mv[e] = (c0 + e <= r) ? msum[e] : 0.f;
+                    }
+                    P::st4(Ls + r * PC + c0, lv);
+                    P::st4(Ms + r * PC + c0, mv);
+                    if (I == J) {
+                        // the diagonal block's inverse (I + L)^-1 at once, in registers (products
+                        // of about fp32 accuracy, from L rounded as stored, like the block
+                        // doubling's reads)
+                        const f32x4 t = invert_unit_lower16<typename AccurateInv<P>::Q>(P::f32(P::cvt(lv)), g4, r16);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Ts[(16 * I + 4 * g4 + e) * PC + 16 * I + r16] = P::from_f32(t[e]);
+                    }
+                }
+            }
+        }
+        if (state_wave) {
+            if (prep && n + 1 < NC) gload(n + 1);
+            if (n > 0) {
+                const int pt0 = t0 - CH, plen = min(CH, T - pt0);
+                for (int vi = tid; vi < CH * VPRV; vi += kChunkThreads / 2) {
+                    const int c = vi / VPRV, cv = vi % VPRV;
+                    if (c < plen)
+                        *reinterpret_cast<uint4 *>(go + tok(pt0 + c) * dv + dv0 + cv * EPV) =
+                            *reinterpret_cast<const uint4 *>(Os + c * PV + cv * EPV);
+                }
+            }
+        }
+        if (prep) {
+            __syncthreads();
+            // ---- P4: the block doubling (C = 32: one level)
+            if constexpr (NCT >= 2) {
+                inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
+                __syncthreads();
+            }
+        }
     }
     if (state_wave && args.S_T) {
 #pragma unroll
