@@ -68,10 +68,14 @@ constexpr int kDVT = 64;  // value columns per tile
 //                                                    registers, and one of (1,0), (3,2),
 //                                                    (2,0), (2,1)
 //   I2        dS^T update                            waves 6, 7: Gram blocks (3,0), (3,1)
-//   I3        dV staged in LDS                       T, level 1 (waves 4, 5); M1 of the
-//                                                    diagonal blocks (waves 6, 7)
-//   I4        stage chunk n - 2                      T, level 2
-//   I5        dV stores; store dS' of chunk n - 1    M1 = T_g diag(beta) below the diagonal
+//   I3        dV staged in LDS; store half of dS'    T, level 1 (waves 4, 5); M1 of the
+//             (the gradient with respect to chunk    diagonal blocks (waves 6, 7)
+//             n - 1's exit state)
+//   I4        stage chunk n - 2; store the other     T, level 2
+//             half of dS'
+//   I5        dV stores                              M1 = T_g diag(beta) below the diagonal
+// (the stores of dS' are spread over the intervals in which the scan has little to do: the
+// vector-memory path takes longer to accept them than the interval's other work)
 // At C = 16 and 32 the prep forms every Gram block in I1, the diagonal blocks of T in I2
 // and all of M1 in I5.  q, k, dO, A and the gates are double-buffered by chunk parity; M1
 // is read by the scan in I1 and rewritten by the prep in I3 and I5; L and T belong to the
@@ -300,6 +304,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
 
+    // scan: the gradient with respect to chunk m's exit state (dS'^T, final after I2), key
+    // tiles [t_lo, t_hi)
+    auto store_dh = [&](int m, int t_lo, int t_hi) {
+        const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+        R *dh = static_cast<R *>(args.dHs) + (static_cast<size_t>(bh) * NC + m) * dv * DK +
+                static_cast<size_t>(dv0 + 16 * rw + r16) * DK + 4 * g4;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+            if (t >= t_lo && t < t_hi) P::st4(dh + 16 * t, sT[t]);
+    };
     // step n: the scan on chunk n (n < NC), the prep on chunk c = n - 1 (c >= 0)
     for (int n = NC; n >= 0; --n) {
         const int c = n - 1;
@@ -464,6 +478,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Vst[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = P::from_f32(dR[mt][e]);
             }
+            if (c >= 0) store_dh(c, 0, NKT / 2);
         } else if (c >= 0) {
             inverse_level1<P, CH, PC>(Ls, Ts, rw, lane);
             if constexpr (NCT == 4) {                  // M1 of the diagonal blocks, final since I2
@@ -475,6 +490,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
         // ============================================================ I4
         if (is_scan) {
             if (n - 2 >= 0) lstore(n - 2, pf);     // slot n & 1, which the scan no longer reads
+            if (c >= 0) store_dh(c, NKT / 2, NKT);
         } else if (c >= 0) {
             inverse_level2<P, CH, PC>(Ls, Ts, rw, lane);
         }
@@ -491,12 +507,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
                             *reinterpret_cast<const uint4 *>(Vst + cr * PV + cv * EPV);
                 }
             }
-            if (c >= 0) {   // gradient with respect to chunk c's exit state
-                R *dh = static_cast<R *>(args.dHs) + (static_cast<size_t>(bh) * NC + c) * dv * DK +
-                        static_cast<size_t>(dv0 + 16 * rw + r16) * DK + 4 * g4;
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) P::st4(dh + 16 * t, sT[t]);
-            }
+
         } else if (c >= 0) {
             // M1 = (H o T) diag(beta) = T_g diag(beta) (lower block triangle)
             if constexpr (NCT == 4) {                  // the six blocks below the diagonal
