@@ -733,9 +733,10 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                                                            Ns, nullptr);
             }
         }
-        __syncthreads();
         // this wave's 16 rows of S and dS', as B operands in octet order (one 16-byte load
-        // per lane and 32 keys; the key fragments they meet are read in the same order)
+        // per lane and 32 keys; the key fragments they meet are read in the same order),
+        // issued as each wave finishes its Gram blocks (the waves finish at different times,
+        // so the loads reach the vector-memory path spread out)
         F sTf[NKT], dsTf[NKT];
 #pragma unroll
         for (int t = 0; t < NKT; t += 2) {
@@ -743,6 +744,7 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             P::ld8(hs + off, sTf[t], sTf[t + 1]);
             P::ld8(dhs + off, dsTf[t], dsTf[t + 1]);
         }
+        __syncthreads();
         // the two block-doubling levels of the inverse (the diagonal blocks are done)
         if constexpr (NCT >= 2) {
             inverse_level1<P, CH, PC>(Ls, Ts, wave, lane);
