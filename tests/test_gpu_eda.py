@@ -42,19 +42,17 @@ def test_eda_chunk_parity(qd, dtype, B, T, H, dk, dv, C, state):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
-def test_eda_chunk_full_size_sampled(qd):
+def test_eda_chunk_full_size(qd):
+    """B8 T4096 H16 d128 C64 bf16, every (b, h) slice against the oracle."""
     print("[eda] chunk full size B8 T4096 H16 d128 C64 bf16", flush=True)
     q, k, v, e, S0 = inputs.eda_inputs(8, 4096, 16, 128, 128, "bf16", seed=9)
     o, S = qd.qdelta_eda_chunk_fwd(dev(q), dev(k), dev(v), dev(e), None, C=64)
     torch.cuda.synchronize()
     o, S = o.float().cpu().numpy(), S.cpu().numpy()
-    for b, h in [(0, 0), (5, 11), (7, 15)]:
-        s = lambda t: t[b:b + 1, :, h:h + 1]
-        ro, rS = oracle.eda_fwd(s(q), s(k), s(v), s(e), None)
-        eo = slice_err(o[b:b + 1, :, h:h + 1], ro, (1, 3))
-        es = slice_err(S[b:b + 1, h:h + 1], rS, (2, 3))
-        print(f"  (b={b}, h={h}) o={eo:.2e} S_T={es:.2e}", flush=True)
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    ro, rS = oracle.eda_fwd(q, k, v, e, None)
+    eo, es = slice_err(o, ro, (1, 3)), slice_err(S, rS, (2, 3))
+    print(f"  max rel err o={eo:.2e} S_T={es:.2e} (bar {TOL['bf16']:g})", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 128, 128), ("f32", 64, 128), ("bf16", 128, 128), ("bf16", 64, 64)])
