@@ -28,13 +28,14 @@
 //   I1        fetch q, v of chunk n + 2; Y from the  the wave's diagonal Gram block on MFMA,
 //             S^T products formed a step ahead;      A and L_g written, its 16x16 block of
 //             Z, O (O staged in LDS)                 T_g inverted in registers
-//   I2        stage q, v of chunk n + 2 (chunk n's   M1 of the diagonal blocks; the six
+//   I2        stage q, v of chunk n + 2 (chunk n's   M1 of the diagonal blocks; four
 //             V was last read in I1, its Q a step    off-diagonal Gram blocks
 //             earlier); fetch k of chunk n + 2;
 //             S^T update over the first half of
 //             the keys, then K S^T and Q S^T of
 //             chunk n + 1 over those keys
-//   I3        the same over the second half          block doubling, level 1 (waves 6, 7)
+//   I3        the same over the second half          the last two Gram blocks (waves 4,
+//                                                    5); block doubling, level 1 (6, 7)
 //   I4        stage k and the gate tables of chunk   block doubling, level 2 (C = 64)
 //             n + 2 (each scan wave writes part of
 //             the tables); store O
@@ -181,10 +182,11 @@ struct PipeLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
-// Gram blocks (i, j), j <= i, of prep wave P in interval PH (1 or 2).  In I1 wave P owns
-// diagonal block P (listed first; it is inverted right after its Gram products) and the
-// blocks level 1 of the block doubling reads in I2; the blocks only level 2 reads (I3)
-// are formed in I2.
+// Gram blocks (i, j), j <= i, of prep wave P in interval PH (1, 2 or 3).  C = 64: in I1 each
+// wave forms its diagonal block (inverted right after its Gram products); in I2 the blocks
+// (1,0) and (3,2) that level 1 of the block doubling reads in I3, and (2,0), (2,1); in I3
+// (waves 4, 5, beside level 1 on waves 6, 7) the last two, (3,0) and (3,1), which only
+// level 2 reads (I4).  C = 32: everything in I1.
 template <int NCT, int P, int PH>
 struct GramPlan { static constexpr int n = 0; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
 template <> struct GramPlan<4, 0, 1> { static constexpr int n = 1; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
