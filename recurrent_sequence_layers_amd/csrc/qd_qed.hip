@@ -149,8 +149,8 @@ struct QedLayout {
     static constexpr int oQ = 0, oK = oQ + NQ, oA = oK + NQ, oAt = oA + NQ, oQt = oAt + 2 * NQ, oKh = oQt + 2 * NQ;
     static constexpr int oL = oKh + 2 * NQ, oM = oL + NCC, oT = oM + NCC, oO = oT + NCC;
     static constexpr int nR = oO + CH * PV;
-    // fp32 arrays: Gm (cumulative log decay, base 2); the w . v tile and exp(Gm_C), two buffers each;
-    // three slots of partial L and M blocks (one f32x4 per lane and matrix)
+    // fp32 arrays: Gm (cumulative log decay, base 2); the w . v tile and exp(Gm_C), two
+    // buffers each; three slots of partial L and M blocks (one f32x4 per lane and matrix)
     static constexpr int fG = 0, fW = fG + CH * PF, fE = fW + 2 * CH * PW, fP = fE + 2 * DK;
     static constexpr int nF = fP + 3 * 2 * 64 * 4;
     static constexpr int bytes = ((nR * P::kBytes + 15) / 16) * 16 + nF * 4;
@@ -188,8 +188,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void qed_chunk_kernel(const QedCh
     constexpr int PK = Lay::PK, PC = Lay::PC, PV = Lay::PV, PF = Lay::PF, PW = Lay::PW;
     constexpr int EPV = 16 / P::kBytes;
     constexpr int VPRV = kDVT / EPV;
-    // staging threads per chunk row (each takes at least one 16-byte vector of q and k) and
-    // key columns per staging thread; threads beyond CH * TPR stage nothing
+    // staging threads per chunk row and key columns per staging thread (at least one 16-byte
+    // run of q and k: 8 columns in bf16, 4 in fp32); threads beyond CH * TPR stage nothing
     constexpr int VMIN = EPV > 4 ? EPV : 4;
     constexpr int NT = kChunkThreads;
     constexpr int TPR = (NT / CH < DK / VMIN) ? NT / CH : DK / VMIN;
