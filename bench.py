@@ -37,7 +37,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+# Untimed calls before each secondary workload's timed region: about 40-60 ms of its own
+# kernels, enough to reach sustained clocks from idle whatever W the caller passes (W is the
+# headline's warm-up; the secondary workloads are reported beside it, not instead of it).
+VARIANT_WARM_CALLS = {"chunk": 300, "backward": 50, "qed": 100, "eda": 150}
 CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd_pipe.hip",
+                        "recurrent_sequence_layers_amd/csrc/qd_chunk_common.h",
                         "recurrent_sequence_layers_amd/csrc/qd_device.h",
                         "recurrent_sequence_layers_amd/csrc/qd_internal.h"]
 STEP_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_step.hip",
@@ -285,7 +290,7 @@ def main():
         grads = qd.qdelta_chunk_bwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, dO, None, C=C, workspace=ws)
         bf = lambda: qd.qdelta_chunk_bwd(x.q, x.k, x.v, x.alpha, x.beta, x.lam, None, dO, None, C=C,
                                          workspace=ws, out=grads)
-        for _ in range(args.warmup):
+        for _ in range(VARIANT_WARM_CALLS["backward"]):
             bf()
         torch.cuda.synchronize()
         b_s, _ = time_region(torch, bf, steps)
@@ -307,7 +312,7 @@ def main():
         qo = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
         qS = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         qf = lambda: qd.qdelta_qed_chunk_fwd(qx.q, qx.k, qx.v, qx.g, qx.b, qx.w, qx.lam_h, None, C=32, o=qo, S_T=qS)
-        for _ in range(args.warmup):
+        for _ in range(VARIANT_WARM_CALLS["qed"]):
             qf()
         torch.cuda.synchronize()
         q_s, _ = time_region(torch, qf, steps)
@@ -348,7 +353,7 @@ def main():
         nws = qd.qdelta_eda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, C, torch.bfloat16)
         ews = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         ef = lambda: qd.qdelta_eda_chunk_fwd(eq, ek, ev, ee, None, C=C, o=eo, S_T=eS, workspace=ews)
-        for _ in range(args.warmup):
+        for _ in range(VARIANT_WARM_CALLS["eda"]):
             ef()
         torch.cuda.synchronize()
         e_s, _ = time_region(torch, ef, steps)
@@ -499,7 +504,7 @@ def main():
         variants["tiny_fp32"]["us_per_call"] = variants["tiny_fp32"]["ms_per_call"] * 1e3
         variants["tiny_fp32"]["bound"] = "launch latency (one workgroup, four chunks)"
         for vname in ("gdn_bf16", "deltanet_bf16"):
-            variants[vname] = chunk_variant(vname, args.steps, min(args.warmup, 50))
+            variants[vname] = chunk_variant(vname, args.steps, VARIANT_WARM_CALLS["chunk"])
     # the decode runs stream the whole HBM for tens of milliseconds; chunk-kernel work follows
     # them before the headline, so its clocks are those of the chunk kernels' own load
     decode = decode_run(256, args.decode_steps, args.seed + 1)
@@ -508,7 +513,7 @@ def main():
         variants["decode_1024x16_beyond_infinity_cache"] = decode_run(1024, 200, args.seed + 11)
         practical = hbm_practical()
         variants["long_64k_bf16"] = chunk_variant("long_64k_bf16", 10, 3)
-        variants["layer_1p3b_backward"] = backward_run(x, max(5, args.steps // 5))
+        variants["layer_1p3b_backward"] = backward_run(x, max(10, args.steps // 2))
         variants["qed_gdn2"] = qed_run(args.steps, 200)
         variants["erase_then_delta"] = eda_run(args.steps, 200)
         variants["layer_1p3b_raw_prologue"] = raw_run(x, max(args.steps, 200))
