@@ -40,7 +40,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 # Untimed calls before each secondary workload's timed region: about 40-60 ms of its own
 # kernels, enough to reach sustained clocks from idle whatever W the caller passes (W is the
 # headline's warm-up; the secondary workloads are reported beside it, not instead of it).
-VARIANT_WARM_CALLS = {"chunk": 300, "backward": 50, "qed": 100, "eda": 150}
+VARIANT_WARM_CALLS = {"chunk": 300, "long": 30, "backward": 50, "qed": 100, "eda": 150}
 CHUNK_KERNEL_SOURCES = ["recurrent_sequence_layers_amd/csrc/qd_chunk_fwd_pipe.hip",
                         "recurrent_sequence_layers_amd/csrc/qd_chunk_common.h",
                         "recurrent_sequence_layers_amd/csrc/qd_device.h",
@@ -480,7 +480,7 @@ def main():
                           "decode_1024x16": decode_run(1024, 200, args.seed + 11)}), flush=True)
         return
     if args.long_only:
-        print(json.dumps({"long_64k_bf16": chunk_variant("long_64k_bf16", args.steps, max(1, min(args.warmup, 20)))}),
+        print(json.dumps({"long_64k_bf16": chunk_variant("long_64k_bf16", args.steps, VARIANT_WARM_CALLS["long"])}),
               flush=True)
         return
 
@@ -512,7 +512,7 @@ def main():
     if not args.headline_only:
         variants["decode_1024x16_beyond_infinity_cache"] = decode_run(1024, 200, args.seed + 11)
         practical = hbm_practical()
-        variants["long_64k_bf16"] = chunk_variant("long_64k_bf16", 10, 3)
+        variants["long_64k_bf16"] = chunk_variant("long_64k_bf16", 10, VARIANT_WARM_CALLS["long"])
         variants["layer_1p3b_backward"] = backward_run(x, max(10, args.steps // 2))
         variants["qed_gdn2"] = qed_run(args.steps, 200)
         variants["erase_then_delta"] = eda_run(args.steps, 200)
