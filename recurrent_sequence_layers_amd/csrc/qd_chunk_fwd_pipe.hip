@@ -210,8 +210,10 @@ constexpr int tile_mask(const int (&t)[4], int n) {
 
 // RAW: q and k arrive unnormalised and alpha, beta, lambda as logits; both are mapped
 // while the chunk is staged into LDS, so everything downstream is the same as without.
-// STATES: no output (nothing of O is formed); keep every chunk's entry state S (bf16,
-// [B][H][NC][d_v][d_k], ChunkArgs::Hs, when not null) for the backward.
+// STATES: no output (neither A nor O is formed); keep every chunk's entry state S (bf16,
+// [B][H][NC][d_v][d_k], ChunkArgs::Hs, when not null) for the backward.  The entry state of
+// chunk n + 1 is stored in I3 and I4 of step n, as its key halves become final; with no O to
+// form, the scan's I1 also takes the first quarter of the state update from I2.
 // EDA: Erase-then-Delta, DeltaNet (beta = 1) over the interleaved sequence e_1, k_1, e_2,
 // k_2, ... read in place: chunk row 2i is an erase token (key e_i, query and value 0) and
 // row 2i + 1 the write token (k_i, q_i, v_i) of token i of the chunk's C / 2; outputs are
@@ -289,7 +291,7 @@ struct PipeKernel {
                     av[e] = (cc <= r) ? f * gq[b][e] : 0.f;
                     lv[e] = (cc < r) ? (f * br) * xk : 0.f;
                 }
-                sts4(As + cc_off<CH>(r, c0), av);
+                if constexpr (!STATES) sts4(As + cc_off<CH>(r, c0), av);   // A serves the output only
                 if (i == j) {
                     tdiag = invert_unit_lower16<Bf16>(lv, g4, r16);
                     sts4(Td + (16 * i + r16) * PC + 16 * i + 4 * g4, tdiag);   // T_g[16i + 4g + e][16i + n]
@@ -625,16 +627,23 @@ struct PipeKernel {
                     }
                 };
 
+                // STATES: the entry state of chunk c (the exit state of chunk n), rounded to bf16,
+                // key pairs [u_lo, u_hi): tiles 2u and 2u + 1 hold the eight consecutive keys
+                // 8 kq(g, u) .. + 7 of the lane's state row, one 16-byte store, so each store
+                // instruction writes 64 contiguous bytes of each of 16 rows
+                auto store_entry = [&](int u_lo, int u_hi) {
+                    uint16_t *hs = static_cast<uint16_t *>(args.Hs) +
+                                   ((static_cast<size_t>(bh) * NC + c) * dv + dv0 + 16 * rw + r16) * DK;
+    #pragma unroll
+                    for (int u = 0; u < NKP; ++u) {
+                        if (u < u_lo || u >= u_hi) continue;
+                        *reinterpret_cast<bf16x8 *>(hs + 8 * kq(g4, u)) = cat8(Bf16::cvt(sT[2 * u]), Bf16::cvt(sT[2 * u + 1]));
+                    }
+                };
+
                 // ======================================================== I1
                 if (n + 2 < NC) gload_qv(n + 2, pfqv);   // slot n & 1: its Q is no longer read
                 if (n >= 0) {
-                    if (STATES && args.Hs) {   // chunk n's entry state, rounded to bf16
-                        uint16_t *hs = static_cast<uint16_t *>(args.Hs) +
-                                       ((static_cast<size_t>(bh) * NC + n) * dv + dv0 + 16 * rw + r16) * DK;
-#pragma unroll
-                        for (int t = 0; t < NKT; ++t)
-                            *reinterpret_cast<bf16x4 *>(hs + 8 * kq(g4, t >> 1) + 4 * (t & 1)) = Bf16::cvt(sT[t]);
-                    }
                     const uint16_t *Vs = Vb(ss), *As = Ab(ss);
                     const float *lam_s = gate(ss, 4), *eg = gate(ss, 1), *egl = gate(ss, 2);
                     // operands of Z: V as the paired B operand (positions 32u + 4g + i and
@@ -696,6 +705,10 @@ struct PipeKernel {
                             for (int e = 0; e < 4; ++e)
                                 Os[(16 * mt + 4 * g4 + e) * PV + 16 * rw + r16] = Bf16::from_f32(o[e]);
                         }
+                    } else {
+                        // without the output, I1 is short on the scan side: the first quarter
+                        // of the state update moves here from I2
+                        state_update(0, NKT / 4);
                     }
                 }
                 __syncthreads();
@@ -703,7 +716,7 @@ struct PipeKernel {
                 // ======================================================== I2
                 if (n + 2 < NC) rstore_qv(n + 2, pfqv);  // V of chunk n was read in I1
                 if (n + 2 < NC) gload_k(n + 2, pfk);
-                if (n >= 0) state_update(0, NKT / 2);
+                if (n >= 0) state_update(STATES ? NKT / 4 : 0, NKT / 2);
                 if (c < NC) {
 #pragma unroll
                     for (int mt = 0; mt < NCT; ++mt) PK_[mt] = PQ[mt] = zero4();
@@ -712,12 +725,16 @@ struct PipeKernel {
                 __syncthreads();
 
                 // ======================================================== I3
+                // (the key tiles of the first half became final in I2; the stores of the entry
+                // state go to I3 and I4, where the scan has less to do than the prep)
+                if (STATES && args.Hs && c < NC) store_entry(0, NKP / 2);
                 if (n >= 0) state_update(NKT / 2, NKT);
                 if (c < NC) lookahead(NKP / 2, NKP);
                 __syncthreads();
 
                 // ======================================================== I4
                 if (n + 2 < NC) rstore_k(n + 2, pfk);    // K and gates of chunk n were read up to I3
+                if (STATES && args.Hs && c < NC) store_entry(NKP / 2, NKP);
                 if (!STATES && n >= 0) {
                     const auto rso = buffer_rsrc(obase + (has_o ? static_cast<size_t>(n) * TPC * H * dv : 0),
                                                  has_o ? (chunk_tok(n) - 1) * rowV + kDVT * 2 : 0);
