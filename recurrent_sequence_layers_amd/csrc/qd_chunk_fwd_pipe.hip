@@ -51,7 +51,8 @@
 //                           tiles (positions 4g..4g+3 and 16+4g..16+4g+3);
 //   L_g        [C][C + 8]   off-diagonal blocks (diagonal blocks stay in registers);
 //   T_g        [C][C + 8]   stored transposed (row c holds column c of T_g);
-//   O staging  [C][72];  gates [2][5][C] fp32.
+//   O staging  [C][72];  gates [2][5][C] fp32 ([2][7][C] in the raw instances, which add
+//                           1/|q| and 1/|k| of each position).
 //
 // Global traffic uses buffer instructions whose resource is re-based at every chunk:
 // the range check returns zeros for rows past the end of the sequence and drops
@@ -99,36 +100,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-// Layer prologue of the raw entry point (the layer of the Q-Delta reading notes §1 and
-// §3.1 normalises q and k and maps the gate logits): row segment of a staging lane,
-// 8 bf16 of one q or k row, L2-normalised over the row, q / sqrt(|q|^2 + 1e-6).  The
-// row's 16 segments sit in the lanes that differ in lane-id bits 0-1 and in the bits of
-// the fragment step: bit 4 for d_k = 64, bits 4-5 for d_k = 128.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-template <int NKP>
-__device__ __forceinline__ u32x4 normalise_row_segment(u32x4 v) {
-    f32x4 lo, hi;                                          // elements 2i and 2i + 1
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo[i] = __builtin_bit_cast(float, v[i] << 16);
-        hi[i] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
-    ss += dpp_f32<0xb1>(ss);                               // lane ^ 1
-    ss += dpp_f32<0x4e>(ss);                               // lane ^ 2
-    if constexpr (NKP >= 2) ss += __shfl_xor(ss, 16);
-    if constexpr (NKP >= 4) ss += __shfl_xor(ss, 32);
-    const float r = __frsqrt_rn(ss + 1e-6f);
-    const bf16x4 a = Bf16::cvt(f32x4{lo[0], hi[0], lo[1], hi[1]} * r);
-    const bf16x4 b = Bf16::cvt(f32x4{lo[2], hi[2], lo[3], hi[3]} * r);
-    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
-    return u32x4{ua.x, ua.y, ub.x, ub.y};
-}
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
 // log(alpha) = -softplus(a) = -(max(a, 0) + log(1 + exp(-|a|)))
 __device__ __forceinline__ float log_decay_from_logit(float a) {
@@ -154,7 +125,7 @@ __device__ __forceinline__ int cc_off(int row, int col) {
     return ((row >> 4) * (CH / 32) + (col >> 5)) * 512 + 8 * frag_slot((c >> 2) & 3, row & 15) + 4 * (c >> 4) + (c & 3);
 }
 
-template <int DK, int CH>
+template <int DK, int CH, int NGATE = 5>
 struct PipeLayout {
     static constexpr int NCT = CH / 16;
     static constexpr int PC = CH + 8;             // chunk x chunk rows, 16 bytes of padding
@@ -174,7 +145,8 @@ struct PipeLayout {
     static constexpr int oO = oTd + NLT;
     static constexpr int nR = oO + NV;
     // byte offset of the fp32 gates
-    static constexpr int kGates = 5;              // g, exp(g), exp(g_last - g), beta, lambda
+    // g, exp(g), exp(g_last - g), beta, lambda; raw instances add 1/|q| and 1/|k|
+    static constexpr int kGates = NGATE;
     static constexpr int oGate = nR * 2;
     static constexpr int bytes = oGate + 2 * kGates * CH * 4;
     static_assert((PC * 2) % 16 == 0 && (PV * 2) % 16 == 0 && oGate % 16 == 0,
@@ -202,14 +174,27 @@ template <> struct GramPlan<4, 1, 3> { static constexpr int n = 1; static conste
 template <> struct GramPlan<2, 0, 1> { static constexpr int n = 2; static constexpr int i[4] = {0, 1, 0, 0}, j[4] = {0, 0, 0, 0}; };
 template <> struct GramPlan<2, 1, 1> { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {1, 0, 0, 0}; };
 
+// The raw instances at C = 32: every off-diagonal block after I1, when the row-norm tables
+// that the diagonal blocks write in I1 are there: (1, 0) on wave 6 in I2, beside nothing.
+template <int NCT, int P, int PH, bool RAW>
+struct GramPlanOf { using type = GramPlan<NCT, P, PH>; };
+struct GramPlanDiag0 { static constexpr int n = 1; static constexpr int i[4] = {0, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+struct GramPlan10 { static constexpr int n = 1; static constexpr int i[4] = {1, 0, 0, 0}, j[4] = {0, 0, 0, 0}; };
+template <> struct GramPlanOf<2, 0, 1, true> { using type = GramPlanDiag0; };
+template <> struct GramPlanOf<2, 2, 2, true> { using type = GramPlan10; };
+
 constexpr int tile_mask(const int (&t)[4], int n) {
     int m = 0;
     for (int b = 0; b < n; ++b) m |= 1 << t[b];
     return m;
 }
 
-// RAW: q and k arrive unnormalised and alpha, beta, lambda as logits; both are mapped
-// while the chunk is staged into LDS, so everything downstream is the same as without.
+// RAW: q and k arrive unnormalised and alpha, beta, lambda as logits.  The gates are mapped
+// while the chunk is staged into LDS.  q and k are staged as they are: q^ = D_q^-1 q and
+// k^ = D_k^-1 k (D = diag(sqrt(|x_t|^2 + 1e-6))) enter every product through per-position
+// factors instead, K^ K^T = D_k^-1 K K^T D_k^-1 and so on, applied to the fp32 products.
+// |k_t|^2 is the diagonal of the diagonal Gram blocks, |q_t|^2 that of one more product
+// Q_i Q_i^T; the diagonal blocks' waves write 1/|q| and 1/|k| to two tables in I1.
 // STATES: no output (neither A nor O is formed); keep every chunk's entry state S (bf16,
 // [B][H][NC][d_v][d_k], ChunkArgs::Hs, when not null) for the backward.  The entry state of
 // chunk n + 1 is stored in I3 and I4 of step n, as its key halves become final; with no O to
@@ -223,7 +208,7 @@ constexpr int tile_mask(const int (&t)[4], int n) {
 template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW, bool STATES = false, bool EDA = false>
 struct PipeKernel {
     static_assert(!EDA || (!HAS_A && !HAS_L && !RAW && !STATES), "Erase-then-Delta is the plain beta = 1 delta rule");
-    using Lay = PipeLayout<DK, CH>;
+    using Lay = PipeLayout<DK, CH, RAW ? 7 : 5>;
     static constexpr int NKT = DK / 16, NKP = DK / 32;
     static constexpr int NCT = CH / 16, NCP = CH / 32;
     static constexpr int PC = Lay::PC, PV = Lay::PV;
@@ -238,16 +223,23 @@ struct PipeKernel {
     // Gram blocks of prep wave P for the chunk in slot ps, then the A and L_g epilogue.
     // Block (i, j): D = K_j [Q_i | K_i]^T, so lane (g, n) holds q_r.k_c and k_r.k_c for
     // r = 16i + n, c = 16j + 4g + e.
+    // RAW: nqs, nks are the chunk's 1/|q| and 1/|k| tables, written here by the diagonal
+    // blocks (I1) and read by the blocks below the diagonal (I2, I3).
     template <int P, int PH>
     __device__ __forceinline__ static void gram(const uint16_t *Qs, const uint16_t *Ks, uint16_t *As, uint16_t *Lg,
                                                 uint16_t *Td, const float *gs, const float *bes, const float *lams,
-                                                int r16, int g4, f32x4 &tdiag) {
-        using Plan = GramPlan<NCT, P, PH>;
+                                                float *nqs, float *nks, int r16, int g4, f32x4 &tdiag) {
+        using Plan = typename GramPlanOf<NCT, P, PH, RAW>::type;
         constexpr int NB = Plan::n;
         if constexpr (NB > 0) {
             f32x4 gq[NB], gk[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) { gq[b] = zero4(); gk[b] = zero4(); }
+            f32x4 gqq[RAW ? NB : 1];
+            if constexpr (RAW) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) gqq[b] = zero4();
+            }
             // 16-row tiles of K and Q this wave reads (each loaded once per key pair); the
             // tiles of the next key pair are issued before the MFMAs of the current one
             constexpr int kmask = tile_mask(Plan::i, NB) | tile_mask(Plan::j, NB);
@@ -271,6 +263,9 @@ struct PipeKernel {
                     const bf16x8 a = kt[u & 1][Plan::j[b]];
                     gq[b] = mfma32(a, qt[u & 1][Plan::i[b]], gq[b]);
                     gk[b] = mfma32(a, kt[u & 1][Plan::i[b]], gk[b]);
+                    // RAW, diagonal block: Q_i Q_i^T for the squared norms of the block's queries
+                    if constexpr (RAW)
+                        if (Plan::i[b] == Plan::j[b]) gqq[b] = mfma32(qt[u & 1][Plan::i[b]], qt[u & 1][Plan::i[b]], gqq[b]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -283,13 +278,45 @@ struct PipeKernel {
                 const float lr = HAS_L ? lams[r] : 0.f;
                 const f32x4 gc = lds_f32x4(gs + c0);
                 f32x4 av, lv;
+                if constexpr (RAW) {
+                    if (i == j) {
+                        // the diagonal of the block's K K^T and Q Q^T: lane (n / 4, n), element n % 4
+                        if ((r16 >> 2) == g4) {
+                            const int e = r16 & 3;
+                            const float k2 = e == 0 ? gk[b][0] : e == 1 ? gk[b][1] : e == 2 ? gk[b][2] : gk[b][3];
+                            const float q2 = e == 0 ? gqq[b][0] : e == 1 ? gqq[b][1] : e == 2 ? gqq[b][2] : gqq[b][3];
+                            nks[r] = __frsqrt_rn(k2 + 1e-6f);
+                            nqs[r] = __frsqrt_rn(q2 + 1e-6f);
+                        }
+                        // the other lanes of the wave read these entries: make the writes
+                        // visible across the wave (without this the compiler may hand each
+                        // lane its own unwritten value instead of reading the table)
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                        __builtin_amdgcn_wave_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    }
+                    // written by this wave just above (diagonal block) or by another in I1
+                    const float rk = nks[r], rq = nqs[r];
+                    const f32x4 rkc = lds_f32x4(nks + c0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int cc = c0 + e;
-                    const float f = HAS_A ? __expf(gr - gc[e]) : 1.f;
-                    const float xk = HAS_L ? gk[b][e] + lr * gq[b][e] : gk[b][e];
-                    av[e] = (cc <= r) ? f * gq[b][e] : 0.f;
-                    lv[e] = (cc < r) ? (f * br) * xk : 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        const int cc = c0 + e;
+                        const float f = HAS_A ? __expf(gr - gc[e]) : 1.f;
+                        const float qk = gq[b][e] * (rq * rkc[e]);
+                        const float kk = gk[b][e] * (rk * rkc[e]);
+                        const float xk = HAS_L ? kk + lr * qk : kk;
+                        av[e] = (cc <= r) ? f * qk : 0.f;
+                        lv[e] = (cc < r) ? (f * br) * xk : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int cc = c0 + e;
+                        const float f = HAS_A ? __expf(gr - gc[e]) : 1.f;
+                        const float xk = HAS_L ? gk[b][e] + lr * gq[b][e] : gk[b][e];
+                        av[e] = (cc <= r) ? f * gq[b][e] : 0.f;
+                        lv[e] = (cc < r) ? (f * br) * xk : 0.f;
+                    }
                 }
                 if constexpr (!STATES) sts4(As + cc_off<CH>(r, c0), av);   // A serves the output only
                 if (i == j) {
@@ -479,11 +506,7 @@ struct PipeKernel {
             uint16_t *Qs = Qb(s), *Vs = Vb(s);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
-                if constexpr (RAW) {
-                    *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = normalise_row_segment<NKP>(pf.q[j]);
-                } else {
-                    if (!erase_rows) *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
-                }
+                if (!erase_rows) *reinterpret_cast<u32x4 *>(Qs + ldsQ[j]) = pf.q[j];
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *reinterpret_cast<u32x4 *>(Vs + ldsV + j * RJV * PV) = pf.v[j];
@@ -493,11 +516,7 @@ struct PipeKernel {
             uint16_t *Ks = Kb(s);
 #pragma unroll
             for (int j = 0; j < NVQ; ++j) {
-                if constexpr (RAW) {
-                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = normalise_row_segment<NKP>(pf.k[j]);
-                } else {
-                    *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
-                }
+                *reinterpret_cast<u32x4 *>(Ks + ldsQ[j]) = pf.k[j];
             }
             // gates of the chunk, lane = position; every scan wave holds them and writes part
             // of the tables (wave 0: g and beta, 1: exp(g), 2: exp(g_last - g), 3: lambda)
@@ -646,6 +665,9 @@ struct PipeKernel {
                 if (n >= 0) {
                     const uint16_t *Vs = Vb(ss), *As = Ab(ss);
                     const float *lam_s = gate(ss, 4), *eg = gate(ss, 1), *egl = gate(ss, 2);
+                    // RAW: 1/|q| and 1/|k| of the chunk's positions (the look-ahead products
+                    // were formed from the raw q and k)
+                    const float *nq = RAW ? gate(ss, 5) : nullptr, *nk = RAW ? gate(ss, 6) : nullptr;
                     // operands of Z: V as the paired B operand (positions 32u + 4g + i and
                     // 32u + 16 + 4g + i) and the M1 fragments
                     bf16x8 Vf[NCP], m1f[NCT][NCP];
@@ -672,7 +694,11 @@ struct PipeKernel {
 #pragma unroll
                     for (int mt = 0; mt < NCT; ++mt) {
                         f32x4 y = PK_[mt];
-                        if constexpr (HAS_L) y += lds_f32x4(lam_s + 16 * mt + 4 * g4) * PQ[mt];
+                        if constexpr (RAW) y *= lds_f32x4(nk + 16 * mt + 4 * g4);
+                        if constexpr (HAS_L && RAW)
+                            y += (lds_f32x4(lam_s + 16 * mt + 4 * g4) * lds_f32x4(nq + 16 * mt + 4 * g4)) * PQ[mt];
+                        else if constexpr (HAS_L)
+                            y += lds_f32x4(lam_s + 16 * mt + 4 * g4) * PQ[mt];
                         if constexpr (HAS_A) y *= lds_f32x4(eg + 16 * mt + 4 * g4);
                         Yg[mt] = Bf16::cvt(-y);
                     }
@@ -692,13 +718,19 @@ struct PipeKernel {
 #pragma unroll
                     for (int mt = 0; mt < NCT; ++mt) {
                         Zf[mt] = Bf16::cvt(Z[mt]);
-                        Zd[mt] = HAS_A ? Bf16::cvt(lds_f32x4(egl + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
+                        if constexpr (RAW) {
+                            const f32x4 d = lds_f32x4(nk + 16 * mt + 4 * g4);
+                            Zd[mt] = Bf16::cvt((HAS_A ? lds_f32x4(egl + 16 * mt + 4 * g4) * d : d) * Z[mt]);
+                        } else {
+                            Zd[mt] = HAS_A ? Bf16::cvt(lds_f32x4(egl + 16 * mt + 4 * g4) * Z[mt]) : Zf[mt];
+                        }
                     }
                     // O = D_g Q S^T + A Z, staged for the row stores of I4
                     if constexpr (!STATES) {
 #pragma unroll
                         for (int mt = 0; mt < NCT; ++mt) {
                             f32x4 o = HAS_A ? lds_f32x4(eg + 16 * mt + 4 * g4) * PQ[mt] : PQ[mt];
+                            if constexpr (RAW) o *= lds_f32x4(nq + 16 * mt + 4 * g4);
 #pragma unroll
                             for (int u = 0; u <= (mt >> 1); ++u) o = mfma32(af[mt][u], cat8(Zf[2 * u], Zf[2 * u + 1]), o);
 #pragma unroll
@@ -761,11 +793,12 @@ struct PipeKernel {
                 const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
                 uint16_t *As = Ab(ps);
                 const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
+                float *const nqs = RAW ? gate(ps, 5) : nullptr, *const nks = RAW ? gate(ps, 6) : nullptr;
                 switch (rw) {
-                    case 0: gram<0, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    case 1: gram<1, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    case 2: gram<2, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                    default: gram<3, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                    case 0: gram<0, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                    case 1: gram<1, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                    case 2: gram<2, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                    default: gram<3, 1>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
                 }
                 }
                 __syncthreads();
@@ -781,11 +814,12 @@ struct PipeKernel {
                     const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
                     uint16_t *As = Ab(ps);
                     const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
+                    float *const nqs = RAW ? gate(ps, 5) : nullptr, *const nks = RAW ? gate(ps, 6) : nullptr;
                     switch (rw) {
-                        case 0: gram<0, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                        case 1: gram<1, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                        case 2: gram<2, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
-                        default: gram<3, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag); break;
+                        case 0: gram<0, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                        case 1: gram<1, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                        case 2: gram<2, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
+                        default: gram<3, 2>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag); break;
                     }
                 }
                 }
@@ -795,8 +829,9 @@ struct PipeKernel {
                     const uint16_t *Qs = Qb(ps), *Ks = Kb(ps);
                     uint16_t *As = Ab(ps);
                     const float *gs = gate(ps, 0), *bes = gate(ps, 3), *lams = gate(ps, 4);
-                    if (rw == 0) gram<0, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag);
-                    else gram<1, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, r16, g4, tdiag);
+                    float *const nqs = RAW ? gate(ps, 5) : nullptr, *const nks = RAW ? gate(ps, 6) : nullptr;
+                    if (rw == 0) gram<0, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag);
+                    else gram<1, 3>(Qs, Ks, As, Lgs, Tds, gs, bes, lams, nqs, nks, r16, g4, tdiag);
                 }
                 if (c < NC && rw >= 2 && rw - 2 < NCT / 2) {
                     // block doubling, level 1: T_g[2a+1][2a] = -T_g[2a+1][2a+1] L_g[2a+1][2a] T_g[2a][2a]
