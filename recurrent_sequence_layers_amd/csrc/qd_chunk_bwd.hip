@@ -605,15 +605,21 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
 
     // The workgroup walks chunks it, it + gridDim.x, ...  The next chunk's q, k, v, dO rows
     // and (wave 0) the lane's gates are prefetched into registers once the current chunk's
-    // global reads are done, so they overlap its last phases; this wave's S^T and dS'^T
-    // fragments (S rows 16 wave + l % 16) are loaded right after the rows are staged, and
-    // arrive during the Gram blocks and the inverse.
+    // global reads are done, so they overlap its last phases: q and k rows after the value
+    // contractions, v, dO rows and the gates halfway through the per-d_k-block phase, which
+    // has no other global traffic (issued all at once, the loads held the waves at the
+    // vector-memory path).  This wave's S^T and dS'^T fragments (S rows 16 wave + l % 16)
+    // are loaded right after the rows are staged, and arrive during the Gram blocks and
+    // the inverse.
     uint4 xq[NLQ], xk[NLQ], xv[NLV], xd[NLV];
     float xa = 1.f, xb = 0.f, xl = 0.f;
-    auto fetch = [&](int it) {
+    // part: kFetchQK (q, k rows), kFetchVD (v, dO rows and the gates), or both
+    constexpr int kFetchQK = 1, kFetchVD = 2;
+    auto fetch = [&](int it, int part) {
         const int n = it % NC, bh = it / NC, b = bh / H, h = bh % H;
         const int t0 = n * CH, clen = min(CH, T - t0);
         auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * H + h; };
+        if (part & kFetchQK)
 #pragma unroll
         for (int j = 0; j < NLQ; ++j) {
             const int vi = tid + NT * j;
@@ -624,6 +630,7 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 xk[j] = *reinterpret_cast<const uint4 *>(gk + off);
             }
         }
+        if (part & kFetchVD)
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int vi = tid + NT * j;
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
                 xd[j] = *reinterpret_cast<const uint4 *>(gdo + off);
             }
         }
-        if (wave == 0) {
+        if ((part & kFetchVD) && wave == 0) {
             const bool ok = lane < clen;
             const size_t gi = tok(t0 + min(lane, clen - 1));
             xa = (HAS_A && ok) ? args.alpha[gi] : 1.f;
@@ -643,7 +650,7 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         }
     };
 
-    if (static_cast<int>(blockIdx.x) < total) fetch(blockIdx.x);
+    if (static_cast<int>(blockIdx.x) < total) fetch(blockIdx.x, kFetchQK | kFetchVD);
     for (int it = blockIdx.x; it < total; it += gridDim.x) {
         // Lane ids and the LDS base are rebuilt from opaque copies for every chunk rather
         // than hoisted out of the loop: LDS addresses held across the loop do not fit the
@@ -920,8 +927,8 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
             }
         }
         __syncthreads();   // T_g, L, v, dO, Z, P are free from here on
-        // the next chunk's rows (this chunk's global reads are done)
-        if (it + static_cast<int>(gridDim.x) < total) fetch(it + gridDim.x);
+        // the next chunk's q and k rows (this chunk's global reads are done)
+        if (it + static_cast<int>(gridDim.x) < total) fetch(it + gridDim.x, kFetchQK);
 
         // ---- dA and dL -> Mq = G o dA + diag(lambda) dLb, dLb = diag(beta) (G o dL); each lane
         // has one row and four consecutive columns, stored with one 8-byte write per matrix
@@ -964,6 +971,8 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
         float wz = 0.f;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
+            // halfway: the next chunk's v and dO rows and gates
+            if (j == NBW / 2 && it + static_cast<int>(gridDim.x) < total) fetch(it + gridDim.x, kFetchVD);
             const int blk = wave + NW * j;
             if (NB % NW == 0 || blk < NB) {
                 const int mt = blk / NKT, kk = blk % NKT;
