@@ -363,7 +363,9 @@ struct PipeKernel {
         sts4(M1s + cc_off<CH>(16 * AB + r16, 16 * CB + 4 * g4), -acc * bc);
     }
 
-    __device__ static void run(const ChunkArgs &args) {
+    // smem: the workgroup's LDS (Lay::bytes); blk, nblk: this workgroup's index within the
+    // grid of workgroups that run this instance, and that grid's size
+    __device__ static void run(const ChunkArgs &args, unsigned char *smem, int blk, int nblk) {
         constexpr int VPRQ = DK / 8;              // 16-byte vectors per q/k row
         constexpr int VPRV = kDVT / 8;
         constexpr int NVQ = CH * VPRQ / kRoleThreads;
@@ -371,7 +373,6 @@ struct PipeKernel {
         constexpr int RJV = kRoleThreads / VPRV;
         static_assert(CH * VPRQ % kRoleThreads == 0 && CH * VPRV % kRoleThreads == 0, "whole vectors per thread");
 
-        __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::bytes];
         uint16_t *const base = reinterpret_cast<uint16_t *>(smem);
         uint16_t *const M1s = base + Lay::oM1;
         uint16_t *const Lgs = base + Lay::oLg;
@@ -393,9 +394,8 @@ struct PipeKernel {
         const int r16 = lane & 15;
         const int g4 = lane >> 4;
 
-        const int nblk = gridDim.x;
-        int logical = blockIdx.x;
-        if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+        int logical = blk;
+        if (args.n_dvt > 1 && (nblk & 7) == 0) logical = (blk & 7) * (nblk >> 3) + (blk >> 3);
         const int dvt = logical % args.n_dvt;
         const int bh = logical / args.n_dvt;
         const int b = bh / args.H;
@@ -865,17 +865,55 @@ struct PipeKernel {
 
 template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(const ChunkArgs args) {
-    PipeKernel<DK, CH, HAS_A, HAS_L, RAW>::run(args);
+    using K = PipeKernel<DK, CH, HAS_A, HAS_L, RAW>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[K::Lay::bytes];
+    K::run(args, smem, blockIdx.x, gridDim.x);
 }
 
 template <int DK, int CH, bool HAS_A, bool HAS_L>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_states_kernel(const ChunkArgs args) {
-    PipeKernel<DK, CH, HAS_A, HAS_L, false, true>::run(args);
+    using K = PipeKernel<DK, CH, HAS_A, HAS_L, false, true>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[K::Lay::bytes];
+    K::run(args, smem, blockIdx.x, gridDim.x);
 }
 
 template <int DK, int CH>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_eda_kernel(const ChunkArgs args) {
-    PipeKernel<DK, CH, false, false, false, false, true>::run(args);
+    using K = PipeKernel<DK, CH, false, false, false, false, true>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[K::Lay::bytes];
+    K::run(args, smem, blockIdx.x, gridDim.x);
+}
+
+// The segmented schedule's first launch for a single sequence: workgroups [0, n0) walk the
+// first segment with its output from the caller's entry state (a0); the rest run the
+// state-only instance over the other segments, the transition maps (am) and then the
+// exit states from zero (ag).  The first segment's workgroups have the lowest indices, so
+// they are dispatched first and its walk, the longest, starts at once; the state-only
+// walks fill the other compute units.
+template <int DK, int CH, bool HAS_A, bool HAS_L>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_overlap_kernel(const ChunkArgs a0, const ChunkArgs am,
+                                                                                  const ChunkArgs ag, int n0, int nm) {
+    using K0 = PipeKernel<DK, CH, HAS_A, HAS_L, false>;
+    using KS = PipeKernel<DK, CH, HAS_A, HAS_L, false, true>;
+    static_assert(static_cast<int>(K0::Lay::bytes) == static_cast<int>(KS::Lay::bytes), "one LDS layout for both instances");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[K0::Lay::bytes];
+    const int bid = blockIdx.x;
+    if (bid < n0) K0::run(a0, smem, bid, n0);
+    else if (bid < n0 + nm) KS::run(am, smem, bid - n0, nm);
+    else KS::run(ag, smem, bid - n0 - nm, static_cast<int>(gridDim.x) - n0 - nm);
+}
+
+template <int DK, int CH>
+hipError_t launch_pipe_overlap(const ChunkArgs &a0, const ChunkArgs &am, const ChunkArgs &ag, hipStream_t stream) {
+    const int n0 = a0.B * a0.H * a0.n_dvt, nm = am.B * am.H * am.n_dvt, ng = ag.B * ag.H * ag.n_dvt;
+    if (n0 + nm + ng == 0) return hipSuccess;
+    const bool ha = a0.alpha != nullptr, hl = a0.lam != nullptr;
+    const dim3 grid(n0 + nm + ng), blk(kPipeThreads);
+    if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    else hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    return hipGetLastError();
 }
 
 template <int DK, int CH>
@@ -924,6 +962,12 @@ hipError_t launch_pipe_typed(const ChunkArgs &a, hipStream_t stream) {
 hipError_t launch_chunk_fwd_pipe_eda(int dk, int C, const ChunkArgs &a, hipStream_t stream) {
     if (dk == 128) return C == 64 ? launch_pipe_eda<128, 64>(a, stream) : launch_pipe_eda<128, 32>(a, stream);
     return C == 64 ? launch_pipe_eda<64, 64>(a, stream) : launch_pipe_eda<64, 32>(a, stream);
+}
+
+hipError_t launch_chunk_fwd_pipe_overlap(int dk, int C, const ChunkArgs &a0, const ChunkArgs &am, const ChunkArgs &ag,
+                                        hipStream_t stream) {
+    if (dk == 128) return C == 64 ? launch_pipe_overlap<128, 64>(a0, am, ag, stream) : launch_pipe_overlap<128, 32>(a0, am, ag, stream);
+    return C == 64 ? launch_pipe_overlap<64, 64>(a0, am, ag, stream) : launch_pipe_overlap<64, 32>(a0, am, ag, stream);
 }
 
 hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream) {

@@ -103,6 +103,10 @@ hipError_t launch_step(int dtype, int dk, int dv, const StepArgs &a, hipStream_t
 // the _states variant also writes ChunkArgs::Hs.
 hipError_t launch_chunk_fwd_pipe(int dk, int C, const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd_pipe_states(int dk, int C, const ChunkArgs &a, hipStream_t stream);
+// One launch of both instances (prepared inputs): a0 walked with its output, am and ag with
+// the state-only instance (the segmented schedule's first step for a single sequence).
+hipError_t launch_chunk_fwd_pipe_overlap(int dk, int C, const ChunkArgs &a0, const ChunkArgs &am, const ChunkArgs &ag,
+                                        hipStream_t stream);
 // Erase-then-Delta over the interleaved sequence read in place (ChunkArgs::e; T real tokens;
 // beta, alpha, lam unused), bf16 C = 32, 64.
 hipError_t launch_chunk_fwd_pipe_eda(int dk, int C, const ChunkArgs &a, hipStream_t stream);

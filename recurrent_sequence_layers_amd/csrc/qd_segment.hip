@@ -16,6 +16,12 @@
 //
 // Each pass has P times the parallelism of the single-pass schedule, for three passes
 // of work.  It pays when the single pass leaves most compute units idle.
+//
+// For a single sequence (B = 1) with prepared inputs, the first segment's entry state is
+// the caller's S0, so that segment needs neither map: it is walked once, with its output,
+// in the same launch as steps 1 and 2 over the other P - 1 segments, on compute units of
+// its own.  Its exit state starts step 3, and step 4 covers the other segments.  It is
+// made longer than the others so that its walk ends with their two state-only walks.
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -122,8 +128,74 @@ size_t chunk_fwd_segment_workspace(int B, int T, int H, int dk, int dv, int P) {
     return nseg * (static_cast<size_t>(dk) * dk + 2 * static_cast<size_t>(dv) * dk) * sizeof(float);
 }
 
+// The single-sequence schedule: the first segment (L0 chunks) walked with its output beside
+// the maps of the other P - 1 segments (L chunks each), then the propagation from its exit
+// state and the other segments' outputs.  Workspace: Mseg, Gseg and Sin of the P - 1
+// segments and the first segment's exit state, within chunk_fwd_segment_workspace(P).
+static hipError_t launch_segmented_overlapped(int dk, int C, const ChunkArgs &a, int P, void *ws,
+                                              hipStream_t stream) {
+    const int H = a.H, dv = a.dv, Q = P - 1;
+    const int NC = a.T / C;
+    const int u0 = H * a.n_dvt;                         // workgroups of one output walk over a segment
+    const int um = H * (dk / 64);                       // ... of one transition-map walk
+    const int cus = device_cu_count();
+    const int spare = cus - u0 > 0 ? cus - u0 : 1;
+    // rounds of the state-only walks on the units the first segment leaves free; a chunk
+    // step of the state-only instance takes about 7/8 of an output step
+    const int rounds = (Q * (um + u0) + spare - 1) / spare;
+    int L = static_cast<int>(NC / (Q + 0.875 * rounds) + 0.5);
+    if (L > (NC - 1) / Q) L = (NC - 1) / Q;
+    if (L < 1) L = 1;
+    const int L0 = NC - Q * L;
+    const size_t nseg = static_cast<size_t>(Q) * H;
+    float *const Mseg = static_cast<float *>(ws);                       // [Q][H][d_k][d_k]
+    float *const Gseg = Mseg + nseg * dk * dk;                          // [Q][H][d_v][d_k]
+    float *const Sin = Gseg + nseg * dv * dk;                           // [Q][H][d_v][d_k]
+    float *const S1 = Sin + nseg * dv * dk;                             // [H][d_v][d_k]
+    const size_t nM = nseg * dk * dk;
+    hipLaunchKernelGGL(identity_fill_kernel, dim3(static_cast<unsigned>((nM + 255) / 256)), dim3(256), 0, stream,
+                       Mseg, dk, nM);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    // the first segment: its own entry state, its output, its exit state into S1
+    ChunkArgs a0 = a;
+    a0.T = L0 * C;
+    a0.S_T = S1;
+    // the other segments as Q batch entries of L C tokens, from token L0 C on
+    const size_t tok = static_cast<size_t>(L0) * C * H;
+    ChunkArgs seg = a;
+    seg.B = Q;
+    seg.T = L * C;
+    seg.q = static_cast<const uint16_t *>(a.q) + tok * dk;
+    seg.k = static_cast<const uint16_t *>(a.k) + tok * dk;
+    seg.v = static_cast<const uint16_t *>(a.v) + tok * dv;
+    seg.alpha = a.alpha ? a.alpha + tok : nullptr;
+    seg.beta = a.beta + tok;
+    seg.lam = a.lam ? a.lam + tok : nullptr;
+    seg.o = a.o ? static_cast<uint16_t *>(a.o) + tok * dv : nullptr;
+    ChunkArgs m = seg;                                  // 1. maps: v = 0, S0 = I, no output
+    m.v = nullptr; m.o = nullptr; m.S0 = Mseg; m.S_T = Mseg; m.dv = dk; m.n_dvt = dk / 64;
+    ChunkArgs g = seg;                                  // 2. exit states from zero, no output
+    g.o = nullptr; g.S0 = nullptr; g.S_T = Gseg;
+    if ((err = launch_chunk_fwd_pipe_overlap(dk, C, a0, m, g, stream)) != hipSuccess) return err;
+    // 3. entry states of the other segments from the first one's exit state
+    const dim3 pg(static_cast<unsigned>(H), static_cast<unsigned>(dv / 8));
+    if (dk == 128)
+        hipLaunchKernelGGL((segment_propagate_kernel<128>), pg, dim3(256), 0, stream, S1, Mseg, Gseg, Sin, a.S_T, Q, H, dv);
+    else
+        hipLaunchKernelGGL((segment_propagate_kernel<64>), pg, dim3(256), 0, stream, S1, Mseg, Gseg, Sin, a.S_T, Q, H, dv);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // 4. the other segments' outputs
+    ChunkArgs f = seg;
+    f.S0 = Sin; f.S_T = nullptr;
+    return launch_chunk_fwd(1, dk, C, f, stream);
+}
+
 hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
                                       hipStream_t stream) {
+    if (a.B == 1 && !a.raw && dtype == 1 && a.o != nullptr && a.v != nullptr && a.T % C == 0 && a.T / C >= 2 * P)
+        return launch_segmented_overlapped(dk, C, a, P, ws, stream);
     const size_t nseg = static_cast<size_t>(a.B) * P * a.H;
     float *const Mseg = static_cast<float *>(ws);                       // [B P][H][d_k][d_k]
     float *const Gseg = Mseg + nseg * dk * dk;                          // [B P][H][d_v][d_k]
