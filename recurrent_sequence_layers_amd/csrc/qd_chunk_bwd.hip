@@ -482,7 +482,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_scan_pipe_kernel(co
         } else if (c >= 0) {
             inverse_level1<P, CH, PC>(Ls, Ts, rw, lane);
             if constexpr (NCT == 4) {                  // M1 of the diagonal blocks, final since I2
-                if (rw >= 2) m1_item(ps, rt - 128 >> 5, rt - 128 >> 5, rt & 31);
+                if (rw >= 2) m1_item(ps, (rt - 128) >> 5, (rt - 128) >> 5, rt & 31);
             }
         }
         __syncthreads();
@@ -589,7 +589,6 @@ __global__ __launch_bounds__(DV * 4, 1) void chunk_bwd_grad_kernel(const BwdArgs
     __shared__ __attribute__((aligned(16))) unsigned char smem_[Lay::bytes];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int r16 = lane & 15, g4 = lane >> 4;
     const int T = args.T, H = args.H;
     const int NC = (T + CH - 1) / CH;
     const int total = args.B * H * NC;
