@@ -340,6 +340,7 @@ SEG = [
     (1, 8192, 1, 64, 64, 32, "zero", "random", None),
     (1, 8192, 2, 128, 64, 64, "zero", "one", 0.05),
     (2, 4096, 1, 64, 128, 64, "random", "one", None),
+    (1, 8192, 1, 64, 128, 32, "random", "random", 0.05),    # maps narrower than the outputs
 ]
 
 
