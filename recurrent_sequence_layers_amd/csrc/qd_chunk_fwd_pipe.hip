@@ -62,6 +62,8 @@
 #include "qd_device.h"
 #include "qd_internal.h"
 
+#include <type_traits>
+
 namespace qd {
 namespace {
 
@@ -884,23 +886,58 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_eda_kernel(con
     K::run(args, smem, blockIdx.x, gridDim.x);
 }
 
+// c ? x : y, field by field (a reference picked among kernel arguments would make the
+// compiler copy the arguments to scratch memory)
+__device__ __forceinline__ ChunkArgs pick_args(bool c, const ChunkArgs &x, const ChunkArgs &y) {
+    ChunkArgs r;
+    r.q = c ? x.q : y.q;
+    r.k = c ? x.k : y.k;
+    r.v = c ? x.v : y.v;
+    r.alpha = c ? x.alpha : y.alpha;
+    r.beta = c ? x.beta : y.beta;
+    r.lam = c ? x.lam : y.lam;
+    r.S0 = c ? x.S0 : y.S0;
+    r.o = c ? x.o : y.o;
+    r.S_T = c ? x.S_T : y.S_T;
+    r.B = c ? x.B : y.B;
+    r.T = c ? x.T : y.T;
+    r.H = c ? x.H : y.H;
+    r.dv = c ? x.dv : y.dv;
+    r.n_dvt = c ? x.n_dvt : y.n_dvt;
+    r.raw = c ? x.raw : y.raw;
+    r.Hs = c ? x.Hs : y.Hs;
+    r.e = c ? x.e : y.e;
+    return r;
+}
+
 // The segmented schedule's first launch for a single sequence: workgroups [0, n0) walk the
 // first segment with its output from the caller's entry state (a0); the rest run the
 // state-only instance over the other segments, the transition maps (am) and then the
 // exit states from zero (ag).  The first segment's workgroups have the lowest indices, so
 // they are dispatched first and its walk, the longest, starts at once; the state-only
-// walks fill the other compute units.
-template <int DK, int CH, bool HAS_A, bool HAS_L>
+// walks fill the other compute units.  Raw inputs have no state-only instance: their
+// state-only walks run the raw instance with the output dropped.
+template <int DK, int CH, bool HAS_A, bool HAS_L, bool RAW>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_overlap_kernel(const ChunkArgs a0, const ChunkArgs am,
                                                                                   const ChunkArgs ag, int n0, int nm) {
-    using K0 = PipeKernel<DK, CH, HAS_A, HAS_L, false>;
-    using KS = PipeKernel<DK, CH, HAS_A, HAS_L, false, true>;
+    using K0 = PipeKernel<DK, CH, HAS_A, HAS_L, RAW>;
+    using KS = typename std::conditional<RAW, K0, PipeKernel<DK, CH, HAS_A, HAS_L, false, true>>::type;
     static_assert(static_cast<int>(K0::Lay::bytes) == static_cast<int>(KS::Lay::bytes), "one LDS layout for both instances");
     __shared__ __attribute__((aligned(16))) unsigned char smem[K0::Lay::bytes];
-    const int bid = blockIdx.x;
-    if (bid < n0) K0::run(a0, smem, bid, n0);
-    else if (bid < n0 + nm) KS::run(am, smem, bid - n0, nm);
-    else KS::run(ag, smem, bid - n0 - nm, static_cast<int>(gridDim.x) - n0 - nm);
+    // each instance's body appears once in the kernel, so the workgroups of the state-only
+    // walks (and, for raw inputs, all of them) run the same code: the arguments are picked
+    // by the workgroup's range instead
+    const int bid = blockIdx.x, ng = static_cast<int>(gridDim.x) - n0 - nm;
+    const bool walk_g = bid >= n0 + nm;
+    const ChunkArgs as = pick_args(walk_g, ag, am);
+    const int bs = walk_g ? bid - n0 - nm : bid - n0, ns = walk_g ? ng : nm;
+    if constexpr (RAW) {
+        const bool first = bid < n0;
+        K0::run(pick_args(first, a0, as), smem, first ? bid : bs, first ? n0 : ns);
+    } else {
+        if (bid < n0) K0::run(a0, smem, bid, n0);
+        else KS::run(as, smem, bs, ns);
+    }
 }
 
 template <int DK, int CH>
@@ -909,10 +946,17 @@ hipError_t launch_pipe_overlap(const ChunkArgs &a0, const ChunkArgs &am, const C
     if (n0 + nm + ng == 0) return hipSuccess;
     const bool ha = a0.alpha != nullptr, hl = a0.lam != nullptr;
     const dim3 grid(n0 + nm + ng), blk(kPipeThreads);
-    if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
-    else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
-    else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
-    else hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    if (a0.raw) {
+        if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, true, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, false, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, true, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, false, true>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    } else {
+        if (ha && hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, true, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else if (ha) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, true, false, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else if (hl) hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, true, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+        else hipLaunchKernelGGL((chunk_fwd_pipe_overlap_kernel<DK, CH, false, false, false>), grid, blk, 0, stream, a0, am, ag, n0, nm);
+    }
     return hipGetLastError();
 }
 

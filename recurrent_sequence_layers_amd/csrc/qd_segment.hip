@@ -17,7 +17,7 @@
 // Each pass has P times the parallelism of the single-pass schedule, for three passes
 // of work.  It pays when the single pass leaves most compute units idle.
 //
-// For a single sequence (B = 1) with prepared inputs, the first segment's entry state is
+// For a single sequence (B = 1), the first segment's entry state is
 // the caller's S0, so that segment needs neither map: it is walked once, with its output,
 // in the same launch as steps 1 and 2 over the other P - 1 segments, on compute units of
 // its own.  Its exit state starts step 3, and step 4 covers the other segments.  It is
@@ -141,9 +141,11 @@ static hipError_t launch_segmented_overlapped(int dk, int C, const ChunkArgs &a,
     const int cus = device_cu_count();
     const int spare = cus - u0 > 0 ? cus - u0 : 1;
     // rounds of the state-only walks on the units the first segment leaves free; a chunk
-    // step of the state-only instance takes about 7/8 of an output step
+    // step of the state-only instance takes about 7/8 of an output step (raw inputs walk
+    // the output instance throughout)
     const int rounds = (Q * (um + u0) + spare - 1) / spare;
-    int L = static_cast<int>(NC / (Q + 0.875 * rounds) + 0.5);
+    const double ratio = a.raw ? 1.0 : 0.875;
+    int L = static_cast<int>(NC / (Q + ratio * rounds) + 0.5);
     if (L > (NC - 1) / Q) L = (NC - 1) / Q;
     if (L < 1) L = 1;
     const int L0 = NC - Q * L;
@@ -194,7 +196,7 @@ static hipError_t launch_segmented_overlapped(int dk, int C, const ChunkArgs &a,
 
 hipError_t launch_chunk_fwd_segmented(int dtype, int dk, int C, const ChunkArgs &a, int P, void *ws,
                                       hipStream_t stream) {
-    if (a.B == 1 && !a.raw && dtype == 1 && a.o != nullptr && a.v != nullptr && a.T % C == 0 && a.T / C >= 2 * P)
+    if (a.B == 1 && dtype == 1 && a.o != nullptr && a.v != nullptr && a.T % C == 0 && a.T / C >= 2 * P)
         return launch_segmented_overlapped(dk, C, a, P, ws, stream);
     const size_t nseg = static_cast<size_t>(a.B) * P * a.H;
     float *const Mseg = static_cast<float *>(ws);                       // [B P][H][d_k][d_k]
