@@ -430,6 +430,20 @@ def test_raw_chunk_fwd(qd, B, T, H, dk, dv, C, lam, alpha):
     check_against_oracle(o.float().cpu(), S.cpu(), x, TOL["bf16"])
 
 
+def test_raw_long_full_size_whole(qd):
+    """The fused prologue over one long sequence (B1 T65536 H16: the segmented schedule with
+    the first segment overlapped, two rounds of state-only walks), every head whole."""
+    print("raw B=1 T=65536 H=16: whole-tensor compare", flush=True)
+    q, k, v, a, b, l = raw_inputs(1, 65536, 16, 128, 128, "bf16", seed=65)
+    S0 = 0.02 * torch.randn(1, 16, 128, 128, generator=torch.Generator().manual_seed(4))
+    assert qd.qdelta_chunk_fwd_workspace_bytes(1, 65536, 16, 128, 128, 64, torch.bfloat16) > 0
+    o, S = qd.qdelta_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), l.cuda(), S0.cuda(), C=64,
+                               raw=True)
+    torch.cuda.synchronize()
+    qh, kh, al, be, la = pro.prologue(q, k, a, b, l)
+    check_against_oracle(o.float().cpu(), S.cpu(), inputs.ChunkInputs(qh, kh, v, al, be, la, S0), TOL["bf16"])
+
+
 @pytest.mark.parametrize("N,H,dk,dv,dt", [(3, 2, 128, 128, "bf16"), (2, 3, 64, 128, "f32"), (2, 2, 64, 64, "bf16")])
 def test_raw_step(qd, N, H, dk, dv, dt):
     q, k, v, a, b, l = raw_inputs(1, N, H, dk, dv, dt, seed=N * H + dk)
