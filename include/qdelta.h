@@ -73,8 +73,11 @@ const char *qdelta_status_string(int status);
  * most compute units idle (bf16, C = 32 or 64): the forward then cuts the sequence
  * into P segments and composes their affine state maps (S_out = S_in M + G, from the
  * recurrence of the Q-Delta reading notes §2.4 acting on the state from the right).
- * The size is B*P*H*(d_k*d_k + 2*d_v*d_k)*4 bytes, P in {2, 4, 8, 16}.  Callers pass a
- * caller-owned, 16-byte aligned device buffer of at least this size. */
+ * The size is B*P*H*(d_k*d_k + 2*d_v*d_k)*4 bytes, P in {2, 4, 8, 16}.  For a single
+ * sequence (B = 1) the first segment, which starts from S0 itself, is walked with its
+ * output beside the other segments' maps and needs no map; that schedule uses part of
+ * the same buffer.  Callers pass a caller-owned, 16-byte aligned device buffer of at
+ * least this size. */
 size_t qdelta_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int C,
                                         int dtype);
 
